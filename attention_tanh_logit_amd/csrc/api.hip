@@ -1,0 +1,308 @@
+// C ABI of the soft-capped attention library: argument validation (fail
+// closed: a requested cap or sink is never dropped), workspace layout and the
+// launch sequence on the caller's stream.
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "attn_softcap.h"
+#include "dispatch.hpp"
+
+namespace atl {
+
+// dsink[h] = sum of its partials, in a fixed order (deterministic)
+__global__ __launch_bounds__(256) void dsink_final_kernel(const float* part, float* dsink, int nper) {
+  const int hq = blockIdx.x;
+  __shared__ float red[256];
+  float s = 0.0f;
+  for (int x = threadIdx.x; x < nper; x += 256) s += part[(long)hq * nper + x];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsink[hq] = red[0];
+}
+
+// Per-token run [start, end) of packed segment ids (non-decreasing per row):
+// lower and upper bound of the token's id in its row.
+__global__ __launch_bounds__(256) void seg_from_ids_kernel(const int* ids, int* seg_lo, int* seg_hi, int S) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= S) return;
+  const int* row = ids + (long)b * S;
+  const int id = row[t];
+  int lo = 0, hi = S;
+  while (lo < hi) {  // first index with row[x] >= id
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] < id) lo = mid + 1; else hi = mid;
+  }
+  const int start = lo;
+  lo = t;
+  hi = S;
+  while (lo < hi) {  // first index with row[x] > id
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] <= id) lo = mid + 1; else hi = mid;
+  }
+  seg_lo[(long)b * S + t] = min(start, t);
+  seg_hi[(long)b * S + t] = max(lo, t + 1);
+}
+
+// Per-token run from cumulative sequence lengths (THD layout, one row)
+__global__ __launch_bounds__(256) void seg_from_cu_kernel(const int* cu, int nseq, int* seg_lo, int* seg_hi, int T) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = nseq + 1;
+  while (lo < hi) {  // first index with cu[x] > t
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid + 1; else hi = mid;
+  }
+  const int s = max(lo - 1, 0);
+  seg_lo[t] = max(min(cu[s], t), 0);
+  seg_hi[t] = max(min(cu[min(s + 1, nseq)], T), t + 1);
+}
+
+}  // namespace atl
+
+using namespace atl;
+
+namespace {
+
+thread_local std::string g_err;
+
+attn_status fail(attn_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kPreRows = 64;      // rows per block of the backward pre-pass
+constexpr int kFillRows = 4;      // rows per block of the dbias zero fill
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool has_segments(const attn_args* a) { return a->segment_ids != nullptr || a->cu_seqlens != nullptr; }
+
+attn_status validate(const attn_args* a) {
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_FP32) return fail(ATTN_INVALID_ARGUMENT, "dtype must be ATTN_BF16 or ATTN_FP32");
+  if (a->B < 0 || a->Sq < 0 || a->Sk < 0) return fail(ATTN_INVALID_ARGUMENT, "B, Sq and Sk must be >= 0");
+  if (a->Hq < 1 || a->Hkv < 1) return fail(ATTN_INVALID_ARGUMENT, "Hq and Hkv must be >= 1");
+  if (a->Hq % a->Hkv != 0) return fail(ATTN_INVALID_ARGUMENT, "Hq must be a multiple of Hkv (GQA groups)");
+  if (a->D != 64 && a->D != 128 && a->D != 256 && a->D != 512)
+    return fail(ATTN_UNSUPPORTED, "head dim D must be 64, 128, 256 or 512");
+  if (!(a->softcap >= 0.0f) || !std::isfinite(a->softcap))
+    return fail(ATTN_INVALID_ARGUMENT, "softcap must be finite and >= 0 (0 turns the cap off)");
+  if (!(a->scale >= 0.0f) || !std::isfinite(a->scale))
+    return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and >= 0 (0 means 1/sqrt(D))");
+  if (a->sink_mode != ATTN_SINK_NONE && a->sink_mode != ATTN_SINK_OFF_BY_ONE && a->sink_mode != ATTN_SINK_LEARNABLE)
+    return fail(ATTN_INVALID_ARGUMENT, "sink_mode must be NONE, OFF_BY_ONE or LEARNABLE");
+  if (a->sink_mode == ATTN_SINK_LEARNABLE && !a->sink)
+    return fail(ATTN_INVALID_ARGUMENT, "LEARNABLE sink needs the sink logits [Hq]");
+  if (a->sink_mode != ATTN_SINK_LEARNABLE && a->sink)
+    return fail(ATTN_INVALID_ARGUMENT, "sink logits given but sink_mode is not LEARNABLE");
+  if (a->segment_ids && a->cu_seqlens) return fail(ATTN_INVALID_ARGUMENT, "give segment_ids or cu_seqlens, not both");
+  if (a->cu_seqlens) {
+    if (a->B != 1) return fail(ATTN_INVALID_ARGUMENT, "cu_seqlens (THD layout) needs B == 1");
+    if (a->nseq < 1) return fail(ATTN_INVALID_ARGUMENT, "cu_seqlens needs nseq >= 1");
+  }
+  if (has_segments(a) && a->Sq != a->Sk) return fail(ATTN_INVALID_ARGUMENT, "packed segments need Sq == Sk");
+  if (a->causal && a->Sq != a->Sk) return fail(ATTN_UNSUPPORTED, "causal masking needs Sq == Sk");
+  const long long maxi = 2147483647LL;
+  if ((long long)a->B * a->Sq > maxi || (long long)a->B * a->Sk > maxi)
+    return fail(ATTN_UNSUPPORTED, "B*S must fit in int32");
+  const size_t elems = (size_t)a->B * (a->Sq + a->Sk);
+  if (elems != 0 && (!a->q || !a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "q, k and v must not be NULL");
+  return ATTN_OK;
+}
+
+size_t seg_bytes(const attn_args* a) { return has_segments(a) ? 2 * align_up((size_t)a->B * a->Sq * sizeof(int)) : 0; }
+
+size_t pre_blocks(const attn_args* a) { return ((size_t)a->Sq + kPreRows - 1) / kPreRows; }
+
+size_t fwd_ws(const attn_args* a) { return seg_bytes(a); }
+
+size_t bwd_ws(const attn_args* a) {
+  size_t s = seg_bytes(a);
+  s += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));  // delta
+  if (a->sink_mode == ATTN_SINK_LEARNABLE) s += align_up((size_t)a->Hq * a->B * pre_blocks(a) * sizeof(float));
+  return s;
+}
+
+const TypeOps& ops(const attn_args* a) { return a->dtype == ATTN_BF16 ? ops_bf16() : ops_f32(); }
+
+hipError_t prep_segments(const attn_args* a, char*& ws, Mask& m, hipStream_t s) {
+  m.seg_lo = nullptr;
+  m.seg_hi = nullptr;
+  if (!has_segments(a)) return hipSuccess;
+  const size_t n = (size_t)a->B * a->Sq;
+  int* lo = reinterpret_cast<int*>(ws);
+  ws += align_up(n * sizeof(int));
+  int* hi = reinterpret_cast<int*>(ws);
+  ws += align_up(n * sizeof(int));
+  if (a->segment_ids) {
+    const dim3 grid((a->Sq + 255) / 256, a->B);
+    seg_from_ids_kernel<<<grid, 256, 0, s>>>(a->segment_ids, lo, hi, a->Sq);
+  } else {
+    seg_from_cu_kernel<<<(a->Sq + 255) / 256, 256, 0, s>>>(a->cu_seqlens, a->nseq, lo, hi, a->Sq);
+  }
+  m.seg_lo = lo;
+  m.seg_hi = hi;
+  return hipGetLastError();
+}
+
+Mask base_mask(const attn_args* a) {
+  Mask m;
+  m.seg_lo = m.seg_hi = nullptr;
+  m.Sq = a->Sq;
+  m.Sk = a->Sk;
+  m.causal = a->causal ? 1 : 0;
+  m.window = a->window > 0 ? a->window : 0;
+  return m;
+}
+
+void fill_consts(const attn_args* a, float& scale, float& sl2, float& xc, float& bc, float& cl2) {
+  scale = a->scale > 0.0f ? a->scale : 1.0f / std::sqrt((float)a->D);
+  sl2 = scale * kLog2e;
+  if (a->softcap > 0.0f) {
+    xc = scale / a->softcap;
+    bc = 1.0f / a->softcap;
+    cl2 = a->softcap * kLog2e;
+  } else {
+    xc = bc = cl2 = 0.0f;
+  }
+}
+
+attn_status hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_HIP_ERROR, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_validate(const attn_args* a) {
+  g_err.clear();
+  return validate(a);
+}
+
+size_t attn_fwd_workspace_size(const attn_args* a) {
+  if (validate(a) != ATTN_OK) return (size_t)-1;
+  return fwd_ws(a);
+}
+
+size_t attn_bwd_workspace_size(const attn_args* a) {
+  if (validate(a) != ATTN_OK) return (size_t)-1;
+  return bwd_ws(a);
+}
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  g_err.clear();
+  attn_status st = validate(a);
+  if (st != ATTN_OK) return st;
+  const size_t need = fwd_ws(a);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(ATTN_INVALID_ARGUMENT, "workspace smaller than attn_fwd_workspace_size");
+  if ((size_t)a->B * a->Sq * a->Hq == 0) return ATTN_OK;
+  if (!out || !lse) return fail(ATTN_INVALID_ARGUMENT, "out and lse must not be NULL");
+  if (a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  FwdParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.bias = a->bias;
+  p.out = out;
+  p.lse = lse;
+  p.mask = base_mask(a);
+  hipError_t e = prep_segments(a, ws, p.mask, s);
+  if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.G = a->Hq / a->Hkv;
+  float scale;
+  fill_consts(a, scale, p.sl2, p.xc, p.bc, p.cl2);
+  p.sink = a->sink;
+  p.sink_mode = a->sink_mode;
+  p.reverse = a->causal ? 1 : 0;
+  const Launch l{a->B, a->Sq, a->Sk, s};
+  e = ops(a).fwd(a->D, a->softcap > 0.0f, a->bias != nullptr, p, l);
+  if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
+  return ATTN_OK;
+}
+
+attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                     void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  attn_status st = validate(a);
+  if (st != ATTN_OK) return st;
+  if (dbias && !a->bias) return fail(ATTN_INVALID_ARGUMENT, "dbias requested without a bias");
+  if (a->sink_mode == ATTN_SINK_LEARNABLE && !dsink)
+    return fail(ATTN_INVALID_ARGUMENT, "LEARNABLE sink needs dsink [Hq] for its gradient");
+  if (a->sink_mode != ATTN_SINK_LEARNABLE && dsink)
+    return fail(ATTN_INVALID_ARGUMENT, "dsink given but the sink is not LEARNABLE");
+  const size_t need = bwd_ws(a);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(ATTN_INVALID_ARGUMENT, "workspace smaller than attn_bwd_workspace_size");
+  if ((size_t)a->B * (a->Sq + a->Sk) * a->Hq == 0) return ATTN_OK;
+  if (!out || !lse || !dout || !dq || !dk || !dv)
+    return fail(ATTN_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv must not be NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  BwdParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.bias = a->bias;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dbias = dbias;
+  p.mask = base_mask(a);
+  hipError_t e = prep_segments(a, ws, p.mask, s);
+  if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
+  float* delta = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));
+  float* part = nullptr;
+  if (a->sink_mode == ATTN_SINK_LEARNABLE) part = reinterpret_cast<float*>(ws);
+  p.delta = delta;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.G = a->Hq / a->Hkv;
+  fill_consts(a, p.scale, p.sl2, p.xc, p.bc, p.cl2);
+  p.reverse = a->causal ? 1 : 0;
+  const Launch l{a->B, a->Sq, a->Sk, s};
+  const TypeOps& o = ops(a);
+  const bool cap = a->softcap > 0.0f, bias = a->bias != nullptr;
+  if (a->Sq > 0) {
+    e = o.pre(a->D, out, dout, lse, delta, part, a->sink, a->sink_mode, a->Hq, kPreRows, l);
+    if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
+    if (part) {
+      dsink_final_kernel<<<a->Hq, 256, 0, s>>>(part, dsink, (int)(a->B * pre_blocks(a)));
+      e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "sink gradient launch");
+    }
+    if (dbias) {
+      e = o.dbias_fill(dbias, p.mask, a->Hq, kFillRows, l);
+      if (e != hipSuccess) return hip_fail(e, "dbias fill launch");
+    }
+    e = o.dq(a->D, cap, bias, p, l);
+    if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
+  } else if (part) {
+    dsink_final_kernel<<<a->Hq, 256, 0, s>>>(part, dsink, 0);
+  }
+  if (a->Sk > 0) {
+    e = o.dkdv(a->D, cap, bias, p, l);
+    if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,250 @@
+// Device building blocks shared by the gfx950 attention kernels: MFMA
+// fragments, LDS tile staging, the soft-cap arithmetic and the visibility
+// ranges of packed / causal / windowed rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace atl {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- fragments
+//
+// Every contraction runs on 32x32 MFMA blocks.  A lane l = r + 32g (r < 32,
+// g in {0,1}) holds, for each group of 16 contraction indices, the 8
+// consecutive indices 8g..8g+7 of row r (A operand) or column r (B operand).
+// bf16 feeds them to one v_mfma_f32_32x32x16_bf16; fp32 feeds them one index
+// at a time to eight v_mfma_f32_32x32x2_f32 (index 8g+s in step s), which is
+// the same pairing of A and B elements, so one fragment layout serves both.
+//
+// The accumulator layout of a 32x32 block: lane r + 32h, register j holds
+// row 8(j/4) + 4h + (j%4), column r.  Operand rows are read through the bit
+// swap `swp` (bits 2 and 3 of the row index exchanged), which turns that into
+// row 16(j/8) + 8h + (j%8): register j of a lane then walks 8 consecutive
+// rows twice, which is exactly the index order the next contraction's B
+// fragment wants (registers 8s..8s+7 = indices 16s + 8g + 0..7), so
+// probabilities and gradients feed the next MFMA with no lane shuffles.
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { using type = bf16x8; };
+template <> struct Frag<float> { using type = f32x8; };
+
+__device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], c, 0, 0, 0);
+}
+
+__host__ __device__ constexpr int swp(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// logical row (after the swp-permuted operand read) of accumulator register j
+__device__ __forceinline__ int acc_row(int h, int j) { return 16 * (j >> 3) + 8 * h + (j & 7); }
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type lds_frag(const T* p);
+template <>
+__device__ __forceinline__ bf16x8 lds_frag<bf16>(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+template <>
+__device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// 8 fp32 accumulator values -> an operand fragment (round to nearest even)
+__device__ __forceinline__ bf16x8 to_frag(const f32x16& c, int base, bf16*) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)c[base + i];
+  return r;
+}
+__device__ __forceinline__ f32x8 to_frag(const f32x16& c, int base, float*) {
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = c[base + i];
+  return r;
+}
+
+// ---------------------------------------------------------------- scalar helpers
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh for the soft-cap.  The bf16 path uses 1 - 2/(1 + e^{2x}) (one exp2,
+// one reciprocal; exact limits +-1 at overflow/underflow, absolute error a
+// few fp32 ulps, far below bf16 rounding).  The fp32 path keeps the device
+// library's tanhf, which stays accurate to a few ulps relative near 0.
+__device__ __forceinline__ float cap_tanh(float x, bf16*) {
+  float e = fast_exp2(x * (2.0f * kLog2e));
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
+}
+__device__ __forceinline__ float cap_tanh(float x, float*) { return tanhf(x); }
+
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
+template <> __device__ __forceinline__ void store8<bf16>(bf16* p, const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x8*>(p) = r;
+}
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  f32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[4 + i]; }
+  reinterpret_cast<f32x4*>(p)[0] = a;
+  reinterpret_cast<f32x4*>(p)[1] = b;
+}
+
+// 8 consecutive values from global memory into fp32 (16-byte aligned for bf16,
+// 32-byte for fp32)
+__device__ __forceinline__ void load8(const bf16* p, float* v) {
+  bf16x8 r = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)r[i];
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+  f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+
+// ---------------------------------------------------------------- LDS staging
+//
+// All threads of the workgroup take part.  Rows at or beyond `nvalid` are
+// written as zeros so that masked-out keys or queries can never inject
+// non-finite values into a contraction.
+
+// lds[(PERM ? swp(r) : r) * LDS_STRIDE + c] = g[(row0 + r) * gstride + col0 + c]
+template <typename T, int ROWS, int COLS, int LDS_STRIDE, bool PERM, int NT>
+__device__ __forceinline__ void stage_rows(T* lds, const T* g, long gstride, int row0, int nvalid, int col0) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CPR = COLS / VEC;
+  constexpr int TOTAL = ROWS * CPR;
+  static_assert(COLS % VEC == 0, "tile width must be a multiple of 16 bytes");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int idx0 = 0; idx0 < TOTAL; idx0 += NT) {
+    const int idx = idx0 + tid;
+    if (TOTAL % NT == 0 || idx < TOTAL) {
+      const int r = idx / CPR;
+      const int c = (idx % CPR) * VEC;
+      uint4 val = {0u, 0u, 0u, 0u};
+      if (row0 + r < nvalid) val = *reinterpret_cast<const uint4*>(g + (long)(row0 + r) * gstride + col0 + c);
+      const int lr = PERM ? swp(r) : r;
+      *reinterpret_cast<uint4*>(lds + lr * LDS_STRIDE + c) = val;
+    }
+  }
+}
+
+// Transposed: lds[(PERM ? swp(c) : c) * LDS_STRIDE + r] = g[(row0 + r) * gstride + col0 + c].
+// Each thread takes two adjacent rows and one 16-byte column chunk and writes
+// packed (row r, row r+1) pairs, so consecutive lanes write consecutive words.
+template <typename T, int ROWS, int COLS, int LDS_STRIDE, bool PERM, int NT>
+__device__ __forceinline__ void stage_rows_t(T* lds, const T* g, long gstride, int row0, int nvalid, int col0) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int RP = ROWS / 2;
+  constexpr int TOTAL = RP * (COLS / VEC);
+  static_assert(ROWS % 2 == 0 && COLS % VEC == 0, "bad transposed tile");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int idx0 = 0; idx0 < TOTAL; idx0 += NT) {
+    const int idx = idx0 + tid;
+    if (TOTAL % NT == 0 || idx < TOTAL) {
+      const int rp = idx % RP;
+      const int c0 = (idx / RP) * VEC;
+      const int r = 2 * rp;
+      T a[VEC], b[VEC];
+      uint4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+      if (row0 + r < nvalid) va = *reinterpret_cast<const uint4*>(g + (long)(row0 + r) * gstride + col0 + c0);
+      if (row0 + r + 1 < nvalid) vb = *reinterpret_cast<const uint4*>(g + (long)(row0 + r + 1) * gstride + col0 + c0);
+      __builtin_memcpy(a, &va, 16);
+      __builtin_memcpy(b, &vb, 16);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int lc = PERM ? swp(c0 + e) : (c0 + e);
+        T pair[2] = {a[e], b[e]};
+        if constexpr (sizeof(T) == 2) {
+          uint32_t w;
+          __builtin_memcpy(&w, pair, 4);
+          *reinterpret_cast<uint32_t*>(lds + lc * LDS_STRIDE + r) = w;
+        } else {
+          f32x2 w;
+          __builtin_memcpy(&w, pair, 8);
+          *reinterpret_cast<f32x2*>(lds + lc * LDS_STRIDE + r) = w;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- visibility
+//
+// Packed segments are contiguous runs; seg_lo[t] / seg_hi[t] are the first and
+// one-past-last token of t's run (absent: the whole row).  With the run, the
+// causal flag and the window, the keys a query sees and the queries a key is
+// seen by are both one contiguous range, and the range ends are
+// non-decreasing in the token index.
+
+struct Mask {
+  const int* seg_lo;   // [B * S] or null
+  const int* seg_hi;
+  int Sq, Sk;
+  int causal, window;
+};
+
+// keys visible to query i of batch row b: [lo, hi)
+__device__ __forceinline__ void keys_of(const Mask& m, int b, int i, int& lo, int& hi) {
+  lo = 0;
+  hi = m.Sk;
+  if (m.seg_lo) {
+    lo = max(m.seg_lo[(long)b * m.Sq + i], 0);
+    hi = min(m.seg_hi[(long)b * m.Sq + i], m.Sk);
+  }
+  if (m.causal) hi = min(hi, i + 1);
+  if (m.window > 0) {
+    lo = max(lo, i - m.window + 1);
+    if (!m.causal) hi = min(hi, i + m.window);
+  }
+  lo = min(lo, m.Sk);  // keeps both ends non-decreasing in i and within [0, Sk]
+  hi = max(hi, lo);
+}
+
+// queries that see key j of batch row b: [lo, hi)
+__device__ __forceinline__ void queries_of(const Mask& m, int b, int j, int& lo, int& hi) {
+  lo = 0;
+  hi = m.Sq;
+  if (m.seg_lo) {
+    lo = max(m.seg_lo[(long)b * m.Sk + j], 0);
+    hi = min(m.seg_hi[(long)b * m.Sk + j], m.Sq);
+  }
+  if (m.causal) lo = max(lo, j);
+  if (m.window > 0) {
+    hi = min(hi, j + m.window);
+    if (!m.causal) lo = max(lo, j - m.window + 1);
+  }
+  lo = min(lo, m.Sq);  // keeps both ends non-decreasing in j and within [0, Sq]
+  hi = max(hi, lo);
+}
+
+// shuffle with the partner lane l ^ 32 (the other half of a 32x32 column)
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+}  // namespace atl

@@ -1,0 +1,191 @@
+// Tile shapes per (element type, head dim) and the launch wrappers.
+//
+// The shapes keep every workgroup's LDS tiles under the 160 KiB of a gfx950
+// CU and every wave's fp32 accumulators at or under 128 registers:
+//   DO  output columns owned by one wave (D/DO waves share a row group),
+//   NQG query groups of 32 per workgroup (forward, dq),
+//   NKG key groups of 32 per workgroup (dkdv),
+//   BN  keys per forward / dq tile,
+//   DC  head-dim columns staged in LDS at a time (DC == D: no chunking).
+#pragma once
+
+#include "kernels.hpp"
+
+namespace atl {
+
+template <typename T, int D> struct FwdCfg;
+template <typename T, int D> struct DqCfg;
+template <typename T, int D> struct DkdvCfg;
+
+#define ATL_FWD(T, D_, DO_, NQG_, BN_, DC_) \
+  template <> struct FwdCfg<T, D_> { static constexpr int DO = DO_, NQG = NQG_, BN = BN_, DC = DC_; };
+#define ATL_DQ(T, D_, DO_, NQG_, BN_, DC_) \
+  template <> struct DqCfg<T, D_> { static constexpr int DO = DO_, NQG = NQG_, BN = BN_, DC = DC_; };
+#define ATL_DKDV(T, D_, DO_, NKG_, DC_) \
+  template <> struct DkdvCfg<T, D_> { static constexpr int DO = DO_, NKG = NKG_, DC = DC_; };
+
+//          T      D    DO  NQG  BN   DC
+ATL_FWD(bf16, 64, 64, 4, 64, 64)
+ATL_FWD(bf16, 128, 128, 4, 64, 128)
+ATL_FWD(bf16, 256, 256, 2, 32, 256)
+ATL_FWD(bf16, 512, 256, 2, 32, 512)
+ATL_FWD(float, 64, 64, 4, 32, 64)
+ATL_FWD(float, 128, 128, 2, 32, 128)
+ATL_FWD(float, 256, 256, 2, 32, 256)
+ATL_FWD(float, 512, 256, 1, 32, 128)
+
+ATL_DQ(bf16, 64, 64, 4, 64, 64)
+ATL_DQ(bf16, 128, 128, 4, 32, 128)
+ATL_DQ(bf16, 256, 256, 2, 32, 256)
+ATL_DQ(bf16, 512, 256, 2, 32, 128)
+ATL_DQ(float, 64, 64, 4, 32, 64)
+ATL_DQ(float, 128, 128, 2, 32, 128)
+ATL_DQ(float, 256, 256, 2, 32, 128)
+ATL_DQ(float, 512, 256, 1, 32, 128)
+
+//           T      D   DO NKG  DC
+ATL_DKDV(bf16, 64, 64, 4, 64)
+ATL_DKDV(bf16, 128, 128, 4, 128)
+ATL_DKDV(bf16, 256, 128, 2, 256)
+ATL_DKDV(bf16, 512, 128, 1, 128)
+ATL_DKDV(float, 64, 64, 4, 64)
+ATL_DKDV(float, 128, 128, 2, 128)
+ATL_DKDV(float, 256, 128, 1, 128)
+ATL_DKDV(float, 512, 128, 1, 128)
+
+#undef ATL_FWD
+#undef ATL_DQ
+#undef ATL_DKDV
+
+struct Launch {
+  int B, Sq, Sk;
+  hipStream_t stream;
+};
+
+template <typename T, int D> constexpr int fwd_rows() { return 32 * FwdCfg<T, D>::NQG; }
+template <typename T, int D> constexpr int dq_rows() { return 32 * DqCfg<T, D>::NQG; }
+template <typename T, int D> constexpr int dkdv_keys() { return 32 * DkdvCfg<T, D>::NKG; }
+
+template <typename T, int D, bool CAP, bool BIAS>
+hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
+  using C = FwdCfg<T, D>;
+  constexpr int BM = 32 * C::NQG;
+  const dim3 grid((l.Sq + BM - 1) / BM, p.Hq, l.B);
+  const dim3 block(64 * C::NQG * (D / C::DO));
+  fwd_kernel<T, D, C::DO, C::NQG, C::BN, C::DC, CAP, BIAS><<<grid, block, 0, l.stream>>>(p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool CAP, bool BIAS>
+hipError_t launch_dq(const BwdParams& p, const Launch& l) {
+  using C = DqCfg<T, D>;
+  constexpr int BM = 32 * C::NQG;
+  const dim3 grid((l.Sq + BM - 1) / BM, p.Hq, l.B);
+  const dim3 block(64 * C::NQG * (D / C::DO));
+  dq_kernel<T, D, C::DO, C::NQG, C::BN, C::DC, CAP, BIAS><<<grid, block, 0, l.stream>>>(p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool CAP, bool BIAS>
+hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
+  using C = DkdvCfg<T, D>;
+  constexpr int BNK = 32 * C::NKG;
+  const dim3 grid((l.Sk + BNK - 1) / BNK, p.Hkv, l.B);
+  const dim3 block(64 * C::NKG * (D / C::DO));
+  dkdv_kernel<T, D, C::DO, C::NKG, C::DC, CAP, BIAS><<<grid, block, 0, l.stream>>>(p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_pre(const T* out, const T* dout, const float* lse, float* delta, float* dsink_part,
+                      const float* sink, int sink_mode, int Hq, int rows_per_block, const Launch& l) {
+  const dim3 grid((l.Sq + rows_per_block - 1) / rows_per_block, Hq, l.B);
+  bwd_pre_kernel<T, D><<<grid, 256, 0, l.stream>>>(out, dout, lse, delta, dsink_part, sink, sink_mode, l.Sq, Hq,
+                                                   rows_per_block);
+  return hipGetLastError();
+}
+
+// Entry points of one element type (defined in attn_bf16.hip / attn_f32.hip).
+struct TypeOps {
+  hipError_t (*fwd)(int D, bool cap, bool bias, const FwdParams&, const Launch&);
+  hipError_t (*dq)(int D, bool cap, bool bias, const BwdParams&, const Launch&);
+  hipError_t (*dkdv)(int D, bool cap, bool bias, const BwdParams&, const Launch&);
+  hipError_t (*pre)(int D, const void* out, const void* dout, const float* lse, float* delta, float* dsink_part,
+                    const float* sink, int sink_mode, int Hq, int rows_per_block, const Launch&);
+  hipError_t (*dbias_fill)(void* dbias, const Mask&, int Hq, int rows_per_block, const Launch&);
+};
+
+const TypeOps& ops_bf16();
+const TypeOps& ops_f32();
+
+}  // namespace atl
+
+// Instantiates the TypeOps of one element type.
+#define ATL_DEFINE_TYPE_OPS(T, NAME)                                                                        \
+  namespace atl {                                                                                           \
+  namespace {                                                                                               \
+  template <int D>                                                                                          \
+  hipError_t fwd_d(bool cap, bool bias, const FwdParams& p, const Launch& l) {                              \
+    if (cap) return bias ? launch_fwd<T, D, true, true>(p, l) : launch_fwd<T, D, true, false>(p, l);         \
+    return bias ? launch_fwd<T, D, false, true>(p, l) : launch_fwd<T, D, false, false>(p, l);                \
+  }                                                                                                         \
+  template <int D>                                                                                          \
+  hipError_t dq_d(bool cap, bool bias, const BwdParams& p, const Launch& l) {                               \
+    if (cap) return bias ? launch_dq<T, D, true, true>(p, l) : launch_dq<T, D, true, false>(p, l);           \
+    return bias ? launch_dq<T, D, false, true>(p, l) : launch_dq<T, D, false, false>(p, l);                  \
+  }                                                                                                         \
+  template <int D>                                                                                          \
+  hipError_t dkdv_d(bool cap, bool bias, const BwdParams& p, const Launch& l) {                             \
+    if (cap) return bias ? launch_dkdv<T, D, true, true>(p, l) : launch_dkdv<T, D, true, false>(p, l);       \
+    return bias ? launch_dkdv<T, D, false, true>(p, l) : launch_dkdv<T, D, false, false>(p, l);              \
+  }                                                                                                         \
+  hipError_t fwd_any(int D, bool cap, bool bias, const FwdParams& p, const Launch& l) {                     \
+    switch (D) {                                                                                            \
+      case 64: return fwd_d<64>(cap, bias, p, l);                                                           \
+      case 128: return fwd_d<128>(cap, bias, p, l);                                                         \
+      case 256: return fwd_d<256>(cap, bias, p, l);                                                         \
+      case 512: return fwd_d<512>(cap, bias, p, l);                                                         \
+    }                                                                                                       \
+    return hipErrorInvalidValue;                                                                            \
+  }                                                                                                         \
+  hipError_t dq_any(int D, bool cap, bool bias, const BwdParams& p, const Launch& l) {                      \
+    switch (D) {                                                                                            \
+      case 64: return dq_d<64>(cap, bias, p, l);                                                            \
+      case 128: return dq_d<128>(cap, bias, p, l);                                                          \
+      case 256: return dq_d<256>(cap, bias, p, l);                                                          \
+      case 512: return dq_d<512>(cap, bias, p, l);                                                          \
+    }                                                                                                       \
+    return hipErrorInvalidValue;                                                                            \
+  }                                                                                                         \
+  hipError_t dkdv_any(int D, bool cap, bool bias, const BwdParams& p, const Launch& l) {                    \
+    switch (D) {                                                                                            \
+      case 64: return dkdv_d<64>(cap, bias, p, l);                                                          \
+      case 128: return dkdv_d<128>(cap, bias, p, l);                                                        \
+      case 256: return dkdv_d<256>(cap, bias, p, l);                                                        \
+      case 512: return dkdv_d<512>(cap, bias, p, l);                                                        \
+    }                                                                                                       \
+    return hipErrorInvalidValue;                                                                            \
+  }                                                                                                         \
+  hipError_t pre_any(int D, const void* out, const void* dout, const float* lse, float* delta,              \
+                     float* part, const float* sink, int sink_mode, int Hq, int rpb, const Launch& l) {     \
+    const T* o = static_cast<const T*>(out);                                                                \
+    const T* g = static_cast<const T*>(dout);                                                               \
+    switch (D) {                                                                                            \
+      case 64: return launch_pre<T, 64>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);               \
+      case 128: return launch_pre<T, 128>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
+      case 256: return launch_pre<T, 256>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
+      case 512: return launch_pre<T, 512>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
+    }                                                                                                       \
+    return hipErrorInvalidValue;                                                                            \
+  }                                                                                                         \
+  hipError_t fill_any(void* dbias, const Mask& m, int Hq, int rpb, const Launch& l) {                       \
+    const dim3 grid((l.Sq + rpb - 1) / rpb, Hq, l.B);                                                       \
+    dbias_fill_kernel<T><<<grid, 256, 0, l.stream>>>(static_cast<T*>(dbias), m, Hq, rpb);                    \
+    return hipGetLastError();                                                                               \
+  }                                                                                                         \
+  }                                                                                                         \
+  const TypeOps& NAME() {                                                                                   \
+    static const TypeOps o = {fwd_any, dq_any, dkdv_any, pre_any, fill_any};                               \
+    return o;                                                                                               \
+  }                                                                                                         \
+  }

@@ -1,0 +1,713 @@
+// gfx950 kernels of the soft-capped attention forward and backward.
+//
+// Forward (one workgroup per batch row, query head and tile of 32*NQG
+// queries): S^T = K Q^T on MFMA, the scale / bias / tanh cap / mask in
+// registers, an online softmax whose running maximum and sum start from the
+// sink logit (so the sink joins each row's normaliser exactly once), and
+// O^T += V^T P^T on MFMA.  Key tiles outside the visible range are never
+// visited; the mask is evaluated only on tiles that are partly visible.
+//
+// Backward, two kernels after a row pre-pass (delta_i = <dO_i, O_i>):
+//  * dq:   one workgroup per query tile, looping over its visible key tiles:
+//          recompute S^T, P^T = exp(s - lse), dP^T = V dO^T,
+//          dU^T = P^T (dP^T - delta) (1 - t^2), dQ^T += K^T dU^T;
+//  * dkdv: one workgroup per KV head and key tile, looping over the query
+//          heads of its GQA group and their visible query tiles:
+//          recompute S, P, dP, dU the same way, dV^T += dO^T P,
+//          dK^T += Q^T dU, and write dbias = dU on the visible pairs.
+// The 1 - tanh^2 factor is formed from the unmasked logit before the mask is
+// applied, and dU (the gradient with respect to the pre-cap logit u) feeds
+// dq, dk and dbias alike ("Support logits soft-capping in the Pallas-Triton
+// attention VJP", PR description).
+//
+// Head dimensions that do not fit LDS in one piece are staged in chunks of
+// DC columns; a wave owns a slice of DO output columns (D/DO waves share the
+// same queries or keys and recompute the same logits).
+#pragma once
+
+#include "common.hpp"
+
+namespace atl {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;
+  void* out;
+  float* lse;
+  Mask mask;
+  int Hq, Hkv, G;
+  float sl2;    // scale * log2(e)            (no cap)
+  float xc;     // scale / softcap            (cap)
+  float bc;     // 1 / softcap                (cap)
+  float cl2;    // softcap * log2(e)          (cap)
+  const float* sink;  // [Hq] or null
+  int sink_mode;      // 0 none, 1 off-by-one, 2 learnable
+  int reverse;        // visit query tiles from the last (heaviest under causal masks)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;
+  const void* dout;
+  const float* lse;    // [B,Hq,Sq] natural log
+  const float* delta;  // [B,Hq,Sq]
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dbias;
+  Mask mask;
+  int Hq, Hkv, G;
+  float scale;
+  float sl2, xc, bc, cl2;
+  int reverse;
+};
+
+template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };
+
+// logits in log2 units from the raw product x and the bias value b
+template <typename T, bool CAP, bool BIAS>
+__device__ __forceinline__ float logit2(float x, float b, float sl2, float xc, float bc, float cl2, float& f) {
+  if constexpr (CAP) {
+    float a = x * xc;
+    if constexpr (BIAS) a = fmaf(b, bc, a);
+    const float t = cap_tanh(a, (T*)nullptr);
+    f = fmaf(-t, t, 1.0f);
+    return t * cl2;
+  } else {
+    f = 1.0f;
+    float a = x * sl2;
+    if constexpr (BIAS) a = fmaf(b, kLog2e, a);
+    return a;
+  }
+}
+
+// ============================================================== forward
+
+template <typename T, int D, int DO, int NQG, int BN, int DC, bool CAP, bool BIAS>
+__global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
+  constexpr int NSL = D / DO;
+  constexpr int NW = NQG * NSL;
+  constexpr int NT = 64 * NW;
+  constexpr int BM = 32 * NQG;
+  constexpr int NKB = BN / 32;
+  constexpr int NOB = DO / 32;
+  constexpr int NCH = D / DC;
+  constexpr bool ONE = (NCH == 1);
+  constexpr int QS = DC + Pad<T>::v;
+  constexpr int KS = DC + Pad<T>::v;
+  constexpr int VS = BN + Pad<T>::v;
+  static_assert(D % DO == 0 && D % DC == 0 && DO % 32 == 0 && DC % 32 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(ONE || DO % DC == 0, "a chunk must not straddle two slices");
+  using F = typename Frag<T>::type;
+
+  __shared__ __attribute__((aligned(16))) T sQ[BM * QS];
+  __shared__ __attribute__((aligned(16))) T sK[BN * KS];
+  __shared__ __attribute__((aligned(16))) T sV[DC * VS];
+
+  const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int hk = hq / p.G;
+  const int Sq = p.mask.Sq, Sk = p.mask.Sk;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int qg = w / NSL;
+  const int sl = w % NSL;
+  const int q0 = qt * BM;
+  const int i = q0 + qg * 32 + n;
+
+  const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
+  const T* kbase = reinterpret_cast<const T*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
+  const T* vbase = reinterpret_cast<const T*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
+  const long qstride = (long)p.Hq * D;
+  const long kstride = (long)p.Hkv * D;
+
+  // visible key range of this lane's query and of the whole tile
+  int lo_i = 0, hi_i = 0;
+  if (i < Sq) keys_of(p.mask, b, i, lo_i, hi_i);
+  const int ilast = min(q0 + BM, Sq) - 1;
+  int lo_first, hi_first, lo_last, hi_last;
+  keys_of(p.mask, b, q0, lo_first, hi_first);
+  keys_of(p.mask, b, ilast, lo_last, hi_last);
+  const bool rows_full = (q0 + BM <= Sq);
+
+  const T* brow = nullptr;
+  if constexpr (BIAS) brow = reinterpret_cast<const T*>(p.bias) + (((long)b * p.Hq + hq) * Sq + min(i, Sq - 1)) * Sk;
+
+  const bool has_sink = p.sink_mode != 0;
+  const float sink2 = p.sink_mode == 2 ? p.sink[hq] * kLog2e : 0.0f;
+  float m = has_sink ? sink2 : -INFINITY;
+  float lsum = 0.0f;
+  f32x16 oacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) oacc[ob] = f32x16{};
+
+  if constexpr (ONE) {
+    stage_rows<T, BM, DC, QS, false, NT>(sQ, qbase, qstride, q0, Sq, 0);
+  }
+
+  const int kbeg = (lo_first / BN) * BN;
+  for (int k0 = kbeg; k0 < hi_last; k0 += BN) {
+    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
+
+    // ---- S^T = K Q^T over the head dimension
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();
+      stage_rows<T, BN, DC, KS, true, NT>(sK, kbase, kstride, k0, Sk, c * DC);
+      if constexpr (!ONE) stage_rows<T, BM, DC, QS, false, NT>(sQ, qbase, qstride, q0, Sq, c * DC);
+      if constexpr (ONE) stage_rows_t<T, BN, DC, VS, true, NT>(sV, vbase, kstride, k0, Sk, 0);
+      __syncthreads();
+#pragma unroll
+      for (int cc = 0; cc < DC / 16; ++cc) {
+        const F bq = lds_frag<T>(sQ + (qg * 32 + n) * QS + cc * 16 + 8 * h);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const F ak = lds_frag<T>(sK + (kb * 32 + n) * KS + cc * 16 + 8 * h);
+          mma(sacc[kb], ak, bq);
+        }
+      }
+    }
+
+    // ---- scale, bias, cap, mask; online softmax
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float bv[16];
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int j0 = k0 + kb * 32 + 16 * hf + 8 * h;
+          if (i < Sq && j0 + 8 <= Sk && (Sk & 7) == 0) {
+            load8(brow + j0, bv + 8 * hf);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[8 * hf + e] = (i < Sq && j0 + e < Sk) ? to_f32(brow[j0 + e]) : 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float f;
+        float s2 = logit2<T, CAP, BIAS>(sacc[kb][j], BIAS ? bv[j] : 0.0f, p.sl2, p.xc, p.bc, p.cl2, f);
+        if (!full) {
+          const int key = k0 + kb * 32 + acc_row(h, j);
+          if (key < lo_i || key >= hi_i) s2 = -INFINITY;
+        }
+        sacc[kb][j] = s2;
+        mx = fmaxf(mx, s2);
+      }
+    }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m, mx);
+    const float base = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m - base);
+    float ps = 0.0f;
+    F pf[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pv = fast_exp2(sacc[kb][j] - base);
+        sacc[kb][j] = pv;
+        ps += pv;
+      }
+      pf[kb][0] = to_frag(sacc[kb], 0, (T*)nullptr);
+      pf[kb][1] = to_frag(sacc[kb], 8, (T*)nullptr);
+    }
+    lsum = lsum * alpha + ps;
+    m = m_new;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) oacc[ob] *= alpha;
+
+    // ---- O^T += V^T P^T over this wave's slice of the head dimension
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if constexpr (!ONE) {
+        __syncthreads();
+        stage_rows_t<T, BN, DC, VS, true, NT>(sV, vbase, kstride, k0, Sk, c * DC);
+        __syncthreads();
+      }
+      const int d0 = c * DC;
+      if (ONE || (d0 >= sl * DO && d0 < (sl + 1) * DO)) {
+#pragma unroll
+        for (int db = 0; db < DC / 32; ++db) {
+          const int ob = ONE ? (db - sl * NOB) : ((d0 - sl * DO) / 32 + db);
+          if (ONE && (db < sl * NOB || db >= (sl + 1) * NOB)) continue;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+              const F av = lds_frag<T>(sV + (db * 32 + n) * VS + kb * 32 + 16 * sb + 8 * h);
+              mma(oacc[ob], av, pf[kb][sb]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: normalise (the sink joins the sum once) and write
+  float ltot = lsum + xor32(lsum);
+  if (has_sink) ltot += fast_exp2(sink2 - m);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (i < Sq) {
+    T* orow = reinterpret_cast<T*>(p.out) + (((long)b * Sq + i) * p.Hq + hq) * D;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float vals[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = oacc[ob][8 * hf + e] * inv;
+        store8<T>(orow + sl * DO + ob * 32 + 16 * hf + 8 * h, vals);
+      }
+    }
+    if (sl == 0 && h == 0) {
+      p.lse[((long)b * p.Hq + hq) * Sq + i] = ltot > 0.0f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// ============================================================== backward: dq
+
+template <typename T, int D, int DO, int NQG, int BN, int DC, bool CAP, bool BIAS>
+__global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
+  constexpr int NSL = D / DO;
+  constexpr int NW = NQG * NSL;
+  constexpr int NT = 64 * NW;
+  constexpr int BM = 32 * NQG;
+  constexpr int NKB = BN / 32;
+  constexpr int NOB = DO / 32;
+  constexpr int NCH = D / DC;
+  constexpr bool ONE = (NCH == 1);
+  constexpr int RS = DC + Pad<T>::v;
+  constexpr int TS = BN + Pad<T>::v;
+  static_assert(ONE || DO % DC == 0, "a chunk must not straddle two slices");
+  using F = typename Frag<T>::type;
+
+  __shared__ __attribute__((aligned(16))) T sQ[BM * RS];
+  __shared__ __attribute__((aligned(16))) T sO[BM * RS];   // dO
+  __shared__ __attribute__((aligned(16))) T sK[BN * RS];
+  __shared__ __attribute__((aligned(16))) T sV[BN * RS];
+  __shared__ __attribute__((aligned(16))) T sKt[DC * TS];
+
+  const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int hk = hq / p.G;
+  const int Sq = p.mask.Sq, Sk = p.mask.Sk;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int qg = w / NSL;
+  const int sl = w % NSL;
+  const int q0 = qt * BM;
+  const int i = q0 + qg * 32 + n;
+
+  const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
+  const T* obase = reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D;
+  const T* kbase = reinterpret_cast<const T*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
+  const T* vbase = reinterpret_cast<const T*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
+  const long qstride = (long)p.Hq * D;
+  const long kstride = (long)p.Hkv * D;
+
+  int lo_i = 0, hi_i = 0;
+  if (i < Sq) keys_of(p.mask, b, i, lo_i, hi_i);
+  const int ilast = min(q0 + BM, Sq) - 1;
+  int lo_first, hi_first, lo_last, hi_last;
+  keys_of(p.mask, b, q0, lo_first, hi_first);
+  keys_of(p.mask, b, ilast, lo_last, hi_last);
+  const bool rows_full = (q0 + BM <= Sq);
+
+  const long row = ((long)b * p.Hq + hq) * Sq + min(i, Sq - 1);
+  const float lse_i = p.lse[row];
+  // a row with no visible key and no sink has lse = -inf: its P is zero
+  const float lse2 = (i < Sq && lse_i != -INFINITY) ? lse_i * kLog2e : INFINITY;
+  const float delta_i = (i < Sq) ? p.delta[row] : 0.0f;
+  const T* brow = nullptr;
+  if constexpr (BIAS) brow = reinterpret_cast<const T*>(p.bias) + row * Sk;
+
+  f32x16 qacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) qacc[ob] = f32x16{};
+
+  if constexpr (ONE) {
+    stage_rows<T, BM, DC, RS, false, NT>(sQ, qbase, qstride, q0, Sq, 0);
+    stage_rows<T, BM, DC, RS, false, NT>(sO, obase, qstride, q0, Sq, 0);
+  }
+
+  const int kbeg = (lo_first / BN) * BN;
+  for (int k0 = kbeg; k0 < hi_last; k0 += BN) {
+    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
+    f32x16 sacc[NKB], dpacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) { sacc[kb] = f32x16{}; dpacc[kb] = f32x16{}; }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();
+      stage_rows<T, BN, DC, RS, true, NT>(sK, kbase, kstride, k0, Sk, c * DC);
+      stage_rows<T, BN, DC, RS, true, NT>(sV, vbase, kstride, k0, Sk, c * DC);
+      if constexpr (!ONE) {
+        stage_rows<T, BM, DC, RS, false, NT>(sQ, qbase, qstride, q0, Sq, c * DC);
+        stage_rows<T, BM, DC, RS, false, NT>(sO, obase, qstride, q0, Sq, c * DC);
+      } else {
+        stage_rows_t<T, BN, DC, TS, true, NT>(sKt, kbase, kstride, k0, Sk, 0);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int cc = 0; cc < DC / 16; ++cc) {
+        const F bq = lds_frag<T>(sQ + (qg * 32 + n) * RS + cc * 16 + 8 * h);
+        const F bo = lds_frag<T>(sO + (qg * 32 + n) * RS + cc * 16 + 8 * h);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const F ak = lds_frag<T>(sK + (kb * 32 + n) * RS + cc * 16 + 8 * h);
+          mma(sacc[kb], ak, bq);
+          const F av = lds_frag<T>(sV + (kb * 32 + n) * RS + cc * 16 + 8 * h);
+          mma(dpacc[kb], av, bo);
+        }
+      }
+    }
+
+    // ---- dU^T = P^T (dP^T - delta) (1 - t^2)
+    F uf[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float bv[16];
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int j0 = k0 + kb * 32 + 16 * hf + 8 * h;
+          if (i < Sq && j0 + 8 <= Sk && (Sk & 7) == 0) {
+            load8(brow + j0, bv + 8 * hf);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[8 * hf + e] = (i < Sq && j0 + e < Sk) ? to_f32(brow[j0 + e]) : 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float f;
+        const float s2 = logit2<T, CAP, BIAS>(sacc[kb][j], BIAS ? bv[j] : 0.0f, p.sl2, p.xc, p.bc, p.cl2, f);
+        float pv = fast_exp2(s2 - lse2);
+        if (!full) {
+          const int key = k0 + kb * 32 + acc_row(h, j);
+          if (key < lo_i || key >= hi_i) pv = 0.0f;
+        }
+        sacc[kb][j] = pv * (dpacc[kb][j] - delta_i) * f;
+      }
+      uf[kb][0] = to_frag(sacc[kb], 0, (T*)nullptr);
+      uf[kb][1] = to_frag(sacc[kb], 8, (T*)nullptr);
+    }
+
+    // ---- dQ^T += K^T dU^T over this wave's slice
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if constexpr (!ONE) {
+        __syncthreads();
+        stage_rows_t<T, BN, DC, TS, true, NT>(sKt, kbase, kstride, k0, Sk, c * DC);
+        __syncthreads();
+      }
+      const int d0 = c * DC;
+      if (ONE || (d0 >= sl * DO && d0 < (sl + 1) * DO)) {
+#pragma unroll
+        for (int db = 0; db < DC / 32; ++db) {
+          const int ob = ONE ? (db - sl * NOB) : ((d0 - sl * DO) / 32 + db);
+          if (ONE && (db < sl * NOB || db >= (sl + 1) * NOB)) continue;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+              const F ak = lds_frag<T>(sKt + (db * 32 + n) * TS + kb * 32 + 16 * sb + 8 * h);
+              mma(qacc[ob], ak, uf[kb][sb]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  if (i < Sq) {
+    T* drow = reinterpret_cast<T*>(p.dq) + (((long)b * Sq + i) * p.Hq + hq) * D;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float vals[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = qacc[ob][8 * hf + e] * p.scale;
+        store8<T>(drow + sl * DO + ob * 32 + 16 * hf + 8 * h, vals);
+      }
+    }
+  }
+}
+
+// ============================================================== backward: dk, dv, dbias
+
+template <typename T, int D, int DO, int NKG, int DC, bool CAP, bool BIAS>
+__global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) {
+  constexpr int NSL = D / DO;
+  constexpr int NW = NKG * NSL;
+  constexpr int NT = 64 * NW;
+  constexpr int BNK = 32 * NKG;
+  constexpr int BMQ = 32;
+  constexpr int NOB = DO / 32;
+  constexpr int NCH = D / DC;
+  constexpr bool ONE = (NCH == 1);
+  constexpr int RS = DC + Pad<T>::v;
+  constexpr int TS = BMQ + Pad<T>::v;
+  static_assert(ONE || DO % DC == 0, "a chunk must not straddle two slices");
+  using F = typename Frag<T>::type;
+
+  __shared__ __attribute__((aligned(16))) T sK[BNK * RS];
+  __shared__ __attribute__((aligned(16))) T sV[BNK * RS];
+  __shared__ __attribute__((aligned(16))) T sQ[BMQ * RS];
+  __shared__ __attribute__((aligned(16))) T sO[BMQ * RS];
+  __shared__ __attribute__((aligned(16))) T sQt[DC * TS];
+  __shared__ __attribute__((aligned(16))) T sOt[DC * TS];
+  __shared__ __attribute__((aligned(16))) float sL[BMQ];
+  __shared__ __attribute__((aligned(16))) float sDl[BMQ];
+
+  const int kt = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int Sq = p.mask.Sq, Sk = p.mask.Sk;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int kg = w / NSL;
+  const int sl = w % NSL;
+  const int k0 = kt * BNK;
+  const int j = k0 + kg * 32 + n;
+
+  const T* kbase = reinterpret_cast<const T*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
+  const T* vbase = reinterpret_cast<const T*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
+  const long qstride = (long)p.Hq * D;
+  const long kstride = (long)p.Hkv * D;
+
+  // queries that see this lane's key, and the query range of the whole tile
+  int lo_j = 0, hi_j = 0;
+  if (j < Sk) queries_of(p.mask, b, j, lo_j, hi_j);
+  const int jlast = min(k0 + BNK, Sk) - 1;
+  int lo_first, hi_first, lo_last, hi_last;
+  queries_of(p.mask, b, k0, lo_first, hi_first);
+  queries_of(p.mask, b, jlast, lo_last, hi_last);
+  const bool keys_full = (k0 + BNK <= Sk);
+
+  f32x16 kacc[NOB], vacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) { kacc[ob] = f32x16{}; vacc[ob] = f32x16{}; }
+
+  if constexpr (ONE) {
+    stage_rows<T, BNK, DC, RS, false, NT>(sK, kbase, kstride, k0, Sk, 0);
+    stage_rows<T, BNK, DC, RS, false, NT>(sV, vbase, kstride, k0, Sk, 0);
+  }
+
+  const int qbeg = (lo_first / BMQ) * BMQ;
+  for (int g = 0; g < p.G; ++g) {
+    const int hq = hk * p.G + g;
+    const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
+    const T* obase = reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D;
+    const long lrow = ((long)b * p.Hq + hq) * Sq;
+    const T* bbase = nullptr;
+    T* dbbase = nullptr;
+    if constexpr (BIAS) {
+      bbase = reinterpret_cast<const T*>(p.bias) + lrow * Sk;
+      if (p.dbias) dbbase = reinterpret_cast<T*>(p.dbias) + lrow * Sk;
+    }
+    for (int q0 = qbeg; q0 < hi_last; q0 += BMQ) {
+      const bool full = keys_full && q0 >= lo_last && q0 + BMQ <= hi_first;
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        stage_rows<T, BMQ, DC, RS, true, NT>(sQ, qbase, qstride, q0, Sq, c * DC);
+        stage_rows<T, BMQ, DC, RS, true, NT>(sO, obase, qstride, q0, Sq, c * DC);
+        if constexpr (!ONE) {
+          stage_rows<T, BNK, DC, RS, false, NT>(sK, kbase, kstride, k0, Sk, c * DC);
+          stage_rows<T, BNK, DC, RS, false, NT>(sV, vbase, kstride, k0, Sk, c * DC);
+        } else {
+          stage_rows_t<T, BMQ, DC, TS, true, NT>(sQt, qbase, qstride, q0, Sq, 0);
+          stage_rows_t<T, BMQ, DC, TS, true, NT>(sOt, obase, qstride, q0, Sq, 0);
+        }
+        if (c == 0 && threadIdx.x < BMQ) {
+          const int qi = q0 + threadIdx.x;
+          float l2 = INFINITY, dl = 0.0f;
+          if (qi < Sq) {
+            const float l = p.lse[lrow + qi];
+            l2 = (l != -INFINITY) ? l * kLog2e : INFINITY;
+            dl = p.delta[lrow + qi];
+          }
+          sL[threadIdx.x] = l2;
+          sDl[threadIdx.x] = dl;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int cc = 0; cc < DC / 16; ++cc) {
+          const F aq = lds_frag<T>(sQ + n * RS + cc * 16 + 8 * h);
+          const F bk = lds_frag<T>(sK + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+          mma(sacc, aq, bk);
+          const F ao = lds_frag<T>(sO + n * RS + cc * 16 + 8 * h);
+          const F bv = lds_frag<T>(sV + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+          mma(dpacc, ao, bv);
+        }
+      }
+
+      // ---- P, dU (lane: key j; register r: query q0 + acc_row(h, r))
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + acc_row(h, r);
+        float bvv = 0.0f;
+        if constexpr (BIAS) bvv = (qi < Sq && j < Sk) ? to_f32(bbase[(long)qi * Sk + j]) : 0.0f;
+        float f;
+        const float s2 = logit2<T, CAP, BIAS>(sacc[r], bvv, p.sl2, p.xc, p.bc, p.cl2, f);
+        float pv = fast_exp2(s2 - sL[acc_row(h, r)]);
+        bool vis = true;
+        if (!full) vis = (qi >= lo_j && qi < hi_j);
+        if (!vis) pv = 0.0f;
+        const float du = pv * (dpacc[r] - sDl[acc_row(h, r)]) * f;
+        sacc[r] = pv;
+        dpacc[r] = du;
+        if constexpr (BIAS) {
+          if (dbbase && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
+        }
+      }
+      F pf[2], uf[2];
+      pf[0] = to_frag(sacc, 0, (T*)nullptr);
+      pf[1] = to_frag(sacc, 8, (T*)nullptr);
+      uf[0] = to_frag(dpacc, 0, (T*)nullptr);
+      uf[1] = to_frag(dpacc, 8, (T*)nullptr);
+
+      // ---- dV^T += dO^T P,  dK^T += Q^T dU  over this wave's slice
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if constexpr (!ONE) {
+          __syncthreads();
+          stage_rows_t<T, BMQ, DC, TS, true, NT>(sQt, qbase, qstride, q0, Sq, c * DC);
+          stage_rows_t<T, BMQ, DC, TS, true, NT>(sOt, obase, qstride, q0, Sq, c * DC);
+          __syncthreads();
+        }
+        const int d0 = c * DC;
+        if (ONE || (d0 >= sl * DO && d0 < (sl + 1) * DO)) {
+#pragma unroll
+          for (int db = 0; db < DC / 32; ++db) {
+            const int ob = ONE ? (db - sl * NOB) : ((d0 - sl * DO) / 32 + db);
+            if (ONE && (db < sl * NOB || db >= (sl + 1) * NOB)) continue;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+              const F ao = lds_frag<T>(sOt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+              mma(vacc[ob], ao, pf[sb]);
+              const F aq = lds_frag<T>(sQt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+              mma(kacc[ob], aq, uf[sb]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  if (j < Sk) {
+    T* krow = reinterpret_cast<T*>(p.dk) + (((long)b * Sk + j) * p.Hkv + hk) * D;
+    T* vrow = reinterpret_cast<T*>(p.dv) + (((long)b * Sk + j) * p.Hkv + hk) * D;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float kv[8], vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kv[e] = kacc[ob][8 * hf + e] * p.scale;
+          vv[e] = vacc[ob][8 * hf + e];
+        }
+        const int d = sl * DO + ob * 32 + 16 * hf + 8 * h;
+        store8<T>(krow + d, kv);
+        store8<T>(vrow + d, vv);
+      }
+    }
+  }
+}
+
+// ============================================================== small kernels
+
+// delta_i = <dO_i, O_i> per row; per-block partial sums of the sink gradient
+// -sum_i exp(sigma - lse_i) delta_i (summed in a fixed order afterwards).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* out, const T* dout, const float* lse, float* delta,
+                                                      float* dsink_part, const float* sink, int sink_mode, int Sq,
+                                                      int Hq, int rows_per_block) {
+  constexpr int LPR = D / 8;            // lanes per row, 8 elements each
+  constexpr int RPP = 256 / LPR;        // rows per pass
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.x * rows_per_block;
+  const int t = threadIdx.x;
+  const int sub = t % LPR;
+  const int rr = t / LPR;
+  float part = 0.0f;
+  const float sig = (sink_mode == 2) ? sink[hq] : 0.0f;
+  for (int base = 0; base < rows_per_block; base += RPP) {
+    const int i = r0 + base + rr;
+    float s = 0.0f;
+    if (base + rr < rows_per_block && i < Sq) {
+      const long off = (((long)b * Sq + i) * Hq + hq) * D + sub * 8;
+      float a[8], c[8];
+      load8(out + off, a);
+      load8(dout + off, c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(a[e], c[e], s);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (sub == 0 && base + rr < rows_per_block && i < Sq) {
+      const long li = ((long)b * Hq + hq) * Sq + i;
+      delta[li] = s;
+      if (sink_mode == 2) {
+        const float l = lse[li];
+        part -= (l == -INFINITY) ? 0.0f : expf(sig - l) * s;
+      }
+    }
+  }
+  if (sink_mode != 2) return;
+  __shared__ float red[256];
+  red[t] = part;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) red[t] += red[t + s];
+    __syncthreads();
+  }
+  if (t == 0) dsink_part[((long)hq * gridDim.z + b) * gridDim.x + blockIdx.x] = red[0];
+}
+
+// dbias = 0 on every pair that no query-key visibility covers (the dkdv
+// kernel writes the visible pairs).  One block per (row group, head, batch).
+template <typename T>
+__global__ __launch_bounds__(256) void dbias_fill_kernel(T* dbias, Mask mask, int Hq, int rows_per_block) {
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int Sq = mask.Sq, Sk = mask.Sk;
+  const int r0 = blockIdx.x * rows_per_block;
+  for (int rr = 0; rr < rows_per_block; ++rr) {
+    const int i = r0 + rr;
+    if (i >= Sq) break;
+    int lo, hi;
+    keys_of(mask, b, i, lo, hi);
+    T* row = dbias + (((long)b * Hq + hq) * Sq + i) * Sk;
+    for (int j = threadIdx.x; j < Sk; j += 256) {
+      if (j < lo || j >= hi) row[j] = (T)0.0f;
+    }
+  }
+}
+
+}  // namespace atl

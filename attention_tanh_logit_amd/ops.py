@@ -1,0 +1,192 @@
+"""Thin Python binding over the C ABI in ``include/attn_softcap.h``.
+
+Argument marshalling only: tensors are passed as raw device pointers with the
+current HIP stream, every step of the computation runs in the HIP library,
+and a missing library raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_softcap.so")
+
+ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_HIP_ERROR = 0, 1, 2, 3
+ATTN_BF16, ATTN_FP32 = 0, 1
+SINK_MODES = {"none": 0, "off_by_one": 1, "learnable": 2}
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("B", ctypes.c_int), ("Sq", ctypes.c_int), ("Sk", ctypes.c_int),
+        ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("D", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("segment_ids", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("nseq", ctypes.c_int),
+        ("causal", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("softcap", ctypes.c_float),
+        ("scale", ctypes.c_float),
+        ("sink_mode", ctypes.c_int),
+        ("sink", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = ("attn_validate", "attn_fwd_workspace_size", "attn_bwd_workspace_size",
+           "attn_fwd", "attn_bwd", "attn_last_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_tanh_logit_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(AttnArgs)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.attn_validate.argtypes = [P]
+    L.attn_validate.restype = ctypes.c_int
+    L.attn_fwd_workspace_size.argtypes = [P]
+    L.attn_fwd_workspace_size.restype = sz
+    L.attn_bwd_workspace_size.argtypes = [P]
+    L.attn_bwd_workspace_size.restype = sz
+    L.attn_fwd.argtypes = [P, vp, vp, vp, sz, vp]
+    L.attn_fwd.restype = ctypes.c_int
+    L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd.restype = ctypes.c_int
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, lib().attn_last_error().decode())
+
+
+def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
+              softcap=0.0, scale=0.0, sink_mode="none", sink=None) -> AttnArgs:
+    """Fill the C argument struct from tensors (BSHD, or THD with cu_seqlens)."""
+    thd = cu_seqlens is not None
+    if thd:
+        if q.dim() != 3:
+            raise ValueError("THD layout: q, k, v must be [T, H, D]")
+        B, Sq, Hq, D = 1, q.shape[0], q.shape[1], q.shape[2]
+        Sk, Hkv = k.shape[0], k.shape[1]
+    else:
+        if q.dim() != 4:
+            raise ValueError("BSHD layout: q, k, v must be [B, S, H, D]")
+        B, Sq, Hq, D = q.shape
+        Sk, Hkv = k.shape[1], k.shape[2]
+    if q.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    elif q.dtype == torch.float32:
+        dt = ATTN_FP32
+    else:
+        raise TypeError("q must be bfloat16 or float32")
+    for name, t in (("k", k), ("v", v), ("bias", bias)):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("bias", bias), ("segment_ids", segment_ids),
+                    ("cu_seqlens", cu_seqlens), ("sink", sink)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if bias is not None and tuple(bias.shape) != (B, Hq, Sq, Sk):
+        raise ValueError(f"bias must be [B, Hq, Sq, Sk] = {(B, Hq, Sq, Sk)}")
+    if segment_ids is not None and (segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) != (B, Sq)):
+        raise ValueError("segment_ids must be int32 [B, Sq]")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
+        raise ValueError("cu_seqlens must be int32 [nseq + 1]")
+    if sink is not None and (sink.dtype != torch.float32 or tuple(sink.shape) != (Hq,)):
+        raise ValueError("sink must be float32 [Hq]")
+    a = AttnArgs()
+    a.dtype = dt
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.D = B, Sq, Sk, Hq, Hkv, D
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.bias = _ptr(bias)
+    a.segment_ids = _ptr(segment_ids)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a.causal = int(bool(causal))
+    a.window = int(window)
+    a.softcap = float(softcap)
+    a.scale = float(scale)
+    a.sink_mode = SINK_MODES[sink_mode]
+    a.sink = _ptr(sink)
+    return a
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0, softcap=0.0,
+             scale=0.0, sink_mode="none", sink=None, out=None, lse=None):
+    """Forward: returns (out, lse); lse is float32 [B, Hq, Sq] ([Hq, T] for THD)."""
+    L = lib()
+    a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
+                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink)
+    _check(L.attn_validate(ctypes.byref(a)))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        shape = (a.Hq, a.Sq) if cu_seqlens is not None else (a.B, a.Hq, a.Sq)
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+    nws = L.attn_fwd_workspace_size(ctypes.byref(a))
+    ws = _workspace(nws, q.device)
+    _check(L.attn_fwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(q)))
+    return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
+             softcap=0.0, scale=0.0, sink_mode="none", sink=None, want_dbias=None):
+    """Backward: returns (dq, dk, dv, dbias or None, dsink or None)."""
+    L = lib()
+    a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
+                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink)
+    _check(L.attn_validate(ctypes.byref(a)))
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q (shape, dtype, contiguous)")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != a.B * a.Hq * a.Sq:
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    want_dbias = (bias is not None) if want_dbias is None else want_dbias
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dbias = torch.empty_like(bias) if (want_dbias and bias is not None) else None
+    dsink = torch.empty(a.Hq, dtype=torch.float32, device=q.device) if sink_mode == "learnable" else None
+    nws = L.attn_bwd_workspace_size(ctypes.byref(a))
+    ws = _workspace(nws, q.device)
+    _check(L.attn_bwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      _ptr(dbias), _ptr(dsink), _ptr(ws), nws, _stream(q)))
+    return dq, dk, dv, dbias, dsink

@@ -1,0 +1,137 @@
+/*
+ * attn_softcap.h -- C ABI of a fused attention forward and backward for the
+ * AMD MI355X (gfx950) with tanh logit soft-capping and a softmax sink.
+ *
+ * What is computed (per batch row b, query head h, query i, key j; the KV
+ * head of h is h / (Hq/Hkv), so GQA/MQA read K and V without copies):
+ *
+ *   u_ij  = scale * <q_i, k_j> + bias_ij                  (bias optional)
+ *   s_ij  = softcap * tanh(u_ij / softcap)   if softcap > 0, else s_ij = u_ij
+ *   visible(i,j) = same packed segment  and  (!causal or j <= i)  and
+ *                  (window <= 0 or (causal ? i-j < window : |i-j| < window))
+ *   softmax over the visible j of row i, plus one sink column of logit
+ *   sigma_h counted exactly once per row (sink modes below);
+ *   out_i = sum_j P_ij v_j,   lse_i = ln(sum_j e^{s_ij} + [sink] e^{sigma_h}).
+ *
+ * Sources (cited by page title and section):
+ *  - "Thread tanh logit softcapping through FlashAttention (FA2, opt-in
+ *    FA3)", intro and "What changed": the cap cap*tanh(x/cap) on attention
+ *    logits; softcap = 0 is the default and changes nothing; a requested cap
+ *    is never dropped silently (every entry point fails closed instead).
+ *  - "Support logits soft-capping in the Pallas-Triton attention VJP", PR
+ *    description: the cap goes after the bias add and before masking; the
+ *    backward chains 1 - tanh(u/c)^2 into ds, taken before masking, and dk
+ *    and dbias are gradients with respect to the pre-cap logits.
+ *  - MaxText commit message quoted on that page: packed segments (causal
+ *    inside each segment), varlen cu_seqlens, sliding window, native GQA,
+ *    head_dim above 256.
+ *  - "learnable softmax sink with context-parallel p2p" (TransformerEngine
+ *    PR #3551), "What changed": softmax_type learnable / off-by-one, one
+ *    offset per head, the sink as one more softmax column counted once per
+ *    query row, and its gradient summed over the query rows.
+ *
+ * Layouts (all contiguous, row-major):
+ *  - q, out, dout, dq : [B, Sq, Hq, D]   (BSHD)
+ *  - k, v, dk, dv     : [B, Sk, Hkv, D]
+ *  - THD (varlen): pass cu_seqlens, B = 1 and Sq = Sk = total tokens T; the
+ *    tensors are then [T, H, D], which is the same memory as [1, T, H, D].
+ *  - bias, dbias      : [B, Hq, Sq, Sk], same dtype as q.
+ *  - lse              : [B, Hq, Sq] float32, natural log, sink included.
+ *  - segment_ids      : [B, Sq] int32, non-decreasing along each row (packed
+ *                       rows); a key is visible only inside its own run.
+ *  - cu_seqlens       : [nseq + 1] int32, cu[0] = 0, non-decreasing, cu[nseq] = T.
+ *  - sink / dsink     : [Hq] float32.
+ *
+ * Ownership: the caller allocates every buffer (device memory unless noted)
+ * and keeps it alive until the work on `stream` has finished.  The library
+ * allocates nothing and keeps no state between calls.  `stream` is a
+ * hipStream_t (NULL = the default stream); calls enqueue work and return
+ * without synchronising.
+ *
+ * Errors: every entry point validates its arguments on the host first.  Any
+ * status other than ATTN_OK means that no work was enqueued; the reason is
+ * available from attn_last_error() (thread-local, valid until the next call
+ * on the same thread).
+ */
+#ifndef ATTN_SOFTCAP_H
+#define ATTN_SOFTCAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_INVALID_ARGUMENT = 1, /* a null pointer, bad size or inconsistent option */
+  ATTN_UNSUPPORTED = 2,      /* a well-formed request this library does not implement */
+  ATTN_HIP_ERROR = 3         /* a launch failed; nothing further was enqueued */
+} attn_status;
+
+typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype;
+
+/* Softmax sink ("softmax_type"): none (vanilla), off-by-one (a sink column
+ * with its logit fixed at 0 and no gradient), learnable (logit sink[h], with
+ * gradient dsink[h]). */
+typedef enum attn_sink_mode {
+  ATTN_SINK_NONE = 0,
+  ATTN_SINK_OFF_BY_ONE = 1,
+  ATTN_SINK_LEARNABLE = 2
+} attn_sink_mode;
+
+typedef struct attn_args {
+  int dtype;                   /* attn_dtype of q, k, v, bias, out, dout, dq, dk, dv, dbias */
+  int B, Sq, Sk, Hq, Hkv, D;   /* D in {64, 128, 256, 512}; Hq % Hkv == 0 */
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;            /* nullable: additive bias after the scale, before the cap */
+  const int32_t* segment_ids;  /* nullable: packed rows (needs Sq == Sk) */
+  const int32_t* cu_seqlens;   /* nullable: THD varlen (needs B == 1, Sq == Sk); not with segment_ids */
+  int nseq;                    /* number of sequences in cu_seqlens */
+  int causal;                  /* nonzero: key j visible only for j <= i (needs Sq == Sk) */
+  int window;                  /* <= 0: none; else causal: 0 <= i-j < window, non-causal: |i-j| < window */
+  float softcap;               /* 0: off; > 0: s = softcap * tanh(u / softcap) */
+  float scale;                 /* 0: 1/sqrt(D) */
+  int sink_mode;               /* attn_sink_mode */
+  const float* sink;           /* [Hq] sink logits; required iff sink_mode == ATTN_SINK_LEARNABLE */
+} attn_args;
+
+/* Host-only check of `a` (no device access, nothing launched).  Returns the
+ * status attn_fwd would return for these arguments before launching. */
+attn_status attn_validate(const attn_args* a);
+
+/* Device workspace (bytes) that attn_fwd / attn_bwd need for `a`
+ * (0 if none).  Returns (size_t)-1 if `a` is invalid. */
+size_t attn_fwd_workspace_size(const attn_args* a);
+size_t attn_bwd_workspace_size(const attn_args* a);
+
+/* Forward.  Writes out [B,Sq,Hq,D] (dtype) and lse [B,Hq,Sq] (float32).
+ * A query row that sees no key and has no sink gets out = 0, lse = -inf.
+ * workspace: device buffer of at least attn_fwd_workspace_size(a) bytes,
+ * 256-byte aligned (may be NULL when that size is 0); its contents on entry
+ * do not matter. */
+attn_status attn_fwd(const attn_args* a, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward by recomputation, from the forward's out and lse and dout.
+ * Writes dq, dk, dv (dk/dv per KV head: the GQA group sum is taken inside),
+ * dbias (nullable; requires a->bias; written in full, exactly 0 where
+ * masked) and dsink (required iff sink_mode == ATTN_SINK_LEARNABLE, else must
+ * be NULL; summed over every batch row and query row).  Results are
+ * deterministic (no floating-point atomics).
+ * workspace: at least attn_bwd_workspace_size(a) bytes, 256-byte aligned. */
+attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, void* dbias, float* dsink,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SOFTCAP_H */

@@ -1,0 +1,130 @@
+"""Shared test plumbing: seeded inputs, the GPU call, the oracle call, the metric.
+
+The GPU side goes through ``attention_tanh_logit_amd`` (the C ABI); the
+reference side through ``oracle`` (fp64 NumPy).  Both get the same seeded
+values: bf16 inputs are drawn in fp32, rounded to bf16, and the oracle sees
+those rounded values widened to fp64.
+
+Error metric (normwise, per output tensor): max|x - ref| / max|ref|.
+Tolerances: fp32 path 1e-5, bf16 path 1e-2.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import attention_backward, attention_forward
+
+TOL = {"fp32": 1e-5, "bf16": 1e-2}
+
+
+def rel_err(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    fin = np.isfinite(ref)
+    if not np.array_equal(fin, np.isfinite(x)):
+        return float("inf")
+    if not np.array_equal(np.where(fin, 0, ref), np.where(fin, 0, x)):   # same infinities
+        return float("inf")
+    d = np.abs(np.where(fin, x, 0.0) - np.where(fin, ref, 0.0)).max()
+    s = np.abs(np.where(fin, ref, 0.0)).max()
+    return float(d / s) if s > 0 else float(d)
+
+
+def tdtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_dev(x, dtype: str, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=tdtype(dtype))
+
+
+def case(dtype="bf16", B=2, S=200, Hq=4, Hkv=2, D=64, causal=True, window=0, softcap=30.0, q_scale=4.0,
+         sink_mode="none", bias=False, segments=None, seed=0, Sk=None):
+    """Random inputs for one case (numpy fp32 values, bf16-rounded for bf16)."""
+    rng = np.random.default_rng(seed)
+    Sk = S if Sk is None else Sk
+    f = np.float32
+    q = rng.standard_normal((B, S, Hq, D), dtype=f) * f(q_scale)
+    k = rng.standard_normal((B, Sk, Hkv, D), dtype=f)
+    v = rng.standard_normal((B, Sk, Hkv, D), dtype=f)
+    do = rng.standard_normal((B, S, Hq, D), dtype=f)
+    sink = None
+    if sink_mode == "learnable":
+        sink = rng.standard_normal(Hq, dtype=f) * f(5.0)
+    b = rng.standard_normal((B, Hq, S, Sk), dtype=f) * f(0.5) if bias else None
+    seg = None
+    if segments is not None:
+        seg = np.zeros((B, S), dtype=np.int32)
+        for bb in range(B):
+            for c in segments[bb % len(segments)]:
+                seg[bb, c:] += 1
+    if dtype == "bf16":
+        q, k, v, do = (W.round_to_bf16(x) for x in (q, k, v, do))
+        if b is not None:
+            b = W.round_to_bf16(b)
+    return dict(dtype=dtype, q=q, k=k, v=v, dout=do, sink=sink, sink_mode=sink_mode, bias=b, segment_ids=seg,
+                causal=causal, window=window, softcap=softcap)
+
+
+def run_gpu(c, backward=True, thd=False):
+    import attention_tanh_logit_amd as A
+    dt = c["dtype"]
+    q, k, v = (to_dev(c[n], dt) for n in ("q", "k", "v"))
+    kw = dict(causal=c["causal"], window=c["window"], softcap=c["softcap"], sink_mode=c["sink_mode"])
+    if c["sink"] is not None:
+        kw["sink"] = torch.from_numpy(c["sink"]).cuda()
+    if c["bias"] is not None:
+        kw["bias"] = to_dev(c["bias"], dt)
+    if thd:
+        cu = W.cu_seqlens_from_segments(c["segment_ids"])
+        kw["cu_seqlens"] = torch.from_numpy(cu).cuda()
+        q, k, v = (x.reshape(-1, *x.shape[2:]) for x in (q, k, v))
+    elif c["segment_ids"] is not None:
+        kw["segment_ids"] = torch.from_numpy(c["segment_ids"]).cuda()
+    out, lse = A.attn_fwd(q, k, v, **kw)
+    res = {"out": out, "lse": lse}
+    if backward:
+        do = to_dev(c["dout"], dt)
+        if thd:
+            do = do.reshape(-1, *do.shape[2:])
+        dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, **kw)
+        res.update(dq=dq, dk=dk, dv=dv, dbias=dbias, dsink=dsink)
+    torch.cuda.synchronize()
+    res = {n: (None if t is None else t.float().cpu().numpy()) for n, t in res.items()}
+    if thd:  # back to the BSHD view of the same rows
+        B, S = c["q"].shape[:2]
+        for n in ("out", "dq", "dk", "dv"):
+            if res.get(n) is not None:
+                res[n] = res[n].reshape(B, S, *res[n].shape[1:])
+        res["lse"] = res["lse"].reshape(-1, B, S).transpose(1, 0, 2)
+    return res
+
+
+def run_oracle(c, backward=True, groups=None):
+    kw = dict(causal=c["causal"], window=c["window"], softcap=c["softcap"], bias=c["bias"],
+              segment_ids=c["segment_ids"], sink=c["sink"] if c["sink_mode"] == "learnable"
+              else (np.zeros(c["q"].shape[2]) if c["sink_mode"] == "off_by_one" else None), groups=groups)
+    out, lse = attention_forward(c["q"], c["k"], c["v"], **kw)
+    res = {"out": out, "lse": lse}
+    if backward:
+        dq, dk, dv, dbias, dsink = attention_backward(c["q"], c["k"], c["v"], c["dout"], **kw)
+        res.update(dq=dq, dk=dk, dv=dv, dbias=dbias, dsink=dsink if c["sink_mode"] == "learnable" else None)
+    return res
+
+
+def compare(gpu, ref, dtype, names=("out", "lse", "dq", "dk", "dv", "dbias", "dsink")):
+    """Normwise errors per tensor; returns {name: err}."""
+    errs = {}
+    for n in names:
+        if ref.get(n) is None:
+            assert gpu.get(n) is None, f"{n}: GPU produced a tensor the oracle did not"
+            continue
+        g = gpu[n]
+        r = ref[n]
+        assert g.shape == r.shape, f"{n}: shape {g.shape} vs {r.shape}"
+        errs[n] = rel_err(g, r)
+    return errs

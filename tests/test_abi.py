@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+fails closed on bad arguments (status code and message, nothing launched).
+
+``attn_validate`` touches no device memory, so these run on the CPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_tanh_logit_amd as A
+from attention_tanh_logit_amd.ops import AttnArgs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn_softcap.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:attn_status|size_t|const char\*)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(A.ops.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = A.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def _args(**kw):
+    a = AttnArgs()
+    a.dtype, a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.D = 0, 2, 256, 256, 8, 2, 128
+    a.q = a.k = a.v = 0x1000
+    a.causal, a.window, a.softcap, a.scale, a.sink_mode = 1, 0, 30.0, 0.0, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _status(a):
+    L = A.lib()
+    s = L.attn_validate(ctypes.byref(a))
+    return s, L.attn_last_error().decode()
+
+
+def test_valid_arguments_pass():
+    assert _status(_args()) == (0, "")
+    assert _status(_args(sink_mode=1)) == (0, "")
+    assert _status(_args(sink_mode=2, sink=0x2000))[0] == 0
+    assert _status(_args(causal=0, Sk=300))[0] == 0
+
+
+BAD = {
+    "negative_softcap": (dict(softcap=-1.0), 1, "softcap"),
+    "nan_softcap": (dict(softcap=float("nan")), 1, "softcap"),
+    "inf_softcap": (dict(softcap=float("inf")), 1, "softcap"),
+    "gqa_not_divisible": (dict(Hq=6, Hkv=4), 1, "multiple"),
+    "head_dim_unsupported": (dict(D=96), 2, "head dim"),
+    "learnable_without_sink": (dict(sink_mode=2), 1, "sink"),
+    "sink_without_mode": (dict(sink=0x2000), 1, "sink"),
+    "off_by_one_with_logits": (dict(sink_mode=1, sink=0x2000), 1, "sink"),
+    "bad_sink_mode": (dict(sink_mode=7), 1, "sink_mode"),
+    "causal_lengths_differ": (dict(Sk=300), 2, "causal"),
+    "segments_and_cu_seqlens": (dict(segment_ids=0x3000, cu_seqlens=0x4000, nseq=2), 1, "not both"),
+    "cu_seqlens_batch": (dict(cu_seqlens=0x4000, nseq=2), 1, "B == 1"),
+    "cu_seqlens_empty": (dict(B=1, cu_seqlens=0x4000, nseq=0), 1, "nseq"),
+    "segments_lengths_differ": (dict(causal=0, Sk=300, segment_ids=0x3000), 1, "Sq == Sk"),
+    "bad_dtype": (dict(dtype=5), 1, "dtype"),
+    "null_q": (dict(q=None), 1, "NULL"),
+    "negative_scale": (dict(scale=-0.1), 1, "scale"),
+    "zero_heads": (dict(Hkv=0), 1, "Hkv"),
+}
+
+
+@pytest.mark.parametrize("name", list(BAD))
+def test_bad_arguments_fail_closed(name):
+    kw, code, word = BAD[name]
+    s, msg = _status(_args(**kw))
+    assert s == code, (s, msg)
+    assert word.lower() in msg.lower(), msg
+
+
+def test_workspace_sizes():
+    L = A.lib()
+    a = _args()
+    assert L.attn_fwd_workspace_size(ctypes.byref(a)) == 0
+    assert L.attn_bwd_workspace_size(ctypes.byref(a)) >= 2 * 8 * 256 * 4
+    a = _args(segment_ids=0x3000)
+    assert L.attn_fwd_workspace_size(ctypes.byref(a)) >= 2 * 2 * 256 * 4
+    a = _args(D=96)
+    assert L.attn_fwd_workspace_size(ctypes.byref(a)) == ctypes.c_size_t(-1).value
+
+
+def test_fwd_rejects_before_any_launch():
+    """A failing call returns its status without touching the (bogus) pointers."""
+    L = A.lib()
+    a = _args(softcap=-3.0)
+    s = L.attn_fwd(ctypes.byref(a), 0x10, 0x20, None, 0, None)
+    assert s == 1
+    a = _args(sink_mode=2, sink=0x2000)
+    s = L.attn_bwd(ctypes.byref(a), 0x10, 0x20, 0x30, 0x40, 0x50, 0x60, None, None, None, 1 << 30, None)
+    assert s == 1 and "dsink" in L.attn_last_error().decode()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import attention_tanh_logit_amd.ops as ops
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.lib()

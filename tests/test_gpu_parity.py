@@ -1,0 +1,99 @@
+"""GPU parity against the fp64 oracle at sizes that span several tiles with ragged tails.
+
+Every case compares out, lse, dq, dk, dv (and dbias, dsink when present)
+element by element with the oracle run on the same (bf16-rounded) inputs;
+the bar is the normwise error max|x - ref| / max|ref| <= 1e-5 (fp32 path) or
+1e-2 (bf16 path).
+"""
+import numpy as np
+import pytest
+
+from harness import TOL, case, compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(c, thd=False, backward=True):
+    print(f"case: dtype={c['dtype']} q={c['q'].shape} k={c['k'].shape} causal={c['causal']} window={c['window']} "
+          f"cap={c['softcap']} sink={c['sink_mode']} bias={c['bias'] is not None} "
+          f"seg={c['segment_ids'] is not None} thd={thd}", flush=True)
+    gpu = run_gpu(c, backward=backward, thd=thd)
+    ref = run_oracle(c, backward=backward)
+    errs = compare(gpu, ref, c["dtype"])
+    print("errors:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL[c["dtype"]]}
+    assert not bad, f"over tolerance {TOL[c['dtype']]}: {bad}"
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+def test_causal_gqa_cap(dtype, D):
+    _check(case(dtype=dtype, D=D, B=2, S=200, Hq=4, Hkv=2, softcap=30.0, q_scale=4.0))
+
+
+FEATURES = {
+    "window": dict(window=37),
+    "segments": dict(segments=[[45, 70, 190], [128]]),
+    "bias": dict(bias=True, softcap=50.0),
+    "sink_learnable": dict(sink_mode="learnable"),
+    "sink_off_by_one": dict(sink_mode="off_by_one"),
+    "no_causal": dict(causal=False),
+    "no_cap": dict(softcap=0.0),
+    "bias_and_sink": dict(bias=True, sink_mode="learnable", softcap=20.0),
+    "gqa_packing_window": dict(Hq=6, Hkv=2, segments=[[13, 100], [77, 78, 150]], window=50),
+    "everything": dict(Hq=8, Hkv=2, segments=[[60, 61, 131]], window=40, bias=True, sink_mode="learnable"),
+    "noncausal_window_segments": dict(causal=False, window=29, segments=[[99]]),
+    "mqa": dict(Hq=4, Hkv=1),
+}
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+@pytest.mark.parametrize("feat", list(FEATURES))
+def test_feature_matrix(dtype, D, feat):
+    kw = dict(dtype=dtype, D=D, B=2, S=203, Hq=4, Hkv=2)
+    kw.update(FEATURES[feat])
+    _check(case(**kw))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_cross_attention_lengths_differ(dtype):
+    _check(case(dtype=dtype, D=64, B=1, S=77, Sk=301, causal=False, Hq=2, Hkv=1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_thd_varlen_matches_oracle(dtype):
+    c = case(dtype=dtype, D=128, B=2, S=160, segments=[[7, 64, 65, 130], [100]], sink_mode="learnable")
+    _check(c, thd=True)
+
+
+def test_thd_equals_segment_ids_bitwise():
+    c = case(dtype="bf16", D=64, B=2, S=192, segments=[[50, 51, 120], [64, 128]])
+    a = run_gpu(c)
+    b = run_gpu(c, thd=True)
+    for n in ("out", "dq", "dk", "dv"):
+        assert np.array_equal(a[n].reshape(b[n].shape), b[n]), n
+
+
+def test_single_token_and_tiny_lengths():
+    for S in (1, 2, 31, 33):
+        _check(case(dtype="fp32", D=64, B=1, S=S, Hq=2, Hkv=1))
+
+
+def test_large_logits_cap_saturates_without_nan():
+    """Pre-cap logits of several hundred, cap 30: no overflow in the 1 - t^2 factor."""
+    c = case(dtype="fp32", D=64, B=1, S=150, Hq=2, Hkv=2, q_scale=60.0, softcap=30.0, window=20,
+             segments=[[70]])
+    errs = _check(c)
+    assert all(np.isfinite(v) for v in errs.values())
+
+
+def test_fully_masked_rows_give_zero_and_minus_inf():
+    """Non-causal window with Sq > Sk: late rows see no key."""
+    c = case(dtype="fp32", D=64, B=1, S=96, Sk=32, causal=False, window=40, Hq=2, Hkv=1)
+    gpu = run_gpu(c)
+    ref = run_oracle(c)
+    assert np.all(gpu["out"][0, 72:] == 0.0)
+    assert np.all(np.isneginf(gpu["lse"][0, :, 72:]))
+    errs = compare(gpu, ref, "fp32")
+    assert all(v <= TOL["fp32"] for v in errs.values()), errs
