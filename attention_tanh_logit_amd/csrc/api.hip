@@ -236,22 +236,32 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* workspace,
   return ATTN_OK;
 }
 
-attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, const void* dout, void* dq, void* dk,
-                     void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes, void* stream) {
+// The three backward phases share one workspace: segment runs, delta and
+// the sink-gradient partials are written by the pre-pass and read by the
+// dq and dk/dv kernels.
+enum { kPhasePre = 1, kPhaseDq = 2, kPhaseDkdv = 4 };
+
+static attn_status bwd_impl(const attn_args* a, const void* out, const float* lse, const void* dout, void* dq,
+                            void* dk, void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes,
+                            void* stream, int phases) {
   g_err.clear();
   attn_status st = validate(a);
   if (st != ATTN_OK) return st;
   if (dbias && !a->bias) return fail(ATTN_INVALID_ARGUMENT, "dbias requested without a bias");
-  if (a->sink_mode == ATTN_SINK_LEARNABLE && !dsink)
-    return fail(ATTN_INVALID_ARGUMENT, "LEARNABLE sink needs dsink [Hq] for its gradient");
-  if (a->sink_mode != ATTN_SINK_LEARNABLE && dsink)
-    return fail(ATTN_INVALID_ARGUMENT, "dsink given but the sink is not LEARNABLE");
+  if (phases & kPhasePre) {
+    if (a->sink_mode == ATTN_SINK_LEARNABLE && !dsink)
+      return fail(ATTN_INVALID_ARGUMENT, "LEARNABLE sink needs dsink [Hq] for its gradient");
+    if (a->sink_mode != ATTN_SINK_LEARNABLE && dsink)
+      return fail(ATTN_INVALID_ARGUMENT, "dsink given but the sink is not LEARNABLE");
+  }
   const size_t need = bwd_ws(a);
   if (workspace_bytes < need || (need && !workspace))
     return fail(ATTN_INVALID_ARGUMENT, "workspace smaller than attn_bwd_workspace_size");
-  if ((size_t)a->B * (a->Sq + a->Sk) * a->Hq == 0) return ATTN_OK;
-  if (!out || !lse || !dout || !dq || !dk || !dv)
-    return fail(ATTN_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv must not be NULL");
+  if ((size_t)a->B * (a->Sq + a->Sk) == 0) return ATTN_OK;
+  if (!lse || !dout) return fail(ATTN_INVALID_ARGUMENT, "lse and dout must not be NULL");
+  if ((phases & kPhasePre) && !out) return fail(ATTN_INVALID_ARGUMENT, "out must not be NULL");
+  if ((phases & kPhaseDq) && !dq) return fail(ATTN_INVALID_ARGUMENT, "dq must not be NULL");
+  if ((phases & kPhaseDkdv) && (!dk || !dv)) return fail(ATTN_INVALID_ARGUMENT, "dk and dv must not be NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   BwdParams p;
@@ -266,8 +276,16 @@ attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, cons
   p.dv = dv;
   p.dbias = dbias;
   p.mask = base_mask(a);
-  hipError_t e = prep_segments(a, ws, p.mask, s);
-  if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
+  hipError_t e = hipSuccess;
+  if (phases & kPhasePre) {
+    e = prep_segments(a, ws, p.mask, s);
+    if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
+  } else if (has_segments(a)) {
+    const size_t n = align_up((size_t)a->B * a->Sq * sizeof(int));
+    p.mask.seg_lo = reinterpret_cast<int*>(ws);
+    p.mask.seg_hi = reinterpret_cast<int*>(ws + n);
+    ws += 2 * n;
+  }
   float* delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));
   float* part = nullptr;
@@ -281,28 +299,54 @@ attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, cons
   const Launch l{a->B, a->Sq, a->Sk, s};
   const TypeOps& o = ops(a);
   const bool cap = a->softcap > 0.0f, bias = a->bias != nullptr;
-  if (a->Sq > 0) {
-    e = o.pre(a->D, out, dout, lse, delta, part, a->sink, a->sink_mode, a->Hq, kPreRows, l);
-    if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
+  if (phases & kPhasePre) {
+    if (a->Sq > 0) {
+      e = o.pre(a->D, out, dout, lse, delta, part, a->sink, a->sink_mode, a->Hq, kPreRows, l);
+      if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
+    }
     if (part) {
       dsink_final_kernel<<<a->Hq, 256, 0, s>>>(part, dsink, (int)(a->B * pre_blocks(a)));
       e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(e, "sink gradient launch");
     }
-    if (dbias) {
+    if (dbias && a->Sq > 0 && a->Sk > 0) {
       e = o.dbias_fill(dbias, p.mask, a->Hq, kFillRows, l);
       if (e != hipSuccess) return hip_fail(e, "dbias fill launch");
     }
+  }
+  if ((phases & kPhaseDq) && a->Sq > 0) {
     e = o.dq(a->D, cap, bias, p, l);
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
-  } else if (part) {
-    dsink_final_kernel<<<a->Hq, 256, 0, s>>>(part, dsink, 0);
   }
-  if (a->Sk > 0) {
+  if ((phases & kPhaseDkdv) && a->Sk > 0) {
     e = o.dkdv(a->D, cap, bias, p, l);
     if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
   }
   return ATTN_OK;
+}
+
+attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                     void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(a, out, lse, dout, dq, dk, dv, dbias, dsink, workspace, workspace_bytes, stream,
+                  kPhasePre | kPhaseDq | kPhaseDkdv);
+}
+
+attn_status attn_bwd_pre(const attn_args* a, const void* out, const float* lse, const void* dout, void* dbias,
+                         float* dsink, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(a, out, lse, dout, nullptr, nullptr, nullptr, dbias, dsink, workspace, workspace_bytes, stream,
+                  kPhasePre);
+}
+
+attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, void* dq, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return bwd_impl(a, nullptr, lse, dout, dq, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+                  kPhaseDq);
+}
+
+attn_status attn_bwd_dkdv(const attn_args* a, const float* lse, const void* dout, void* dk, void* dv, void* dbias,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(a, nullptr, lse, dout, nullptr, dk, dv, dbias, nullptr, workspace, workspace_bytes, stream,
+                  kPhaseDkdv);
 }
 
 }  // extern "C"

@@ -39,7 +39,7 @@ class AttnArgs(ctypes.Structure):
 
 
 EXPORTS = ("attn_validate", "attn_fwd_workspace_size", "attn_bwd_workspace_size",
-           "attn_fwd", "attn_bwd", "attn_last_error")
+           "attn_fwd", "attn_bwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv", "attn_last_error")
 
 _lib = None
 
@@ -70,6 +70,12 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = ctypes.c_int
     L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd.restype = ctypes.c_int
+    L.attn_bwd_pre.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd_pre.restype = ctypes.c_int
+    L.attn_bwd_dq.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd_dq.restype = ctypes.c_int
+    L.attn_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd_dkdv.restype = ctypes.c_int
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -168,8 +174,13 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
 
 
 def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
-             softcap=0.0, scale=0.0, sink_mode="none", sink=None, want_dbias=None):
-    """Backward: returns (dq, dk, dv, dbias or None, dsink or None)."""
+             softcap=0.0, scale=0.0, sink_mode="none", sink=None, want_dbias=None, events=None):
+    """Backward: returns (dq, dk, dv, dbias or None, dsink or None).
+
+    With ``events`` (four torch.cuda.Event) the three phases are launched
+    through their own entry points with an event recorded before the
+    pre-pass and after each phase, on the current stream.
+    """
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink)
@@ -187,6 +198,18 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
     dsink = torch.empty(a.Hq, dtype=torch.float32, device=q.device) if sink_mode == "learnable" else None
     nws = L.attn_bwd_workspace_size(ctypes.byref(a))
     ws = _workspace(nws, q.device)
-    _check(L.attn_bwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                      _ptr(dbias), _ptr(dsink), _ptr(ws), nws, _stream(q)))
+    st = _stream(q)
+    if events is None:
+        _check(L.attn_bwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(dbias), _ptr(dsink), _ptr(ws), nws, st))
+    else:
+        events[0].record()
+        _check(L.attn_bwd_pre(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dbias), _ptr(dsink),
+                              _ptr(ws), nws, st))
+        events[1].record()
+        _check(L.attn_bwd_dq(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(ws), nws, st))
+        events[2].record()
+        _check(L.attn_bwd_dkdv(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv), _ptr(dbias),
+                               _ptr(ws), nws, st))
+        events[3].record()
     return dq, dk, dv, dbias, dsink

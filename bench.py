@@ -1,0 +1,225 @@
+#!/usr/bin/env python
+"""Benchmark: fused soft-capped attention forward + backward on one MI355X.
+
+One step = the whole hot path on one batch: attn_fwd (forward kernel) then
+the backward's three phases (pre-pass, dq kernel, dk/dv kernel), all on the
+current stream with inputs already resident in HBM.  Prints ONE JSON line.
+
+Throughput counts algorithmic work only: 4*D flop per visible (query, key)
+pair in the forward and 10*D in the backward (14*D per step), summed over
+batch rows and query heads; masked pairs, partial-tile waste and the dq
+kernel's recomputation earn nothing.
+
+  python bench.py [--steps K] [--warmup W] [--workload causal_gqa] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix, published
+CLOCK_PEAK_BF16 = 256 * 4096 * 2.4e9 / 1e12   # 256 CUs x 4096 flop/clk x 2.4 GHz
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(w, seg=None) -> int:
+    """Visible (query, key) pairs per (batch row, query head), summed over batch rows."""
+    S, W = w.S, w.window
+    if seg is not None:
+        total = 0
+        for b in range(seg.shape[0]):
+            _, counts = __import__("numpy").unique(seg[b], return_counts=True)
+            for L in counts:
+                L = int(L)
+                total += sum(min(i + 1, W) for i in range(L)) if W > 0 else L * (L + 1) // 2
+        return total
+    per_row = sum(min(i + 1, W) for i in range(S)) if (w.causal and W > 0) else (
+        S * (S + 1) // 2 if w.causal else S * S)
+    return per_row * w.B
+
+
+def workload(name):
+    import workloads as W
+    table = {
+        "causal_gqa": W.causal_gqa(30.0),
+        "sink_gqa": W.sink_gqa("learnable", 30.0),
+        "window_d256": W.window_large_d(256, "bf16"),
+        "window_d512": W.window_large_d(512, "bf16"),
+        "window_d256_fp32": W.window_large_d(256, "fp32"),
+        "window_d512_fp32": W.window_large_d(512, "fp32"),
+        "packed_varlen": W.packed_varlen(),
+        "tiny": W.tiny_fp32(),
+    }
+    return table[name]
+
+
+def to_gpu(w, d):
+    import numpy as np
+    import torch
+    import workloads as W
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)  # noqa: E731
+    g = {"q": t(d["q"]), "k": t(d["k"]), "v": t(d["v"]), "dout": t(d["dout"])}
+    kw = dict(causal=w.causal, window=w.window, softcap=w.softcap, sink_mode=w.sink_mode)
+    if d["sink"] is not None and w.sink_mode == "learnable":
+        kw["sink"] = torch.from_numpy(d["sink"]).cuda()
+    if d["segment_ids"] is not None:
+        kw["segment_ids"] = torch.from_numpy(d["segment_ids"]).cuda()
+    if w.bias_std > 0:
+        bias = torch.empty((w.B, w.Hq, w.S, w.S), dtype=dt, device="cuda")
+        for b in range(w.B):
+            for h in range(w.Hq):
+                bias[b, h] = t(W.bias_slab(w, b, h))
+        kw["bias"] = bias
+    return g, kw
+
+
+def run_steps(g, kw, steps, warmup):
+    """Warm up, then time exactly `steps` steps; returns (ms_per_step, per-phase ms)."""
+    import torch
+    import attention_tanh_logit_amd as A
+    for _ in range(warmup):
+        out, lse = A.attn_fwd(g["q"], g["k"], g["v"], **kw)
+        A.attn_bwd(g["q"], g["k"], g["v"], out, lse, g["dout"], **kw)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        e = ev[s]
+        e[0].record()
+        out, lse = A.attn_fwd(g["q"], g["k"], g["v"], **kw)
+        e[1].record()
+        A.attn_bwd(g["q"], g["k"], g["v"], out, lse, g["dout"], events=e[2:6], **kw)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = {"fwd": 0.0, "bwd_pre": 0.0, "dq": 0.0, "dkdv": 0.0}
+    for e in ev:
+        ph["fwd"] += e[0].elapsed_time(e[1])
+        ph["bwd_pre"] += e[2].elapsed_time(e[3])
+        ph["dq"] += e[3].elapsed_time(e[4])
+        ph["dkdv"] += e[4].elapsed_time(e[5])
+    return wall * 1e3 / steps, {k: v / steps for k, v in ph.items()}
+
+
+def cpu_baseline(w, d, budget_s=30.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample: whole (b, kv-head) groups."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import group_backward, group_forward
+    G = w.G
+    sink = d["sink"]
+    seg = d["segment_ids"]
+    done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    groups = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    for b, h in groups:
+        hs = slice(h * G, (h + 1) * G)
+        kw = dict(softcap=w.softcap, causal=w.causal, window=w.window,
+                  seg=None if seg is None else seg[b],
+                  sink=None if w.sink_mode == "none" else (sink[hs] if sink is not None else np.zeros(G)))
+        q, k, v, do = d["q"][b, :, hs], d["k"][b, :, h], d["v"][b, :, h], d["dout"][b, :, hs]
+        group_forward(q, k, v, **kw)
+        group_backward(q, k, v, do, **kw)
+        done += 1
+        one = w.with_(B=1)
+        flops += 14.0 * w.D * visible_pairs(one, None if seg is None else seg[b:b + 1]) * G
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(groups)} (batch row, KV head) groups ({done * G} query heads x {w.S} rows), "
+                      f"fp64 NumPy forward+backward, {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_gqa")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cap-ratio", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path here has no "
+              f"multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import attention_tanh_logit_amd as A
+    A.lib()
+    w = workload(args.workload)
+    log(f"[bench] workload {w.name}: drawing inputs")
+    d = W.draw(w)
+    g, kw = to_gpu(w, d)
+    pairs = visible_pairs(w, d["segment_ids"]) * w.Hq
+    flop_fwd = 4.0 * w.D * pairs
+    flop_bwd = 10.0 * w.D * pairs
+    flop_step = flop_fwd + flop_bwd
+    per_kernel_flop = {"fwd": 4.0 * w.D * pairs, "dq": 6.0 * w.D * pairs, "dkdv": 8.0 * w.D * pairs}
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    ms, ph = run_steps(g, kw, args.steps, args.warmup)
+    log(f"[bench] {ms:.3f} ms/step  phases {ph}")
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    value = flop_step / (ms * 1e-3) / 1e12
+    fwd_tflops = flop_fwd / (ph["fwd"] * 1e-3) / 1e12
+    bwd_ms = ph["bwd_pre"] + ph["dq"] + ph["dkdv"]
+
+    cap_ratio = None
+    if not args.no_cap_ratio and w.softcap > 0:
+        kw0 = dict(kw, softcap=0.0)
+        ms0, ph0 = run_steps(g, kw0, args.steps, 1)
+        bwd0 = ph0["bwd_pre"] + ph0["dq"] + ph0["dkdv"]
+        cap_ratio = {"fwd": ph["fwd"] / ph0["fwd"], "bwd": bwd_ms / bwd0,
+                     "fwd_bwd": (ph["fwd"] + bwd_ms) / (ph0["fwd"] + bwd0),
+                     "uncapped_ms_per_step": ms0}
+        log(f"[bench] uncapped {ms0:.3f} ms/step; cap ratio {cap_ratio}")
+
+    dom = max(("fwd", "dq", "dkdv"), key=lambda k: ph[k])
+    achieved = per_kernel_flop[dom] / (ph[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None,
+                "flop_per_launch": per_kernel_flop[dom], "avg_launch_ms": ph[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, d)
+        log(f"[bench] cpu baseline {cpu}")
+
+    line = {
+        "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak; capped/uncapped time ratio",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32", "data": "synthetic (seeded, workloads.py)",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "causal": w.causal, "window": w.window, "softcap": w.softcap, "sink": w.sink_mode,
+                   "bias": w.bias_std > 0, "packed": w.n_segments is not None},
+        "frac_of_peak": value / peak,
+        "fwd_tflops": fwd_tflops, "fwd_frac_of_peak": fwd_tflops / peak,
+        "bwd_tflops": flop_bwd / (bwd_ms * 1e-3) / 1e12,
+        "kernel_ms": ph, "cap_ratio": cap_ratio,
+        "peak_tflops": peak, "peak_tflops_from_clock": CLOCK_PEAK_BF16 if w.dtype == "bf16" else None,
+        "algorithmic_flop_per_step": flop_step, "visible_pairs": pairs,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -127,6 +127,24 @@ attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, cons
                      void* dq, void* dk, void* dv, void* dbias, float* dsink,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same backward in three phases, for callers that time or overlap them
+ * (attn_bwd == pre, then dq and dkdv).  All three take the same arguments and
+ * the same workspace, which carries the pre-pass results (segment runs,
+ * delta = rowsum(dout * out), sink-gradient partials) to the other two, so
+ * it must stay untouched between them; dq and dkdv only read it and may run
+ * concurrently on two streams once pre has finished.
+ *  - attn_bwd_pre:  segment runs, delta, dsink (required iff LEARNABLE) and
+ *                   the zeros of dbias on the masked pairs (dbias nullable);
+ *  - attn_bwd_dq:   dq;
+ *  - attn_bwd_dkdv: dk, dv and dbias on the visible pairs (dbias nullable,
+ *                   complete only together with attn_bwd_pre). */
+attn_status attn_bwd_pre(const attn_args* a, const void* out, const float* lse, const void* dout,
+                         void* dbias, float* dsink, void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, void* dq,
+                        void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_bwd_dkdv(const attn_args* a, const float* lse, const void* dout, void* dk, void* dv,
+                          void* dbias, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* attn_last_error(void);
 

@@ -25,9 +25,11 @@ import numpy as np
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    # finite inputs stay below 0xFF800000, so adding at most 0x8000 cannot wrap
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(x.shape)
 
 
 @dataclasses.dataclass
