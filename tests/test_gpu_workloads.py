@@ -1,0 +1,92 @@
+"""Full-size parity for every sub-run of the five workloads, in the launch
+configuration bench.py times.
+
+The GPU runs the whole problem; the fp64 oracle recomputes whole
+(batch row, KV head) groups -- every query row, key and head of the group --
+and the two are compared element by element on those groups (normwise error
+max|x - ref| / max|ref| per tensor, 1e-5 for the fp32 path, 1e-2 for bf16).
+The sink gradient is checked where the sampled groups cover every batch row
+of a head (B = 1 workloads).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from harness import TOL, rel_err
+from oracle import group_backward, group_forward, visibility
+
+pytestmark = pytest.mark.gpu
+
+SUBRUNS = {w.name: w for w in W.all_workloads()}
+
+
+def _groups(w):
+    """Sampled (b, kv_head) groups: the last one (longest causal rows) and the first."""
+    last = (w.B - 1, w.Hkv - 1)
+    return [last] if last == (0, 0) else [last, (0, 0)]
+
+
+@pytest.mark.parametrize("name", list(SUBRUNS))
+def test_workload_matches_oracle_on_sampled_groups(name):
+    import attention_tanh_logit_amd as A
+    w = SUBRUNS[name]
+    print(f"workload {name}: drawing", flush=True)
+    d = W.draw(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)  # noqa: E731
+    q, k, v, do = t(d["q"]), t(d["k"]), t(d["v"]), t(d["dout"])
+    kw = dict(causal=w.causal, window=w.window, softcap=w.softcap, sink_mode=w.sink_mode)
+    if w.sink_mode == "learnable":
+        kw["sink"] = torch.from_numpy(d["sink"]).cuda()
+    seg = d["segment_ids"]
+    if seg is not None:
+        kw["segment_ids"] = torch.from_numpy(seg).cuda()
+    groups = _groups(w)
+    slabs = {}
+    if w.bias_std > 0:
+        bias = torch.empty((w.B, w.Hq, w.S, w.S), dtype=dt, device="cuda")
+        for b in range(w.B):
+            for h in range(w.Hq):
+                s = W.bias_slab(w, b, h)
+                bias[b, h] = t(s)
+                if (b, h // w.G) in groups:
+                    slabs[(b, h)] = s
+        kw["bias"] = bias
+    print(f"workload {name}: GPU forward + backward", flush=True)
+    out, lse = A.attn_fwd(q, k, v, **kw)
+    dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, **kw)
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+    G = w.G
+    for (b, hk) in groups:
+        hs = slice(hk * G, (hk + 1) * G)
+        print(f"workload {name}: oracle on group b={b} kv_head={hk}", flush=True)
+        okw = dict(softcap=w.softcap, causal=w.causal, window=w.window, seg=None if seg is None else seg[b],
+                   sink=None if w.sink_mode == "none" else (d["sink"][hs] if w.sink_mode == "learnable"
+                                                            else np.zeros(G)))
+        bg = None
+        if w.bias_std > 0:
+            bg = np.stack([slabs[(b, h)] for h in range(hk * G, (hk + 1) * G)])
+        qg, kg, vg, dog = d["q"][b, :, hs], d["k"][b, :, hk], d["v"][b, :, hk], d["dout"][b, :, hs]
+        ro, rl = group_forward(qg, kg, vg, bias=bg, **okw)
+        rq, rk, rv, rb, rs = group_backward(qg, kg, vg, dog, bias=bg, **okw)
+        f = lambda x: x.float().cpu().numpy()  # noqa: E731
+        errs = {
+            "out": rel_err(f(out[b, :, hs]), ro), "lse": rel_err(f(lse[b, hs]), rl),
+            "dq": rel_err(f(dq[b, :, hs]), rq), "dk": rel_err(f(dk[b, :, hk]), rk),
+            "dv": rel_err(f(dv[b, :, hk]), rv),
+        }
+        if dbias is not None:
+            gb = f(dbias[b, hs])
+            errs["dbias"] = rel_err(gb, rb)
+            # exact zeros wherever the pair is masked (no leakage across segments)
+            vis = visibility(w.S, w.S, w.causal, w.window, None if seg is None else seg[b],
+                             None if seg is None else seg[b])
+            assert np.all(gb[:, ~vis] == 0.0), f"{name}: nonzero dbias on masked pairs"
+        if dsink is not None and w.B == 1:
+            errs["dsink"] = rel_err(dsink[hs].cpu().numpy(), rs)
+        print(f"workload {name} group ({b},{hk}) errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+              flush=True)
+        bad = {k: v for k, v in errs.items() if not v <= tol}
+        assert not bad, f"{name}: over tolerance {tol}: {bad}"
