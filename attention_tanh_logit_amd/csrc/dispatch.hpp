@@ -9,7 +9,9 @@
 //   DC  head-dim columns staged in LDS at a time (DC == D: no chunking).
 #pragma once
 
-#include "kernels.hpp"
+#include <type_traits>
+
+#include "fast.hpp"
 
 namespace atl {
 
@@ -66,8 +68,18 @@ template <typename T, int D> constexpr int fwd_rows() { return 32 * FwdCfg<T, D>
 template <typename T, int D> constexpr int dq_rows() { return 32 * DqCfg<T, D>::NQG; }
 template <typename T, int D> constexpr int dkdv_keys() { return 32 * DkdvCfg<T, D>::NKG; }
 
+// bf16 with D <= 128 takes the pipelined kernels of fast.hpp
+template <typename T, int D> constexpr bool use_fast() { return std::is_same<T, bf16>::value && (D == 64 || D == 128); }
+
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
+  if constexpr (use_fast<T, D>()) {
+    if (!BIAS || (l.Sk % 8 == 0 && l.Sk >= 8)) {  // the fast path reads bias rows 8 keys at a time
+      const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
+      fwd_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      return hipGetLastError();
+    }
+  }
   using C = FwdCfg<T, D>;
   constexpr int BM = 32 * C::NQG;
   const dim3 grid((l.Sq + BM - 1) / BM, p.Hq, l.B);
@@ -78,6 +90,13 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
 
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dq(const BwdParams& p, const Launch& l) {
+  if constexpr (use_fast<T, D>()) {
+    if (!BIAS || (l.Sk % 8 == 0 && l.Sk >= 8)) {  // the fast path reads bias rows 8 keys at a time
+      const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
+      dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      return hipGetLastError();
+    }
+  }
   using C = DqCfg<T, D>;
   constexpr int BM = 32 * C::NQG;
   const dim3 grid((l.Sq + BM - 1) / BM, p.Hq, l.B);
@@ -88,6 +107,13 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
 
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
+  if constexpr (use_fast<T, D>()) {
+    if (!BIAS || (l.Sk % 8 == 0 && l.Sk >= 8)) {  // the fast path reads bias rows 8 keys at a time
+      const dim3 grid((l.Sk + 127) / 128, p.Hkv, l.B);
+      dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      return hipGetLastError();
+    }
+  }
   using C = DkdvCfg<T, D>;
   constexpr int BNK = 32 * C::NKG;
   const dim3 grid((l.Sk + BNK - 1) / BNK, p.Hkv, l.B);
