@@ -38,8 +38,14 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (needs ROCm)")
 
 
+# Per-unit extra flags.  The bf16 unit keeps MFMA accumulators in VGPR form:
+# its dk/dv kernel holds two 32x128 fp32 accumulators and, left to the
+# default heuristic, round-trips them through AGPRs on every tile.
+UNIT_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [_hipcc(), *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, *UNIT_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

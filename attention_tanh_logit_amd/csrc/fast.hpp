@@ -38,15 +38,24 @@ __device__ __forceinline__ int swp2(int a) { return ((a & 1) << 1) | ((a >> 1) &
 
 // ---------------------------------------------------------------- swizzled tiles
 //
-// Tile element (R, col) of a D-wide bf16 tile sits at R*D + 8*(col/8 ^ f(R)) +
-// col%8 with f(R) = 2*(R%4) + (R/4)%2.  Eight consecutive rows then map one
-// logical 16-byte slot to eight different bank groups (plain fragment reads),
-// and four consecutive rows map a 32-byte column pair to eight different bank
-// groups (transposing reads).
-__device__ __forceinline__ int swz_f(int R) { return 2 * (R & 3) + ((R >> 2) & 1); }
+// gfx950 LDS has 64 four-byte banks (256 bytes); a 16-byte read is serviced
+// 16 lanes at a time and an 8-byte read 32 lanes at a time, each group
+// conflict-free only if it touches distinct banks.  Tile element (R, col) of
+// a D-wide bf16 tile sits at R*D + 8*(col/8 ^ f(R)) + col%8, with f chosen so
+// that 16 consecutive rows put one logical 16-byte slot into 16 different bank
+// slots (plain fragment reads) and 4 consecutive rows x 64 bytes of columns
+// cover 32 different 8-byte bank pairs (transposing reads):
+//   D = 128 (256-byte rows):     f(R) = 4*(R%4) + (R/4)%4
+//   D = 64  (two rows per 256):  f(R) = 4*((R/2)%2) + (R/4)%4
+// Both have period 16 in R, so row offsets that are multiples of 16 are
+// plain constants.
+template <int D>
+__device__ __forceinline__ int swz_f(int R) {
+  return D >= 128 ? 4 * (R & 3) + ((R >> 2) & 3) : 4 * ((R >> 1) & 1) + ((R >> 2) & 3);
+}
 template <int D>
 __device__ __forceinline__ int sw_idx(int R, int col) {
-  return R * D + (((col >> 3) ^ swz_f(R)) << 3) + (col & 7);
+  return R * D + (((col >> 3) ^ swz_f<D>(R)) << 3) + (col & 7);
 }
 
 // Direct HBM -> LDS load of a ROWS x D tile.  global_load_lds writes lane i's
@@ -68,7 +77,7 @@ __device__ __forceinline__ void load_tile(bf16* lds, const bf16* g, long gstride
     const int R = p / CPR;
     const int s = p % CPR;
     const int grow = min(row0 + (PERM ? swp(R) : R), nvalid - 1);
-    const bf16* src = g + (long)grow * gstride + 8 * (s ^ swz_f(R));
+    const bf16* src = g + (long)grow * gstride + 8 * (s ^ swz_f<D>(R));
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + pw * 8), 16, 0, 0);
   }
 }
@@ -80,32 +89,64 @@ __device__ __forceinline__ v4i16 ds_tr16(const bf16* p) {
       (__attribute__((address_space(3))) v4i16*)(const_cast<bf16*>(p)));
 }
 
-// Plain A/B fragment: lane r + 32g holds tile row R, columns col0 + 8g .. +8.
-template <int D>
-__device__ __forceinline__ bf16x8 frag(const bf16* tile, int R, int col) {
-  return *reinterpret_cast<const bf16x8*>(tile + sw_idx<D>(R, col));
+// Per-lane fragment offsets of a swizzled tile.  With f(R) = 4*fa(R) + fb(R)
+// (fa, fb two-bit fields), XOR-ing a compile-time slot offset with f
+// separates into XORs on independent bit fields, so a read at a compile-time
+// (row, column block) is a per-lane base, one XOR with a constant and a
+// constant add -- a few registers instead of one per read.
+//
+// Plain fragment of contraction step cc at tile rows row0 + 0..31 (lane
+// r + 32g: row r, columns 16cc + 8g .. +8): slot 2cc + g ^ f(r).
+// Transposing fragment of output column block ob at rows row0 + ...: lane
+// r + 32g receives X[row0 + 8g + i][32ob + swp(r)], i = 0..7 (with ROWPERM
+// the tile's rows are stored through swp and the fragment still walks
+// logical rows row0 + 8g + i).  ds_read_b64_tr_b16 hands lane j of each
+// 16-lane group element j&3 of the 4-element chunk read by lane (j>>2) + 4e,
+// e = 0..3; each source lane's row and column group are chosen accordingly.
+// Hides an integer's known bits from the optimiser.  LDS offsets built from
+// it stay additions, which fold into the ds instruction's immediate offset
+// field (a buffer's base address included), instead of becoming disjoint ORs
+// that need one register per (buffer, fragment) pair.
+__device__ __forceinline__ int opaque(int x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
-// A fragment of X^T from the swizzled tile X: lane r + 32g receives
-// X[row0 + 8g + i][col0 + swp(r)] for i = 0..7 (COLPERM) or ...[col0 + r].
-// With ROWPERM the tile's rows are stored through swp (tile row swp(k) holds
-// logical row k) and the fragment still walks logical rows row0 + 8g + i.
-// ds_read_b64_tr_b16 hands lane j of each 16-lane group element j&3 of the
-// 4-element chunk read by lane (j>>2) + 4e, for e = 0..3; choosing each
-// source lane's row and column group accordingly yields the fragment.
-template <int D, bool COLPERM, bool ROWPERM>
-__device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int row0, int col0, int lane) {
-  const int G = lane >> 4;
-  const int s = lane & 15;
-  const int R = row0 + (ROWPERM ? 4 : 8) * (G >> 1) + (s >> 2);
-  const int c = col0 + 16 * (G & 1) + 4 * (COLPERM ? swp2(s & 3) : (s & 3));
-  const v4i16 a = ds_tr16(tile + sw_idx<D>(R, c));
-  const v4i16 b = ds_tr16(tile + sw_idx<D>(R + (ROWPERM ? 8 : 4), c));
-  bf16x8 r;
-  __builtin_memcpy(&r, &a, 8);
-  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
-  return r;
-}
+template <int D, bool ROWPERM>
+struct FragOfs {
+  static constexpr int NCC = D / 16;
+  static constexpr int NOB = D / 32;
+  int pbase;    // plain: row offset + the slot bits that do not move with cc
+  int pxor;     // plain: 16 * (f(r) >> 1), XOR-ed with 16 * cc
+  int tbase[2]; // transposing reads: everything but the column block
+  int txor;     // transposing reads: 32 * (slot-block bits of f), XOR-ed with 32 * ob
+  __device__ __forceinline__ explicit FragOfs(int lane) {
+    const int n = lane & 31, h = lane >> 5;
+    const int fn = swz_f<D>(n);
+    pbase = opaque(n * D + 8 * ((h ^ fn) & 1));
+    pxor = opaque(16 * (fn >> 1));
+    const int G = lane >> 4, s = lane & 15;
+    const int R = (ROWPERM ? 4 : 8) * (G >> 1) + (s >> 2);
+    const int R2 = R + (ROWPERM ? 8 : 4);
+    const int c = 16 * (G & 1) + 4 * swp2(s & 3);   // column inside a 32-column block
+    // slot (4 ob + c/8) ^ f(R) = 4 (ob ^ (f >> 2)) + ((c/8) ^ (f & 3)); f >> 2 agrees for R and R2
+    tbase[0] = opaque(R * D + 8 * (((c >> 3) ^ swz_f<D>(R)) & 3) + (c & 7));
+    tbase[1] = opaque(R2 * D + 8 * (((c >> 3) ^ swz_f<D>(R2)) & 3) + (c & 7));
+    txor = opaque(32 * (swz_f<D>(R) >> 2));
+  }
+  __device__ __forceinline__ bf16x8 frag(const bf16* tile, int row0, int cc) const {
+    return *reinterpret_cast<const bf16x8*>(tile + row0 * D + pbase + ((16 * cc) ^ pxor));
+  }
+  __device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int row0, int ob) const {
+    const int x = (32 * ob) ^ txor;
+    const v4i16 a = ds_tr16(tile + row0 * D + tbase[0] + x);
+    const v4i16 b = ds_tr16(tile + row0 * D + tbase[1] + x);
+    bf16x8 r;
+    __builtin_memcpy(&r, &a, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
+    return r;
+  }
+};
 
 // Log2-unit logit constants of the bf16 fast path (see the header comment).
 struct LogitK {
@@ -136,19 +177,67 @@ __device__ __forceinline__ float logit_fast(float x, float bias, const LogitK& k
 
 template <bool B> using bool_c = std::integral_constant<bool, B>;
 
+// Per-thread plan of a direct tile load: this thread's 16-byte chunk u sits
+// NT/(D/8) rows below chunk u-1 (a multiple of 16 rows, where swp and the
+// swizzle repeat), so one element offset off0 relative to the tile's first
+// global row serves every chunk, and issuing a full tile costs one add per
+// chunk (rows past the end take the clamped path, once per kernel at most).
+template <int ROWS, int D, int NT, bool PERM>
+struct TilePlan {
+  static constexpr int CPR = D / 8;
+  static constexpr int N = ROWS * CPR / NT;
+  static constexpr int RSTEP = NT / CPR;
+  static_assert((ROWS * CPR) % NT == 0 && RSTEP % 16 == 0, "tile must split evenly over the threads");
+  int off0;
+  __device__ __forceinline__ explicit TilePlan(long gstride) {
+    const int p = threadIdx.x;
+    const int R = p / CPR, s = p % CPR;
+    off0 = (PERM ? swp(R) : R) * (int)gstride + 8 * (s ^ swz_f<D>(R));
+  }
+  __device__ __forceinline__ void issue(bf16* lds, const bf16* g, long gstride, int row0, int nvalid) const {
+    const int w = threadIdx.x >> 6;
+    if (row0 + ROWS <= nvalid) {
+#pragma unroll
+      for (int u = 0; u < N; ++u) {
+        const bf16* base = g + (long)(row0 + u * RSTEP) * gstride;
+        __builtin_amdgcn_global_load_lds(base + off0, (__attribute__((address_space(3))) void*)(lds + (u * NT + w * 64) * 8),
+                                         16, 0, 0);
+      }
+    } else {
+      load_tile<ROWS, D, NT, PERM>(lds, g, gstride, row0, nvalid);
+    }
+  }
+};
+
 // ============================================================== forward
 
+// With PIPE the loop is software-pipelined over key tiles: while the softmax
+// of tile t runs on the VALU, the MFMAs of S_{t+1} = K_{t+1} Q^T are already
+// in flight (they sit in the same straight-line block, so the scheduler
+// interleaves them).  K tiles are then fetched two tiles ahead and V tiles
+// one ahead; two LDS buffers of each suffice.  The pipelined form holds two
+// score tiles, which fits the register file at D = 64 but not at D = 128.
+//
+// Capped logits are tracked through r = 1/(1 + 2^y) (s2 = c2 - 2 c2 r is
+// decreasing in r): the row maximum is c2 - 2 c2 min(r), and the probability
+// 2^(s2 - m) = 2^(fma(r, -2 c2, c2 - m)) needs no separate subtraction.
 template <int D, bool CAP, bool BIAS>
 __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
   constexpr int NT = 256;
   constexpr int BM = 128;
   constexpr int BN = 64;
+  constexpr bool PIPE = D <= 64;
+  constexpr bool ROWPERM_TR = false;  // V rows in key order
   constexpr int NKB = BN / 32;
   constexpr int NOB = D / 32;
   constexpr int NCC = D / 16;
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * D];
+  // two LDS buffers per tile as distinct objects: the compiler can then see
+  // that reading one never aliases the DMA filling the other
+  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
 
   const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
   const int hq = blockIdx.y;
@@ -162,10 +251,13 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
   const int q0 = qt * BM;
   const int i = q0 + w * 32 + n;
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
+  const FragOfs<D, ROWPERM_TR> fo(lane);
 
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
   const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
   const long kstride = (long)p.Hkv * D;
+  const TilePlan<BN, D, NT, true> kplan(kstride);
+  const TilePlan<BN, D, NT, false> vplan(kstride);
 
   int lo_i = 0, hi_i = 0;
   if (i < Sq) keys_of(p.mask, b, i, lo_i, hi_i);
@@ -194,35 +286,48 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
   for (int ob = 0; ob < NOB; ++ob) oacc[ob] = f32x16{};
 
   const int kbeg = (lo_first / BN) * BN;
-  if (kbeg < hi_last) {
-    load_tile<BN, D, NT, true>(sK[0], kbase, kstride, kbeg, Sk);
-    load_tile<BN, D, NT, false>(sV[0], vbase, kstride, kbeg, Sk);
-  }
-  wait_loads();
-  __syncthreads();
+  const int ntiles = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
 
-  int buf = 0;
-  for (int k0 = kbeg; k0 < hi_last; k0 += BN, buf ^= 1) {
-    if (k0 + BN < hi_last) {
-      load_tile<BN, D, NT, true>(sK[buf ^ 1], kbase, kstride, k0 + BN, Sk);
-      load_tile<BN, D, NT, false>(sV[buf ^ 1], vbase, kstride, k0 + BN, Sk);
-    }
-    const bf16* tK = sK[buf];
-    const bf16* tV = sV[buf];
-
-    // ---- S^T = K Q^T (tile row kb*32 + r holds key kb*32 + swp(r))
-    f32x16 sacc[NKB];
+  // S^T = K Q^T of the tile in LDS (tile row kb*32 + r holds key kb*32 + swp(r))
+  auto qk = [&](const bf16* tK, f32x16* s) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mma(sacc[kb], frag<D>(tK, kb * 32 + n, 16 * cc + 8 * h), qf[cc]);
+      for (int kb = 0; kb < NKB; ++kb) mma(s[kb], fo.frag(tK, kb * 32, cc), qf[cc]);
     }
+  };
 
-    // ---- logits (log2 units), mask on partly visible tiles, running max
-    float mx = -INFINITY;
-    auto logits = [&](auto masked) {
+  f32x16 scur[NKB];
+  if (ntiles > 0) {
+    kplan.issue(sK0, kbase, kstride, kbeg, Sk);
+    vplan.issue(sV0, vbase, kstride, kbeg, Sk);
+    if (PIPE && ntiles > 1) kplan.issue(sK1, kbase, kstride, kbeg + BN, Sk);
+  }
+  wait_loads();
+  __syncthreads();
+  if (PIPE && ntiles > 0) qk(sK0, scur);
+
+  // tile t: PIPE: softmax of scur (tile t) while S of tile t+1 comes from
+  // tK, DMA K_{t+2} -> wK; otherwise S of tile t from tK, DMA K_{t+1} -> wK.
+  // Both: PV from tV, DMA V_{t+1} -> wV.
+  auto step = [&](const bf16* tK, const bf16* tV, bf16* wK, bf16* wV, int t) {
+    const int k0 = kbeg + t * BN;
+    if (t + (PIPE ? 2 : 1) < ntiles) kplan.issue(wK, kbase, kstride, k0 + (PIPE ? 2 : 1) * BN, Sk);
+    if (t + 1 < ntiles) vplan.issue(wV, vbase, kstride, k0 + BN, Sk);
+    const bool next = t + 1 < ntiles;
+
+    {
+      f32x16 snext[NKB];
+      if constexpr (PIPE) {
+        if (next) qk(tK, snext);
+      } else {
+        qk(tK, scur);
+      }
+      // logits: CAP keeps r = 1/(1+2^y) (masked: +inf), else y (masked: -inf)
+      float ext = CAP ? INFINITY : -INFINITY;
+      auto logits = [&](auto masked) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float bv[16];
@@ -232,62 +337,81 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float f;
-          float s2 = logit_fast<CAP, BIAS, false>(sacc[kb][j], BIAS ? bv[j] : 0.0f, lk, f);
+          float y = scur[kb][j] * lk.a;
+          if constexpr (BIAS) y = fmaf(bv[j], lk.bb, y);
+          float v;
+          if constexpr (CAP) v = __builtin_amdgcn_rcpf(1.0f + fast_exp2(y));
+          else v = y;
           if constexpr (decltype(masked)::value) {
             const int key = k0 + kb * 32 + acc_row(h, j);
-            s2 = (key >= lo_i && key < hi_i) ? s2 : -INFINITY;
+            v = (key >= lo_i && key < hi_i) ? v : (CAP ? INFINITY : -INFINITY);
           }
-          sacc[kb][j] = s2;
-          mx = fmaxf(mx, s2);
+          scur[kb][j] = v;
+          ext = CAP ? fminf(ext, v) : fmaxf(ext, v);
         }
       }
-    };
-    if (rows_full && k0 >= lo_last && k0 + BN <= hi_first) logits(bool_c<false>{});
-    else logits(bool_c<true>{});
-    mx = fmaxf(mx, xor32(mx));
+      };
+      if (rows_full && k0 >= lo_last && k0 + BN <= hi_first) logits(bool_c<false>{});
+      else logits(bool_c<true>{});
+      ext = CAP ? fminf(ext, xor32(ext)) : fmaxf(ext, xor32(ext));
+      const float mx = CAP ? fmaf(ext, -2.0f * lk.c2, lk.c2) : ext;
 
-    // ---- lazy rescale: move the reference maximum only when it grew by > 8
-    const bool grow = mx > m + 8.0f;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m;
-      const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2(m - m_new);
-      lsum *= alpha;
+      // lazy rescale: move the reference maximum only when it grew by > 8
+      const bool grow = mx > m + 8.0f;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m;
+        const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2(m - m_new);
+        lsum *= alpha;
 #pragma unroll
-      for (int ob = 0; ob < NOB; ++ob) oacc[ob] *= alpha;
-      m = m_new;
-    }
-    const float base = (m == -INFINITY) ? 0.0f : m;
-
-    // ---- probabilities -> bf16 fragments
-    bf16x8 pf[NKB][2];
-    float ps = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float pv = fast_exp2(sacc[kb][j] - base);
-        sacc[kb][j] = pv;
-        ps += pv;
+        for (int ob = 0; ob < NOB; ++ob) oacc[ob] *= alpha;
+        m = m_new;
       }
-      pf[kb][0] = to_frag(sacc[kb], 0, (bf16*)nullptr);
-      pf[kb][1] = to_frag(sacc[kb], 8, (bf16*)nullptr);
-    }
-    lsum += ps;
+      const float base = (m == -INFINITY) ? 0.0f : m;
 
-    // ---- O^T += V^T P^T (V^T fragments by transposing LDS reads)
-#pragma unroll
-    for (int ob = 0; ob < NOB; ++ob) {
+      bf16x8 pf[NKB][2];
+      float ps = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-          mma(oacc[ob], frag_tr<D, true, false>(tV, kb * 32 + 16 * sb, ob * 32, lane), pf[kb][sb]);
+        for (int j = 0; j < 16; ++j) {
+          const float pv = CAP ? fast_exp2(fmaf(scur[kb][j], -2.0f * lk.c2, lk.c2 - base))
+                               : fast_exp2(scur[kb][j] - base);
+          scur[kb][j] = pv;
+          ps += pv;
+        }
+        pf[kb][0] = to_frag(scur[kb], 0, (bf16*)nullptr);
+        pf[kb][1] = to_frag(scur[kb], 8, (bf16*)nullptr);
+      }
+      lsum += ps;
+
+      // O^T += V^T P^T (V^T fragments by transposing LDS reads)
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) mma(oacc[ob], fo.frag_tr(tV, kb * 32 + 16 * sb, ob), pf[kb][sb]);
+        }
+      }
+      if constexpr (PIPE) {
+        if (next) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
+        }
       }
     }
 
     wait_loads();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    if constexpr (PIPE) {
+      step(sK1, sV0, sK0, sV1, t);
+      if (t + 1 < ntiles) step(sK0, sV1, sK1, sV0, t + 1);
+    } else {
+      step(sK0, sV0, sK1, sV1, t);
+      if (t + 1 < ntiles) step(sK1, sV1, sK0, sV0, t + 1);
+    }
   }
 
   // ---- epilogue
@@ -312,10 +436,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
 
 // ============================================================== backward: dk, dv, dbias
 
-// One workgroup = 4 waves = 128 keys of one KV head; K^T and V^T fragments of
-// each wave's 32 keys stay in registers, dK^T / dV^T accumulate in registers
-// over the GQA group's query heads and their visible 32-query tiles, which
-// stream through a double-buffered LDS tile (rows stored through swp).
+// One workgroup = 4 waves = 128 keys of one KV head; the K^T fragments of
+// each wave's 32 keys stay in registers and the workgroup's V rows stay in
+// LDS (keeping the wave under 256 registers with both accumulators),
+// dK^T / dV^T accumulate in registers over the GQA group's query heads and
+// their visible 32-query tiles, which stream through a double-buffered LDS
+// tile (rows stored through swp).
 template <int D, bool CAP, bool BIAS>
 __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParams p) {
   constexpr int NT = 256;
@@ -324,10 +450,15 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   constexpr int NOB = D / 32;
   constexpr int NCC = D / 16;
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][BMQ * D];
-  __shared__ __attribute__((aligned(16))) bf16 sO[2][BMQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][BMQ];
-  __shared__ __attribute__((aligned(16))) float sDl[2][BMQ];
+  __shared__ __attribute__((aligned(16))) bf16 sVr[BNK * D];
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sQ1[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sO0[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sO1[BMQ * D];
+  __shared__ __attribute__((aligned(16))) float sL0[BMQ];
+  __shared__ __attribute__((aligned(16))) float sL1[BMQ];
+  __shared__ __attribute__((aligned(16))) float sD0[BMQ];
+  __shared__ __attribute__((aligned(16))) float sD1[BMQ];
 
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
@@ -341,18 +472,16 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   const int jc = min(j, Sk - 1);
   const long qstride = (long)p.Hq * D;
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
+  const FragOfs<D, true> fo(lane);
 
-  bf16x8 kf[NCC], vf[NCC];
+  bf16x8 kf[NCC];
   {
-    const long off = (((long)b * Sk + jc) * p.Hkv + hk) * D;
-    const bf16* krow = reinterpret_cast<const bf16*>(p.k) + off;
-    const bf16* vrow = reinterpret_cast<const bf16*>(p.v) + off;
+    const bf16* krow = reinterpret_cast<const bf16*>(p.k) + (((long)b * Sk + jc) * p.Hkv + hk) * D;
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-      kf[cc] = *reinterpret_cast<const bf16x8*>(krow + 16 * cc + 8 * h);
-      vf[cc] = *reinterpret_cast<const bf16x8*>(vrow + 16 * cc + 8 * h);
-    }
+    for (int cc = 0; cc < NCC; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(krow + 16 * cc + 8 * h);
   }
+  load_tile<BNK, D, NT, false>(sVr, reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D,
+                               (long)p.Hkv * D, k0, Sk);
 
   int lo_j = 0, hi_j = 0;
   if (j < Sk) queries_of(p.mask, b, j, lo_j, hi_j);
@@ -375,12 +504,12 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   // item's work so the load latency overlaps it.
   float nl = 0.0f, nd = 0.0f;
   int nq = 0;
-  auto fetch = [&](int it, int bf) {
+  auto fetch = [&](int it, bf16* nQ, bf16* nO) {
     const int hq = hk * p.G + it / nqt;
     const int q0 = qbeg + (it % nqt) * BMQ;
     const long hoff = ((long)b * Sq * p.Hq + hq) * D;
-    load_tile<BMQ, D, NT, true>(sQ[bf], reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
-    load_tile<BMQ, D, NT, true>(sO[bf], reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
+    load_tile<BMQ, D, NT, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
+    load_tile<BMQ, D, NT, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
     if (threadIdx.x < BMQ) {
       nq = q0 + threadIdx.x;
       const long li = ((long)b * p.Hq + hq) * Sq + min(nq, Sq - 1);
@@ -388,56 +517,40 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
       nd = p.delta[li];
     }
   };
-  auto put_stats = [&](int bf) {
+  auto put_stats = [&](float* nL, float* nD) {
     if (threadIdx.x < BMQ) {
       // a query past the end, or one that sees nothing, contributes P = 0
-      sL[bf][threadIdx.x] = (nq < Sq && nl != -INFINITY) ? nl * kLog2e : INFINITY;
-      sDl[bf][threadIdx.x] = nd;
+      nL[threadIdx.x] = (nq < Sq && nl != -INFINITY) ? nl * kLog2e : INFINITY;
+      nD[threadIdx.x] = nd;
     }
   };
   if (nitems > 0) {
-    fetch(0, 0);
-    put_stats(0);
+    fetch(0, sQ0, sO0);
+    put_stats(sL0, sD0);
   }
   wait_loads();
   __syncthreads();
 
-  int buf = 0;
-  for (int it = 0; it < nitems; ++it, buf ^= 1) {
+  auto step = [&](const bf16* tQ, const bf16* tO, const float* tL, const float* tD, bf16* nQ, bf16* nO, float* nL,
+                  float* nD, int it) {
     const bool more = it + 1 < nitems;
-    if (more) fetch(it + 1, buf ^ 1);
+    if (more) fetch(it + 1, nQ, nO);
     const int hq = hk * p.G + it / nqt;
     const int q0 = qbeg + (it % nqt) * BMQ;
-    const bf16* tQ = sQ[buf];
-    const bf16* tO = sO[buf];
 
     // ---- S = Q K^T, dP = dO V^T (rows: queries through swp; columns: this wave's keys)
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
-      mma(sacc, frag<D>(tQ, n, 16 * cc + 8 * h), kf[cc]);
-      mma(dpacc, frag<D>(tO, n, 16 * cc + 8 * h), vf[cc]);
+      mma(sacc, fo.frag(tQ, 0, cc), kf[cc]);
+      mma(dpacc, fo.frag(tO, 0, cc), fo.frag(sVr, w * 32, cc));
     }
 
     // ---- P and dU = P (dP - delta) (1 - t^2); register r <-> query q0 + acc_row(h, r)
-    float lv[16], dl[16];
-    {
-      const f32x4* L4 = reinterpret_cast<const f32x4*>(sL[buf]);
-      const f32x4* D4 = reinterpret_cast<const f32x4*>(sDl[buf]);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const f32x4 a = L4[(16 * hf + 8 * h) / 4 + x];
-          const f32x4 c = D4[(16 * hf + 8 * h) / 4 + x];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lv[8 * hf + 4 * x + e] = a[e];
-            dl[8 * hf + 4 * x + e] = c[e];
-          }
-        }
-      }
-    }
+    // lse (log2 units) and delta of the 16 queries this lane holds, read from
+    // LDS four at a time where they are used
+    const f32x4* L4 = reinterpret_cast<const f32x4*>(tL);
+    const f32x4* D4 = reinterpret_cast<const f32x4*>(tD);
     const bf16* bcol = nullptr;
     bf16* dbcol = nullptr;
     if constexpr (BIAS) {
@@ -449,13 +562,16 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + acc_row(h, r);
+        const int q4 = (16 * (r >> 3) + 8 * h) / 4 + ((r >> 2) & 1);   // f32x4 holding query acc_row(h, r)
+        const float lr = L4[q4][r & 3];
+        const float dr = D4[q4][r & 3];
         float bvv = 0.0f;
         if constexpr (BIAS) bvv = (float)bcol[(long)min(qi, Sq - 1) * Sk];
         float f;
         const float s2 = logit_fast<CAP, BIAS, true>(sacc[r], bvv, lk, f);
-        float pv = fast_exp2(s2 - lv[r]);
+        float pv = fast_exp2(s2 - lr);
         if constexpr (decltype(masked)::value) pv = (qi >= lo_j && qi < hi_j) ? pv : 0.0f;
-        const float du = pv * (dpacc[r] - dl[r]) * f;
+        const float du = pv * (dpacc[r] - dr) * f;
         sacc[r] = pv;
         dpacc[r] = du;
         if constexpr (BIAS) {
@@ -477,14 +593,18 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        mma(vacc[ob], frag_tr<D, true, true>(tO, 16 * sb, ob * 32, lane), pf[sb]);
-        mma(kacc[ob], frag_tr<D, true, true>(tQ, 16 * sb, ob * 32, lane), uf[sb]);
+        mma(vacc[ob], fo.frag_tr(tO, 16 * sb, ob), pf[sb]);
+        mma(kacc[ob], fo.frag_tr(tQ, 16 * sb, ob), uf[sb]);
       }
     }
 
-    if (more) put_stats(buf ^ 1);
+    if (more) put_stats(nL, nD);
     wait_loads();
     __syncthreads();
+  };
+  for (int it = 0; it < nitems; it += 2) {
+    step(sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1, it);
+    if (it + 1 < nitems) step(sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, it + 1);
   }
 
   if (j < Sk) {
@@ -520,11 +640,16 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   constexpr int NT = 256;
   constexpr int BM = 128;
   constexpr int BN = 32;
+  constexpr bool ROWPERM_TR = true;   // K rows stored through swp
   constexpr int NOB = D / 32;
   constexpr int NCC = D / 16;
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * D];
+  // two LDS buffers per tile as distinct objects: the compiler can then see
+  // that reading one never aliases the DMA filling the other
+  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
 
   const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
   const int hq = blockIdx.y;
@@ -538,6 +663,7 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   const int q0 = qt * BM;
   const int i = q0 + w * 32 + n;
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
+  const FragOfs<D, ROWPERM_TR> fo(lane);
 
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
   const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
@@ -576,27 +702,24 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
 
   const int kbeg = (lo_first / BN) * BN;
   if (kbeg < hi_last) {
-    load_tile<BN, D, NT, true>(sK[0], kbase, kstride, kbeg, Sk);
-    load_tile<BN, D, NT, true>(sV[0], vbase, kstride, kbeg, Sk);
+    load_tile<BN, D, NT, true>(sK0, kbase, kstride, kbeg, Sk);
+    load_tile<BN, D, NT, true>(sV0, vbase, kstride, kbeg, Sk);
   }
   wait_loads();
   __syncthreads();
 
-  int buf = 0;
-  for (int k0 = kbeg; k0 < hi_last; k0 += BN, buf ^= 1) {
+  auto step = [&](const bf16* tK, const bf16* tV, bf16* nK, bf16* nV, int k0) {
     if (k0 + BN < hi_last) {
-      load_tile<BN, D, NT, true>(sK[buf ^ 1], kbase, kstride, k0 + BN, Sk);
-      load_tile<BN, D, NT, true>(sV[buf ^ 1], vbase, kstride, k0 + BN, Sk);
+      load_tile<BN, D, NT, true>(nK, kbase, kstride, k0 + BN, Sk);
+      load_tile<BN, D, NT, true>(nV, vbase, kstride, k0 + BN, Sk);
     }
-    const bf16* tK = sK[buf];
-    const bf16* tV = sV[buf];
 
     // ---- S^T = K Q^T, dP^T = V dO^T
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
-      mma(sacc, frag<D>(tK, n, 16 * cc + 8 * h), qf[cc]);
-      mma(dpacc, frag<D>(tV, n, 16 * cc + 8 * h), of[cc]);
+      mma(sacc, fo.frag(tK, 0, cc), qf[cc]);
+      mma(dpacc, fo.frag(tV, 0, cc), of[cc]);
     }
 
     // ---- dU^T = P^T (dP^T - delta) (1 - t^2)
@@ -628,11 +751,15 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) mma(qacc[ob], frag_tr<D, true, true>(tK, 16 * sb, ob * 32, lane), uf[sb]);
+      for (int sb = 0; sb < 2; ++sb) mma(qacc[ob], fo.frag_tr(tK, 16 * sb, ob), uf[sb]);
     }
 
     wait_loads();
     __syncthreads();
+  };
+  for (int k0 = kbeg; k0 < hi_last; k0 += 2 * BN) {
+    step(sK0, sV0, sK1, sV1, k0);
+    if (k0 + BN < hi_last) step(sK1, sV1, sK0, sV0, k0 + BN);
   }
 
   if (i < Sq) {
