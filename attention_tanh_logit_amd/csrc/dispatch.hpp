@@ -71,10 +71,19 @@ template <typename T, int D> constexpr int dkdv_keys() { return 32 * DkdvCfg<T, 
 // bf16 with D <= 128 takes the pipelined kernels of fast.hpp
 template <typename T, int D> constexpr bool use_fast() { return std::is_same<T, bf16>::value && (D == 64 || D == 128); }
 
+// The fast kernels address a streamed tile through a buffer resource with
+// 32-bit byte offsets: 128 rows of the widest token stride must stay below
+// 2^31 bytes.  The fast path reads bias rows 8 keys at a time.
+template <int D, class Params>
+bool fast_fits(const Params& p, const Launch& l, bool bias) {
+  const long stride = (long)(p.Hq > p.Hkv ? p.Hq : p.Hkv) * D;
+  return 128L * stride * 2 < (1L << 31) && (!bias || (l.Sk % 8 == 0 && l.Sk >= 8));
+}
+
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (!BIAS || (l.Sk % 8 == 0 && l.Sk >= 8)) {  // the fast path reads bias rows 8 keys at a time
+    if (fast_fits<D>(p, l, BIAS)) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       fwd_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
       return hipGetLastError();
@@ -91,7 +100,7 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dq(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (!BIAS || (l.Sk % 8 == 0 && l.Sk >= 8)) {  // the fast path reads bias rows 8 keys at a time
+    if (fast_fits<D>(p, l, BIAS)) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
       return hipGetLastError();
@@ -108,7 +117,7 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (!BIAS || (l.Sk % 8 == 0 && l.Sk >= 8)) {  // the fast path reads bias rows 8 keys at a time
+    if (fast_fits<D>(p, l, BIAS)) {
       const dim3 grid((l.Sk + 127) / 128, p.Hkv, l.B);
       dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
       return hipGetLastError();

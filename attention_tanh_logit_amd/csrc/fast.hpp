@@ -4,7 +4,7 @@
 // gfx950 throughput:
 //  * operands that stay fixed for a workgroup's whole loop (Q in the forward
 //    and dq, K and V in dk/dv) live in registers as MFMA fragments;
-//  * streamed tiles go straight from HBM into LDS with global_load_lds
+//  * streamed tiles go straight from HBM into LDS with buffer loads
 //    (no registers held across the loop), issued one tile ahead into a
 //    double-buffered LDS tile; one barrier per tile separates producers and
 //    consumers and the HBM latency hides behind the current tile's MFMAs;
@@ -58,11 +58,30 @@ __device__ __forceinline__ int sw_idx(int R, int col) {
   return R * D + (((col >> 3) ^ swz_f<D>(R)) << 3) + (col & 7);
 }
 
-// Direct HBM -> LDS load of a ROWS x D tile.  global_load_lds writes lane i's
-// 16 bytes at the instruction's LDS base + 16*i, so each wave instruction fills
-// one contiguous KiB: lane chunk p is tile row R = p/(D/8), physical slot
+// Buffer resource (V#) over rows row0 .. nvalid-1 of a row-strided bf16
+// tensor: base at row row0, range (nvalid - row0) rows.  Buffer reads whose
+// offset lies past the range return zeros, so a tile that runs past the last
+// row needs no clamping.  Word 3 is the gfx9 raw-buffer format word.  Tile
+// offsets stay below 2^31 bytes (the host only picks these kernels then).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* g, long gstride, int row0, int nvalid) {
+  const long bytes = (long)max(nvalid - row0, 0) * gstride * 2;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g + (long)row0 * gstride), 0,
+                                           (int)min(bytes, 0x7fffffffL), 0x00020000);
+}
+
+// One 16-byte buffer read straight into LDS: lane i's bytes land at the LDS
+// base + 16*i.  A buffer (not global) load so that the LDS DMA counts in
+// vmcnt alone and LDS reads issued meanwhile can still be waited for one at
+// a time.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff_bytes, bf16* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff_bytes, 0,
+                                           0, 0);
+}
+
+// Direct HBM -> LDS load of a ROWS x D tile.  Each wave instruction fills one
+// contiguous KiB: lane chunk p is tile row R = p/(D/8), physical slot
 // s = p%(D/8), and so takes logical column chunk s ^ f(R) of global row
-// (PERM ? swp(R) : R); rows at or beyond nvalid repeat row nvalid-1.
+// row0 + (PERM ? swp(R) : R); rows at or beyond nvalid read as zeros.
 template <int ROWS, int D, int NT, bool PERM>
 __device__ __forceinline__ void load_tile(bf16* lds, const bf16* g, long gstride, int row0, int nvalid) {
   constexpr int CPR = D / 8;
@@ -70,15 +89,14 @@ __device__ __forceinline__ void load_tile(bf16* lds, const bf16* g, long gstride
   static_assert((ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const auto rsrc = rows_rsrc(g, gstride, row0, nvalid);
 #pragma unroll
   for (int u = 0; u < N; ++u) {
     const int pw = u * NT + w * 64;
     const int p = pw + lane;
     const int R = p / CPR;
     const int s = p % CPR;
-    const int grow = min(row0 + (PERM ? swp(R) : R), nvalid - 1);
-    const bf16* src = g + (long)grow * gstride + 8 * (s ^ swz_f<D>(R));
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + pw * 8), 16, 0, 0);
+    dma16(rsrc, 2 * ((PERM ? swp(R) : R) * (int)gstride + 8 * (s ^ swz_f<D>(R))), lds + pw * 8);
   }
 }
 
@@ -179,9 +197,8 @@ template <bool B> using bool_c = std::integral_constant<bool, B>;
 
 // Per-thread plan of a direct tile load: this thread's 16-byte chunk u sits
 // NT/(D/8) rows below chunk u-1 (a multiple of 16 rows, where swp and the
-// swizzle repeat), so one element offset off0 relative to the tile's first
-// global row serves every chunk, and issuing a full tile costs one add per
-// chunk (rows past the end take the clamped path, once per kernel at most).
+// swizzle repeat), so one byte offset off0 relative to the tile's first row
+// serves every chunk; rows past the end read as zeros through the buffer range.
 template <int ROWS, int D, int NT, bool PERM>
 struct TilePlan {
   static constexpr int CPR = D / 8;
@@ -189,25 +206,34 @@ struct TilePlan {
   static constexpr int RSTEP = NT / CPR;
   static_assert((ROWS * CPR) % NT == 0 && RSTEP % 16 == 0, "tile must split evenly over the threads");
   int off0;
+  int ustep;   // bytes between consecutive chunks of one thread
   __device__ __forceinline__ explicit TilePlan(long gstride) {
     const int p = threadIdx.x;
     const int R = p / CPR, s = p % CPR;
-    off0 = (PERM ? swp(R) : R) * (int)gstride + 8 * (s ^ swz_f<D>(R));
+    off0 = 2 * ((PERM ? swp(R) : R) * (int)gstride + 8 * (s ^ swz_f<D>(R)));
+    ustep = 2 * RSTEP * (int)gstride;
   }
   __device__ __forceinline__ void issue(bf16* lds, const bf16* g, long gstride, int row0, int nvalid) const {
     const int w = threadIdx.x >> 6;
-    if (row0 + ROWS <= nvalid) {
+    const auto rsrc = rows_rsrc(g, gstride, row0, nvalid);
 #pragma unroll
-      for (int u = 0; u < N; ++u) {
-        const bf16* base = g + (long)(row0 + u * RSTEP) * gstride;
-        __builtin_amdgcn_global_load_lds(base + off0, (__attribute__((address_space(3))) void*)(lds + (u * NT + w * 64) * 8),
-                                         16, 0, 0);
-      }
-    } else {
-      load_tile<ROWS, D, NT, PERM>(lds, g, gstride, row0, nvalid);
-    }
+    for (int u = 0; u < N; ++u) dma16(rsrc, off0 + u * ustep, lds + (u * NT + w * 64) * 8);
   }
 };
+
+// Scheduling hint for a block of NMFMA MFMAs that each consume PER LDS reads:
+// AHEAD reads are issued up front and every MFMA is followed by the next PER
+// reads, so that reads stay in flight instead of each one being waited for
+// right before its MFMA.  (A macro: the hint must sit in the caller's own
+// scheduling region.)
+#define ATL_READ_AHEAD(AHEAD, PER, NMFMA)                        \
+  do {                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x100, (AHEAD), 0);     \
+    _Pragma("unroll") for (int x_ = 0; x_ < (NMFMA); ++x_) {     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         \
+      __builtin_amdgcn_sched_group_barrier(0x100, (PER), 0);     \
+    }                                                            \
+  } while (0)
 
 // ============================================================== forward
 
@@ -450,7 +476,11 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   constexpr int NOB = D / 32;
   constexpr int NCC = D / 16;
 
+  // at D > 64 the K rows stay in LDS as well, which leaves the register file
+  // to the two accumulators and to fragments read ahead of their MFMAs
+  constexpr bool KLDS = D > 64;
   __shared__ __attribute__((aligned(16))) bf16 sVr[BNK * D];
+  __shared__ __attribute__((aligned(16))) bf16 sKr[KLDS ? BNK * D : 8];
   __shared__ __attribute__((aligned(16))) bf16 sQ0[BMQ * D];
   __shared__ __attribute__((aligned(16))) bf16 sQ1[BMQ * D];
   __shared__ __attribute__((aligned(16))) bf16 sO0[BMQ * D];
@@ -474,8 +504,11 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const FragOfs<D, true> fo(lane);
 
-  bf16x8 kf[NCC];
-  {
+  bf16x8 kf[KLDS ? 1 : NCC];
+  if constexpr (KLDS) {
+    load_tile<BNK, D, NT, false>(sKr, reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D,
+                                 (long)p.Hkv * D, k0, Sk);
+  } else {
     const bf16* krow = reinterpret_cast<const bf16*>(p.k) + (((long)b * Sk + jc) * p.Hkv + hk) * D;
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(krow + 16 * cc + 8 * h);
@@ -542,9 +575,12 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
-      mma(sacc, fo.frag(tQ, 0, cc), kf[cc]);
+      mma(sacc, fo.frag(tQ, 0, cc), KLDS ? fo.frag(sKr, w * 32, cc) : kf[KLDS ? 0 : cc]);
       mma(dpacc, fo.frag(tO, 0, cc), fo.frag(sVr, w * 32, cc));
     }
+    // issue the fragment reads ahead of their MFMAs (a single wave per SIMD
+    // has nothing else to hide the LDS latency behind)
+    if constexpr (KLDS) ATL_READ_AHEAD(8, 2, 2 * NCC);
 
     // ---- P and dU = P (dP - delta) (1 - t^2); register r <-> query q0 + acc_row(h, r)
     // lse (log2 units) and delta of the 16 queries this lane holds, read from
@@ -589,12 +625,29 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
     uf[1] = to_frag(dpacc, 8, (bf16*)nullptr);
 
     // ---- dV^T += dO^T P,  dK^T += Q^T dU
+    // The transposing reads keep their source order through scheduling, so
+    // the fragments of column block ob + 1 are requested before the MFMAs of
+    // block ob: eight reads stay in flight behind four MFMAs.
+    bf16x8 tr_o[2][2], tr_q[2][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      tr_o[0][sb] = fo.frag_tr(tO, 16 * sb, 0);
+      tr_q[0][sb] = fo.frag_tr(tQ, 16 * sb, 0);
+    }
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
+      const int c = ob & 1;
+      if (ob + 1 < NOB) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          tr_o[c ^ 1][sb] = fo.frag_tr(tO, 16 * sb, ob + 1);
+          tr_q[c ^ 1][sb] = fo.frag_tr(tQ, 16 * sb, ob + 1);
+        }
+      }
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        mma(vacc[ob], fo.frag_tr(tO, 16 * sb, ob), pf[sb]);
-        mma(kacc[ob], fo.frag_tr(tQ, 16 * sb, ob), uf[sb]);
+        mma(vacc[ob], tr_o[c][sb], pf[sb]);
+        mma(kacc[ob], tr_q[c][sb], uf[sb]);
       }
     }
 

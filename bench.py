@@ -33,6 +33,54 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources and the C header (what the counters were taken on)."""
+    import hashlib
+    hsh = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_tanh_logit_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))] + [os.path.join(ROOT, "include", "attn_softcap.h")]
+    for f in files:
+        with open(f, "rb") as fh:
+            hsh.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload_name: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary.
+
+    The summary (profiles/hbm_traffic_<workload>.md) carries one line
+    ``bench-traffic: {json}`` with the calibrated FETCH_SIZE + WRITE_SIZE bytes
+    per launch and the source digest the counters were taken on; a different
+    digest means the kernels changed since, and the traffic is reported as None.
+    """
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_name}.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("bench-traffic:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("source_sha256") != kernel_source_digest():
+                    return None, "kernels changed since the counters were taken"
+                k = rec.get("kernels", {}).get(kernel)
+                if k is None:
+                    return None, f"no counters for {kernel}"
+                return k["fetch_bytes"] + k["write_bytes"], "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+    return None, "summary has no bench-traffic line"
+
+
+def calibration_copy(mib: int) -> None:
+    """A plain elementwise kernel that reads and writes `mib` MiB each (counter calibration)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def visible_pairs(w, seg=None) -> int:
     """Visible (query, key) pairs per (batch row, query head), summed over batch rows."""
     S, W = w.S, w.window
@@ -152,6 +200,8 @@ def main():
     ap.add_argument("--workload", default="causal_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cap-ratio", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain copy of this many MiB first (to scale HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path here has no "
@@ -163,6 +213,9 @@ def main():
     import attention_tanh_logit_amd as A
     A.lib()
     w = workload(args.workload)
+    if args.calib_copy_mib > 0:
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+        calibration_copy(args.calib_copy_mib)
     log(f"[bench] workload {w.name}: drawing inputs")
     d = W.draw(w)
     g, kw = to_gpu(w, d)
@@ -192,8 +245,10 @@ def main():
 
     dom = max(("fwd", "dq", "dkdv"), key=lambda k: ph[k])
     achieved = per_kernel_flop[dom] / (ph[dom] * 1e-3) / 1e12
+    traffic, traffic_src = measured_traffic(args.workload, dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None,
+                "frac": achieved / peak, "traffic": traffic, "traffic_source": traffic_src,
+                "traffic_gbps": None if traffic is None else traffic / (ph[dom] * 1e-3) / 1e9,
                 "flop_per_launch": per_kernel_flop[dom], "avg_launch_ms": ph[dom]}
 
     cpu = None
