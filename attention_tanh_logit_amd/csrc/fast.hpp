@@ -178,20 +178,23 @@ struct LogitK {
   }
 };
 
-// s2 = capped logit in log2 units; f = d s / d u (1 - tanh^2; 1 without a cap)
-template <bool CAP, bool BIAS, bool WANT_F>
-__device__ __forceinline__ float logit_fast(float x, float bias, const LogitK& k, float& f) {
+// Backward probability P = 2^(s2 - lse2) with Lc = (cap ? c2 : 0) - lse2
+// folded into one fma, and g = (1 - tanh^2)/4 = r(1 - r) (1 without a cap);
+// the gradients carry the factor 4 in their final scale (kGrad4).
+template <bool CAP, bool BIAS>
+__device__ __forceinline__ float prob_fast(float x, float bias, const LogitK& k, float Lc, float& g) {
   float y = x * k.a;
   if constexpr (BIAS) y = fmaf(bias, k.bb, y);
   if constexpr (CAP) {
     const float r = __builtin_amdgcn_rcpf(1.0f + fast_exp2(y));
-    if constexpr (WANT_F) f = 4.0f * r * (1.0f - r);
-    return fmaf(r, -2.0f * k.c2, k.c2);
+    g = fmaf(-r, r, r);
+    return fast_exp2(fmaf(r, -2.0f * k.c2, Lc));
   } else {
-    if constexpr (WANT_F) f = 1.0f;
-    return y;
+    g = 1.0f;
+    return fast_exp2(y + Lc);
   }
 }
+template <bool CAP> constexpr float kGrad4 = CAP ? 4.0f : 1.0f;
 
 template <bool B> using bool_c = std::integral_constant<bool, B>;
 
@@ -553,8 +556,8 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   auto put_stats = [&](float* nL, float* nD) {
     if (threadIdx.x < BMQ) {
       // a query past the end, or one that sees nothing, contributes P = 0
-      nL[threadIdx.x] = (nq < Sq && nl != -INFINITY) ? nl * kLog2e : INFINITY;
-      nD[threadIdx.x] = nd;
+      nL[threadIdx.x] = (nq < Sq && nl != -INFINITY) ? (CAP ? p.cl2 : 0.0f) - nl * kLog2e : -INFINITY;
+      nD[threadIdx.x] = -nd;
     }
   };
   if (nitems > 0) {
@@ -571,8 +574,21 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
     const int hq = hk * p.G + it / nqt;
     const int q0 = qbeg + (it % nqt) * BMQ;
 
-    // ---- S = Q K^T, dP = dO V^T (rows: queries through swp; columns: this wave's keys)
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    // ---- S = Q K^T, dP - delta = dO V^T - delta (rows: queries through swp;
+    // columns: this wave's keys).  Per query the LDS stats hold
+    // Lc = (cap ? c2 : 0) - lse2 and -delta; register r <-> query
+    // q0 + acc_row(h, r), whose stats sit in f32x4 number
+    // 4*(r/8) + 2h + (r/4)%2, element r%4.  The dP accumulator starts from
+    // the -delta of its rows.
+    const f32x4* L4 = reinterpret_cast<const f32x4*>(tL);
+    const f32x4* D4 = reinterpret_cast<const f32x4*>(tD);
+    f32x16 sacc = f32x16{}, dpacc;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 nd4 = D4[4 * (e4 >> 1) + 2 * h + (e4 & 1)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dpacc[4 * e4 + e] = nd4[e];
+    }
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
       mma(sacc, fo.frag(tQ, 0, cc), KLDS ? fo.frag(sKr, w * 32, cc) : kf[KLDS ? 0 : cc]);
@@ -582,11 +598,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
     // has nothing else to hide the LDS latency behind)
     if constexpr (KLDS) ATL_READ_AHEAD(8, 2, 2 * NCC);
 
-    // ---- P and dU = P (dP - delta) (1 - t^2); register r <-> query q0 + acc_row(h, r)
-    // lse (log2 units) and delta of the 16 queries this lane holds, read from
-    // LDS four at a time where they are used
-    const f32x4* L4 = reinterpret_cast<const f32x4*>(tL);
-    const f32x4* D4 = reinterpret_cast<const f32x4*>(tD);
+    // ---- P and dU/4 = P (dP - delta) (1 - t^2)/4
     const bf16* bcol = nullptr;
     bf16* dbcol = nullptr;
     if constexpr (BIAS) {
@@ -598,21 +610,18 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + acc_row(h, r);
-        const int q4 = (16 * (r >> 3) + 8 * h) / 4 + ((r >> 2) & 1);   // f32x4 holding query acc_row(h, r)
-        const float lr = L4[q4][r & 3];
-        const float dr = D4[q4][r & 3];
+        const float lc = L4[4 * (r >> 3) + 2 * h + ((r >> 2) & 1)][r & 3];
         float bvv = 0.0f;
         if constexpr (BIAS) bvv = (float)bcol[(long)min(qi, Sq - 1) * Sk];
-        float f;
-        const float s2 = logit_fast<CAP, BIAS, true>(sacc[r], bvv, lk, f);
-        float pv = fast_exp2(s2 - lr);
+        float g;
+        float pv = prob_fast<CAP, BIAS>(sacc[r], bvv, lk, lc, g);
         if constexpr (decltype(masked)::value) pv = (qi >= lo_j && qi < hi_j) ? pv : 0.0f;
-        const float du = pv * (dpacc[r] - dr) * f;
+        const float du = pv * dpacc[r] * g;
         sacc[r] = pv;
         dpacc[r] = du;
         if constexpr (BIAS) {
           const bool vis = decltype(masked)::value ? (qi >= lo_j && qi < hi_j) : true;
-          if (dbcol && vis) dbcol[(long)qi * Sk] = (bf16)du;
+          if (dbcol && vis) dbcol[(long)qi * Sk] = (bf16)(du * kGrad4<CAP>);
         }
       }
     };
@@ -671,7 +680,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
         float kv[8], vv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          kv[e] = kacc[ob][8 * hf + e] * p.scale;
+          kv[e] = kacc[ob][8 * hf + e] * (p.scale * kGrad4<CAP>);
           vv[e] = vacc[ob][8 * hf + e];
         }
         const int d = ob * 32 + 16 * hf + 8 * h;
@@ -732,7 +741,8 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
 
   const long row = ((long)b * p.Hq + hq) * Sq + min(i, Sq - 1);
   const float lse_i = p.lse[row];
-  const float lse2 = (i < Sq && lse_i != -INFINITY) ? lse_i * kLog2e : INFINITY;
+  // Lc = (cap ? c2 : 0) - lse2; a query past the end or seeing nothing gets P = 0
+  const float lc_i = (i < Sq && lse_i != -INFINITY) ? (CAP ? p.cl2 : 0.0f) - lse_i * kLog2e : -INFINITY;
   const float delta_i = p.delta[row];
 
   bf16x8 qf[NCC], of[NCC];
@@ -775,7 +785,7 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
       mma(dpacc, fo.frag(tV, 0, cc), of[cc]);
     }
 
-    // ---- dU^T = P^T (dP^T - delta) (1 - t^2)
+    // ---- dU^T/4 = P^T (dP^T - delta) (1 - t^2)/4
     float bv[16];
     if constexpr (BIAS) {
 #pragma unroll
@@ -784,14 +794,13 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
     auto grads = [&](auto masked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float f;
-        const float s2 = logit_fast<CAP, BIAS, true>(sacc[r], BIAS ? bv[r] : 0.0f, lk, f);
-        float pv = fast_exp2(s2 - lse2);
+        float g;
+        float pv = prob_fast<CAP, BIAS>(sacc[r], BIAS ? bv[r] : 0.0f, lk, lc_i, g);
         if constexpr (decltype(masked)::value) {
           const int key = k0 + acc_row(h, r);
           pv = (key >= lo_i && key < hi_i) ? pv : 0.0f;
         }
-        sacc[r] = pv * (dpacc[r] - delta_i) * f;
+        sacc[r] = pv * (dpacc[r] - delta_i) * g;
       }
     };
     if (rows_full && k0 >= lo_last && k0 + BN <= hi_first) grads(bool_c<false>{});
@@ -823,7 +832,7 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
       for (int hf = 0; hf < 2; ++hf) {
         float vals[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = qacc[ob][8 * hf + e] * p.scale;
+        for (int e = 0; e < 8; ++e) vals[e] = qacc[ob][8 * hf + e] * (p.scale * kGrad4<CAP>);
         store8<bf16>(drow + ob * 32 + 16 * hf + 8 * h, vals);
       }
     }
