@@ -493,14 +493,26 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   __shared__ __attribute__((aligned(16))) float sD0[BMQ];
   __shared__ __attribute__((aligned(16))) float sD1[BMQ];
 
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroups go to the 8 XCDs round-robin by linear id.  Renumber them so
+  // that each XCD takes whole (batch row, KV head) groups: all key blocks of
+  // a group then sweep the same query tiles (from the last one backwards, in
+  // step with each other) through one L2.
+  int kb, hk, b;
+  {
+    const int nkb = gridDim.x;
+    const int N = nkb * gridDim.y * gridDim.z;
+    const int L = blockIdx.x + nkb * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
+    kb = Lp % nkb;
+    hk = (Lp / nkb) % gridDim.y;
+    b = Lp / (nkb * gridDim.y);
+  }
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n = lane & 31;
   const int h = lane >> 5;
-  const int k0 = blockIdx.x * BNK;
+  const int k0 = kb * BNK;
   const int j = k0 + w * 32 + n;
   const int jc = min(j, Sk - 1);
   const long qstride = (long)p.Hq * D;
@@ -534,15 +546,15 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) { kacc[ob] = f32x16{}; vacc[ob] = f32x16{}; }
 
-  // item it = (query head it / nqt of the group, query tile it % nqt); its
-  // Q and dO tiles go straight to LDS, its lse and delta (one row per thread
-  // of the first 32) through registers, written to LDS after the current
-  // item's work so the load latency overlaps it.
+  // item it = (query tile nqt - 1 - it / G counted from the end, query head
+  // it % G of the group); its Q and dO tiles go straight to LDS, its lse and
+  // delta (one row per thread of the first 32) through registers, written to
+  // LDS after the current item's work so the load latency overlaps it.
   float nl = 0.0f, nd = 0.0f;
   int nq = 0;
   auto fetch = [&](int it, bf16* nQ, bf16* nO) {
-    const int hq = hk * p.G + it / nqt;
-    const int q0 = qbeg + (it % nqt) * BMQ;
+    const int hq = hk * p.G + it % p.G;
+    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
     const long hoff = ((long)b * Sq * p.Hq + hq) * D;
     load_tile<BMQ, D, NT, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
     load_tile<BMQ, D, NT, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
@@ -571,8 +583,8 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
                   float* nD, int it) {
     const bool more = it + 1 < nitems;
     if (more) fetch(it + 1, nQ, nO);
-    const int hq = hk * p.G + it / nqt;
-    const int q0 = qbeg + (it % nqt) * BMQ;
+    const int hq = hk * p.G + it % p.G;
+    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
 
     // ---- S = Q K^T, dP - delta = dO V^T - delta (rows: queries through swp;
     // columns: this wave's keys).  Per query the LDS stats hold
