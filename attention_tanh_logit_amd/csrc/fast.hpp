@@ -268,9 +268,21 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
 
-  const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroups go to the 8 XCDs round-robin by linear id; renumber them so
+  // that each XCD takes whole heads (and so, with the heads of a GQA group
+  // adjacent, whole K/V streams), whose query tiles sweep the same key tiles
+  // in step through one L2.  With `reverse` the longest tiles start first.
+  int qt, hq, b;
+  {
+    const int nqt = gridDim.x;
+    const int N = nqt * gridDim.y * gridDim.z;
+    const int L = blockIdx.x + nqt * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
+    const int x = Lp % nqt;
+    qt = p.reverse ? nqt - 1 - x : x;
+    hq = (Lp / nqt) % gridDim.y;
+    b = Lp / (nqt * gridDim.y);
+  }
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
@@ -725,9 +737,21 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
 
-  const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroups go to the 8 XCDs round-robin by linear id; renumber them so
+  // that each XCD takes whole heads (and so, with the heads of a GQA group
+  // adjacent, whole K/V streams), whose query tiles sweep the same key tiles
+  // in step through one L2.  With `reverse` the longest tiles start first.
+  int qt, hq, b;
+  {
+    const int nqt = gridDim.x;
+    const int N = nqt * gridDim.y * gridDim.z;
+    const int L = blockIdx.x + nqt * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
+    const int x = Lp % nqt;
+    qt = p.reverse ? nqt - 1 - x : x;
+    hq = (Lp / nqt) % gridDim.y;
+    b = Lp / (nqt * gridDim.y);
+  }
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
