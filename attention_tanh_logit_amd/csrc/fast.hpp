@@ -634,12 +634,13 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + acc_row(h, r);
-        const float lc = L4[4 * (r >> 3) + 2 * h + ((r >> 2) & 1)][r & 3];
+        float lc = L4[4 * (r >> 3) + 2 * h + ((r >> 2) & 1)][r & 3];
+        // a masked pair gets Lc = -inf, hence P = 0, without a branch
+        if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j) ? lc : -INFINITY;
         float bvv = 0.0f;
         if constexpr (BIAS) bvv = (float)bcol[(long)min(qi, Sq - 1) * Sk];
         float g;
-        float pv = prob_fast<CAP, BIAS>(sacc[r], bvv, lk, lc, g);
-        if constexpr (decltype(masked)::value) pv = (qi >= lo_j && qi < hi_j) ? pv : 0.0f;
+        const float pv = prob_fast<CAP, BIAS>(sacc[r], bvv, lk, lc, g);
         const float du = pv * dpacc[r] * g;
         sacc[r] = pv;
         dpacc[r] = du;
