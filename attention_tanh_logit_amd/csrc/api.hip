@@ -123,10 +123,27 @@ size_t pre_blocks(const attn_args* a) { return ((size_t)a->Sq + kPreRows - 1) / 
 
 size_t fwd_ws(const attn_args* a) { return seg_bytes(a); }
 
+// The bf16 kernels for head dims 64/128 hand dU from the dk/dv kernel to the
+// dq kernel through the workspace (bf16, 32-key x 32-query blocks), so that
+// dq needs neither exponentials nor a second pass over the logits; the
+// buffer holds every block of [B, Hq, Sq, Sk] and is used only while it
+// stays below kDuMaxBytes (else dq recomputes the probabilities).
+constexpr size_t kDuMaxBytes = (size_t)16 << 30;
+
+size_t du_raw_bytes(const attn_args* a) {
+  return (size_t)a->B * a->Hq * (((size_t)a->Sk + 31) / 32) * (((size_t)a->Sq + 31) / 32) * 2048;
+}
+
+bool du_path(const attn_args* a) {
+  return fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr) &&
+         du_raw_bytes(a) <= kDuMaxBytes;
+}
+
 size_t bwd_ws(const attn_args* a) {
   size_t s = seg_bytes(a);
   s += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));  // delta
   if (a->sink_mode == ATTN_SINK_LEARNABLE) s += align_up((size_t)a->Hq * a->B * pre_blocks(a) * sizeof(float));
+  if (du_path(a)) s += align_up(du_raw_bytes(a));
   return s;
 }
 
@@ -289,7 +306,14 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
   float* delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));
   float* part = nullptr;
-  if (a->sink_mode == ATTN_SINK_LEARNABLE) part = reinterpret_cast<float*>(ws);
+  if (a->sink_mode == ATTN_SINK_LEARNABLE) {
+    part = reinterpret_cast<float*>(ws);
+    ws += align_up((size_t)a->Hq * a->B * pre_blocks(a) * sizeof(float));
+  }
+  p.du = nullptr;
+  p.nkb32 = (a->Sk + 31) / 32;
+  p.nqb32 = (a->Sq + 31) / 32;
+  if (du_path(a)) p.du = ws;
   p.delta = delta;
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;
@@ -314,13 +338,14 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
       if (e != hipSuccess) return hip_fail(e, "dbias fill launch");
     }
   }
-  if ((phases & kPhaseDq) && a->Sq > 0) {
-    e = o.dq(a->D, cap, bias, p, l);
-    if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
-  }
+  // dk/dv before dq: on the dU path the dq kernel reads what dk/dv wrote
   if ((phases & kPhaseDkdv) && a->Sk > 0) {
     e = o.dkdv(a->D, cap, bias, p, l);
     if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
+  }
+  if ((phases & kPhaseDq) && a->Sq > 0) {
+    e = o.dq(a->D, cap, bias, p, l);
+    if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
   }
   return ATTN_OK;
 }

@@ -74,10 +74,14 @@ template <typename T, int D> constexpr bool use_fast() { return std::is_same<T, 
 // The fast kernels address a streamed tile through a buffer resource with
 // 32-bit byte offsets: 128 rows of the widest token stride must stay below
 // 2^31 bytes.  The fast path reads bias rows 8 keys at a time.
+inline bool fast_ok(bool bf16_input, int D, int Hq, int Hkv, int Sk, bool bias) {
+  const long stride = (long)(Hq > Hkv ? Hq : Hkv) * D;
+  return bf16_input && (D == 64 || D == 128) && 128L * stride * 2 < (1L << 31) &&
+         (!bias || (Sk % 8 == 0 && Sk >= 8));
+}
 template <int D, class Params>
 bool fast_fits(const Params& p, const Launch& l, bool bias) {
-  const long stride = (long)(p.Hq > p.Hkv ? p.Hq : p.Hkv) * D;
-  return 128L * stride * 2 < (1L << 31) && (!bias || (l.Sk % 8 == 0 && l.Sk >= 8));
+  return fast_ok(true, D, p.Hq, p.Hkv, l.Sk, bias);
 }
 
 template <typename T, int D, bool CAP, bool BIAS>
@@ -102,7 +106,8 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
     if (fast_fits<D>(p, l, BIAS)) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
-      dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      if (p.du) dq_du_kernel<D, CAP><<<grid, 256, 0, l.stream>>>(p);
+      else dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
       return hipGetLastError();
     }
   }

@@ -333,10 +333,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
   auto qk = [&](const bf16* tK, f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    // key block by key block, so that the logits of block 0 can run while
+    // the MFMAs of block 1 do
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mma(s[kb], fo.frag(tK, kb * 32, cc), qf[cc]);
+      for (int cc = 0; cc < NCC; ++cc) mma(s[kb], fo.frag(tK, kb * 32, cc), qf[cc]);
     }
   };
 
@@ -409,7 +411,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
       }
       const float base = (m == -INFINITY) ? 0.0f : m;
 
-      bf16x8 pf[NKB][2];
+      // probabilities of key block kb, then O^T += V^T P^T for that block
+      // (V^T fragments by transposing LDS reads): the exponentials of block
+      // kb + 1 can run while the MFMAs of block kb do
       float ps = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -420,20 +424,16 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
           scur[kb][j] = pv;
           ps += pv;
         }
-        pf[kb][0] = to_frag(scur[kb], 0, (bf16*)nullptr);
-        pf[kb][1] = to_frag(scur[kb], 8, (bf16*)nullptr);
-      }
-      lsum += ps;
-
-      // O^T += V^T P^T (V^T fragments by transposing LDS reads)
+        bf16x8 pf[2];
+        pf[0] = to_frag(scur[kb], 0, (bf16*)nullptr);
+        pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
 #pragma unroll
-      for (int ob = 0; ob < NOB; ++ob) {
+        for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int sb = 0; sb < 2; ++sb) mma(oacc[ob], fo.frag_tr(tV, kb * 32 + 16 * sb, ob), pf[kb][sb]);
+          for (int sb = 0; sb < 2; ++sb) mma(oacc[ob], fo.frag_tr(tV, kb * 32 + 16 * sb, ob), pf[sb]);
         }
       }
+      lsum += ps;
       if constexpr (PIPE) {
         if (next) {
 #pragma unroll
@@ -657,6 +657,15 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
     pf[1] = to_frag(sacc, 8, (bf16*)nullptr);
     uf[0] = to_frag(dpacc, 0, (bf16*)nullptr);
     uf[1] = to_frag(dpacc, 8, (bf16*)nullptr);
+    // dU^T of this (32-key, 32-query) block for the dq kernel, as the
+    // fragments stand: element (key n, query 16sb + 8h + e) at
+    // sb*512 + (n + 32h)*8 + e; one contiguous KiB per store instruction
+    if (p.du && k0 + 32 * w < Sk) {
+      bf16* blk = reinterpret_cast<bf16*>(p.du) +
+                  ((((long)b * p.Hq + hq) * p.nkb32 + (k0 >> 5) + w) * p.nqb32 + (q0 >> 5)) * 1024 + lane * 8;
+      *reinterpret_cast<bf16x8*>(blk) = uf[0];
+      *reinterpret_cast<bf16x8*>(blk + 512) = uf[1];
+    }
 
     // ---- dV^T += dO^T P,  dK^T += Q^T dU
     // The transposing reads keep their source order through scheduling, so
@@ -711,6 +720,154 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
         const int d = ob * 32 + 16 * hf + 8 * h;
         store8<bf16>(krow + d, kv);
         store8<bf16>(vrow + d, vv);
+      }
+    }
+  }
+}
+
+// ============================================================== backward: dq from dU
+
+// A dU^T block of the workspace in LDS: 128 chunks of 16 bytes, chunk c
+// (c = 64 sb + 32 h + key n, holding queries 16 sb + 8 h .. + 7) stored in
+// slot c ^ (4 * ((c >> 5) & 3)), which makes the gather below conflict-free.
+__device__ __forceinline__ int du_slot(int c) { return c ^ (((c >> 5) & 3) << 2); }
+
+// B fragment of dQ^T += K^T dU^T for keys 16 sb .. 16 sb + 15 of the block:
+// lane n + 32 g receives dU(key 16 sb + 8 g + i, query n), i = 0..7, from two
+// transposing reads.  ds_read_b64_tr_b16 hands lane j of each 16-lane group
+// element j % 4 of the 4-element chunk read by lane j / 4 + 4 e, e = 0..3, so
+// source lane s points at key 16 sb + 8 g + 4 t + s / 4 and the four queries
+// starting at 16 (G % 2) + 4 (s % 4) (G = lane / 16, t = which read).
+__device__ __forceinline__ bf16x8 du_frag(const bf16* blk, int lane, int sb) {
+  const int G = lane >> 4, s = lane & 15;
+  const int c0 = (G & 1) * 64 + ((s & 3) >> 1) * 32 + 8 * (G >> 1) + (s >> 2) + 16 * sb;
+  const v4i16 a = ds_tr16(blk + du_slot(c0) * 8 + 4 * (s & 1));
+  const v4i16 b = ds_tr16(blk + du_slot(c0 + 4) * 8 + 4 * (s & 1));
+  bf16x8 r;
+  __builtin_memcpy(&r, &a, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
+  return r;
+}
+
+// dQ from the dU^T blocks the dk/dv kernel left in the workspace.  One
+// workgroup = 4 waves = 128 queries of one query head; per 32-key block that
+// some query of the wave sees, dQ^T += K^T dU^T on the MFMAs, with K^T from
+// the shared key tile and dU^T from the wave's own 2 KiB block, both through
+// transposing LDS reads.  No exponentials and no masks: the dk/dv kernel
+// stored masked pairs as zeros, and it wrote every block that holds a
+// visible pair (blocks no query of the wave sees are skipped, never read).
+template <int D, bool CAP>
+__global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
+  constexpr int NT = 256;
+  constexpr int BM = 128;
+  constexpr int BN = 64;
+  constexpr int NKB = BN / 32;
+  constexpr int NOB = D / 32;
+
+  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sU0[4 * NKB * 1024];
+  __shared__ __attribute__((aligned(16))) bf16 sU1[4 * NKB * 1024];
+
+  // XCD-aware numbering as in the other kernels
+  int qt, hq, b;
+  {
+    const int nqt = gridDim.x;
+    const int N = nqt * gridDim.y * gridDim.z;
+    const int L = blockIdx.x + nqt * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
+    const int x = Lp % nqt;
+    qt = p.reverse ? nqt - 1 - x : x;
+    hq = (Lp / nqt) % gridDim.y;
+    b = Lp / (nqt * gridDim.y);
+  }
+  const int hk = hq / p.G;
+  const int Sq = p.mask.Sq, Sk = p.mask.Sk;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int q0 = qt * BM;
+  const int qw = q0 + 32 * w;        // this wave's first query
+  const int i = qw + n;
+  const FragOfs<D, true> fo(lane);
+
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
+  const long kstride = (long)p.Hkv * D;
+
+  const int ilast = min(q0 + BM, Sq) - 1;
+  int lo_first, hi_first, lo_last, hi_last;
+  keys_of(p.mask, b, q0, lo_first, hi_first);
+  keys_of(p.mask, b, ilast, lo_last, hi_last);
+  // keys seen by some query of this wave: one interval (each query's
+  // visible keys are an interval holding its own position, and the bounds
+  // never decrease along the queries)
+  int wlo = 0, whi = 0;
+  if (qw < Sq) {
+    int x0, x1;
+    keys_of(p.mask, b, qw, wlo, x0);
+    keys_of(p.mask, b, min(qw + 31, Sq - 1), x1, whi);
+  }
+  const bf16* ublocks = reinterpret_cast<const bf16*>(p.du) +
+                        (((long)b * p.Hq + hq) * p.nkb32 * p.nqb32 + (qw >> 5)) * 1024;
+  const long ukstride = (long)p.nqb32 * 1024;   // elements between key blocks
+
+  f32x16 qacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) qacc[ob] = f32x16{};
+
+  auto visible = [&](int kb32) { return kb32 < whi && kb32 + 32 > wlo && kb32 < Sk; };
+  // the tile's K rows (all waves) and this wave's dU^T blocks
+  auto fetch = [&](int k0, bf16* tK, bf16* tU) {
+    load_tile<BN, D, NT, true>(tK, kbase, kstride, k0, Sk);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) {
+      if (visible(k0 + 32 * kk)) {
+        const bf16* blk = ublocks + (long)((k0 >> 5) + kk) * ukstride;
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(blk), 0, 2048, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dma16(rsrc, 16 * du_slot(64 * u + lane), tU + (w * NKB + kk) * 1024 + 64 * u * 8);
+      }
+    }
+  };
+
+  const int kbeg = (lo_first / BN) * BN;
+  if (kbeg < hi_last) fetch(kbeg, sK0, sU0);
+  wait_loads();
+  __syncthreads();
+
+  auto step = [&](const bf16* tK, const bf16* tU, bf16* nK, bf16* nU, int k0) {
+    if (k0 + BN < hi_last) fetch(k0 + BN, nK, nU);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) {
+      if (visible(k0 + 32 * kk)) {
+        const bf16* blk = tU + (w * NKB + kk) * 1024;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const bf16x8 uf = du_frag(blk, lane, sb);
+#pragma unroll
+          for (int ob = 0; ob < NOB; ++ob) mma(qacc[ob], fo.frag_tr(tK, 32 * kk + 16 * sb, ob), uf);
+        }
+      }
+    }
+    wait_loads();
+    __syncthreads();
+  };
+  for (int k0 = kbeg; k0 < hi_last; k0 += 2 * BN) {
+    step(sK0, sU0, sK1, sU1, k0);
+    if (k0 + BN < hi_last) step(sK1, sU1, sK0, sU0, k0 + BN);
+  }
+
+  if (i < Sq) {
+    bf16* drow = reinterpret_cast<bf16*>(p.dq) + (((long)b * Sq + i) * p.Hq + hq) * D;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float vals[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = qacc[ob][8 * hf + e] * (p.scale * kGrad4<CAP>);
+        store8<bf16>(drow + ob * 32 + 16 * hf + 8 * h, vals);
       }
     }
   }

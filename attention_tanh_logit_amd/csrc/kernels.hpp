@@ -59,6 +59,10 @@ struct BwdParams {
   void* dk;
   void* dv;
   void* dbias;
+  // dU^T in 32-key x 32-query blocks (bf16), written by the dk/dv kernel and
+  // read by the dq kernel; null when dq recomputes the probabilities itself
+  void* du;
+  int nkb32, nqb32;  // blocks along keys and along queries
   Mask mask;
   int Hq, Hkv, G;
   float scale;

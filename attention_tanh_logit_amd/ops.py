@@ -178,8 +178,9 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
     """Backward: returns (dq, dk, dv, dbias or None, dsink or None).
 
     With ``events`` (four torch.cuda.Event) the three phases are launched
-    through their own entry points with an event recorded before the
-    pre-pass and after each phase, on the current stream.
+    through their own entry points (pre-pass, dk/dv, dq, in that order) with
+    an event recorded before the pre-pass and after each phase, on the
+    current stream.
     """
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
@@ -207,9 +208,9 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
         _check(L.attn_bwd_pre(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dbias), _ptr(dsink),
                               _ptr(ws), nws, st))
         events[1].record()
-        _check(L.attn_bwd_dq(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(ws), nws, st))
-        events[2].record()
         _check(L.attn_bwd_dkdv(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv), _ptr(dbias),
                                _ptr(ws), nws, st))
+        events[2].record()
+        _check(L.attn_bwd_dq(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(ws), nws, st))
         events[3].record()
     return dq, dk, dv, dbias, dsink

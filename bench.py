@@ -2,7 +2,7 @@
 """Benchmark: fused soft-capped attention forward + backward on one MI355X.
 
 One step = the whole hot path on one batch: attn_fwd (forward kernel) then
-the backward's three phases (pre-pass, dq kernel, dk/dv kernel), all on the
+the backward's three phases (pre-pass, dk/dv kernel, dq kernel), all on the
 current stream with inputs already resident in HBM.  Prints ONE JSON line.
 
 Throughput counts algorithmic work only: 4*D flop per visible (query, key)
@@ -155,8 +155,8 @@ def run_steps(g, kw, steps, warmup):
     for e in ev:
         ph["fwd"] += e[0].elapsed_time(e[1])
         ph["bwd_pre"] += e[2].elapsed_time(e[3])
-        ph["dq"] += e[3].elapsed_time(e[4])
-        ph["dkdv"] += e[4].elapsed_time(e[5])
+        ph["dkdv"] += e[3].elapsed_time(e[4])
+        ph["dq"] += e[4].elapsed_time(e[5])
     return wall * 1e3 / steps, {k: v / steps for k, v in ph.items()}
 
 

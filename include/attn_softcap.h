@@ -104,7 +104,10 @@ typedef struct attn_args {
 attn_status attn_validate(const attn_args* a);
 
 /* Device workspace (bytes) that attn_fwd / attn_bwd need for `a`
- * (0 if none).  Returns (size_t)-1 if `a` is invalid. */
+ * (0 if none).  Returns (size_t)-1 if `a` is invalid.  For bf16 with D = 64
+ * or 128 the backward workspace includes B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB
+ * for dU (bf16) while that stays within 16 GiB, e.g. 4 GiB at B=4, Hq=32,
+ * S=4096; beyond that dq recomputes the probabilities instead. */
 size_t attn_fwd_workspace_size(const attn_args* a);
 size_t attn_bwd_workspace_size(const attn_args* a);
 
@@ -127,12 +130,13 @@ attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, cons
                      void* dq, void* dk, void* dv, void* dbias, float* dsink,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* The same backward in three phases, for callers that time or overlap them
- * (attn_bwd == pre, then dq and dkdv).  All three take the same arguments and
- * the same workspace, which carries the pre-pass results (segment runs,
- * delta = rowsum(dout * out), sink-gradient partials) to the other two, so
- * it must stay untouched between them; dq and dkdv only read it and may run
- * concurrently on two streams once pre has finished.
+/* The same backward in three phases, for callers that time them
+ * (attn_bwd == pre, then dkdv, then dq).  All three take the same arguments
+ * and the same workspace, which carries the pre-pass results (segment runs,
+ * delta = rowsum(dout * out), sink-gradient partials) to the other two and,
+ * for bf16 with D = 64 or 128, the dU blocks that dkdv writes and dq reads;
+ * so it must stay untouched between them and the phases must run in that
+ * order (on one stream, or with the caller ordering them).
  *  - attn_bwd_pre:  segment runs, delta, dsink (required iff LEARNABLE) and
  *                   the zeros of dbias on the masked pairs (dbias nullable);
  *  - attn_bwd_dq:   dq;
