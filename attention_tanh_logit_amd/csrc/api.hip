@@ -2,6 +2,7 @@
 // closed: a requested cap or sink is never dropped), workspace layout and the
 // launch sequence on the caller's stream.
 #include <cmath>
+#include <cstdlib>
 #include <cstdio>
 #include <string>
 
@@ -127,8 +128,17 @@ size_t fwd_ws(const attn_args* a) { return seg_bytes(a); }
 // dq kernel through the workspace (bf16, 32-key x 32-query blocks), so that
 // dq needs neither exponentials nor a second pass over the logits; the
 // buffer holds every block of [B, Hq, Sq, Sk] and is used only while it
-// stays below kDuMaxBytes (else dq recomputes the probabilities).
-constexpr size_t kDuMaxBytes = (size_t)16 << 30;
+// stays within a limit (else dq recomputes the probabilities): 16 GiB, or
+// the byte count in the environment variable ATTN_SOFTCAP_DU_MAX_BYTES.
+size_t du_max_bytes() {
+  const char* e = std::getenv("ATTN_SOFTCAP_DU_MAX_BYTES");
+  if (e && *e) {
+    char* end = nullptr;
+    const unsigned long long v = std::strtoull(e, &end, 10);
+    if (end && *end == '\0') return (size_t)v;
+  }
+  return (size_t)16 << 30;
+}
 
 size_t du_raw_bytes(const attn_args* a) {
   return (size_t)a->B * a->Hq * (((size_t)a->Sk + 31) / 32) * (((size_t)a->Sq + 31) / 32) * 2048;
@@ -136,7 +146,7 @@ size_t du_raw_bytes(const attn_args* a) {
 
 bool du_path(const attn_args* a) {
   return fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr) &&
-         du_raw_bytes(a) <= kDuMaxBytes;
+         du_raw_bytes(a) <= du_max_bytes();
 }
 
 size_t bwd_ws(const attn_args* a) {

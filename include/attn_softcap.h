@@ -106,8 +106,11 @@ attn_status attn_validate(const attn_args* a);
 /* Device workspace (bytes) that attn_fwd / attn_bwd need for `a`
  * (0 if none).  Returns (size_t)-1 if `a` is invalid.  For bf16 with D = 64
  * or 128 the backward workspace includes B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB
- * for dU (bf16) while that stays within 16 GiB, e.g. 4 GiB at B=4, Hq=32,
- * S=4096; beyond that dq recomputes the probabilities instead. */
+ * for dU (bf16) while that stays within 16 GiB (or within the byte count
+ * in the environment variable ATTN_SOFTCAP_DU_MAX_BYTES), e.g. 4 GiB at
+ * B=4, Hq=32, S=4096; beyond that dq recomputes the probabilities instead.
+ * The choice is made again on every call: keep the variable unchanged
+ * between attn_bwd_workspace_size and the backward calls it sizes. */
 size_t attn_fwd_workspace_size(const attn_args* a);
 size_t attn_bwd_workspace_size(const attn_args* a);
 

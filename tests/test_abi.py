@@ -111,3 +111,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ops.lib()
+
+
+def test_bwd_workspace_carries_du_blocks_for_bf16_d64_d128(monkeypatch):
+    """bf16 with D = 64/128: B*Hq*ceil(Sk/32)*ceil(Sq/32) blocks of 2 KiB for dU, unless the limit is lower."""
+    L = A.lib()
+    monkeypatch.delenv("ATTN_SOFTCAP_DU_MAX_BYTES", raising=False)
+    a = _args()                       # bf16, B=2, Hq=8, S=256, D=128
+    with_du = L.attn_bwd_workspace_size(ctypes.byref(a))
+    monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", "0")
+    without = L.attn_bwd_workspace_size(ctypes.byref(a))
+    assert with_du - without == 2 * 8 * 8 * 8 * 2048
+    monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", str(2 * 8 * 8 * 8 * 2048))
+    assert L.attn_bwd_workspace_size(ctypes.byref(a)) == with_du
+    a = _args(Sq=250, Sk=250)         # ragged: still 8 blocks per side
+    assert L.attn_bwd_workspace_size(ctypes.byref(a)) - without <= 2 * 8 * 8 * 8 * 2048 + 256
+    monkeypatch.delenv("ATTN_SOFTCAP_DU_MAX_BYTES", raising=False)
+    f32 = _args(dtype=1)
+    g32 = _args(dtype=1, D=256)
+    assert L.attn_bwd_workspace_size(ctypes.byref(f32)) == without
+    assert L.attn_bwd_workspace_size(ctypes.byref(g32)) == without

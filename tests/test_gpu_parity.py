@@ -56,6 +56,16 @@ def test_feature_matrix(dtype, D, feat):
     _check(case(**kw))
 
 
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("feat", list(FEATURES))
+def test_feature_matrix_dq_recomputed(D, feat, monkeypatch):
+    """bf16 D<=128 with the dU hand-off switched off: dq recomputes the probabilities."""
+    monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", "0")
+    kw = dict(dtype="bf16", D=D, B=2, S=203, Hq=4, Hkv=2)
+    kw.update(FEATURES[feat])
+    _check(case(**kw))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_cross_attention_lengths_differ(dtype):
     _check(case(dtype=dtype, D=64, B=1, S=77, Sk=301, causal=False, Hq=2, Hkv=1))
