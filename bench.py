@@ -7,8 +7,8 @@ current stream with inputs already resident in HBM.  Prints ONE JSON line.
 
 Throughput counts algorithmic work only: 4*D flop per visible (query, key)
 pair in the forward and 10*D in the backward (14*D per step), summed over
-batch rows and query heads; masked pairs, partial-tile waste and the dq
-kernel's recomputation earn nothing.
+batch rows and query heads; masked pairs, partial-tile waste and any
+recomputation earn nothing.
 
   python bench.py [--steps K] [--warmup W] [--workload causal_gqa] [--no-cpu-baseline]
 """
@@ -223,7 +223,13 @@ def main():
     flop_fwd = 4.0 * w.D * pairs
     flop_bwd = 10.0 * w.D * pairs
     flop_step = flop_fwd + flop_bwd
-    per_kernel_flop = {"fwd": 4.0 * w.D * pairs, "dq": 6.0 * w.D * pairs, "dkdv": 8.0 * w.D * pairs}
+    # the dq kernel recomputes S and dP (6*D per pair) unless the dk/dv kernel
+    # hands it dU through the workspace (bf16, D = 64/128): then only dQ = dU K
+    du_bytes = w.B * w.Hq * (-(-w.S // 32)) ** 2 * 2048
+    du_limit = int(os.environ.get("ATTN_SOFTCAP_DU_MAX_BYTES", 16 << 30) or 0)
+    du_path = w.dtype == "bf16" and w.D in (64, 128) and du_bytes <= du_limit
+    per_kernel_flop = {"fwd": 4.0 * w.D * pairs, "dq": (2.0 if du_path else 6.0) * w.D * pairs,
+                       "dkdv": 8.0 * w.D * pairs}
 
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
     ms, ph = run_steps(g, kw, args.steps, args.warmup)
