@@ -238,6 +238,27 @@ struct TilePlan {
     }                                                            \
   } while (0)
 
+// Workgroup numbering for the 8 XCDs (each with its own L2), which receive
+// workgroups round-robin by linear id.  A grid of ntile x ngroup workgroups
+// (a group = one head, or one KV head, of one batch row) is renumbered so
+// that XCD x works on groups x*ngroup/8 .. (x+1)*ngroup/8 - 1 only -- their
+// tiles share K/V (or Q/dO) through that XCD's L2 -- and hands them out tile
+// index by tile index across those groups, so that tile 0 (the longest
+// under a causal mask) of every group is dispatched before any tile 1, and
+// so on: longest first over the whole XCD, which keeps the tail short.
+__device__ __forceinline__ void xcd_order(int ntile, int ngroup, int& tile, int& group) {
+  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if (ngroup % 8 == 0) {
+    const int gpx = ngroup / 8;
+    const int t = L / 8;
+    tile = t / gpx;
+    group = (L % 8) * gpx + t % gpx;
+  } else {
+    tile = L % ntile;
+    group = L / ntile;
+  }
+}
+
 // ============================================================== forward
 
 // With PIPE the loop is software-pipelined over key tiles: while the softmax
@@ -268,20 +289,15 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
 
-  // Workgroups go to the 8 XCDs round-robin by linear id; renumber them so
-  // that each XCD takes whole heads (and so, with the heads of a GQA group
-  // adjacent, whole K/V streams), whose query tiles sweep the same key tiles
-  // in step through one L2.  With `reverse` the longest tiles start first.
+  // each XCD takes whole heads (with the heads of a GQA group adjacent, whole
+  // K/V streams); with `reverse` the longest query tiles go first
   int qt, hq, b;
   {
-    const int nqt = gridDim.x;
-    const int N = nqt * gridDim.y * gridDim.z;
-    const int L = blockIdx.x + nqt * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
-    const int x = Lp % nqt;
-    qt = p.reverse ? nqt - 1 - x : x;
-    hq = (Lp / nqt) % gridDim.y;
-    b = Lp / (nqt * gridDim.y);
+    int x, grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, x, grp);
+    qt = p.reverse ? gridDim.x - 1 - x : x;
+    hq = grp % gridDim.y;
+    b = grp / gridDim.y;
   }
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
@@ -505,19 +521,15 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   __shared__ __attribute__((aligned(16))) float sD0[BMQ];
   __shared__ __attribute__((aligned(16))) float sD1[BMQ];
 
-  // Workgroups go to the 8 XCDs round-robin by linear id.  Renumber them so
-  // that each XCD takes whole (batch row, KV head) groups: all key blocks of
-  // a group then sweep the same query tiles (from the last one backwards, in
-  // step with each other) through one L2.
+  // each XCD takes whole (batch row, KV head) groups, key block 0 (the
+  // longest under a causal mask) first; all key blocks of a group sweep the
+  // same query tiles (from the last one backwards, in step) through one L2
   int kb, hk, b;
   {
-    const int nkb = gridDim.x;
-    const int N = nkb * gridDim.y * gridDim.z;
-    const int L = blockIdx.x + nkb * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
-    kb = Lp % nkb;
-    hk = (Lp / nkb) % gridDim.y;
-    b = Lp / (nkb * gridDim.y);
+    int grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, kb, grp);
+    hk = grp % gridDim.y;
+    b = grp / gridDim.y;
   }
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
@@ -769,17 +781,14 @@ __global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sU0[4 * NKB * 1024];
   __shared__ __attribute__((aligned(16))) bf16 sU1[4 * NKB * 1024];
 
-  // XCD-aware numbering as in the other kernels
+  // XCD-aware, longest-first numbering as in the other kernels
   int qt, hq, b;
   {
-    const int nqt = gridDim.x;
-    const int N = nqt * gridDim.y * gridDim.z;
-    const int L = blockIdx.x + nqt * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
-    const int x = Lp % nqt;
-    qt = p.reverse ? nqt - 1 - x : x;
-    hq = (Lp / nqt) % gridDim.y;
-    b = Lp / (nqt * gridDim.y);
+    int x, grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, x, grp);
+    qt = p.reverse ? gridDim.x - 1 - x : x;
+    hq = grp % gridDim.y;
+    b = grp / gridDim.y;
   }
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
@@ -895,20 +904,15 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
 
-  // Workgroups go to the 8 XCDs round-robin by linear id; renumber them so
-  // that each XCD takes whole heads (and so, with the heads of a GQA group
-  // adjacent, whole K/V streams), whose query tiles sweep the same key tiles
-  // in step through one L2.  With `reverse` the longest tiles start first.
+  // each XCD takes whole heads (with the heads of a GQA group adjacent, whole
+  // K/V streams); with `reverse` the longest query tiles go first
   int qt, hq, b;
   {
-    const int nqt = gridDim.x;
-    const int N = nqt * gridDim.y * gridDim.z;
-    const int L = blockIdx.x + nqt * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int Lp = (N % 8 == 0) ? (L % 8) * (N / 8) + L / 8 : L;
-    const int x = Lp % nqt;
-    qt = p.reverse ? nqt - 1 - x : x;
-    hq = (Lp / nqt) % gridDim.y;
-    b = Lp / (nqt * gridDim.y);
+    int x, grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, x, grp);
+    qt = p.reverse ? gridDim.x - 1 - x : x;
+    hq = grp % gridDim.y;
+    b = grp / gridDim.y;
   }
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
