@@ -123,8 +123,15 @@ template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
     if (fast_fits<D>(p, l, BIAS)) {
-      const dim3 grid((l.Sk + 127) / 128, p.Hkv, l.B);
-      dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      if constexpr (D == 128) {
+        // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64 queries)
+        constexpr int NW = 8, BMQ = 64;
+        const dim3 grid((l.Sk + 16 * NW - 1) / (16 * NW), p.Hkv, l.B);
+        dkdv16_kernel<D, CAP, BIAS, NW, BMQ><<<grid, 64 * NW, 0, l.stream>>>(p);
+      } else {
+        const dim3 grid((l.Sk + 127) / 128, p.Hkv, l.B);
+        dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      }
       return hipGetLastError();
     }
   }

@@ -32,6 +32,7 @@
 namespace atl {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // swap the two bits of a 2-bit index
 __device__ __forceinline__ int swp2(int a) { return ((a & 1) << 1) | ((a >> 1) & 1); }
@@ -82,7 +83,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff_byte
 // contiguous KiB: lane chunk p is tile row R = p/(D/8), physical slot
 // s = p%(D/8), and so takes logical column chunk s ^ f(R) of global row
 // row0 + (PERM ? swp(R) : R); rows at or beyond nvalid read as zeros.
-template <int ROWS, int D, int NT, bool PERM>
+// Row swizzle of tiles read by 16x16x32 fragments (D = 128): f(R) =
+// 2*(R%8) + (R/8)%2.  Plain fragment reads (16 lanes: 16 consecutive rows,
+// one logical slot) need f one-to-one on 16 rows; the transposing reads of
+// such fragments (32 lanes: 8 consecutive rows x one aligned 32-byte slot
+// pair) need f/2 one-to-one on 8 consecutive rows.  Period 16.
+__device__ __forceinline__ int swz16(int R) { return 2 * (R & 7) + ((R >> 3) & 1); }
+
+template <int ROWS, int D, int NT, bool PERM, bool SW16 = false>
 __device__ __forceinline__ void load_tile(bf16* lds, const bf16* g, long gstride, int row0, int nvalid) {
   constexpr int CPR = D / 8;
   constexpr int N = ROWS * CPR / NT;
@@ -96,7 +104,7 @@ __device__ __forceinline__ void load_tile(bf16* lds, const bf16* g, long gstride
     const int p = pw + lane;
     const int R = p / CPR;
     const int s = p % CPR;
-    dma16(rsrc, 2 * ((PERM ? swp(R) : R) * (int)gstride + 8 * (s ^ swz_f<D>(R))), lds + pw * 8);
+    dma16(rsrc, 2 * ((PERM ? swp(R) : R) * (int)gstride + 8 * (s ^ (SW16 ? swz16(R) : swz_f<D>(R)))), lds + pw * 8);
   }
 }
 
@@ -165,6 +173,63 @@ struct FragOfs {
     return r;
   }
 };
+
+// Per-lane fragment offsets for v_mfma_f32_16x16x32_bf16 operands from a
+// D = 128 tile stored with swz16.  Lane r + 16g:
+//  * frag(row0, c): row row0 + r, columns 8(c + 4g) .. + 7 (the A or B
+//    operand of a product that contracts over the columns; lanes 16 apart
+//    take chunks 64 bytes apart, which measured free of bank conflicts where
+//    adjacent chunks (columns 32c + 8g) conflicted two ways);
+//  * frag_tr(row0, ob): X[row0 + sigma(g, i)][16 ob + r], i = 0..7, with
+//    sigma(g, i) = 4g + i for i < 4 and 16 + 4g + i - 4 after, which is the
+//    query order in which a 16x16 accumulator pair (rows 16qb + 4g + e) hands
+//    its values to the next product.  Two ds_read_b64_tr_b16: source lane
+//    s + 16g points at row 4g + s/4 (+16), columns 16 ob + 4(s%4) .. + 3.
+template <int D>
+struct Frag16Ofs {
+  static_assert(D == 128, "laid out for 256-byte rows");
+  int pbase, pxor, tbase, txor;
+  __device__ __forceinline__ explicit Frag16Ofs(int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const int fr = swz16(r);
+    // slot (c + 4g) ^ f = 4 (g ^ (f >> 2)) + (c ^ (f & 3))
+    pbase = opaque(r * D + 32 * (g ^ (fr >> 2)));
+    pxor = opaque(8 * (fr & 3));
+    const int R1 = 4 * g + (r >> 2);
+    const int f = swz16(R1);
+    // slot (2 ob + (r%4)/2) ^ f = ((2 ob) ^ (f & 14)) + (((r%4)/2 ^ f) & 1)
+    tbase = opaque(R1 * D + 8 * ((((r & 3) >> 1) ^ f) & 1) + 4 * (r & 1));
+    txor = opaque(8 * (f & 14));
+  }
+  __device__ __forceinline__ bf16x8 frag(const bf16* tile, int row0, int c) const {
+    return *reinterpret_cast<const bf16x8*>(tile + row0 * D + pbase + ((8 * c) ^ pxor));
+  }
+  __device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int row0, int ob) const {
+    const bf16* a = tile + row0 * D + tbase + ((16 * ob) ^ txor);
+    const v4i16 x = ds_tr16(a);
+    const v4i16 y = ds_tr16(a + 16 * D);
+    bf16x8 r;
+    __builtin_memcpy(&r, &x, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &y, 8);
+    return r;
+  }
+};
+
+__device__ __forceinline__ void mma16(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two 16x16 accumulators (query blocks 2kc, 2kc+1) -> one operand fragment
+// whose 8 contraction indices are the queries sigma(g, 0..7).
+__device__ __forceinline__ bf16x8 pack8(const f32x4& a, const f32x4& b) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)a[e];
+    r[4 + e] = (bf16)b[e];
+  }
+  return r;
+}
 
 // Log2-unit logit constants of the bf16 fast path (see the header comment).
 struct LogitK {
@@ -737,6 +802,231 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   }
 }
 
+// ============================================================== backward: dk, dv with 16-key waves
+
+// D = 128.  One workgroup = 4 waves = 64 keys of one KV head, 16 keys per
+// wave on v_mfma_f32_16x16x32_bf16: the wave's K and V rows stay in
+// registers as fragments (16 registers each) and dK^T, dV^T take 64, so a
+// wave needs well under 256 registers and two run per SIMD, each hiding the
+// other's exponentials and LDS latency behind its MFMAs.  Per 32-query item:
+//   S = Q K^T and dP - delta = dO V^T in 16x16 blocks (lane: key r, queries
+//   16qb + 4g + e), P and dU/4 in place, then dV^T += dO^T P and
+//   dK^T += Q^T dU with the accumulator pair of each quantity as the B
+//   operand directly (contraction order sigma) and dO^T, Q^T fragments from
+//   transposing reads of the same row-major tiles.
+// The dU hand-off block (32 keys x 32 queries, 2 KiB) takes the two waves of
+// a 32-key pair as its halves: half kh = w % 2, then chunk lane' = key
+// kappa + 16 g' holding dU(16 kh + kappa, queries sigma(g', 0..7)).
+template <int D, bool CAP, bool BIAS, int NW, int BMQ>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
+  constexpr int NT = 64 * NW;
+  constexpr int BNK = 16 * NW;
+  constexpr int NQB = BMQ / 16;
+  constexpr int NKC = BMQ / 32;
+  constexpr int NC = D / 32;
+  constexpr int NOB = D / 16;
+
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sQ1[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sO0[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sO1[BMQ * D];
+  __shared__ __attribute__((aligned(16))) float sL0[BMQ];
+  __shared__ __attribute__((aligned(16))) float sL1[BMQ];
+  __shared__ __attribute__((aligned(16))) float sD0[BMQ];
+  __shared__ __attribute__((aligned(16))) float sD1[BMQ];
+
+  // XCD-aware, longest-first numbering and a lockstep query sweep, as in
+  // the 32-key kernel
+  int kb, hk, b;
+  {
+    int grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, kb, grp);
+    hk = grp % gridDim.y;
+    b = grp / gridDim.y;
+  }
+  const int Sq = p.mask.Sq, Sk = p.mask.Sk;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int k0 = kb * BNK;
+  const int kw = k0 + 16 * w;
+  const int j = kw + r;
+  const int jc = min(j, Sk - 1);
+  const long qstride = (long)p.Hq * D;
+  const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
+  const Frag16Ofs<D> fo(lane);
+
+  // K and V fragments of this wave's keys: lane r + 16g holds columns
+  // 8(c + 4g) .. + 7 of key kw + r (the B operand of S = Q K^T, dP = dO V^T)
+  bf16x8 kf[NC], vf[NC];
+  {
+    const long off = (((long)b * Sk + jc) * p.Hkv + hk) * D;
+    const bf16* krow = reinterpret_cast<const bf16*>(p.k) + off;
+    const bf16* vrow = reinterpret_cast<const bf16*>(p.v) + off;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kf[c] = *reinterpret_cast<const bf16x8*>(krow + 8 * c + 32 * g);
+      vf[c] = *reinterpret_cast<const bf16x8*>(vrow + 8 * c + 32 * g);
+    }
+  }
+
+  int lo_j = 0, hi_j = 0;
+  if (j < Sk) queries_of(p.mask, b, j, lo_j, hi_j);
+  const int jlast = min(k0 + BNK, Sk) - 1;
+  int lo_first, hi_first, lo_last, hi_last;
+  queries_of(p.mask, b, k0, lo_first, hi_first);
+  queries_of(p.mask, b, jlast, lo_last, hi_last);
+  const bool keys_full = (k0 + BNK <= Sk);
+  const int qbeg = (lo_first / BMQ) * BMQ;
+  const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
+  const int nitems = p.G * nqt;
+
+  f32x4 kacc[NOB], vacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) { kacc[ob] = f32x4{}; vacc[ob] = f32x4{}; }
+
+  float nl = 0.0f, nd = 0.0f;
+  int nq = 0;
+  auto fetch = [&](int it, bf16* nQ, bf16* nO) {
+    const int hq = hk * p.G + it % p.G;
+    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
+    const long hoff = ((long)b * Sq * p.Hq + hq) * D;
+    load_tile<BMQ, D, NT, false, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
+    load_tile<BMQ, D, NT, false, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
+    if (threadIdx.x < BMQ) {
+      nq = q0 + threadIdx.x;
+      const long li = ((long)b * p.Hq + hq) * Sq + min(nq, Sq - 1);
+      nl = p.lse[li];
+      nd = p.delta[li];
+    }
+  };
+  auto put_stats = [&](float* nL, float* nD) {
+    if (threadIdx.x < BMQ) {
+      nL[threadIdx.x] = (nq < Sq && nl != -INFINITY) ? (CAP ? p.cl2 : 0.0f) - nl * kLog2e : -INFINITY;
+      nD[threadIdx.x] = -nd;
+    }
+  };
+  if (nitems > 0) {
+    fetch(0, sQ0, sO0);
+    put_stats(sL0, sD0);
+  }
+  wait_loads();
+  __syncthreads();
+
+  auto step = [&](const bf16* tQ, const bf16* tO, const float* tL, const float* tD, bf16* nQ, bf16* nO, float* nL,
+                  float* nD, int it) {
+    const bool more = it + 1 < nitems;
+    if (more) fetch(it + 1, nQ, nO);
+    const int hq = hk * p.G + it % p.G;
+    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
+
+    // S and dP - delta; the stats of queries 16qb + 4g .. + 3 are one f32x4
+    const f32x4* L4 = reinterpret_cast<const f32x4*>(tL);
+    const f32x4* D4 = reinterpret_cast<const f32x4*>(tD);
+    f32x4 sacc[NQB], dpacc[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      sacc[qb] = f32x4{};
+      dpacc[qb] = D4[4 * qb + g];
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        mma16(sacc[qb], fo.frag(tQ, 16 * qb, c), kf[c]);
+        mma16(dpacc[qb], fo.frag(tO, 16 * qb, c), vf[c]);
+      }
+    }
+
+    const bf16* bcol = nullptr;
+    bf16* dbcol = nullptr;
+    if constexpr (BIAS) {
+      const long boff = (((long)b * p.Hq + hq) * Sq) * Sk + jc;
+      bcol = reinterpret_cast<const bf16*>(p.bias) + boff;
+      if (p.dbias) dbcol = reinterpret_cast<bf16*>(p.dbias) + boff;
+    }
+    auto grads = [&](auto masked) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const f32x4 l4 = L4[4 * qb + g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qi = q0 + 16 * qb + 4 * g + e;
+          float lc = l4[e];
+          if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j) ? lc : -INFINITY;
+          float bvv = 0.0f;
+          if constexpr (BIAS) bvv = (float)bcol[(long)min(qi, Sq - 1) * Sk];
+          float gg;
+          const float pv = prob_fast<CAP, BIAS>(sacc[qb][e], bvv, lk, lc, gg);
+          const float du = pv * dpacc[qb][e] * gg;
+          sacc[qb][e] = pv;
+          dpacc[qb][e] = du;
+          if constexpr (BIAS) {
+            const bool vis = decltype(masked)::value ? (qi >= lo_j && qi < hi_j) : true;
+            if (dbcol && vis) dbcol[(long)qi * Sk] = (bf16)(du * kGrad4<CAP>);
+          }
+        }
+      }
+    };
+    if (keys_full && q0 >= lo_last && q0 + BMQ <= hi_first) grads(bool_c<false>{});
+    else grads(bool_c<true>{});
+    bf16x8 pf[NKC], uf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      pf[kc] = pack8(sacc[2 * kc], sacc[2 * kc + 1]);
+      uf[kc] = pack8(dpacc[2 * kc], dpacc[2 * kc + 1]);
+    }
+    // this wave's half of the dU block (32-key block of the pair, query block q0/32 + kc)
+    if (p.du && k0 + 16 * (w & ~1) < Sk) {
+      bf16* blk = reinterpret_cast<bf16*>(p.du) +
+                  ((((long)b * p.Hq + hq) * p.nkb32 + (kw >> 5)) * p.nqb32 + (q0 >> 5)) * 1024 + (w & 1) * 512 +
+                  lane * 8;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        // a ragged last item may end before its second 32-query block
+        if (kc == 0 || q0 + 32 * kc < Sq) *reinterpret_cast<bf16x8*>(blk + kc * 1024) = uf[kc];
+      }
+    }
+
+    // dV^T += dO^T P, dK^T += Q^T dU (rows: columns 16 ob + 4g + e; lane's key r)
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        mma16(vacc[ob], fo.frag_tr(tO, 32 * kc, ob), pf[kc]);
+        mma16(kacc[ob], fo.frag_tr(tQ, 32 * kc, ob), uf[kc]);
+      }
+    }
+
+    if (more) put_stats(nL, nD);
+    wait_loads();
+    __syncthreads();
+  };
+  for (int it = 0; it < nitems; it += 2) {
+    step(sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1, it);
+    if (it + 1 < nitems) step(sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, it + 1);
+  }
+
+  if (j < Sk) {
+    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    bf16* krow = reinterpret_cast<bf16*>(p.dk) + off;
+    bf16* vrow = reinterpret_cast<bf16*>(p.dv) + off;
+    const float ks = p.scale * kGrad4<CAP>;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      bf16x4 kv, vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[e] = (bf16)(kacc[ob][e] * ks);
+        vv[e] = (bf16)vacc[ob][e];
+      }
+      *reinterpret_cast<bf16x4*>(krow + 16 * ob + 4 * g) = kv;
+      *reinterpret_cast<bf16x4*>(vrow + 16 * ob + 4 * g) = vv;
+    }
+  }
+}
+
 // ============================================================== backward: dq from dU
 
 // A dU^T block of the workspace in LDS: 128 chunks of 16 bytes, chunk c
@@ -761,6 +1051,23 @@ __device__ __forceinline__ bf16x8 du_frag(const bf16* blk, int lane, int sb) {
   return r;
 }
 
+// The same fragment from a block written by 16-key waves (D = 128): chunk c
+// = 64 sb + kappa + 16 g' (key 16 sb + kappa, queries sigma(g', 0..7): the
+// first 8 bytes queries 4g' .. + 3, the last 8 bytes 16 + 4g' .. + 3) sits in
+// slot c ^ (4 * ((c >> 4) & 3)).  Source lane s of group G reads key
+// 8 (G/2) + 4t + s/4 at the four queries 4 (4 (G%2) + s%4) .. + 3.
+__device__ __forceinline__ int du_slot16(int c) { return c ^ (((c >> 4) & 3) << 2); }
+__device__ __forceinline__ bf16x8 du_frag16(const bf16* blk, int lane, int sb) {
+  const int G = lane >> 4, s = lane & 15;
+  const int c0 = 64 * sb + 8 * (G >> 1) + (s >> 2) + 16 * (s & 3);
+  const v4i16 a = ds_tr16(blk + du_slot16(c0) * 8 + 4 * (G & 1));
+  const v4i16 b = ds_tr16(blk + du_slot16(c0 + 4) * 8 + 4 * (G & 1));
+  bf16x8 r;
+  __builtin_memcpy(&r, &a, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
+  return r;
+}
+
 // dQ from the dU^T blocks the dk/dv kernel left in the workspace.  One
 // workgroup = 4 waves = 128 queries of one query head; per 32-key block that
 // some query of the wave sees, dQ^T += K^T dU^T on the MFMAs, with K^T from
@@ -775,6 +1082,7 @@ __global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
   constexpr int BN = 64;
   constexpr int NKB = BN / 32;
   constexpr int NOB = D / 32;
+  constexpr bool DU16 = D == 128;   // blocks written by dkdv16_kernel
 
   __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
@@ -835,7 +1143,9 @@ __global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
         const bf16* blk = ublocks + (long)((k0 >> 5) + kk) * ukstride;
         const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(blk), 0, 2048, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) dma16(rsrc, 16 * du_slot(64 * u + lane), tU + (w * NKB + kk) * 1024 + 64 * u * 8);
+        for (int u = 0; u < 2; ++u)
+          dma16(rsrc, 16 * (DU16 ? du_slot16(64 * u + lane) : du_slot(64 * u + lane)),
+                tU + (w * NKB + kk) * 1024 + 64 * u * 8);
       }
     }
   };
@@ -853,7 +1163,7 @@ __global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
         const bf16* blk = tU + (w * NKB + kk) * 1024;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          const bf16x8 uf = du_frag(blk, lane, sb);
+          const bf16x8 uf = DU16 ? du_frag16(blk, lane, sb) : du_frag(blk, lane, sb);
 #pragma unroll
           for (int ob = 0; ob < NOB; ++ob) mma(qacc[ob], fo.frag_tr(tK, 32 * kk + 16 * sb, ob), uf);
         }

@@ -1,0 +1,82 @@
+"""Host-side check of the dU hand-off between the bf16 dk/dv and dq kernels.
+
+The dk/dv kernel stores dU in 2 KiB blocks (one per head, 32-key block and
+32-query block; two 1 KiB halves of 16 keys each) and the dq kernel reads a
+block whenever some query of its 32-query tile sees some key of the 32-key
+block.  This test walks the store rule of both dk/dv kernels (32-key waves at
+D = 64; 16-key waves, 8 per workgroup, 64-query items at D = 128) and the read
+rule of the dq kernel over ragged causal / windowed / full masks and checks
+that every store lands inside the workspace region, no half is stored twice,
+and every half the dq kernel reads has been stored.  No GPU needed.
+"""
+import pytest
+
+
+def visible_queries(j, Sq, causal, window):
+    """Queries that see key j: an interval [lo, hi) (Sq == Sk when causal)."""
+    lo, hi = (j, Sq) if causal else (0, Sq)
+    if window > 0:
+        if causal:
+            hi = min(hi, j + window)
+        else:
+            lo, hi = max(lo, j - window + 1), min(hi, j + window)
+    return lo, hi
+
+
+def stores(B, Hq, Hkv, Sq, Sk, causal, window, keys_per_wave, nw, bmq):
+    """Yield (b, hq, key block, query block, half) for every dU store."""
+    G = Hq // Hkv
+    bnk = keys_per_wave * nw
+    for b in range(B):
+        for hk in range(Hkv):
+            for kb in range((Sk + bnk - 1) // bnk):
+                k0 = kb * bnk
+                lo_first, _ = visible_queries(k0, Sq, causal, window)
+                _, hi_last = visible_queries(min(k0 + bnk, Sk) - 1, Sq, causal, window)
+                qbeg = (lo_first // bmq) * bmq
+                nqt = (hi_last - qbeg + bmq - 1) // bmq if hi_last > qbeg else 0
+                for it in range(G * nqt):
+                    hq = hk * G + it % G
+                    q0 = qbeg + (nqt - 1 - it // G) * bmq
+                    for w in range(nw):
+                        kw = k0 + keys_per_wave * w
+                        if keys_per_wave == 32:
+                            if kw < Sk:
+                                for half in (0, 1):
+                                    yield b, hq, kw // 32, q0 // 32, half
+                        elif k0 + 16 * (w & ~1) < Sk:
+                            for kc in range(bmq // 32):
+                                if kc == 0 or q0 + 32 * kc < Sq:
+                                    yield b, hq, kw // 32, q0 // 32 + kc, w & 1
+
+
+def reads(B, Hq, Sq, Sk, causal, window):
+    for b in range(B):
+        for hq in range(Hq):
+            for qb in range((Sq + 31) // 32):
+                qs = range(qb * 32, min(qb * 32 + 32, Sq))
+                for kb in range((Sk + 31) // 32):
+                    keys = range(kb * 32, min(kb * 32 + 32, Sk))
+                    if any(visible_queries(j, Sq, causal, window)[0] <= q < visible_queries(j, Sq, causal, window)[1]
+                           for j in keys for q in qs):
+                        yield b, hq, kb, qb, 0
+                        yield b, hq, kb, qb, 1
+
+
+CASES = [(200, True, 0), (200, False, 0), (97, True, 0), (333, True, 50), (333, False, 40), (64, True, 0),
+         (1, True, 0), (129, False, 0), (161, True, 16)]
+
+
+@pytest.mark.parametrize("S,causal,window", CASES)
+@pytest.mark.parametrize("keys_per_wave,nw,bmq", [(32, 4, 32), (16, 8, 64), (16, 4, 32)])
+def test_du_blocks_cover_dq_reads(S, causal, window, keys_per_wave, nw, bmq):
+    B, Hq, Hkv = 1, 4, 2
+    nkb32, nqb32 = (S + 31) // 32, (S + 31) // 32
+    seen = set()
+    for b, hq, kb, qb, half in stores(B, Hq, Hkv, S, S, causal, window, keys_per_wave, nw, bmq):
+        assert 0 <= kb < nkb32 and 0 <= qb < nqb32, (kb, qb)
+        key = (b, hq, kb, qb, half)
+        assert key not in seen, f"half stored twice: {key}"
+        seen.add(key)
+    missing = [r for r in reads(B, Hq, S, S, causal, window) if r not in seen]
+    assert not missing, f"dq reads unwritten halves, e.g. {missing[:3]}"
