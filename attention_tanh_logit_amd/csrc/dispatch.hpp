@@ -89,7 +89,9 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
     if (fast_fits<D>(p, l, BIAS)) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
-      fwd_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      // capped logits with 2 c log2(e) <= 120 keep a fixed reference maximum
+      if (CAP && p.cl2 <= 60.0f) fwd_fast_kernel<D, CAP, BIAS, CAP><<<grid, 256, 0, l.stream>>>(p);
+      else fwd_fast_kernel<D, CAP, BIAS, false><<<grid, 256, 0, l.stream>>>(p);
       return hipGetLastError();
     }
   }

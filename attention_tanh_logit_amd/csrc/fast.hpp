@@ -336,8 +336,15 @@ __device__ __forceinline__ void xcd_order(int ntile, int ngroup, int& tile, int&
 // Capped logits are tracked through r = 1/(1 + 2^y) (s2 = c2 - 2 c2 r is
 // decreasing in r): the row maximum is c2 - 2 c2 min(r), and the probability
 // 2^(s2 - m) = 2^(fma(r, -2 c2, c2 - m)) needs no separate subtraction.
-template <int D, bool CAP, bool BIAS>
+//
+// FIXM (capped logits with 2 c2 <= 120): a capped logit never exceeds c2, so
+// the reference maximum stays at c2 for the whole row -- no running maximum,
+// no rescaling -- and 2^(s2 - c2) = 2^(-2 c2 r) lies in [2^-120, 1], inside the
+// normal range of fp32 and bf16.  The reciprocal then produces -2 c2 r
+// directly: 1 / fma(e, k, k) with k = -1/(2 c2) equals -2 c2 / (1 + e).
+template <int D, bool CAP, bool BIAS, bool FIXM>
 __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
+  static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
   constexpr int NT = 256;
   constexpr int BM = 128;
   constexpr int BN = 64;
@@ -401,7 +408,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
 
   const bool has_sink = p.sink_mode != 0;
   const float sink2 = p.sink_mode == 2 ? p.sink[hq] * kLog2e : 0.0f;
-  float m = has_sink ? sink2 : -INFINITY;
+  float m = FIXM ? lk.c2 : (has_sink ? sink2 : -INFINITY);
+  const float kfix = -0.5f / lk.c2;
   float lsum = 0.0f;
   f32x16 oacc[NOB];
 #pragma unroll
@@ -464,33 +472,37 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
           float y = scur[kb][j] * lk.a;
           if constexpr (BIAS) y = fmaf(bv[j], lk.bb, y);
           float v;
-          if constexpr (CAP) v = __builtin_amdgcn_rcpf(1.0f + fast_exp2(y));
+          if constexpr (FIXM) v = __builtin_amdgcn_rcpf(fmaf(fast_exp2(y), kfix, kfix));
+          else if constexpr (CAP) v = __builtin_amdgcn_rcpf(1.0f + fast_exp2(y));
           else v = y;
           if constexpr (decltype(masked)::value) {
             const int key = k0 + kb * 32 + acc_row(h, j);
-            v = (key >= lo_i && key < hi_i) ? v : (CAP ? INFINITY : -INFINITY);
+            v = (key >= lo_i && key < hi_i) ? v : ((CAP && !FIXM) ? INFINITY : -INFINITY);
           }
           scur[kb][j] = v;
-          ext = CAP ? fminf(ext, v) : fmaxf(ext, v);
+          if constexpr (!FIXM) ext = CAP ? fminf(ext, v) : fmaxf(ext, v);
         }
       }
       };
       if (rows_full && k0 >= lo_last && k0 + BN <= hi_first) logits(bool_c<false>{});
       else logits(bool_c<true>{});
-      ext = CAP ? fminf(ext, xor32(ext)) : fmaxf(ext, xor32(ext));
-      const float mx = CAP ? fmaf(ext, -2.0f * lk.c2, lk.c2) : ext;
+      float base = 0.0f;
+      if constexpr (!FIXM) {
+        ext = CAP ? fminf(ext, xor32(ext)) : fmaxf(ext, xor32(ext));
+        const float mx = CAP ? fmaf(ext, -2.0f * lk.c2, lk.c2) : ext;
 
-      // lazy rescale: move the reference maximum only when it grew by > 8
-      const bool grow = mx > m + 8.0f;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m;
-        const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2(m - m_new);
-        lsum *= alpha;
+        // lazy rescale: move the reference maximum only when it grew by > 8
+        const bool grow = mx > m + 8.0f;
+        if (__any(grow)) {
+          const float m_new = grow ? mx : m;
+          const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2(m - m_new);
+          lsum *= alpha;
 #pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) oacc[ob] *= alpha;
-        m = m_new;
+          for (int ob = 0; ob < NOB; ++ob) oacc[ob] *= alpha;
+          m = m_new;
+        }
+        base = (m == -INFINITY) ? 0.0f : m;
       }
-      const float base = (m == -INFINITY) ? 0.0f : m;
 
       // probabilities of key block kb, then O^T += V^T P^T for that block
       // (V^T fragments by transposing LDS reads): the exponentials of block
@@ -500,8 +512,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float pv = CAP ? fast_exp2(fmaf(scur[kb][j], -2.0f * lk.c2, lk.c2 - base))
-                               : fast_exp2(scur[kb][j] - base);
+          const float pv = FIXM  ? fast_exp2(scur[kb][j])
+                           : CAP ? fast_exp2(fmaf(scur[kb][j], -2.0f * lk.c2, lk.c2 - base))
+                                 : fast_exp2(scur[kb][j] - base);
           scur[kb][j] = pv;
           ps += pv;
         }
@@ -538,8 +551,17 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
 
   // ---- epilogue
   float ltot = lsum + xor32(lsum);
+  float oscale = 1.0f;
+  if constexpr (FIXM) {
+    // the sink logit is not capped: move the reference to it if it is larger
+    if (has_sink && sink2 > m) {
+      oscale = fast_exp2(m - sink2);
+      ltot *= oscale;
+      m = sink2;
+    }
+  }
   if (has_sink) ltot += fast_exp2(sink2 - m);
-  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  const float inv = ltot > 0.0f ? oscale / ltot : 0.0f;
   if (i < Sq) {
     bf16* orow = reinterpret_cast<bf16*>(p.out) + (((long)b * Sq + i) * p.Hq + hq) * D;
 #pragma unroll

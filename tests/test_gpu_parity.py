@@ -66,6 +66,15 @@ def test_feature_matrix_dq_recomputed(D, feat, monkeypatch):
     _check(case(**kw))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_learnable_sink_above_the_cap(D):
+    """Sink logits above the cap: the forward's fixed reference maximum (the
+    cap) moves to the sink in the epilogue."""
+    c = case(dtype="bf16", D=D, B=2, S=203, Hq=4, Hkv=2, softcap=30.0, sink_mode="learnable")
+    c["sink"] = np.array([45.0, -3.0, 60.0, 29.5], dtype=np.float32)
+    _check(c)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_cross_attention_lengths_differ(dtype):
     _check(case(dtype=dtype, D=64, B=1, S=77, Sk=301, causal=False, Hq=2, Hkv=1))
