@@ -108,7 +108,9 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
     if (fast_fits<D>(p, l, BIAS)) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
-      if (p.du) dq_du_kernel<D, CAP><<<grid, 256, 0, l.stream>>>(p);
+      // 32-key tiles, two stages, four workgroups per CU (measured against
+      // 64-key tiles and against three stages)
+      if (p.du) dq_du_kernel<D, CAP, 32, 2><<<grid, 256, 0, l.stream>>>(p);
       else dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
       return hipGetLastError();
     }

@@ -1097,19 +1097,23 @@ __device__ __forceinline__ bf16x8 du_frag16(const bf16* blk, int lane, int sb) {
 // transposing LDS reads.  No exponentials and no masks: the dk/dv kernel
 // stored masked pairs as zeros, and it wrote every block that holds a
 // visible pair (blocks no query of the wave sees are skipped, never read).
-template <int D, bool CAP>
-__global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
+template <int D, bool CAP, int BN, int NST>
+__global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams p) {
   constexpr int NT = 256;
   constexpr int BM = 128;
-  constexpr int BN = 64;
   constexpr int NKB = BN / 32;
   constexpr int NOB = D / 32;
   constexpr bool DU16 = D == 128;   // blocks written by dkdv16_kernel
+  static_assert(NST == 2 || NST == 3, "two or three tile stages");
 
+  // NST stages of (K tile, this workgroup's dU blocks), distinct objects so
+  // that the compiler sees a read of one never alias the DMA into another
   __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sK2[NST > 2 ? BN * D : 8];
   __shared__ __attribute__((aligned(16))) bf16 sU0[4 * NKB * 1024];
   __shared__ __attribute__((aligned(16))) bf16 sU1[4 * NKB * 1024];
+  __shared__ __attribute__((aligned(16))) bf16 sU2[NST > 2 ? 4 * NKB * 1024 : 8];
 
   // XCD-aware, longest-first numbering as in the other kernels
   int qt, hq, b;
@@ -1156,29 +1160,41 @@ __global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
   for (int ob = 0; ob < NOB; ++ob) qacc[ob] = f32x16{};
 
   auto visible = [&](int kb32) { return kb32 < whi && kb32 + 32 > wlo && kb32 < Sk; };
-  // the tile's K rows (all waves) and this wave's dU^T blocks
+  // the tile's K rows (all waves) and this wave's dU^T blocks; every thread
+  // issues the same number of loads per tile (a block no query of the wave
+  // sees is read through an empty range, which fills zeros and touches no
+  // memory), so the loads of a later tile can be left in flight by count
   auto fetch = [&](int k0, bf16* tK, bf16* tU) {
     load_tile<BN, D, NT, true>(tK, kbase, kstride, k0, Sk);
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
-      if (visible(k0 + 32 * kk)) {
-        const bf16* blk = ublocks + (long)((k0 >> 5) + kk) * ukstride;
-        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(blk), 0, 2048, 0x00020000);
+      const bool vis = visible(k0 + 32 * kk);
+      const bf16* blk = ublocks + (vis ? (long)((k0 >> 5) + kk) * ukstride : 0);
+      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(blk), 0, vis ? 2048 : 0, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          dma16(rsrc, 16 * (DU16 ? du_slot16(64 * u + lane) : du_slot(64 * u + lane)),
-                tU + (w * NKB + kk) * 1024 + 64 * u * 8);
-      }
+      for (int u = 0; u < 2; ++u)
+        dma16(rsrc, 16 * (DU16 ? du_slot16(64 * u + lane) : du_slot(64 * u + lane)),
+              tU + (w * NKB + kk) * 1024 + 64 * u * 8);
     }
   };
 
   const int kbeg = (lo_first / BN) * BN;
-  if (kbeg < hi_last) fetch(kbeg, sK0, sU0);
-  wait_loads();
+  const int nt = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
+  if (nt > 0) fetch(kbeg, sK0, sU0);
+  if (NST > 2 && nt > 1) fetch(kbeg + BN, sK1, sU1);
+  if (NST > 2 && nt > 1) {
+    // tile 0 landed, tile 1 may stay in flight
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(BN * D / 8 / NT + 2 * NKB) : "memory");
+  } else {
+    wait_loads();
+  }
   __syncthreads();
 
-  auto step = [&](const bf16* tK, const bf16* tU, bf16* nK, bf16* nU, int k0) {
-    if (k0 + BN < hi_last) fetch(k0 + BN, nK, nU);
+  // tile t from (tK, tU); tile t + NST - 1 into (nK, nU), the buffers of tile t - 1
+  auto step = [&](const bf16* tK, const bf16* tU, bf16* nK, bf16* nU, int t) __attribute__((always_inline)) {
+    const int k0 = kbeg + t * BN;
+    const bool issued = t + NST - 1 < nt;
+    if (issued) fetch(kbeg + (t + NST - 1) * BN, nK, nU);
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
       if (visible(k0 + 32 * kk)) {
@@ -1191,12 +1207,22 @@ __global__ __launch_bounds__(256, 2) void dq_du_kernel(BwdParams p) {
         }
       }
     }
-    wait_loads();
+    // tile t + 1 landed; with three stages tile t + 2 may stay in flight
+    if (NST > 2 && issued) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(BN * D / 8 / NT + 2 * NKB) : "memory");
+    else wait_loads();
     __syncthreads();
   };
-  for (int k0 = kbeg; k0 < hi_last; k0 += 2 * BN) {
-    step(sK0, sU0, sK1, sU1, k0);
-    if (k0 + BN < hi_last) step(sK1, sU1, sK0, sU0, k0 + BN);
+  if constexpr (NST == 2) {
+    for (int t = 0; t < nt; t += 2) {
+      step(sK0, sU0, sK1, sU1, t);
+      if (t + 1 < nt) step(sK1, sU1, sK0, sU0, t + 1);
+    }
+  } else {
+    for (int t = 0; t < nt; t += 3) {
+      step(sK0, sU0, sK2, sU2, t);
+      if (t + 1 < nt) step(sK1, sU1, sK0, sU0, t + 1);
+      if (t + 2 < nt) step(sK2, sU2, sK1, sU1, t + 2);
+    }
   }
 
   if (i < Sq) {
