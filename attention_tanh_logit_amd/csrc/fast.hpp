@@ -960,6 +960,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
         mma16(dpacc[qb], fo.frag(tO, 16 * qb, c), vf[c]);
       }
     }
+    // keep fragment reads in flight ahead of their MFMAs
+    ATL_READ_AHEAD(8, 1, 2 * NC * NQB);
 
     const bf16* bcol = nullptr;
     bf16* dbcol = nullptr;
@@ -1012,12 +1014,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     }
 
     // dV^T += dO^T P, dK^T += Q^T dU (rows: columns 16 ob + 4g + e; lane's key r)
+    // transposing reads keep their order through scheduling: request the
+    // fragments of column block ob + TRA before the MFMAs of block ob
+    constexpr int TRA = 2;
+    bf16x8 tro[TRA + 1][NKC], trq[TRA + 1][NKC];
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob) {
+    for (int a = 0; a < TRA; ++a) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        mma16(vacc[ob], fo.frag_tr(tO, 32 * kc, ob), pf[kc]);
-        mma16(kacc[ob], fo.frag_tr(tQ, 32 * kc, ob), uf[kc]);
+        tro[a][kc] = fo.frag_tr(tO, 32 * kc, a);
+        trq[a][kc] = fo.frag_tr(tQ, 32 * kc, a);
+      }
+    }
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      if (ob + TRA < NOB) {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          tro[(ob + TRA) % (TRA + 1)][kc] = fo.frag_tr(tO, 32 * kc, ob + TRA);
+          trq[(ob + TRA) % (TRA + 1)][kc] = fo.frag_tr(tQ, 32 * kc, ob + TRA);
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        mma16(vacc[ob], tro[ob % (TRA + 1)][kc], pf[kc]);
+        mma16(kacc[ob], trq[ob % (TRA + 1)][kc], uf[kc]);
       }
     }
 
