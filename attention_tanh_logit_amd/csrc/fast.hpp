@@ -521,10 +521,24 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
         bf16x8 pf[2];
         pf[0] = to_frag(scur[kb], 0, (bf16*)nullptr);
         pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
+        // V^T fragments of column block ob + 2 requested before the MFMAs of block ob
+        {
+          constexpr int TA = 2;
+          bf16x8 tv[TA + 1][2];
 #pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) {
+          for (int a2 = 0; a2 < TA; ++a2) {
 #pragma unroll
-          for (int sb = 0; sb < 2; ++sb) mma(oacc[ob], fo.frag_tr(tV, kb * 32 + 16 * sb, ob), pf[sb]);
+            for (int sb = 0; sb < 2; ++sb) tv[a2][sb] = fo.frag_tr(tV, kb * 32 + 16 * sb, a2);
+          }
+#pragma unroll
+          for (int ob = 0; ob < NOB; ++ob) {
+            if (ob + TA < NOB) {
+#pragma unroll
+              for (int sb = 0; sb < 2; ++sb) tv[(ob + TA) % (TA + 1)][sb] = fo.frag_tr(tV, kb * 32 + 16 * sb, ob + TA);
+            }
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) mma(oacc[ob], tv[ob % (TA + 1)][sb], pf[sb]);
+          }
         }
       }
       lsum += ps;
