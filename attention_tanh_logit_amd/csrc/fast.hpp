@@ -594,25 +594,23 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
 
 // ============================================================== backward: dk, dv, dbias
 
-// One workgroup = 4 waves = 128 keys of one KV head; the K^T fragments of
-// each wave's 32 keys stay in registers and the workgroup's V rows stay in
-// LDS (keeping the wave under 256 registers with both accumulators),
-// dK^T / dV^T accumulate in registers over the GQA group's query heads and
-// their visible 32-query tiles, which stream through a double-buffered LDS
-// tile (rows stored through swp).
+// D = 64.  One workgroup = 4 waves = 128 keys of one KV head; the K^T
+// fragments of each wave's 32 keys stay in registers and the workgroup's V
+// rows stay in LDS (keeping the wave under 256 registers with both
+// accumulators), dK^T / dV^T accumulate in registers over the GQA group's
+// query heads and their visible 32-query tiles, which stream through a
+// double-buffered LDS tile (rows stored through swp).  (D = 128 runs
+// dkdv16_kernel.)
 template <int D, bool CAP, bool BIAS>
-__global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
+  static_assert(D == 64, "32-key waves at D = 64 only");
   constexpr int NT = 256;
   constexpr int BNK = 128;
   constexpr int BMQ = 32;
   constexpr int NOB = D / 32;
   constexpr int NCC = D / 16;
 
-  // at D > 64 the K rows stay in LDS as well, which leaves the register file
-  // to the two accumulators and to fragments read ahead of their MFMAs
-  constexpr bool KLDS = D > 64;
   __shared__ __attribute__((aligned(16))) bf16 sVr[BNK * D];
-  __shared__ __attribute__((aligned(16))) bf16 sKr[KLDS ? BNK * D : 8];
   __shared__ __attribute__((aligned(16))) bf16 sQ0[BMQ * D];
   __shared__ __attribute__((aligned(16))) bf16 sQ1[BMQ * D];
   __shared__ __attribute__((aligned(16))) bf16 sO0[BMQ * D];
@@ -644,11 +642,8 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const FragOfs<D, true> fo(lane);
 
-  bf16x8 kf[KLDS ? 1 : NCC];
-  if constexpr (KLDS) {
-    load_tile<BNK, D, NT, false>(sKr, reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D,
-                                 (long)p.Hkv * D, k0, Sk);
-  } else {
+  bf16x8 kf[NCC];
+  {
     const bf16* krow = reinterpret_cast<const bf16*>(p.k) + (((long)b * Sk + jc) * p.Hkv + hk) * D;
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(krow + 16 * cc + 8 * h);
@@ -728,12 +723,9 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void dkdv_fast_kernel(BwdParam
     }
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
-      mma(sacc, fo.frag(tQ, 0, cc), KLDS ? fo.frag(sKr, w * 32, cc) : kf[KLDS ? 0 : cc]);
+      mma(sacc, fo.frag(tQ, 0, cc), kf[cc]);
       mma(dpacc, fo.frag(tO, 0, cc), fo.frag(sVr, w * 32, cc));
     }
-    // issue the fragment reads ahead of their MFMAs (a single wave per SIMD
-    // has nothing else to hide the LDS latency behind)
-    if constexpr (KLDS) ATL_READ_AHEAD(8, 2, 2 * NCC);
 
     // ---- P and dU/4 = P (dP - delta) (1 - t^2)/4
     const bf16* bcol = nullptr;
