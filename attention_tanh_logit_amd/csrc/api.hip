@@ -149,11 +149,31 @@ bool du_path(const attn_args* a) {
          du_raw_bytes(a) <= du_max_bytes();
 }
 
+// Query-head splits of the bf16 dk/dv kernels (both take 128 keys per
+// workgroup): the smallest divisor of G that gives at least 1024 workgroups
+// (four per CU), so that a small batch with a wide GQA group does not leave
+// the GPU to a few long workgroups; 1 when there are enough already.
+int head_split(const attn_args* a) {
+  if (!fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr)) return 1;
+  const long wgs = (long)((a->Sk + 127) / 128) * a->Hkv * a->B;
+  const int G = a->Hq / a->Hkv;
+  int hs = 1;
+  for (int s = 2; s <= G && wgs * hs < 1024; ++s)
+    if (G % s == 0) hs = s;
+  return hs;
+}
+
+size_t dkv_part_bytes(const attn_args* a) {
+  const int hs = head_split(a);
+  return hs > 1 ? (size_t)2 * hs * a->B * a->Sk * a->Hkv * a->D * sizeof(float) : 0;
+}
+
 size_t bwd_ws(const attn_args* a) {
   size_t s = seg_bytes(a);
   s += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));  // delta
   if (a->sink_mode == ATTN_SINK_LEARNABLE) s += align_up((size_t)a->Hq * a->B * pre_blocks(a) * sizeof(float));
   if (du_path(a)) s += align_up(du_raw_bytes(a));
+  s += align_up(dkv_part_bytes(a));
   return s;
 }
 
@@ -323,7 +343,12 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
   p.du = nullptr;
   p.nkb32 = (a->Sk + 31) / 32;
   p.nqb32 = (a->Sq + 31) / 32;
-  if (du_path(a)) p.du = ws;
+  if (du_path(a)) {
+    p.du = ws;
+    ws += align_up(du_raw_bytes(a));
+  }
+  p.hsplit = head_split(a);
+  p.dkv_part = p.hsplit > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   p.delta = delta;
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;

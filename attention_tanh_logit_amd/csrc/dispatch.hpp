@@ -130,11 +130,17 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
       if constexpr (D == 128) {
         // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64 queries)
         constexpr int NW = 8, BMQ = 64;
-        const dim3 grid((l.Sk + 16 * NW - 1) / (16 * NW), p.Hkv, l.B);
+        const dim3 grid((l.Sk + 16 * NW - 1) / (16 * NW), p.Hkv * p.hsplit, l.B);
         dkdv16_kernel<D, CAP, BIAS, NW, BMQ><<<grid, 64 * NW, 0, l.stream>>>(p);
       } else {
-        const dim3 grid((l.Sk + 127) / 128, p.Hkv, l.B);
+        const dim3 grid((l.Sk + 127) / 128, p.Hkv * p.hsplit, l.B);
         dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+      }
+      if (p.hsplit > 1) {
+        const long nel = (long)l.B * l.Sk * p.Hkv * D;
+        const float kscale = p.scale * (CAP ? 4.0f : 1.0f);
+        dkv_reduce_kernel<bf16><<<(unsigned)((nel / 4 + 255) / 256), 256, 0, l.stream>>>(
+            p.dkv_part, p.hsplit, nel, kscale, reinterpret_cast<bf16*>(p.dk), reinterpret_cast<bf16*>(p.dv));
       }
       return hipGetLastError();
     }

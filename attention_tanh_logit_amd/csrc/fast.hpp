@@ -623,13 +623,16 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   // each XCD takes whole (batch row, KV head) groups, key block 0 (the
   // longest under a causal mask) first; all key blocks of a group sweep the
   // same query tiles (from the last one backwards, in step) through one L2
-  int kb, hk, b;
+  int kb, hk, b, split;
   {
     int grp;
     xcd_order(gridDim.x, gridDim.y * gridDim.z, kb, grp);
-    hk = grp % gridDim.y;
+    const int y = grp % gridDim.y;   // the splits of one KV head are adjacent
+    hk = y / p.hsplit;
+    split = y % p.hsplit;
     b = grp / gridDim.y;
   }
+  const int GS = p.G / p.hsplit;     // query heads of this workgroup
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -660,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   const bool keys_full = (k0 + BNK <= Sk);
   const int qbeg = (lo_first / BMQ) * BMQ;
   const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
-  const int nitems = p.G * nqt;
+  const int nitems = GS * nqt;
 
   f32x16 kacc[NOB], vacc[NOB];
 #pragma unroll
@@ -673,8 +676,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   float nl = 0.0f, nd = 0.0f;
   int nq = 0;
   auto fetch = [&](int it, bf16* nQ, bf16* nO) {
-    const int hq = hk * p.G + it % p.G;
-    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
+    const int hq = hk * p.G + split * GS + it % GS;
+    const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
     const long hoff = ((long)b * Sq * p.Hq + hq) * D;
     load_tile<BMQ, D, NT, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
     load_tile<BMQ, D, NT, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
@@ -703,8 +706,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
                   float* nD, int it) {
     const bool more = it + 1 < nitems;
     if (more) fetch(it + 1, nQ, nO);
-    const int hq = hk * p.G + it % p.G;
-    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
+    const int hq = hk * p.G + split * GS + it % GS;
+    const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
 
     // ---- S = Q K^T, dP - delta = dO V^T - delta (rows: queries through swp;
     // columns: this wave's keys).  Per query the LDS stats hold
@@ -808,7 +811,31 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
     if (it + 1 < nitems) step(sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, it + 1);
   }
 
-  if (j < Sk) {
+  if (j < Sk && p.hsplit > 1) {
+    // unscaled fp32 partials of this split
+    const long nel = (long)gridDim.z * Sk * p.Hkv * D;
+    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    float* kp = p.dkv_part + (long)split * nel + off;
+    float* vp = p.dkv_part + (long)(p.hsplit + split) * nel + off;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int d = ob * 32 + 16 * hf + 8 * h;
+#pragma unroll
+        for (int e4 = 0; e4 < 2; ++e4) {
+          f32x4 kv, vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[e] = kacc[ob][8 * hf + 4 * e4 + e];
+            vv[e] = vacc[ob][8 * hf + 4 * e4 + e];
+          }
+          *reinterpret_cast<f32x4*>(kp + d + 4 * e4) = kv;
+          *reinterpret_cast<f32x4*>(vp + d + 4 * e4) = vv;
+        }
+      }
+    }
+  } else if (j < Sk) {
     const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
     bf16* krow = reinterpret_cast<bf16*>(p.dk) + off;
     bf16* vrow = reinterpret_cast<bf16*>(p.dv) + off;
@@ -865,13 +892,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
 
   // XCD-aware, longest-first numbering and a lockstep query sweep, as in
   // the 32-key kernel
-  int kb, hk, b;
+  int kb, hk, b, split;
   {
     int grp;
     xcd_order(gridDim.x, gridDim.y * gridDim.z, kb, grp);
-    hk = grp % gridDim.y;
+    const int y = grp % gridDim.y;   // the splits of one KV head are adjacent
+    hk = y / p.hsplit;
+    split = y % p.hsplit;
     b = grp / gridDim.y;
   }
+  const int GS = p.G / p.hsplit;     // query heads of this workgroup
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -908,7 +938,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   const bool keys_full = (k0 + BNK <= Sk);
   const int qbeg = (lo_first / BMQ) * BMQ;
   const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
-  const int nitems = p.G * nqt;
+  const int nitems = GS * nqt;
 
   f32x4 kacc[NOB], vacc[NOB];
 #pragma unroll
@@ -917,8 +947,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   float nl = 0.0f, nd = 0.0f;
   int nq = 0;
   auto fetch = [&](int it, bf16* nQ, bf16* nO) {
-    const int hq = hk * p.G + it % p.G;
-    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
+    const int hq = hk * p.G + split * GS + it % GS;
+    const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
     const long hoff = ((long)b * Sq * p.Hq + hq) * D;
     load_tile<BMQ, D, NT, false, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
     load_tile<BMQ, D, NT, false, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
@@ -946,8 +976,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
                   float* nD, int it) {
     const bool more = it + 1 < nitems;
     if (more) fetch(it + 1, nQ, nO);
-    const int hq = hk * p.G + it % p.G;
-    const int q0 = qbeg + (nqt - 1 - it / p.G) * BMQ;
+    const int hq = hk * p.G + split * GS + it % GS;
+    const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
 
     // S and dP - delta; the stats of queries 16qb + 4g .. + 3 are one f32x4
     const f32x4* L4 = reinterpret_cast<const f32x4*>(tL);
@@ -1057,7 +1087,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     if (it + 1 < nitems) step(sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, it + 1);
   }
 
-  if (j < Sk) {
+  if (j < Sk && p.hsplit > 1) {
+    // unscaled fp32 partials of this split
+    const long nel = (long)gridDim.z * Sk * p.Hkv * D;
+    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    float* kp = p.dkv_part + (long)split * nel + off;
+    float* vp = p.dkv_part + (long)(p.hsplit + split) * nel + off;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      *reinterpret_cast<f32x4*>(kp + 16 * ob + 4 * g) = kacc[ob];
+      *reinterpret_cast<f32x4*>(vp + 16 * ob + 4 * g) = vacc[ob];
+    }
+  } else if (j < Sk) {
     const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
     bf16* krow = reinterpret_cast<bf16*>(p.dk) + off;
     bf16* vrow = reinterpret_cast<bf16*>(p.dv) + off;
@@ -1074,6 +1115,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       *reinterpret_cast<bf16x4*>(vrow + 16 * ob + 4 * g) = vv;
     }
   }
+}
+
+// ============================================================== backward: split reduction
+
+// dk = kscale * sum of the dK partials, dv = sum of the dV partials, over the
+// hsplit query-head splits in a fixed order (deterministic); 4 elements per
+// thread, nel = B * Sk * Hkv * D (a multiple of 4).
+template <typename T>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* part, int hsplit, long nel, float kscale, T* dk,
+                                                        T* dv) {
+  static_assert(std::is_same<T, bf16>::value, "bf16 outputs");
+  const long i = 4 * ((long)blockIdx.x * 256 + threadIdx.x);
+  if (i >= nel) return;
+  f32x4 sk = f32x4{}, sv = f32x4{};
+  for (int s = 0; s < hsplit; ++s) {
+    sk += *reinterpret_cast<const f32x4*>(part + (long)s * nel + i);
+    sv += *reinterpret_cast<const f32x4*>(part + (long)(hsplit + s) * nel + i);
+  }
+  bf16x4 ok, ov;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ok[e] = (bf16)(sk[e] * kscale);
+    ov[e] = (bf16)sv[e];
+  }
+  *reinterpret_cast<bf16x4*>(dk + i) = ok;
+  *reinterpret_cast<bf16x4*>(dv + i) = ov;
 }
 
 // ============================================================== backward: dq from dU

@@ -68,6 +68,12 @@ struct BwdParams {
   float scale;
   float sl2, xc, bc, cl2;
   int reverse;
+  // bf16 dk/dv kernels: the GQA group's query heads split over hsplit
+  // workgroups per key block (grid.y = Hkv * hsplit); with hsplit > 1 each
+  // writes unscaled fp32 partial dK, dV to dkv_part ([2][hsplit][B, Sk, Hkv, D])
+  // and dkv_reduce_kernel sums them in a fixed order
+  int hsplit;
+  float* dkv_part;
 };
 
 template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };

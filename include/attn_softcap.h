@@ -110,7 +110,12 @@ attn_status attn_validate(const attn_args* a);
  * in the environment variable ATTN_SOFTCAP_DU_MAX_BYTES), e.g. 4 GiB at
  * B=4, Hq=32, S=4096; beyond that dq recomputes the probabilities instead.
  * The choice is made again on every call: keep the variable unchanged
- * between attn_bwd_workspace_size and the backward calls it sizes. */
+ * between attn_bwd_workspace_size and the backward calls it sizes.
+ * For the same bf16 cases, when B*Hkv*ceil(Sk/128) < 1024 the dk/dv kernel
+ * splits each GQA group's query heads over s workgroups (s the smallest
+ * divisor of Hq/Hkv reaching 1024 workgroups, else the largest) and the
+ * workspace also holds 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial dK/dV, summed
+ * in a fixed order (the results stay deterministic). */
 size_t attn_fwd_workspace_size(const attn_args* a);
 size_t attn_bwd_workspace_size(const attn_args* a);
 

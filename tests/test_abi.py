@@ -129,5 +129,37 @@ def test_bwd_workspace_carries_du_blocks_for_bf16_d64_d128(monkeypatch):
     monkeypatch.delenv("ATTN_SOFTCAP_DU_MAX_BYTES", raising=False)
     f32 = _args(dtype=1)
     g32 = _args(dtype=1, D=256)
-    assert L.attn_bwd_workspace_size(ctypes.byref(f32)) == without
-    assert L.attn_bwd_workspace_size(ctypes.byref(g32)) == without
+    # the bf16 run also carries the fp32 dK/dV partials of its head split
+    assert L.attn_bwd_workspace_size(ctypes.byref(f32)) == without - _split_partials(_args())
+    assert L.attn_bwd_workspace_size(ctypes.byref(g32)) == without - _split_partials(_args())
+
+
+def _head_split(B, Sk, Hq, Hkv):
+    """Smallest divisor s of G = Hq/Hkv with ceil(Sk/128)*Hkv*B*s >= 1024 (else the largest tried)."""
+    wgs, G, hs = -(-Sk // 128) * Hkv * B, Hq // Hkv, 1
+    for s in range(2, G + 1):
+        if wgs * hs >= 1024:
+            break
+        if G % s == 0:
+            hs = s
+    return hs
+
+
+def _split_partials(a):
+    hs = _head_split(a.B, a.Sk, a.Hq, a.Hkv)
+    n = 2 * hs * a.B * a.Sk * a.Hkv * a.D * 4 if hs > 1 else 0
+    return (n + 255) // 256 * 256
+
+
+def test_bwd_workspace_carries_split_partials_only_for_small_grids(monkeypatch):
+    """bf16 dk/dv splits a GQA group's query heads over workgroups when the grid is small:
+    fp32 partial dK/dV for each split in the workspace; none for a grid of >= 1024 workgroups."""
+    L = A.lib()
+    monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", "0")
+    for B, S, Hq, Hkv, D, hs in ((2, 256, 8, 2, 128, 4), (1, 4096, 64, 8, 64, 4), (4, 4096, 32, 8, 128, 1),
+                                 (1, 4096, 24, 8, 128, 3)):
+        assert _head_split(B, S, Hq, Hkv) == hs
+        bf = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D)
+        fp = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D, dtype=1)
+        diff = L.attn_bwd_workspace_size(ctypes.byref(bf)) - L.attn_bwd_workspace_size(ctypes.byref(fp))
+        assert diff == _split_partials(bf), (B, S, Hq, Hkv, D)
