@@ -83,15 +83,20 @@ template <int D, class Params>
 bool fast_fits(const Params& p, const Launch& l, bool bias) {
   return fast_ok(true, D, p.Hq, p.Hkv, l.Sk, bias);
 }
+// the forward also takes D = 256 (output columns split over two waves)
+inline bool fast_fwd_ok(int D, int Hq, int Hkv, int Sk, bool bias) {
+  return D == 256 ? fast_ok(true, 128, 2 * Hq, 2 * Hkv, Sk, bias) : fast_ok(true, D, Hq, Hkv, Sk, bias);
+}
 
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
-  if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS)) {
+  if constexpr (use_fast<T, D>() || (std::is_same<T, bf16>::value && D == 256)) {
+    if (fast_fwd_ok(D, p.Hq, p.Hkv, l.Sk, BIAS)) {
+      constexpr int NT = D > 128 ? 512 : 256;
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // capped logits with 2 c log2(e) <= 120 keep a fixed reference maximum
-      if (CAP && p.cl2 <= 60.0f) fwd_fast_kernel<D, CAP, BIAS, CAP><<<grid, 256, 0, l.stream>>>(p);
-      else fwd_fast_kernel<D, CAP, BIAS, false><<<grid, 256, 0, l.stream>>>(p);
+      if (CAP && p.cl2 <= 60.0f) fwd_fast_kernel<D, CAP, BIAS, CAP><<<grid, NT, 0, l.stream>>>(p);
+      else fwd_fast_kernel<D, CAP, BIAS, false><<<grid, NT, 0, l.stream>>>(p);
       return hipGetLastError();
     }
   }

@@ -342,16 +342,22 @@ __device__ __forceinline__ void xcd_order(int ntile, int ngroup, int& tile, int&
 // no rescaling -- and 2^(s2 - c2) = 2^(-2 c2 r) lies in [2^-120, 1], inside the
 // normal range of fp32 and bf16.  The reciprocal then produces -2 c2 r
 // directly: 1 / fma(e, k, k) with k = -1/(2 c2) equals -2 c2 / (1 + e).
+//
+// D = 256: the output columns split over NSL = 2 waves per 32-row group (8
+// waves, 128 rows); both compute the row's logits and probabilities, each
+// accumulates its 128 columns of O, so O fits the register file beside the
+// whole row of Q^T fragments.
 template <int D, bool CAP, bool BIAS, bool FIXM>
-__global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
+__global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast_kernel(FwdParams p) {
   static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
-  constexpr int NT = 256;
+  constexpr int NSL = D > 128 ? 2 : 1;     // column slices of O per row group
+  constexpr int NT = 256 * NSL;
   constexpr int BM = 128;
-  constexpr int BN = 64;
+  constexpr int BN = D > 128 ? 32 : 64;  // D = 256: one 32-key block per tile (registers)
   constexpr bool PIPE = D <= 64;
   constexpr bool ROWPERM_TR = false;  // V rows in key order
   constexpr int NKB = BN / 32;
-  constexpr int NOB = D / 32;
+  constexpr int NOB = D / 32 / NSL;     // this wave's output column blocks
   constexpr int NCC = D / 16;
 
   // two LDS buffers per tile as distinct objects: the compiler can then see
@@ -377,10 +383,15 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
   const int w = threadIdx.x >> 6;
   const int n = lane & 31;
   const int h = lane >> 5;
+  const int rg = w / NSL;               // row group
+  const int sl = w % NSL;               // output column slice: columns 32 NOB sl ..
   const int q0 = qt * BM;
-  const int i = q0 + w * 32 + n;
+  const int i = q0 + rg * 32 + n;
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const FragOfs<D, ROWPERM_TR> fo(lane);
+  // the swizzle permutes 16-byte slots inside 128-column groups only, so a
+  // slice's V^T fragments are those of column block ob at a column offset
+  const int colofs = 32 * NOB * sl;
 
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
   const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
@@ -523,18 +534,19 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
         pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
         // V^T fragments of column block ob + 2 requested before the MFMAs of block ob
         {
-          constexpr int TA = 2;
+          constexpr int TA = D > 128 ? 1 : 2;
           bf16x8 tv[TA + 1][2];
 #pragma unroll
           for (int a2 = 0; a2 < TA; ++a2) {
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) tv[a2][sb] = fo.frag_tr(tV, kb * 32 + 16 * sb, a2);
+            for (int sb = 0; sb < 2; ++sb) tv[a2][sb] = fo.frag_tr(tV + colofs, kb * 32 + 16 * sb, a2);
           }
 #pragma unroll
           for (int ob = 0; ob < NOB; ++ob) {
             if (ob + TA < NOB) {
 #pragma unroll
-              for (int sb = 0; sb < 2; ++sb) tv[(ob + TA) % (TA + 1)][sb] = fo.frag_tr(tV, kb * 32 + 16 * sb, ob + TA);
+              for (int sb = 0; sb < 2; ++sb)
+                tv[(ob + TA) % (TA + 1)][sb] = fo.frag_tr(tV + colofs, kb * 32 + 16 * sb, ob + TA);
             }
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) mma(oacc[ob], tv[ob % (TA + 1)][sb], pf[sb]);
@@ -585,10 +597,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fast_kernel(FwdParams p) {
         float vals[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vals[e] = oacc[ob][8 * hf + e] * inv;
-        store8<bf16>(orow + ob * 32 + 16 * hf + 8 * h, vals);
+        store8<bf16>(orow + colofs + ob * 32 + 16 * hf + 8 * h, vals);
       }
     }
-    if (h == 0) p.lse[((long)b * p.Hq + hq) * Sq + i] = ltot > 0.0f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+    if (h == 0 && sl == 0) p.lse[((long)b * p.Hq + hq) * Sq + i] = ltot > 0.0f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
   }
 }
 
