@@ -69,29 +69,28 @@ template <typename T, int D> constexpr int dq_rows() { return 32 * DqCfg<T, D>::
 template <typename T, int D> constexpr int dkdv_keys() { return 32 * DkdvCfg<T, D>::NKG; }
 
 // bf16 with D <= 128 takes the pipelined kernels of fast.hpp
-template <typename T, int D> constexpr bool use_fast() { return std::is_same<T, bf16>::value && (D == 64 || D == 128); }
+template <typename T, int D> constexpr bool use_fast() {
+  return std::is_same<T, bf16>::value && (D == 64 || D == 128 || D == 256);
+}
 
 // The fast kernels address a streamed tile through a buffer resource with
 // 32-bit byte offsets: 128 rows of the widest token stride must stay below
 // 2^31 bytes.  The fast path reads bias rows 8 keys at a time.
 inline bool fast_ok(bool bf16_input, int D, int Hq, int Hkv, int Sk, bool bias) {
   const long stride = (long)(Hq > Hkv ? Hq : Hkv) * D;
-  return bf16_input && (D == 64 || D == 128) && 128L * stride * 2 < (1L << 31) &&
+  return bf16_input && (D == 64 || D == 128 || D == 256) && 128L * stride * 2 < (1L << 31) &&
          (!bias || (Sk % 8 == 0 && Sk >= 8));
 }
 template <int D, class Params>
 bool fast_fits(const Params& p, const Launch& l, bool bias) {
   return fast_ok(true, D, p.Hq, p.Hkv, l.Sk, bias);
 }
-// the forward also takes D = 256 (output columns split over two waves)
-inline bool fast_fwd_ok(int D, int Hq, int Hkv, int Sk, bool bias) {
-  return D == 256 ? fast_ok(true, 128, 2 * Hq, 2 * Hkv, Sk, bias) : fast_ok(true, D, Hq, Hkv, Sk, bias);
-}
+
 
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
-  if constexpr (use_fast<T, D>() || (std::is_same<T, bf16>::value && D == 256)) {
-    if (fast_fwd_ok(D, p.Hq, p.Hkv, l.Sk, BIAS)) {
+  if constexpr (use_fast<T, D>()) {
+    if (fast_fits<D>(p, l, BIAS)) {
       constexpr int NT = D > 128 ? 512 : 256;
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // capped logits with 2 c log2(e) <= 120 keep a fixed reference maximum
@@ -115,9 +114,15 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // 32-key tiles, two stages, four workgroups per CU (measured against
       // 64-key tiles and against three stages)
-      if (p.du) dq_du_kernel<D, CAP, 32, 2><<<grid, 256, 0, l.stream>>>(p);
-      else dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
-      return hipGetLastError();
+      if (p.du) {
+        dq_du_kernel<D, CAP, 32, 2><<<grid, 256, 0, l.stream>>>(p);
+        return hipGetLastError();
+      }
+      // the recomputing dq kernel holds whole Q and dO rows: D <= 128 only
+      if constexpr (D <= 128) {
+        dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+        return hipGetLastError();
+      }
     }
   }
   using C = DqCfg<T, D>;
@@ -132,10 +137,11 @@ template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
     if (fast_fits<D>(p, l, BIAS)) {
-      if constexpr (D == 128) {
-        // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64 queries)
-        constexpr int NW = 8, BMQ = 64;
-        const dim3 grid((l.Sk + 16 * NW - 1) / (16 * NW), p.Hkv * p.hsplit, l.B);
+      if constexpr (D >= 128) {
+        // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64
+        // queries); at D = 256 two waves per 16 keys and 32-query items
+        constexpr int NW = 8, BMQ = D > 128 ? 32 : 64, BNK = D > 128 ? 64 : 128;
+        const dim3 grid((l.Sk + BNK - 1) / BNK, p.Hkv * p.hsplit, l.B);
         dkdv16_kernel<D, CAP, BIAS, NW, BMQ><<<grid, 64 * NW, 0, l.stream>>>(p);
       } else {
         const dim3 grid((l.Sk + 127) / 128, p.Hkv * p.hsplit, l.B);

@@ -176,10 +176,11 @@ struct FragOfs {
 
 // Per-lane fragment offsets for v_mfma_f32_16x16x32_bf16 operands from a
 // D = 128 tile stored with swz16.  Lane r + 16g:
-//  * frag(row0, c): row row0 + r, columns 8(c + 4g) .. + 7 (the A or B
-//    operand of a product that contracts over the columns; lanes 16 apart
-//    take chunks 64 bytes apart, which measured free of bank conflicts where
-//    adjacent chunks (columns 32c + 8g) conflicted two ways);
+//  * frag(row0, c): row row0 + r, 16-byte chunk (c % 4) + 4g + 16 (c / 4)
+//    (the A or B operand of a product that contracts over the columns;
+//    lanes 16 apart take chunks 64 bytes apart, which measured free of bank
+//    conflicts where adjacent chunks (columns 32c + 8g) conflicted two ways;
+//    the swizzle permutes chunks inside 128-column groups only);
 //  * frag_tr(row0, ob): X[row0 + sigma(g, i)][16 ob + r], i = 0..7, with
 //    sigma(g, i) = 4g + i for i < 4 and 16 + 4g + i - 4 after, which is the
 //    query order in which a 16x16 accumulator pair (rows 16qb + 4g + e) hands
@@ -187,7 +188,7 @@ struct FragOfs {
 //    s + 16g points at row 4g + s/4 (+16), columns 16 ob + 4(s%4) .. + 3.
 template <int D>
 struct Frag16Ofs {
-  static_assert(D == 128, "laid out for 256-byte rows");
+  static_assert(D == 128 || D == 256, "laid out for 256- or 512-byte rows");
   int pbase, pxor, tbase, txor;
   __device__ __forceinline__ explicit Frag16Ofs(int lane) {
     const int r = lane & 15, g = lane >> 4;
@@ -202,7 +203,7 @@ struct Frag16Ofs {
     txor = opaque(8 * (f & 14));
   }
   __device__ __forceinline__ bf16x8 frag(const bf16* tile, int row0, int c) const {
-    return *reinterpret_cast<const bf16x8*>(tile + row0 * D + pbase + ((8 * c) ^ pxor));
+    return *reinterpret_cast<const bf16x8*>(tile + row0 * D + pbase + ((8 * (c & 3)) ^ pxor) + 128 * (c >> 2));
   }
   __device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int row0, int ob) const {
     const bf16* a = tile + row0 * D + tbase + ((16 * ob) ^ txor);
@@ -886,12 +887,15 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
 // kappa + 16 g' holding dU(16 kh + kappa, queries sigma(g', 0..7)).
 template <int D, bool CAP, bool BIAS, int NW, int BMQ>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
+  // D = 256: waves w and w + 1 share 16 keys and split dK^T, dV^T by columns
+  // (each recomputes S, dP and the gradients of the pair's keys)
+  constexpr int NSL = D > 128 ? 2 : 1;
   constexpr int NT = 64 * NW;
-  constexpr int BNK = 16 * NW;
+  constexpr int BNK = 16 * NW / NSL;
   constexpr int NQB = BMQ / 16;
   constexpr int NKC = BMQ / 32;
   constexpr int NC = D / 32;
-  constexpr int NOB = D / 16;
+  constexpr int NOB = D / 16 / NSL;     // this wave's 16-column blocks
 
   __shared__ __attribute__((aligned(16))) bf16 sQ0[BMQ * D];
   __shared__ __attribute__((aligned(16))) bf16 sQ1[BMQ * D];
@@ -916,11 +920,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   const int GS = p.G / p.hsplit;     // query heads of this workgroup
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = threadIdx.x >> 6 ;
+  const int kgi = w / NSL;              // key group
+  const int sl = w % NSL;               // column slice: columns 16 NOB sl ..
+  const int colofs = 16 * NOB * sl;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int k0 = kb * BNK;
-  const int kw = k0 + 16 * w;
+  const int kw = k0 + 16 * kgi;
   const int j = kw + r;
   const int jc = min(j, Sk - 1);
   const long qstride = (long)p.Hq * D;
@@ -936,8 +943,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     const bf16* vrow = reinterpret_cast<const bf16*>(p.v) + off;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      kf[c] = *reinterpret_cast<const bf16x8*>(krow + 8 * c + 32 * g);
-      vf[c] = *reinterpret_cast<const bf16x8*>(vrow + 8 * c + 32 * g);
+      kf[c] = *reinterpret_cast<const bf16x8*>(krow + 8 * (c & 3) + 32 * g + 128 * (c >> 2));
+      vf[c] = *reinterpret_cast<const bf16x8*>(vrow + 8 * (c & 3) + 32 * g + 128 * (c >> 2));
     }
   }
 
@@ -1036,7 +1043,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
           dpacc[qb][e] = du;
           if constexpr (BIAS) {
             const bool vis = decltype(masked)::value ? (qi >= lo_j && qi < hi_j) : true;
-            if (dbcol && vis) dbcol[(long)qi * Sk] = (bf16)(du * kGrad4<CAP>);
+            if (dbcol && vis && sl == 0) dbcol[(long)qi * Sk] = (bf16)(du * kGrad4<CAP>);
           }
         }
       }
@@ -1050,9 +1057,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       uf[kc] = pack8(dpacc[2 * kc], dpacc[2 * kc + 1]);
     }
     // this wave's half of the dU block (32-key block of the pair, query block q0/32 + kc)
-    if (p.du && k0 + 16 * (w & ~1) < Sk) {
+    if (p.du && sl == 0 && k0 + 16 * (kgi & ~1) < Sk) {
       bf16* blk = reinterpret_cast<bf16*>(p.du) +
-                  ((((long)b * p.Hq + hq) * p.nkb32 + (kw >> 5)) * p.nqb32 + (q0 >> 5)) * 1024 + (w & 1) * 512 +
+                  ((((long)b * p.Hq + hq) * p.nkb32 + (kw >> 5)) * p.nqb32 + (q0 >> 5)) * 1024 + (kgi & 1) * 512 +
                   lane * 8;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
@@ -1070,8 +1077,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     for (int a = 0; a < TRA; ++a) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        tro[a][kc] = fo.frag_tr(tO, 32 * kc, a);
-        trq[a][kc] = fo.frag_tr(tQ, 32 * kc, a);
+        tro[a][kc] = fo.frag_tr(tO + colofs, 32 * kc, a);
+        trq[a][kc] = fo.frag_tr(tQ + colofs, 32 * kc, a);
       }
     }
 #pragma unroll
@@ -1079,8 +1086,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       if (ob + TRA < NOB) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          tro[(ob + TRA) % (TRA + 1)][kc] = fo.frag_tr(tO, 32 * kc, ob + TRA);
-          trq[(ob + TRA) % (TRA + 1)][kc] = fo.frag_tr(tQ, 32 * kc, ob + TRA);
+          tro[(ob + TRA) % (TRA + 1)][kc] = fo.frag_tr(tO + colofs, 32 * kc, ob + TRA);
+          trq[(ob + TRA) % (TRA + 1)][kc] = fo.frag_tr(tQ + colofs, 32 * kc, ob + TRA);
         }
       }
 #pragma unroll
@@ -1107,8 +1114,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     float* vp = p.dkv_part + (long)(p.hsplit + split) * nel + off;
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
-      *reinterpret_cast<f32x4*>(kp + 16 * ob + 4 * g) = kacc[ob];
-      *reinterpret_cast<f32x4*>(vp + 16 * ob + 4 * g) = vacc[ob];
+      *reinterpret_cast<f32x4*>(kp + colofs + 16 * ob + 4 * g) = kacc[ob];
+      *reinterpret_cast<f32x4*>(vp + colofs + 16 * ob + 4 * g) = vacc[ob];
     }
   } else if (j < Sk) {
     const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
@@ -1123,8 +1130,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
         kv[e] = (bf16)(kacc[ob][e] * ks);
         vv[e] = (bf16)vacc[ob][e];
       }
-      *reinterpret_cast<bf16x4*>(krow + 16 * ob + 4 * g) = kv;
-      *reinterpret_cast<bf16x4*>(vrow + 16 * ob + 4 * g) = vv;
+      *reinterpret_cast<bf16x4*>(krow + colofs + 16 * ob + 4 * g) = kv;
+      *reinterpret_cast<bf16x4*>(vrow + colofs + 16 * ob + 4 * g) = vv;
     }
   }
 }
@@ -1209,7 +1216,7 @@ __global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams 
   constexpr int BM = 128;
   constexpr int NKB = BN / 32;
   constexpr int NOB = D / 32;
-  constexpr bool DU16 = D == 128;   // blocks written by dkdv16_kernel
+  constexpr bool DU16 = D >= 128;   // blocks written by dkdv16_kernel
   static_assert(NST == 2 || NST == 3, "two or three tile stages");
 
   // NST stages of (K tile, this workgroup's dU blocks), distinct objects so
