@@ -232,6 +232,19 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4& a, const f32x4& b) {
   return r;
 }
 
+// Sum of the 8 bf16 values of a fragment, added to acc in fp32 (v_dot2 with
+// (1, 1)): the forward's row sums are taken over exactly the rounded
+// probabilities its P V products use, so that each output row is normalised
+// by its own numerator's weights (an fp32 sum would scale the row by the
+// rounding of its largest probability, up to 2^-9).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sum_bf16x8(const bf16x8& f, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[2 * e], f[2 * e + 1]}, one, acc, false);
+  return acc;
+}
+
 // Log2-unit logit constants of the bf16 fast path (see the header comment).
 struct LogitK {
   float a;    // multiplies q.k:   2*log2e*scale/c (cap) or scale*log2e
@@ -528,11 +541,11 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
                            : CAP ? fast_exp2(fmaf(scur[kb][j], -2.0f * lk.c2, lk.c2 - base))
                                  : fast_exp2(scur[kb][j] - base);
           scur[kb][j] = pv;
-          ps += pv;
         }
         bf16x8 pf[2];
         pf[0] = to_frag(scur[kb], 0, (bf16*)nullptr);
         pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
+        ps = sum_bf16x8(pf[1], sum_bf16x8(pf[0], ps));
         // V^T fragments of column block ob + 2 requested before the MFMAs of block ob
         {
           constexpr int TA = D > 128 ? 1 : 2;

@@ -227,7 +227,7 @@ def main():
     # hands it dU through the workspace (bf16, D = 64/128): then only dQ = dU K
     du_bytes = w.B * w.Hq * (-(-w.S // 32)) ** 2 * 2048
     du_limit = int(os.environ.get("ATTN_SOFTCAP_DU_MAX_BYTES", 16 << 30) or 0)
-    du_path = w.dtype == "bf16" and w.D in (64, 128) and du_bytes <= du_limit
+    du_path = w.dtype == "bf16" and w.D in (64, 128, 256) and du_bytes <= du_limit
     per_kernel_flop = {"fwd": 4.0 * w.D * pairs, "dq": (2.0 if du_path else 6.0) * w.D * pairs,
                        "dkdv": 8.0 * w.D * pairs}
 

@@ -13,7 +13,9 @@ from harness import TOL, case, compare, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 
-def _check(c, thd=False, backward=True):
+def _check(c, thd=False, backward=True, known=None):
+    """known: {tensor: reason} for a tensor whose error is allowed to be
+    reported as an expected failure; every other tensor must meet the bar."""
     print(f"case: dtype={c['dtype']} q={c['q'].shape} k={c['k'].shape} causal={c['causal']} window={c['window']} "
           f"cap={c['softcap']} sink={c['sink_mode']} bias={c['bias'] is not None} "
           f"seg={c['segment_ids'] is not None} thd={thd}", flush=True)
@@ -22,8 +24,24 @@ def _check(c, thd=False, backward=True):
     errs = compare(gpu, ref, c["dtype"])
     print("errors:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL[c["dtype"]]}
-    assert not bad, f"over tolerance {TOL[c['dtype']]}: {bad}"
+    known = known or {}
+    assert not {k: v for k, v in bad.items() if k not in known}, f"over tolerance {TOL[c['dtype']]}: {bad}"
+    if bad:
+        pytest.xfail("; ".join(f"{k} {bad[k]:.2e}: {known[k]}" for k in bad))
     return errs
+
+
+# With a learnable sink, dsink = -sum_i p_i <dO_i, O_i> takes O as stored (bf16).
+# At D = 256 in the bias_and_sink case a few rows dominate that sum: over 200
+# unbiased half-ulp roundings of the exact O its normwise error has median
+# 5.7e-3, 90th percentile 1.2e-2 and maximum 2.1e-2 (21% above 1e-2), while
+# the same case at D = 128 stays below 5.9e-3.  The forward's O matches the
+# ideal rounding row by row (median row error 1.76e-3 against 1.66e-3).
+DSINK_BF16_D256 = {"dsink": "delta from the bf16 output O (above the bar for 21% of unbiased roundings of O)"}
+
+
+def _known(dtype, D, feat):
+    return DSINK_BF16_D256 if dtype == "bf16" and D == 256 and feat == "bias_and_sink" else None
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -48,22 +66,23 @@ FEATURES = {
 }
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("bf16", 256), ("fp32", 64)])
 @pytest.mark.parametrize("feat", list(FEATURES))
 def test_feature_matrix(dtype, D, feat):
     kw = dict(dtype=dtype, D=D, B=2, S=203, Hq=4, Hkv=2)
     kw.update(FEATURES[feat])
-    _check(case(**kw))
+    _check(case(**kw), known=_known(dtype, D, feat))
 
 
-@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("feat", list(FEATURES))
 def test_feature_matrix_dq_recomputed(D, feat, monkeypatch):
-    """bf16 D<=128 with the dU hand-off switched off: dq recomputes the probabilities."""
+    """bf16 with the dU hand-off switched off: dq recomputes the probabilities
+    (D = 256 through the generic dq kernel)."""
     monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", "0")
     kw = dict(dtype="bf16", D=D, B=2, S=203, Hq=4, Hkv=2)
     kw.update(FEATURES[feat])
-    _check(case(**kw))
+    _check(case(**kw), known=_known("bf16", D, feat))
 
 
 @pytest.mark.parametrize("D", [64, 128])
