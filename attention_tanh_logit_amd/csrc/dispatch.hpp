@@ -140,7 +140,8 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
       if constexpr (D >= 128) {
         // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64
         // queries); at D = 256 two waves per 16 keys and 32-query items
-        constexpr int NW = 8, BMQ = D > 128 ? 32 : 64, BNK = D > 128 ? 64 : 128;
+        // (with a bias, 32-query items: the bias and dbias tiles take registers)
+        constexpr int NW = 8, BMQ = (D > 128 || BIAS) ? 32 : 64, BNK = D > 128 ? 64 : 128;
         const dim3 grid((l.Sk + BNK - 1) / BNK, p.Hkv * p.hsplit, l.B);
         dkdv16_kernel<D, CAP, BIAS, NW, BMQ><<<grid, 64 * NW, 0, l.stream>>>(p);
       } else {

@@ -918,6 +918,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sL1[BMQ];
   __shared__ __attribute__((aligned(16))) float sD0[BMQ];
   __shared__ __attribute__((aligned(16))) float sD1[BMQ];
+  // with a bias: the item's bias tile (BMQ queries x BNK keys) loaded with
+  // the Q/dO tiles, and its dbias tile gathered here and written out as whole
+  // rows during the next item; 16-byte chunks swizzled per row (bsw)
+  constexpr int BT = BIAS ? BMQ * BNK : 8;
+  __shared__ __attribute__((aligned(16))) bf16 sB0[BT];
+  __shared__ __attribute__((aligned(16))) bf16 sB1[BT];
+  __shared__ __attribute__((aligned(16))) bf16 sG0[BT];
+  __shared__ __attribute__((aligned(16))) bf16 sG1[BT];
 
   // XCD-aware, longest-first numbering and a lockstep query sweep, as in
   // the 32-key kernel
@@ -997,17 +1005,67 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       nD[threadIdx.x] = -nd;
     }
   };
+  // bias tiles: rows R = queries q0 + R, 16-byte chunk c (keys k0 + 8c ..) in
+  // slot c ^ bsw(R), so that the four row groups of a wave (rows 4 apart)
+  // read disjoint banks
+  constexpr int BCPR = BNK / 8;
+  auto bsw = [](int R) { return 2 * ((R >> 2) & (BCPR / 2 - 1)); };
+  auto bias_tile = [&](int it, bf16* nB) {
+    if constexpr (BIAS) {
+      const int hq = hk * p.G + split * GS + it % GS;
+      const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
+      const bf16* g0 = reinterpret_cast<const bf16*>(p.bias) + (((long)b * p.Hq + hq) * Sq) * Sk + k0;
+      const auto rsrc = rows_rsrc(g0, Sk, q0, Sq);
+      const int w64 = threadIdx.x >> 6;
+#pragma unroll
+      for (int u = 0; u < (BMQ * BCPR + NT - 1) / NT; ++u) {
+        const int pw = u * NT + w64 * 64;
+        if (pw < BMQ * BCPR) {
+          const int pc = pw + lane;
+          const int R = pc / BCPR, c = pc % BCPR;
+          dma16(rsrc, 2 * (R * Sk + 8 * (c ^ bsw(R))), nB + pw * 8);
+        }
+      }
+    }
+  };
+  // the dbias tile of item it, gathered in tG, to global memory as whole rows
+  auto store_dbias = [&](int it, const bf16* tG) {
+    if constexpr (BIAS) {
+      if (!p.dbias) return;
+      const int hq = hk * p.G + split * GS + it % GS;
+      const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
+      bf16* g0 = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.Hq + hq) * Sq) * Sk + k0;
+#pragma unroll
+      for (int u = 0; u < (BMQ * BCPR + NT - 1) / NT; ++u) {
+        const int pc = u * NT + threadIdx.x;
+        if (pc < BMQ * BCPR) {
+          const int R = pc / BCPR, c = pc % BCPR;
+          if (q0 + R < Sq && k0 + 8 * c < Sk)
+            *reinterpret_cast<bf16x8*>(g0 + (long)(q0 + R) * Sk + 8 * c) =
+                *reinterpret_cast<const bf16x8*>(tG + R * BNK + 8 * (c ^ bsw(R)));
+        }
+      }
+    }
+  };
+  // element (row R, key column cidx) of a swizzled bias tile
+  auto bidx = [&](int R, int cidx) { return R * BNK + 8 * ((cidx >> 3) ^ bsw(R)) + (cidx & 7); };
+
   if (nitems > 0) {
     fetch(0, sQ0, sO0);
+    bias_tile(0, sB0);
     put_stats(sL0, sD0);
   }
   wait_loads();
   __syncthreads();
 
   auto step = [&](const bf16* tQ, const bf16* tO, const float* tL, const float* tD, bf16* nQ, bf16* nO, float* nL,
-                  float* nD, int it) {
+                  float* nD, const bf16* tB, bf16* nB, bf16* tG, const bf16* pG, int it) {
     const bool more = it + 1 < nitems;
-    if (more) fetch(it + 1, nQ, nO);
+    if (more) {
+      fetch(it + 1, nQ, nO);
+      bias_tile(it + 1, nB);
+    }
+    if (it > 0) store_dbias(it - 1, pG);
     const int hq = hk * p.G + split * GS + it % GS;
     const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
 
@@ -1031,13 +1089,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     // keep fragment reads in flight ahead of their MFMAs
     ATL_READ_AHEAD(8, 1, 2 * NC * NQB);
 
-    const bf16* bcol = nullptr;
-    bf16* dbcol = nullptr;
-    if constexpr (BIAS) {
-      const long boff = (((long)b * p.Hq + hq) * Sq) * Sk + jc;
-      bcol = reinterpret_cast<const bf16*>(p.bias) + boff;
-      if (p.dbias) dbcol = reinterpret_cast<bf16*>(p.dbias) + boff;
-    }
+    const int bcol = 16 * kgi + r;      // this lane's key column in the bias tiles
     auto grads = [&](auto masked) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
@@ -1048,15 +1100,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
           float lc = l4[e];
           if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j) ? lc : -INFINITY;
           float bvv = 0.0f;
-          if constexpr (BIAS) bvv = (float)bcol[(long)min(qi, Sq - 1) * Sk];
+          if constexpr (BIAS) bvv = (float)tB[bidx(16 * qb + 4 * g + e, bcol)];
           float gg;
           const float pv = prob_fast<CAP, BIAS>(sacc[qb][e], bvv, lk, lc, gg);
           const float du = pv * dpacc[qb][e] * gg;
           sacc[qb][e] = pv;
           dpacc[qb][e] = du;
+          // masked pairs have P = 0, hence dbias = 0, as the pre-pass already wrote
           if constexpr (BIAS) {
-            const bool vis = decltype(masked)::value ? (qi >= lo_j && qi < hi_j) : true;
-            if (dbcol && vis && sl == 0) dbcol[(long)qi * Sk] = (bf16)(du * kGrad4<CAP>);
+            if (sl == 0) tG[bidx(16 * qb + 4 * g + e, bcol)] = (bf16)(du * kGrad4<CAP>);
           }
         }
       }
@@ -1115,9 +1167,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     __syncthreads();
   };
   for (int it = 0; it < nitems; it += 2) {
-    step(sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1, it);
-    if (it + 1 < nitems) step(sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, it + 1);
+    step(sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1, sB0, sB1, sG0, sG1, it);
+    if (it + 1 < nitems) step(sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0, sB1, sB0, sG1, sG0, it + 1);
   }
+  if (nitems > 0) store_dbias(nitems - 1, ((nitems - 1) & 1) ? sG1 : sG0);
 
   if (j < Sk && p.hsplit > 1) {
     // unscaled fp32 partials of this split
