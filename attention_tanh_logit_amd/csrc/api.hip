@@ -149,6 +149,14 @@ bool du_path(const attn_args* a) {
          du_raw_bytes(a) <= du_max_bytes();
 }
 
+// With a bias, the bf16 dk/dv kernel of D = 128 and 256 writes the whole of
+// dbias, the zeros of the masked pairs included; elsewhere the pre-pass
+// writes those zeros and the dk/dv kernel the visible pairs.
+bool dkdv_writes_dbias_zeros(const attn_args* a) {
+  return a->bias != nullptr && (a->D == 128 || a->D == 256) &&
+         fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, true);
+}
+
 // Query-head splits of the bf16 dk/dv kernels (both take 128 keys per
 // workgroup): the smallest divisor of G that gives at least 1024 workgroups
 // (four per CU), so that a small batch with a wide GQA group does not leave
@@ -368,7 +376,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
       e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(e, "sink gradient launch");
     }
-    if (dbias && a->Sq > 0 && a->Sk > 0) {
+    if (dbias && a->Sq > 0 && a->Sk > 0 && !dkdv_writes_dbias_zeros(a)) {
       e = o.dbias_fill(dbias, p.mask, a->Hq, kFillRows, l);
       if (e != hipSuccess) return hip_fail(e, "dbias fill launch");
     }

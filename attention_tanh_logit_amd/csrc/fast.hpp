@@ -1200,6 +1200,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       *reinterpret_cast<bf16x4*>(vrow + colofs + 16 * ob + 4 * g) = vv;
     }
   }
+
+  // dbias of this key block: the items wrote whole tiles over the query rows
+  // [qbeg, qbeg + nqt BMQ); every other row sees none of the block's keys
+  // (the visible query range of a key moves monotonically with the key), so
+  // its dbias is zero.  Written here rather than by a separate pass, so that
+  // these stores stream out while other workgroups compute.
+  if constexpr (BIAS) {
+    if (p.dbias) {
+      const int z_lo = min(qbeg, Sq);
+      const int z_hi = max(z_lo, min(qbeg + nqt * BMQ, Sq));
+      const int nz = z_lo + (Sq - z_hi);
+      const bf16x8 zero = {};
+      for (int hh = 0; hh < GS; ++hh) {
+        const int hq = hk * p.G + split * GS + hh;
+        bf16* g0 = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.Hq + hq) * Sq) * Sk + k0;
+        for (int u = threadIdx.x; u < nz * BCPR; u += NT) {
+          const int R = u / BCPR, c = u % BCPR;
+          const int i = R < z_lo ? R : z_hi + (R - z_lo);
+          if (k0 + 8 * c < Sk) *reinterpret_cast<bf16x8*>(g0 + (long)i * Sk + 8 * c) = zero;
+        }
+      }
+    }
+  }
 }
 
 // ============================================================== backward: split reduction

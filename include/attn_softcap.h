@@ -142,14 +142,16 @@ attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, cons
  * (attn_bwd == pre, then dkdv, then dq).  All three take the same arguments
  * and the same workspace, which carries the pre-pass results (segment runs,
  * delta = rowsum(dout * out), sink-gradient partials) to the other two and,
- * for bf16 with D = 64 or 128, the dU blocks that dkdv writes and dq reads;
- * so it must stay untouched between them and the phases must run in that
- * order (on one stream, or with the caller ordering them).
- *  - attn_bwd_pre:  segment runs, delta, dsink (required iff LEARNABLE) and
- *                   the zeros of dbias on the masked pairs (dbias nullable);
+ * for bf16 with D = 64, 128 or 256, the dU blocks that dkdv writes and dq
+ * reads; so it must stay untouched between them and the phases must run in
+ * that order (on one stream, or with the caller ordering them).
+ *  - attn_bwd_pre:  segment runs, delta, dsink (required iff LEARNABLE) and,
+ *                   except for bf16 with D = 128 or 256, the zeros of dbias
+ *                   on the masked pairs (dbias nullable);
  *  - attn_bwd_dq:   dq;
- *  - attn_bwd_dkdv: dk, dv and dbias on the visible pairs (dbias nullable,
- *                   complete only together with attn_bwd_pre). */
+ *  - attn_bwd_dkdv: dk, dv and dbias on the visible pairs, and for bf16 with
+ *                   D = 128 or 256 also its zeros (dbias nullable, complete
+ *                   once attn_bwd_pre and attn_bwd_dkdv have both run). */
 attn_status attn_bwd_pre(const attn_args* a, const void* out, const float* lse, const void* dout,
                          void* dbias, float* dsink, void* workspace, size_t workspace_bytes, void* stream);
 attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, void* dq,
