@@ -30,30 +30,30 @@ template <typename T, int D> struct DkdvCfg;
 ATL_FWD(bf16, 64, 64, 4, 64, 64)
 ATL_FWD(bf16, 128, 128, 4, 64, 128)
 ATL_FWD(bf16, 256, 256, 2, 32, 256)
-ATL_FWD(bf16, 512, 256, 2, 32, 512)
+ATL_FWD(bf16, 512, 128, 2, 64, 128)
 ATL_FWD(float, 64, 64, 4, 32, 64)
 ATL_FWD(float, 128, 128, 2, 32, 128)
-ATL_FWD(float, 256, 256, 2, 32, 256)
-ATL_FWD(float, 512, 256, 1, 32, 128)
+ATL_FWD(float, 256, 128, 4, 64, 128)
+ATL_FWD(float, 512, 256, 2, 32, 128)
 
 ATL_DQ(bf16, 64, 64, 4, 64, 64)
 ATL_DQ(bf16, 128, 128, 4, 32, 128)
 ATL_DQ(bf16, 256, 256, 2, 32, 256)
-ATL_DQ(bf16, 512, 256, 2, 32, 128)
+ATL_DQ(bf16, 512, 256, 4, 32, 128)
 ATL_DQ(float, 64, 64, 4, 32, 64)
 ATL_DQ(float, 128, 128, 2, 32, 128)
-ATL_DQ(float, 256, 256, 2, 32, 128)
-ATL_DQ(float, 512, 256, 1, 32, 128)
+ATL_DQ(float, 256, 128, 2, 32, 128)
+ATL_DQ(float, 512, 128, 2, 32, 128)
 
 //           T      D   DO NKG  DC
 ATL_DKDV(bf16, 64, 64, 4, 64)
 ATL_DKDV(bf16, 128, 128, 4, 128)
 ATL_DKDV(bf16, 256, 128, 2, 256)
-ATL_DKDV(bf16, 512, 128, 1, 128)
+ATL_DKDV(bf16, 512, 128, 2, 128)
 ATL_DKDV(float, 64, 64, 4, 64)
 ATL_DKDV(float, 128, 128, 2, 128)
-ATL_DKDV(float, 256, 128, 1, 128)
-ATL_DKDV(float, 512, 128, 1, 128)
+ATL_DKDV(float, 256, 128, 2, 128)
+ATL_DKDV(float, 512, 128, 2, 128)
 
 #undef ATL_FWD
 #undef ATL_DQ
