@@ -78,6 +78,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff_byte
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff_bytes, 0,
                                            0, 0);
 }
+// the same with the non-temporal cache policy: for the dU blocks, which the
+// dk/dv kernel writes once (non-temporal stores) and the dq kernel reads once;
+// streaming both ways moves dU at about 5.3 TB/s instead of 4.5
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t rsrc, int voff_bytes, bf16* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff_bytes, 0,
+                                           0, 2);
+}
 
 // Direct HBM -> LDS load of a ROWS x D tile.  Each wave instruction fills one
 // contiguous KiB: lane chunk p is tile row R = p/(D/8), physical slot
@@ -797,8 +804,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
     if (p.du && k0 + 32 * w < Sk) {
       bf16* blk = reinterpret_cast<bf16*>(p.du) +
                   ((((long)b * p.Hq + hq) * p.nkb32 + (k0 >> 5) + w) * p.nqb32 + (q0 >> 5)) * 1024 + lane * 8;
-      *reinterpret_cast<bf16x8*>(blk) = uf[0];
-      *reinterpret_cast<bf16x8*>(blk + 512) = uf[1];
+      __builtin_nontemporal_store(uf[0], reinterpret_cast<bf16x8*>(blk));
+      __builtin_nontemporal_store(uf[1], reinterpret_cast<bf16x8*>(blk + 512));
     }
 
     // ---- dV^T += dO^T P,  dK^T += Q^T dU
@@ -1129,7 +1136,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         // a ragged last item may end before its second 32-query block
-        if (kc == 0 || q0 + 32 * kc < Sq) *reinterpret_cast<bf16x8*>(blk + kc * 1024) = uf[kc];
+        if (kc == 0 || q0 + 32 * kc < Sq)
+          __builtin_nontemporal_store(uf[kc], reinterpret_cast<bf16x8*>(blk + kc * 1024));
       }
     }
 
@@ -1375,7 +1383,7 @@ __global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams 
       const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(blk), 0, vis ? 2048 : 0, 0x00020000);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        dma16(rsrc, 16 * (DU16 ? du_slot16(64 * u + lane) : du_slot(64 * u + lane)),
+        dma16_nt(rsrc, 16 * (DU16 ? du_slot16(64 * u + lane) : du_slot(64 * u + lane)),
               tU + (w * NKB + kk) * 1024 + 64 * u * 8);
     }
   };
