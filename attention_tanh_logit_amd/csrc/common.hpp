@@ -195,6 +195,96 @@ __device__ __forceinline__ void stage_rows_t(T* lds, const T* g, long gstride, i
   }
 }
 
+// The same two stagings split in two: load() brings the tile's 16-byte
+// chunks into registers, store() writes them to LDS, so that the global
+// loads of the next tile can be in flight while the current one is in use.
+template <typename T, int ROWS, int COLS, int NT>
+struct RowChunks {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int CPR = COLS / VEC;
+  static constexpr int TOTAL = ROWS * CPR;
+  static constexpr int N = (TOTAL + NT - 1) / NT;
+  static_assert(COLS % VEC == 0, "tile width must be a multiple of 16 bytes");
+  uint4 v[N];
+  __device__ __forceinline__ void load(const T* g, long gstride, int row0, int nvalid, int col0) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int idx = u * NT + (int)threadIdx.x;
+      v[u] = uint4{0u, 0u, 0u, 0u};
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const int r = idx / CPR;
+        const int c = (idx % CPR) * VEC;
+        if (row0 + r < nvalid) v[u] = *reinterpret_cast<const uint4*>(g + (long)(row0 + r) * gstride + col0 + c);
+      }
+    }
+  }
+  template <int LDS_STRIDE, bool PERM>
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int idx = u * NT + (int)threadIdx.x;
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const int r = idx / CPR;
+        const int c = (idx % CPR) * VEC;
+        *reinterpret_cast<uint4*>(lds + (PERM ? swp(r) : r) * LDS_STRIDE + c) = v[u];
+      }
+    }
+  }
+};
+
+template <typename T, int ROWS, int COLS, int NT>
+struct RowPairChunks {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int RP = ROWS / 2;
+  static constexpr int TOTAL = RP * (COLS / VEC);
+  static constexpr int N = (TOTAL + NT - 1) / NT;
+  static_assert(ROWS % 2 == 0 && COLS % VEC == 0, "bad transposed tile");
+  uint4 a[N], b[N];
+  __device__ __forceinline__ void load(const T* g, long gstride, int row0, int nvalid, int col0) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int idx = u * NT + (int)threadIdx.x;
+      a[u] = uint4{0u, 0u, 0u, 0u};
+      b[u] = uint4{0u, 0u, 0u, 0u};
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const int r = 2 * (idx % RP);
+        const int c0 = (idx / RP) * VEC;
+        if (row0 + r < nvalid) a[u] = *reinterpret_cast<const uint4*>(g + (long)(row0 + r) * gstride + col0 + c0);
+        if (row0 + r + 1 < nvalid) b[u] = *reinterpret_cast<const uint4*>(g + (long)(row0 + r + 1) * gstride + col0 + c0);
+      }
+    }
+  }
+  // lds[(PERM ? swp(c) : c) * LDS_STRIDE + r] = tile[r][c]
+  template <int LDS_STRIDE, bool PERM>
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int idx = u * NT + (int)threadIdx.x;
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const int r = 2 * (idx % RP);
+        const int c0 = (idx / RP) * VEC;
+        T x[VEC], y[VEC];
+        __builtin_memcpy(x, &a[u], 16);
+        __builtin_memcpy(y, &b[u], 16);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int lc = PERM ? swp(c0 + e) : (c0 + e);
+          T pair[2] = {x[e], y[e]};
+          if constexpr (sizeof(T) == 2) {
+            uint32_t w;
+            __builtin_memcpy(&w, pair, 4);
+            *reinterpret_cast<uint32_t*>(lds + lc * LDS_STRIDE + r) = w;
+          } else {
+            f32x2 w;
+            __builtin_memcpy(&w, pair, 8);
+            *reinterpret_cast<f32x2*>(lds + lc * LDS_STRIDE + r) = w;
+          }
+        }
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------- visibility
 //
 // Packed segments are contiguous runs; seg_lo[t] / seg_hi[t] are the first and

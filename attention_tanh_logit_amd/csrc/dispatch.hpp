@@ -49,11 +49,11 @@ ATL_DQ(float, 512, 128, 2, 32, 128)
 ATL_DKDV(bf16, 64, 64, 4, 64)
 ATL_DKDV(bf16, 128, 128, 4, 128)
 ATL_DKDV(bf16, 256, 128, 2, 256)
-ATL_DKDV(bf16, 512, 128, 2, 128)
+ATL_DKDV(bf16, 512, 128, 1, 128)
 ATL_DKDV(float, 64, 64, 4, 64)
 ATL_DKDV(float, 128, 128, 2, 128)
 ATL_DKDV(float, 256, 128, 2, 128)
-ATL_DKDV(float, 512, 128, 2, 128)
+ATL_DKDV(float, 512, 128, 1, 128)
 
 #undef ATL_FWD
 #undef ATL_DQ

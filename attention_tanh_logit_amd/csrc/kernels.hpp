@@ -526,10 +526,10 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   }
 
   const int qbeg = (lo_first / BMQ) * BMQ;
-  for (int g = 0; g < p.G; ++g) {
-    const int hq = hk * p.G + g;
-    const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
-    const T* obase = reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D;
+
+  // ---- P, dU of one (query head, 32-query tile) item from S and dP
+  // (lane: key j; register r: query q0 + acc_row(h, r)), as operand fragments
+  auto grads = [&](int hq, int q0, bool full, f32x16& sacc, f32x16& dpacc, F* pf, F* uf) {
     const long lrow = ((long)b * p.Hq + hq) * Sq;
     const T* bbase = nullptr;
     T* dbbase = nullptr;
@@ -537,95 +537,174 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       bbase = reinterpret_cast<const T*>(p.bias) + lrow * Sk;
       if (p.dbias) dbbase = reinterpret_cast<T*>(p.dbias) + lrow * Sk;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = q0 + acc_row(h, r);
+      float bvv = 0.0f;
+      if constexpr (BIAS) bvv = (qi < Sq && j < Sk) ? to_f32(bbase[(long)qi * Sk + j]) : 0.0f;
+      float f;
+      const float s2 = logit2<T, CAP, BIAS>(sacc[r], bvv, p.sl2, p.xc, p.bc, p.cl2, f);
+      float pv = fast_exp2(s2 - sL[acc_row(h, r)]);
+      bool vis = true;
+      if (!full) vis = (qi >= lo_j && qi < hi_j);
+      if (!vis) pv = 0.0f;
+      const float du = pv * (dpacc[r] - sDl[acc_row(h, r)]) * f;
+      sacc[r] = pv;
+      dpacc[r] = du;
+      if constexpr (BIAS) {
+        if (dbbase && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
+      }
+    }
+    pf[0] = to_frag(sacc, 0, (T*)nullptr);
+    pf[1] = to_frag(sacc, 8, (T*)nullptr);
+    uf[0] = to_frag(dpacc, 0, (T*)nullptr);
+    uf[1] = to_frag(dpacc, 8, (T*)nullptr);
+  };
+  // lse (log2 units; +inf on rows past the end) and delta of the item's queries
+  auto put_stats = [&](int i, float l, float dl) {
+    if (threadIdx.x < BMQ) {
+      sL[threadIdx.x] = (i < Sq && l != -INFINITY) ? l * kLog2e : INFINITY;
+      sDl[threadIdx.x] = i < Sq ? dl : 0.0f;
+    }
+  };
+  auto get_stats = [&](int hq, int q0, float& l, float& dl) {
+    l = -INFINITY;
+    dl = 0.0f;
+    const int qi = q0 + (int)threadIdx.x;
+    if (threadIdx.x < BMQ && qi < Sq) {
+      const long lrow = ((long)b * p.Hq + hq) * Sq;
+      l = p.lse[lrow + qi];
+      dl = p.delta[lrow + qi];
+    }
+  };
+
+  if constexpr (ONE) {
+  for (int g = 0; g < p.G; ++g) {
+    const int hq = hk * p.G + g;
+    const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
+    const T* obase = reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D;
     for (int q0 = qbeg; q0 < hi_last; q0 += BMQ) {
       const bool full = keys_full && q0 >= lo_last && q0 + BMQ <= hi_first;
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        __syncthreads();
-        stage_rows<T, BMQ, DC, RS, true, NT>(sQ, qbase, qstride, q0, Sq, c * DC);
-        stage_rows<T, BMQ, DC, RS, true, NT>(sO, obase, qstride, q0, Sq, c * DC);
-        if constexpr (!ONE) {
-          stage_rows<T, BNK, DC, RS, false, NT>(sK, kbase, kstride, k0, Sk, c * DC);
-          stage_rows<T, BNK, DC, RS, false, NT>(sV, vbase, kstride, k0, Sk, c * DC);
-        } else {
-          stage_rows_t<T, BMQ, DC, TS, true, NT>(sQt, qbase, qstride, q0, Sq, 0);
-          stage_rows_t<T, BMQ, DC, TS, true, NT>(sOt, obase, qstride, q0, Sq, 0);
-        }
-        if (c == 0 && threadIdx.x < BMQ) {
-          const int qi = q0 + threadIdx.x;
-          float l2 = INFINITY, dl = 0.0f;
-          if (qi < Sq) {
-            const float l = p.lse[lrow + qi];
-            l2 = (l != -INFINITY) ? l * kLog2e : INFINITY;
-            dl = p.delta[lrow + qi];
-          }
-          sL[threadIdx.x] = l2;
-          sDl[threadIdx.x] = dl;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int cc = 0; cc < DC / 16; ++cc) {
-          const F aq = lds_frag<T>(sQ + n * RS + cc * 16 + 8 * h);
-          const F bk = lds_frag<T>(sK + (kg * 32 + n) * RS + cc * 16 + 8 * h);
-          mma(sacc, aq, bk);
-          const F ao = lds_frag<T>(sO + n * RS + cc * 16 + 8 * h);
-          const F bv = lds_frag<T>(sV + (kg * 32 + n) * RS + cc * 16 + 8 * h);
-          mma(dpacc, ao, bv);
-        }
+      __syncthreads();
+      stage_rows<T, BMQ, DC, RS, true, NT>(sQ, qbase, qstride, q0, Sq, 0);
+      stage_rows<T, BMQ, DC, RS, true, NT>(sO, obase, qstride, q0, Sq, 0);
+      stage_rows_t<T, BMQ, DC, TS, true, NT>(sQt, qbase, qstride, q0, Sq, 0);
+      stage_rows_t<T, BMQ, DC, TS, true, NT>(sOt, obase, qstride, q0, Sq, 0);
+      {
+        float l, dl;
+        get_stats(hq, q0, l, dl);
+        put_stats(q0 + (int)threadIdx.x, l, dl);
       }
-
-      // ---- P, dU (lane: key j; register r: query q0 + acc_row(h, r))
+      __syncthreads();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + acc_row(h, r);
-        float bvv = 0.0f;
-        if constexpr (BIAS) bvv = (qi < Sq && j < Sk) ? to_f32(bbase[(long)qi * Sk + j]) : 0.0f;
-        float f;
-        const float s2 = logit2<T, CAP, BIAS>(sacc[r], bvv, p.sl2, p.xc, p.bc, p.cl2, f);
-        float pv = fast_exp2(s2 - sL[acc_row(h, r)]);
-        bool vis = true;
-        if (!full) vis = (qi >= lo_j && qi < hi_j);
-        if (!vis) pv = 0.0f;
-        const float du = pv * (dpacc[r] - sDl[acc_row(h, r)]) * f;
-        sacc[r] = pv;
-        dpacc[r] = du;
-        if constexpr (BIAS) {
-          if (dbbase && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
-        }
+      for (int cc = 0; cc < DC / 16; ++cc) {
+        const F aq = lds_frag<T>(sQ + n * RS + cc * 16 + 8 * h);
+        const F bk = lds_frag<T>(sK + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+        mma(sacc, aq, bk);
+        const F ao = lds_frag<T>(sO + n * RS + cc * 16 + 8 * h);
+        const F bv = lds_frag<T>(sV + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+        mma(dpacc, ao, bv);
       }
       F pf[2], uf[2];
-      pf[0] = to_frag(sacc, 0, (T*)nullptr);
-      pf[1] = to_frag(sacc, 8, (T*)nullptr);
-      uf[0] = to_frag(dpacc, 0, (T*)nullptr);
-      uf[1] = to_frag(dpacc, 8, (T*)nullptr);
-
+      grads(hq, q0, full, sacc, dpacc, pf, uf);
       // ---- dV^T += dO^T P,  dK^T += Q^T dU  over this wave's slice
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        if constexpr (!ONE) {
-          __syncthreads();
-          stage_rows_t<T, BMQ, DC, TS, true, NT>(sQt, qbase, qstride, q0, Sq, c * DC);
-          stage_rows_t<T, BMQ, DC, TS, true, NT>(sOt, obase, qstride, q0, Sq, c * DC);
-          __syncthreads();
+      for (int ob = 0; ob < NOB; ++ob) {
+        const int db = sl * NOB + ob;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const F ao = lds_frag<T>(sOt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+          mma(vacc[ob], ao, pf[sb]);
+          const F aq = lds_frag<T>(sQt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+          mma(kacc[ob], aq, uf[sb]);
         }
-        const int d0 = c * DC;
-        if (ONE || (d0 >= sl * DO && d0 < (sl + 1) * DO)) {
+      }
+    }
+  }
+  } else {
+  // Head dimension in NCH chunks: every chunk of Q, dO, K, V (for S and dP)
+  // and then of Q^T, dO^T (for dV, dK) passes through LDS, one stage after
+  // the other; each stage's global loads are issued into registers while the
+  // previous stage's MFMAs run, across the items of the (query head,
+  // 32-query tile) sweep.
+  const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
+  const int nitems = p.G * nqt;
+  auto head_of = [&](int it) { return hk * p.G + it / nqt; };
+  auto q0_of = [&](int it) { return qbeg + (it % nqt) * BMQ; };
+  auto qb_of = [&](int hq) { return reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D; };
+  auto ob_of = [&](int hq) { return reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D; };
+  RowChunks<T, BMQ, DC, NT> rq, ro;
+  RowChunks<T, BNK, DC, NT> rk, rv;
+  RowPairChunks<T, BMQ, DC, NT> rqt, rot;
+  float nl = -INFINITY, ndl = 0.0f;
+  auto load_s = [&](int it, int c) {   // stage c of S / dP
+    const int hq = head_of(it), q0 = q0_of(it);
+    rq.load(qb_of(hq), qstride, q0, Sq, c * DC);
+    ro.load(ob_of(hq), qstride, q0, Sq, c * DC);
+    rk.load(kbase, kstride, k0, Sk, c * DC);
+    rv.load(vbase, kstride, k0, Sk, c * DC);
+    if (c == 0) get_stats(hq, q0, nl, ndl);
+  };
+  auto load_t = [&](int it, int c) {   // stage c of dV / dK
+    const int hq = head_of(it), q0 = q0_of(it);
+    rqt.load(qb_of(hq), qstride, q0, Sq, c * DC);
+    rot.load(ob_of(hq), qstride, q0, Sq, c * DC);
+  };
+  if (nitems > 0) load_s(0, 0);
+  for (int it = 0; it < nitems; ++it) {
+    const int hq = head_of(it), q0 = q0_of(it);
+    const bool full = keys_full && q0 >= lo_last && q0 + BMQ <= hi_first;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-          for (int db = 0; db < DC / 32; ++db) {
-            const int ob = ONE ? (db - sl * NOB) : ((d0 - sl * DO) / 32 + db);
-            if (ONE && (db < sl * NOB || db >= (sl + 1) * NOB)) continue;
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();
+      rq.template store<RS, true>(sQ);
+      ro.template store<RS, true>(sO);
+      rk.template store<RS, false>(sK);
+      rv.template store<RS, false>(sV);
+      if (c == 0) put_stats(q0 + (int)threadIdx.x, nl, ndl);
+      __syncthreads();
+      if (c + 1 < NCH) load_s(it, c + 1);
+      else load_t(it, 0);
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-              const F ao = lds_frag<T>(sOt + (db * 32 + n) * TS + 16 * sb + 8 * h);
-              mma(vacc[ob], ao, pf[sb]);
-              const F aq = lds_frag<T>(sQt + (db * 32 + n) * TS + 16 * sb + 8 * h);
-              mma(kacc[ob], aq, uf[sb]);
-            }
+      for (int cc = 0; cc < DC / 16; ++cc) {
+        const F aq = lds_frag<T>(sQ + n * RS + cc * 16 + 8 * h);
+        const F bk = lds_frag<T>(sK + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+        mma(sacc, aq, bk);
+        const F ao = lds_frag<T>(sO + n * RS + cc * 16 + 8 * h);
+        const F bv = lds_frag<T>(sV + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+        mma(dpacc, ao, bv);
+      }
+    }
+    F pf[2], uf[2];
+    grads(hq, q0, full, sacc, dpacc, pf, uf);
+    // ---- dV^T += dO^T P,  dK^T += Q^T dU  over this wave's slice
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();
+      rqt.template store<TS, true>(sQt);
+      rot.template store<TS, true>(sOt);
+      __syncthreads();
+      if (c + 1 < NCH) load_t(it, c + 1);
+      else if (it + 1 < nitems) load_s(it + 1, 0);
+      // chunk c belongs to slice c / (DO / DC), at its column block (c % (DO / DC)) DC / 32
+      constexpr int CPS = DO / DC;
+      if (sl == c / CPS) {
+#pragma unroll
+        for (int db = 0; db < DC / 32; ++db) {
+          const int ob = (c % CPS) * (DC / 32) + db;
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            const F ao = lds_frag<T>(sOt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+            mma(vacc[ob], ao, pf[sb]);
+            const F aq = lds_frag<T>(sQt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+            mma(kacc[ob], aq, uf[sb]);
           }
         }
       }
     }
+  }
   }
 
   if (j < Sk) {
