@@ -352,45 +352,10 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) qacc[ob] = f32x16{};
 
-  if constexpr (ONE) {
-    stage_rows<T, BM, DC, RS, false, NT>(sQ, qbase, qstride, q0, Sq, 0);
-    stage_rows<T, BM, DC, RS, false, NT>(sO, obase, qstride, q0, Sq, 0);
-  }
-
   const int kbeg = (lo_first / BN) * BN;
-  for (int k0 = kbeg; k0 < hi_last; k0 += BN) {
-    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
-    f32x16 sacc[NKB], dpacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) { sacc[kb] = f32x16{}; dpacc[kb] = f32x16{}; }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      __syncthreads();
-      stage_rows<T, BN, DC, RS, true, NT>(sK, kbase, kstride, k0, Sk, c * DC);
-      stage_rows<T, BN, DC, RS, true, NT>(sV, vbase, kstride, k0, Sk, c * DC);
-      if constexpr (!ONE) {
-        stage_rows<T, BM, DC, RS, false, NT>(sQ, qbase, qstride, q0, Sq, c * DC);
-        stage_rows<T, BM, DC, RS, false, NT>(sO, obase, qstride, q0, Sq, c * DC);
-      } else {
-        stage_rows_t<T, BN, DC, TS, true, NT>(sKt, kbase, kstride, k0, Sk, 0);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int cc = 0; cc < DC / 16; ++cc) {
-        const F bq = lds_frag<T>(sQ + (qg * 32 + n) * RS + cc * 16 + 8 * h);
-        const F bo = lds_frag<T>(sO + (qg * 32 + n) * RS + cc * 16 + 8 * h);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const F ak = lds_frag<T>(sK + (kb * 32 + n) * RS + cc * 16 + 8 * h);
-          mma(sacc[kb], ak, bq);
-          const F av = lds_frag<T>(sV + (kb * 32 + n) * RS + cc * 16 + 8 * h);
-          mma(dpacc[kb], av, bo);
-        }
-      }
-    }
 
-    // ---- dU^T = P^T (dP^T - delta) (1 - t^2)
-    F uf[NKB][2];
+  // ---- dU^T = P^T (dP^T - delta) (1 - t^2) of one key tile, as fragments
+  auto grads = [&](int k0, bool full, f32x16* sacc, const f32x16* dpacc, F (*uf)[2]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float bv[16];
@@ -420,21 +385,112 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
       uf[kb][0] = to_frag(sacc[kb], 0, (T*)nullptr);
       uf[kb][1] = to_frag(sacc[kb], 8, (T*)nullptr);
     }
+  };
 
+  if constexpr (ONE) {
+  stage_rows<T, BM, DC, RS, false, NT>(sQ, qbase, qstride, q0, Sq, 0);
+  stage_rows<T, BM, DC, RS, false, NT>(sO, obase, qstride, q0, Sq, 0);
+  for (int k0 = kbeg; k0 < hi_last; k0 += BN) {
+    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
+    f32x16 sacc[NKB], dpacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) { sacc[kb] = f32x16{}; dpacc[kb] = f32x16{}; }
+    __syncthreads();
+    stage_rows<T, BN, DC, RS, true, NT>(sK, kbase, kstride, k0, Sk, 0);
+    stage_rows<T, BN, DC, RS, true, NT>(sV, vbase, kstride, k0, Sk, 0);
+    stage_rows_t<T, BN, DC, TS, true, NT>(sKt, kbase, kstride, k0, Sk, 0);
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < DC / 16; ++cc) {
+      const F bq = lds_frag<T>(sQ + (qg * 32 + n) * RS + cc * 16 + 8 * h);
+      const F bo = lds_frag<T>(sO + (qg * 32 + n) * RS + cc * 16 + 8 * h);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const F ak = lds_frag<T>(sK + (kb * 32 + n) * RS + cc * 16 + 8 * h);
+        mma(sacc[kb], ak, bq);
+        const F av = lds_frag<T>(sV + (kb * 32 + n) * RS + cc * 16 + 8 * h);
+        mma(dpacc[kb], av, bo);
+      }
+    }
+    F uf[NKB][2];
+    grads(k0, full, sacc, dpacc, uf);
+    // ---- dQ^T += K^T dU^T over this wave's slice
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      const int db = sl * NOB + ob;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const F ak = lds_frag<T>(sKt + (db * 32 + n) * TS + kb * 32 + 16 * sb + 8 * h);
+          mma(qacc[ob], ak, uf[kb][sb]);
+        }
+      }
+    }
+  }
+  } else {
+  // Head dimension in NCH chunks: per key tile, the chunks of K, V, Q, dO
+  // (for S and dP) and then of K^T (for dQ) pass through LDS stage by stage;
+  // each stage's global loads are issued into registers while the previous
+  // stage's MFMAs run.
+  const int ntile = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
+  RowChunks<T, BN, DC, NT> rk, rv;
+  RowChunks<T, BM, DC, NT> rq, ro;
+  RowPairChunks<T, BN, DC, NT> rkt;
+  auto load_s = [&](int t, int c) {
+    const int k0 = kbeg + t * BN;
+    rk.load(kbase, kstride, k0, Sk, c * DC);
+    rv.load(vbase, kstride, k0, Sk, c * DC);
+    rq.load(qbase, qstride, q0, Sq, c * DC);
+    ro.load(obase, qstride, q0, Sq, c * DC);
+  };
+  auto load_t = [&](int t, int c) { rkt.load(kbase, kstride, kbeg + t * BN, Sk, c * DC); };
+  if (ntile > 0) load_s(0, 0);
+  for (int t = 0; t < ntile; ++t) {
+    const int k0 = kbeg + t * BN;
+    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
+    f32x16 sacc[NKB], dpacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) { sacc[kb] = f32x16{}; dpacc[kb] = f32x16{}; }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();
+      rk.template store<RS, true>(sK);
+      rv.template store<RS, true>(sV);
+      rq.template store<RS, false>(sQ);
+      ro.template store<RS, false>(sO);
+      __syncthreads();
+      if (c + 1 < NCH) load_s(t, c + 1);
+      else load_t(t, 0);
+#pragma unroll
+      for (int cc = 0; cc < DC / 16; ++cc) {
+        const F bq = lds_frag<T>(sQ + (qg * 32 + n) * RS + cc * 16 + 8 * h);
+        const F bo = lds_frag<T>(sO + (qg * 32 + n) * RS + cc * 16 + 8 * h);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const F ak = lds_frag<T>(sK + (kb * 32 + n) * RS + cc * 16 + 8 * h);
+          mma(sacc[kb], ak, bq);
+          const F av = lds_frag<T>(sV + (kb * 32 + n) * RS + cc * 16 + 8 * h);
+          mma(dpacc[kb], av, bo);
+        }
+      }
+    }
+    F uf[NKB][2];
+    grads(k0, full, sacc, dpacc, uf);
     // ---- dQ^T += K^T dU^T over this wave's slice
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if constexpr (!ONE) {
-        __syncthreads();
-        stage_rows_t<T, BN, DC, TS, true, NT>(sKt, kbase, kstride, k0, Sk, c * DC);
-        __syncthreads();
-      }
-      const int d0 = c * DC;
-      if (ONE || (d0 >= sl * DO && d0 < (sl + 1) * DO)) {
+      __syncthreads();
+      rkt.template store<TS, true>(sKt);
+      __syncthreads();
+      if (c + 1 < NCH) load_t(t, c + 1);
+      else if (t + 1 < ntile) load_s(t + 1, 0);
+      // chunk c belongs to slice c / (DO / DC), at its column block (c % (DO / DC)) DC / 32
+      constexpr int CPS = DO / DC;
+      if (sl == c / CPS) {
 #pragma unroll
         for (int db = 0; db < DC / 32; ++db) {
-          const int ob = ONE ? (db - sl * NOB) : ((d0 - sl * DO) / 32 + db);
-          if (ONE && (db < sl * NOB || db >= (sl + 1) * NOB)) continue;
+          const int ob = (c % CPS) * (DC / 32) + db;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -446,6 +502,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
         }
       }
     }
+  }
   }
 
   if (i < Sq) {
