@@ -158,37 +158,10 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) oacc[ob] = f32x16{};
 
-  if constexpr (ONE) {
-    stage_rows<T, BM, DC, QS, false, NT>(sQ, qbase, qstride, q0, Sq, 0);
-  }
-
   const int kbeg = (lo_first / BN) * BN;
-  for (int k0 = kbeg; k0 < hi_last; k0 += BN) {
-    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
 
-    // ---- S^T = K Q^T over the head dimension
-    f32x16 sacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      __syncthreads();
-      stage_rows<T, BN, DC, KS, true, NT>(sK, kbase, kstride, k0, Sk, c * DC);
-      if constexpr (!ONE) stage_rows<T, BM, DC, QS, false, NT>(sQ, qbase, qstride, q0, Sq, c * DC);
-      if constexpr (ONE) stage_rows_t<T, BN, DC, VS, true, NT>(sV, vbase, kstride, k0, Sk, 0);
-      __syncthreads();
-#pragma unroll
-      for (int cc = 0; cc < DC / 16; ++cc) {
-        const F bq = lds_frag<T>(sQ + (qg * 32 + n) * QS + cc * 16 + 8 * h);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const F ak = lds_frag<T>(sK + (kb * 32 + n) * KS + cc * 16 + 8 * h);
-          mma(sacc[kb], ak, bq);
-        }
-      }
-    }
-
-    // ---- scale, bias, cap, mask; online softmax
+  // ---- scale, bias, cap, mask; online softmax of one key tile (S -> P fragments)
+  auto softmax = [&](int k0, bool full, f32x16* sacc, F (*pf)[2]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -222,7 +195,6 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
     const float base = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = fast_exp2(m - base);
     float ps = 0.0f;
-    F pf[NKB][2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -238,21 +210,100 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
     m = m_new;
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) oacc[ob] *= alpha;
+  };
 
+  if constexpr (ONE) {
+  stage_rows<T, BM, DC, QS, false, NT>(sQ, qbase, qstride, q0, Sq, 0);
+  for (int k0 = kbeg; k0 < hi_last; k0 += BN) {
+    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
+    // ---- S^T = K Q^T over the head dimension
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+    __syncthreads();
+    stage_rows<T, BN, DC, KS, true, NT>(sK, kbase, kstride, k0, Sk, 0);
+    stage_rows_t<T, BN, DC, VS, true, NT>(sV, vbase, kstride, k0, Sk, 0);
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < DC / 16; ++cc) {
+      const F bq = lds_frag<T>(sQ + (qg * 32 + n) * QS + cc * 16 + 8 * h);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const F ak = lds_frag<T>(sK + (kb * 32 + n) * KS + cc * 16 + 8 * h);
+        mma(sacc[kb], ak, bq);
+      }
+    }
+    F pf[NKB][2];
+    softmax(k0, full, sacc, pf);
+    // ---- O^T += V^T P^T over this wave's slice of the head dimension
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      const int db = sl * NOB + ob;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const F av = lds_frag<T>(sV + (db * 32 + n) * VS + kb * 32 + 16 * sb + 8 * h);
+          mma(oacc[ob], av, pf[kb][sb]);
+        }
+      }
+    }
+  }
+  } else {
+  // Head dimension in NCH chunks: per key tile, the chunks of K and Q (for S)
+  // and then of V^T (for O) pass through LDS stage by stage; each stage's
+  // global loads are issued into registers while the previous stage's MFMAs
+  // run.
+  const int ntile = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
+  RowChunks<T, BN, DC, NT> rk;
+  RowChunks<T, BM, DC, NT> rq;
+  RowPairChunks<T, BN, DC, NT> rvt;
+  auto load_s = [&](int t, int c) {
+    rk.load(kbase, kstride, kbeg + t * BN, Sk, c * DC);
+    rq.load(qbase, qstride, q0, Sq, c * DC);
+  };
+  auto load_v = [&](int t, int c) { rvt.load(vbase, kstride, kbeg + t * BN, Sk, c * DC); };
+  if (ntile > 0) load_s(0, 0);
+  for (int t = 0; t < ntile; ++t) {
+    const int k0 = kbeg + t * BN;
+    const bool full = rows_full && k0 >= lo_last && k0 + BN <= hi_first;
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();
+      rk.template store<KS, true>(sK);
+      rq.template store<QS, false>(sQ);
+      __syncthreads();
+      if (c + 1 < NCH) load_s(t, c + 1);
+      else load_v(t, 0);
+#pragma unroll
+      for (int cc = 0; cc < DC / 16; ++cc) {
+        const F bq = lds_frag<T>(sQ + (qg * 32 + n) * QS + cc * 16 + 8 * h);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const F ak = lds_frag<T>(sK + (kb * 32 + n) * KS + cc * 16 + 8 * h);
+          mma(sacc[kb], ak, bq);
+        }
+      }
+    }
+    F pf[NKB][2];
+    softmax(k0, full, sacc, pf);
     // ---- O^T += V^T P^T over this wave's slice of the head dimension
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if constexpr (!ONE) {
-        __syncthreads();
-        stage_rows_t<T, BN, DC, VS, true, NT>(sV, vbase, kstride, k0, Sk, c * DC);
-        __syncthreads();
-      }
-      const int d0 = c * DC;
-      if (ONE || (d0 >= sl * DO && d0 < (sl + 1) * DO)) {
+      __syncthreads();
+      rvt.template store<VS, true>(sV);
+      __syncthreads();
+      if (c + 1 < NCH) load_v(t, c + 1);
+      else if (t + 1 < ntile) load_s(t + 1, 0);
+      // chunk c belongs to slice c / (DO / DC), at its column block (c % (DO / DC)) DC / 32
+      constexpr int CPS = DO / DC;
+      if (sl == c / CPS) {
 #pragma unroll
         for (int db = 0; db < DC / 32; ++db) {
-          const int ob = ONE ? (db - sl * NOB) : ((d0 - sl * DO) / 32 + db);
-          if (ONE && (db < sl * NOB || db >= (sl + 1) * NOB)) continue;
+          const int ob = (c % CPS) * (DC / 32) + db;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -264,6 +315,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
         }
       }
     }
+  }
   }
 
   // ---- epilogue: normalise (the sink joins the sum once) and write
