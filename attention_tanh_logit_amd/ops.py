@@ -162,11 +162,15 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink)
     _check(L.attn_validate(ctypes.byref(a)))
+    shape = (a.Hq, a.Sq) if cu_seqlens is not None else (a.B, a.Hq, a.Sq)
     if out is None:
         out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be contiguous with the shape, dtype and device of q")
     if lse is None:
-        shape = (a.Hq, a.Sq) if cu_seqlens is not None else (a.B, a.Hq, a.Sq)
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+    elif tuple(lse.shape) != shape or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError(f"lse must be contiguous float32 {list(shape)}")
     nws = L.attn_fwd_workspace_size(ctypes.byref(a))
     ws = _workspace(nws, q.device)
     _check(L.attn_fwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(q)))
@@ -174,13 +178,15 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
 
 
 def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
-             softcap=0.0, scale=0.0, sink_mode="none", sink=None, want_dbias=None, events=None):
+             softcap=0.0, scale=0.0, sink_mode="none", sink=None, want_dbias=None, events=None, outputs=None):
     """Backward: returns (dq, dk, dv, dbias or None, dsink or None).
 
     With ``events`` (four torch.cuda.Event) the three phases are launched
     through their own entry points (pre-pass, dk/dv, dq, in that order) with
     an event recorded before the pre-pass and after each phase, on the
-    current stream.
+    current stream.  ``outputs`` may hold preallocated result tensors under
+    "dq", "dk", "dv", "dbias", each contiguous with the shape, dtype and
+    device of q, k, v, bias; every element of each is overwritten.
     """
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
@@ -192,10 +198,23 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
     if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != a.B * a.Hq * a.Sq:
         raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
     want_dbias = (bias is not None) if want_dbias is None else want_dbias
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    dbias = torch.empty_like(bias) if (want_dbias and bias is not None) else None
+    given = outputs or {}
+    unknown = set(given) - {"dq", "dk", "dv", "dbias"}
+    if unknown:
+        raise ValueError(f"unknown outputs: {sorted(unknown)}")
+
+    def result(name, like):
+        t = given.get(name)
+        if t is None:
+            return torch.empty_like(like)
+        if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
+            raise ValueError(f"outputs[{name!r}] must be contiguous with the shape, dtype and device of its input")
+        return t
+
+    dq = result("dq", q)
+    dk = result("dk", k)
+    dv = result("dv", v)
+    dbias = result("dbias", bias) if (want_dbias and bias is not None) else None
     dsink = torch.empty(a.Hq, dtype=torch.float32, device=q.device) if sink_mode == "learnable" else None
     nws = L.attn_bwd_workspace_size(ctypes.byref(a))
     ws = _workspace(nws, q.device)

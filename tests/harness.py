@@ -85,13 +85,20 @@ def run_gpu(c, backward=True, thd=False):
         q, k, v = (x.reshape(-1, *x.shape[2:]) for x in (q, k, v))
     elif c["segment_ids"] is not None:
         kw["segment_ids"] = torch.from_numpy(c["segment_ids"]).cuda()
-    out, lse = A.attn_fwd(q, k, v, **kw)
+    # results land in NaN-filled buffers, so an element the kernels leave unwritten shows up
+    nan = float("nan")
+    lse_shape = (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
+    out, lse = A.attn_fwd(q, k, v, out=torch.full_like(q, nan),
+                          lse=torch.full(lse_shape, nan, dtype=torch.float32, device=q.device), **kw)
     res = {"out": out, "lse": lse}
     if backward:
         do = to_dev(c["dout"], dt)
         if thd:
             do = do.reshape(-1, *do.shape[2:])
-        dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, **kw)
+        outs = {"dq": torch.full_like(q, nan), "dk": torch.full_like(k, nan), "dv": torch.full_like(v, nan)}
+        if "bias" in kw:
+            outs["dbias"] = torch.full_like(kw["bias"], nan)
+        dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, outputs=outs, **kw)
         res.update(dq=dq, dk=dk, dv=dv, dbias=dbias, dsink=dsink)
     torch.cuda.synchronize()
     res = {n: (None if t is None else t.float().cpu().numpy()) for n, t in res.items()}

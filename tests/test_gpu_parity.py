@@ -75,6 +75,27 @@ def test_feature_matrix(dtype, D, feat):
     _check(case(**kw), known=_known(dtype, D, feat))
 
 
+# The bf16 fast kernels take a bias only when Sk is a multiple of 8 (bias rows are read 16
+# bytes at a time), which S = 203 above is not: these cases run them, including the dk/dv
+# kernel's bias / dbias tiles and the dbias zeros it writes outside its visible query tiles.
+BIAS_FAST = {
+    "causal": dict(),
+    "window": dict(window=37),
+    "segments": dict(segments=[[45, 70, 190], [128]]),
+    "no_causal": dict(causal=False),
+    "no_causal_window": dict(causal=False, window=29),
+    "sink_gqa_packing": dict(Hq=6, Hkv=2, segments=[[13, 100], [77, 78, 150]], window=50, sink_mode="learnable"),
+}
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("feat", list(BIAS_FAST))
+def test_bias_on_the_fast_path(D, feat):
+    kw = dict(dtype="bf16", D=D, B=2, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0)
+    kw.update(BIAS_FAST[feat])
+    _check(case(**kw))
+
+
 @pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("feat", list(FEATURES))
 def test_feature_matrix_dq_recomputed(D, feat, monkeypatch):
