@@ -324,26 +324,6 @@ struct TilePlan {
     }                                                            \
   } while (0)
 
-// Workgroup numbering for the 8 XCDs (each with its own L2), which receive
-// workgroups round-robin by linear id.  A grid of ntile x ngroup workgroups
-// (a group = one head, or one KV head, of one batch row) is renumbered so
-// that XCD x works on groups x*ngroup/8 .. (x+1)*ngroup/8 - 1 only -- their
-// tiles share K/V (or Q/dO) through that XCD's L2 -- and hands them out tile
-// index by tile index across those groups, so that tile 0 (the longest
-// under a causal mask) of every group is dispatched before any tile 1, and
-// so on: longest first over the whole XCD, which keeps the tail short.
-__device__ __forceinline__ void xcd_order(int ntile, int ngroup, int& tile, int& group) {
-  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  if (ngroup % 8 == 0) {
-    const int gpx = ngroup / 8;
-    const int t = L / 8;
-    tile = t / gpx;
-    group = (L % 8) * gpx + t % gpx;
-  } else {
-    tile = L % ntile;
-    group = L / ntile;
-  }
-}
 
 // ============================================================== forward
 

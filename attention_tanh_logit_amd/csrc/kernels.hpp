@@ -118,9 +118,16 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) T sK[BN * KS];
   __shared__ __attribute__((aligned(16))) T sV[DC * VS];
 
-  const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  // XCD-aware, longest-first numbering: the query tiles of a head share its K/V
+  // stream through one XCD's L2
+  int qt, hq, b;
+  {
+    int x, grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, x, grp);
+    qt = p.reverse ? gridDim.x - 1 - x : x;
+    hq = grp % gridDim.y;
+    b = grp / gridDim.y;
+  }
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int w = threadIdx.x >> 6;
@@ -363,9 +370,16 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T sV[BN * RS];
   __shared__ __attribute__((aligned(16))) T sKt[DC * TS];
 
-  const int qt = p.reverse ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  // XCD-aware, longest-first numbering: the query tiles of a head share its K/V
+  // stream through one XCD's L2
+  int qt, hq, b;
+  {
+    int x, grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, x, grp);
+    qt = p.reverse ? gridDim.x - 1 - x : x;
+    hq = grp % gridDim.y;
+    b = grp / gridDim.y;
+  }
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int w = threadIdx.x >> 6;
@@ -598,9 +612,15 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   __shared__ __attribute__((aligned(16))) float sL[BMQ];
   __shared__ __attribute__((aligned(16))) float sDl[BMQ];
 
-  const int kt = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
+  // XCD-aware numbering: neighbouring key blocks of a KV head, which see mostly
+  // the same query tiles, run on one XCD and share them through its L2
+  int kt, hk, b;
+  {
+    int grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, kt, grp);
+    hk = grp % gridDim.y;
+    b = grp / gridDim.y;
+  }
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
