@@ -607,8 +607,12 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   __shared__ __attribute__((aligned(16))) T sV[BNK * RS];
   __shared__ __attribute__((aligned(16))) T sQ[BMQ * RS];
   __shared__ __attribute__((aligned(16))) T sO[BMQ * RS];
-  __shared__ __attribute__((aligned(16))) T sQt[DC * TS];
-  __shared__ __attribute__((aligned(16))) T sOt[DC * TS];
+  // With the head dimension in chunks and LDS to spare, the Q^T and dO^T
+  // chunks of an item all stay in LDS: staged with Q and dO (the same global
+  // lines, loaded back to back) instead of read again for the gradient stages.
+  constexpr bool QTALL = !ONE && (2 * BNK * RS + 2 * BMQ * RS + 2 * NCH * DC * TS) * sizeof(T) <= 150 * 1024;
+  __shared__ __attribute__((aligned(16))) T sQt[(QTALL ? NCH : 1) * DC * TS];
+  __shared__ __attribute__((aligned(16))) T sOt[(QTALL ? NCH : 1) * DC * TS];
   __shared__ __attribute__((aligned(16))) float sL[BMQ];
   __shared__ __attribute__((aligned(16))) float sDl[BMQ];
 
@@ -771,6 +775,10 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
     const int hq = head_of(it), q0 = q0_of(it);
     rq.load(qb_of(hq), qstride, q0, Sq, c * DC);
     ro.load(ob_of(hq), qstride, q0, Sq, c * DC);
+    if constexpr (QTALL) {
+      rqt.load(qb_of(hq), qstride, q0, Sq, c * DC);
+      rot.load(ob_of(hq), qstride, q0, Sq, c * DC);
+    }
     rk.load(kbase, kstride, k0, Sk, c * DC);
     rv.load(vbase, kstride, k0, Sk, c * DC);
     if (c == 0) get_stats(hq, q0, nl, ndl);
@@ -792,10 +800,19 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       ro.template store<RS, true>(sO);
       rk.template store<RS, false>(sK);
       rv.template store<RS, false>(sV);
+      if constexpr (QTALL) {
+        rqt.template store<TS, true>(sQt + c * DC * TS);
+        rot.template store<TS, true>(sOt + c * DC * TS);
+      }
       if (c == 0) put_stats(q0 + (int)threadIdx.x, nl, ndl);
       __syncthreads();
-      if (c + 1 < NCH) load_s(it, c + 1);
-      else load_t(it, 0);
+      if (c + 1 < NCH) {
+        load_s(it, c + 1);
+      } else if constexpr (QTALL) {
+        if (it + 1 < nitems) load_s(it + 1, 0);
+      } else {
+        load_t(it, 0);
+      }
 #pragma unroll
       for (int cc = 0; cc < DC / 16; ++cc) {
         const F aq = lds_frag<T>(sQ + n * RS + cc * 16 + 8 * h);
@@ -811,12 +828,16 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
     // ---- dV^T += dO^T P,  dK^T += Q^T dU  over this wave's slice
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      __syncthreads();
-      rqt.template store<TS, true>(sQt);
-      rot.template store<TS, true>(sOt);
-      __syncthreads();
-      if (c + 1 < NCH) load_t(it, c + 1);
-      else if (it + 1 < nitems) load_s(it + 1, 0);
+      if constexpr (!QTALL) {
+        __syncthreads();
+        rqt.template store<TS, true>(sQt);
+        rot.template store<TS, true>(sOt);
+        __syncthreads();
+        if (c + 1 < NCH) load_t(it, c + 1);
+        else if (it + 1 < nitems) load_s(it + 1, 0);
+      }
+      const T* tQt = sQt + (QTALL ? c * DC * TS : 0);
+      const T* tOt = sOt + (QTALL ? c * DC * TS : 0);
       // chunk c belongs to slice c / (DO / DC), at its column block (c % (DO / DC)) DC / 32
       constexpr int CPS = DO / DC;
       if (sl == c / CPS) {
@@ -825,9 +846,9 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
           const int ob = (c % CPS) * (DC / 32) + db;
 #pragma unroll
           for (int sb = 0; sb < 2; ++sb) {
-            const F ao = lds_frag<T>(sOt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+            const F ao = lds_frag<T>(tOt + (db * 32 + n) * TS + 16 * sb + 8 * h);
             mma(vacc[ob], ao, pf[sb]);
-            const F aq = lds_frag<T>(sQt + (db * 32 + n) * TS + 16 * sb + 8 * h);
+            const F aq = lds_frag<T>(tQt + (db * 32 + n) * TS + 16 * sb + 8 * h);
             mma(kacc[ob], aq, uf[sb]);
           }
         }
