@@ -556,10 +556,10 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
       }
       lsum += ps;
       if constexpr (PIPE) {
-        if (next) {
+        // unconditional: after the last tile scur is not read again, and a
+        // select per element would cost a VALU instruction per pair
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
-        }
+        for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
       }
     }
 
