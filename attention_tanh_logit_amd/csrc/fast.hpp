@@ -909,6 +909,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   // the Q/dO tiles, and its dbias tile gathered here and written out as whole
   // rows during the next item; 16-byte chunks swizzled per row (bsw)
   constexpr int BT = BIAS ? BMQ * BNK : 8;
+  // D = 256: the two waves of a key group each take half of an item's query
+  // blocks for S, dP and the gradients, then swap their P and dU values
+  // through LDS (both need all of them for their column slices of dV, dK)
+  constexpr bool QSPLIT = NSL == 2;
+  constexpr int QPW = NQB / NSL;          // query blocks per wave
+  __shared__ __attribute__((aligned(16))) bf16 sX[QSPLIT ? NW * 64 * 8 * QPW : 8];
   __shared__ __attribute__((aligned(16))) bf16 sB0[BT];
   __shared__ __attribute__((aligned(16))) bf16 sB1[BT];
   __shared__ __attribute__((aligned(16))) bf16 sG0[BT];
@@ -1059,27 +1065,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     // S and dP - delta; the stats of queries 16qb + 4g .. + 3 are one f32x4
     const f32x4* L4 = reinterpret_cast<const f32x4*>(tL);
     const f32x4* D4 = reinterpret_cast<const f32x4*>(tD);
-    f32x4 sacc[NQB], dpacc[NQB];
+    // this wave's query blocks: all of them, or (QSPLIT) qb = sl QPW + i
+    constexpr int NQL = QSPLIT ? QPW : NQB;
+    const int qb0 = QSPLIT ? sl * QPW : 0;
+    f32x4 sacc[NQL], dpacc[NQL];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      sacc[qb] = f32x4{};
-      dpacc[qb] = D4[4 * qb + g];
+    for (int i = 0; i < NQL; ++i) {
+      sacc[i] = f32x4{};
+      dpacc[i] = D4[4 * (qb0 + i) + g];
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        mma16(sacc[qb], fo.frag(tQ, 16 * qb, c), kf[c]);
-        mma16(dpacc[qb], fo.frag(tO, 16 * qb, c), vf[c]);
+      for (int i = 0; i < NQL; ++i) {
+        mma16(sacc[i], fo.frag(tQ, 16 * (qb0 + i), c), kf[c]);
+        mma16(dpacc[i], fo.frag(tO, 16 * (qb0 + i), c), vf[c]);
       }
     }
     // keep fragment reads in flight ahead of their MFMAs
-    ATL_READ_AHEAD(8, 1, 2 * NC * NQB);
+    ATL_READ_AHEAD(8, 1, 2 * NC * NQL);
 
     const int bcol = 16 * kgi + r;      // this lane's key column in the bias tiles
     auto grads = [&](auto masked) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
+      for (int i = 0; i < NQL; ++i) {
+        const int qb = qb0 + i;
         const f32x4 l4 = L4[4 * qb + g];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1089,13 +1099,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
           float bvv = 0.0f;
           if constexpr (BIAS) bvv = (float)tB[bidx(16 * qb + 4 * g + e, bcol)];
           float gg;
-          const float pv = prob_fast<CAP, BIAS>(sacc[qb][e], bvv, lk, lc, gg);
-          const float du = pv * dpacc[qb][e] * gg;
-          sacc[qb][e] = pv;
-          dpacc[qb][e] = du;
-          // masked pairs have P = 0, hence dbias = 0, as the pre-pass already wrote
+          const float pv = prob_fast<CAP, BIAS>(sacc[i][e], bvv, lk, lc, gg);
+          const float du = pv * dpacc[i][e] * gg;
+          sacc[i][e] = pv;
+          dpacc[i][e] = du;
+          // masked pairs have P = 0 and are written as zeros; each query block
+          // by the one wave that computed it
           if constexpr (BIAS) {
-            if (sl == 0) tG[bidx(16 * qb + 4 * g + e, bcol)] = (bf16)(du * kGrad4<CAP>);
+            if (QSPLIT || sl == 0) tG[bidx(16 * qb + 4 * g + e, bcol)] = (bf16)(du * kGrad4<CAP>);
           }
         }
       }
@@ -1103,10 +1114,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     if (keys_full && q0 >= lo_last && q0 + BMQ <= hi_first) grads(bool_c<false>{});
     else grads(bool_c<true>{});
     bf16x8 pf[NKC], uf[NKC];
+    if constexpr (QSPLIT) {
+      static_assert(QPW == 1 && NKC == 1, "query split laid out for 32-query items");
+      // lane's P and dU of its query block (bf16) out, the partner's in
+      bf16x8 mine;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      pf[kc] = pack8(sacc[2 * kc], sacc[2 * kc + 1]);
-      uf[kc] = pack8(dpacc[2 * kc], dpacc[2 * kc + 1]);
+      for (int e = 0; e < 4; ++e) {
+        mine[e] = (bf16)sacc[0][e];
+        mine[4 + e] = (bf16)dpacc[0][e];
+      }
+      *reinterpret_cast<bf16x8*>(sX + (w * 64 + lane) * 8) = mine;
+      __syncthreads();
+      const bf16x8 other = *reinterpret_cast<const bf16x8*>(sX + ((w ^ 1) * 64 + lane) * 8);
+      const bf16x8 lo = sl == 0 ? mine : other, hi = sl == 0 ? other : mine;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[0][e] = lo[e];
+        pf[0][4 + e] = hi[e];
+        uf[0][e] = lo[4 + e];
+        uf[0][4 + e] = hi[4 + e];
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        pf[kc] = pack8(sacc[2 * kc], sacc[2 * kc + 1]);
+        uf[kc] = pack8(dpacc[2 * kc], dpacc[2 * kc + 1]);
+      }
     }
     // this wave's half of the dU block (32-key block of the pair, query block q0/32 + kc)
     if (p.du && sl == 0 && k0 + 16 * (kgi & ~1) < Sk) {
