@@ -52,7 +52,7 @@ ATL_DKDV(bf16, 256, 128, 2, 256)
 ATL_DKDV(bf16, 512, 128, 1, 128)
 ATL_DKDV(float, 64, 64, 4, 64)
 ATL_DKDV(float, 128, 128, 2, 128)
-ATL_DKDV(float, 256, 128, 2, 128)
+ATL_DKDV(float, 256, 64, 1, 64)
 ATL_DKDV(float, 512, 128, 1, 128)
 
 #undef ATL_FWD

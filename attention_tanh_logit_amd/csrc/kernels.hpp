@@ -21,8 +21,10 @@
 // attention VJP", PR description).
 //
 // Head dimensions that do not fit LDS in one piece are staged in chunks of
-// DC columns; a wave owns a slice of DO output columns (D/DO waves share the
-// same queries or keys and recompute the same logits).
+// DC columns; a wave owns a slice of DO output columns.  The D/DO waves that
+// share the same queries or keys split the logits' contraction over the head
+// dimension between them and sum their partial products through LDS, where
+// LDS has room for the partials; otherwise each computes the whole logits.
 #pragma once
 
 #include "common.hpp"
@@ -95,6 +97,45 @@ __device__ __forceinline__ float logit2(float x, float b, float sl2, float xc, f
   }
 }
 
+// Sum of partial accumulators over the NSL waves of one row (or key) group,
+// each of which holds the contraction over its own share of the head
+// dimension.  Every wave of the group gets the same total, added in slice
+// order, so the waves agree bit for bit.  Wave w of the group at slice sl
+// writes red[w], so red holds NW * NA * 4 KiB; the caller puts a barrier
+// between two uses.
+template <int NSL, int NA>
+__device__ __forceinline__ void slice_sum(float* red, int w, int sl, f32x16 (&acc)[NA]) {
+  const int lane = threadIdx.x & 63;
+  float4* r4 = reinterpret_cast<float4*>(red);
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r4[((w * NA + a) * 4 + q) * 64 + lane] = make_float4(acc[a][4 * q], acc[a][4 * q + 1], acc[a][4 * q + 2], acc[a][4 * q + 3]);
+  }
+  __syncthreads();
+  const int g0 = w - sl;
+#pragma unroll
+  for (int a = 0; a < NA; ++a) acc[a] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < NSL; ++s) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = r4[(((g0 + s) * NA + a) * 4 + q) * 64 + lane];
+        acc[a][4 * q] += v.x;
+        acc[a][4 * q + 1] += v.y;
+        acc[a][4 * q + 2] += v.z;
+        acc[a][4 * q + 3] += v.w;
+      }
+    }
+  }
+}
+
+// LDS budget of a workgroup, leaving a little for the compiler's own layout
+constexpr int kLdsBudget = 158 * 1024;
+
 // ============================================================== forward
 
 template <typename T, int D, int DO, int NQG, int BN, int DC, bool CAP, bool BIAS>
@@ -117,6 +158,13 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) T sQ[BM * QS];
   __shared__ __attribute__((aligned(16))) T sK[BN * KS];
   __shared__ __attribute__((aligned(16))) T sV[DC * VS];
+  // the slices of a row group split each chunk's contraction for S
+  // (fp32 only: with bf16 the partial sums cost the forward more than the
+  // MFMA work they save)
+  constexpr bool SPLIT = sizeof(T) == 4 && !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
+                         (BM * QS + BN * KS + DC * VS) * (int)sizeof(T) + NW * NKB * 4096 <= kLdsBudget;
+  constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;   // 16-column steps per wave and chunk
+  __shared__ __attribute__((aligned(16))) float sRed[SPLIT ? NW * NKB * 1024 : 4];
 
   // XCD-aware, longest-first numbering: the query tiles of a head share its K/V
   // stream through one XCD's L2
@@ -286,7 +334,8 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
       if (c + 1 < NCH) load_s(t, c + 1);
       else load_v(t, 0);
 #pragma unroll
-      for (int cc = 0; cc < DC / 16; ++cc) {
+      for (int ci = 0; ci < CPW; ++ci) {
+        const int cc = SPLIT ? ci * NSL + sl : ci;
         const F bq = lds_frag<T>(sQ + (qg * 32 + n) * QS + cc * 16 + 8 * h);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -295,6 +344,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
         }
       }
     }
+    if constexpr (SPLIT) slice_sum<NSL, NKB>(sRed, w, sl, sacc);
     F pf[NKB][2];
     softmax(k0, full, sacc, pf);
     // ---- O^T += V^T P^T over this wave's slice of the head dimension
@@ -369,6 +419,11 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T sK[BN * RS];
   __shared__ __attribute__((aligned(16))) T sV[BN * RS];
   __shared__ __attribute__((aligned(16))) T sKt[DC * TS];
+  // the slices of a row group split each chunk's contraction for S and dP
+  constexpr bool SPLIT = !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
+                         (2 * BM * RS + 2 * BN * RS + DC * TS) * (int)sizeof(T) + NW * 2 * NKB * 4096 <= kLdsBudget;
+  constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;
+  __shared__ __attribute__((aligned(16))) float sRed[SPLIT ? NW * 2 * NKB * 1024 : 4];
 
   // XCD-aware, longest-first numbering: the query tiles of a head share its K/V
   // stream through one XCD's L2
@@ -529,7 +584,8 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
       if (c + 1 < NCH) load_s(t, c + 1);
       else load_t(t, 0);
 #pragma unroll
-      for (int cc = 0; cc < DC / 16; ++cc) {
+      for (int ci = 0; ci < CPW; ++ci) {
+        const int cc = SPLIT ? ci * NSL + sl : ci;
         const F bq = lds_frag<T>(sQ + (qg * 32 + n) * RS + cc * 16 + 8 * h);
         const F bo = lds_frag<T>(sO + (qg * 32 + n) * RS + cc * 16 + 8 * h);
 #pragma unroll
@@ -540,6 +596,14 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
           mma(dpacc[kb], av, bo);
         }
       }
+    }
+    if constexpr (SPLIT) {
+      f32x16 sd[2 * NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) { sd[kb] = sacc[kb]; sd[NKB + kb] = dpacc[kb]; }
+      slice_sum<NSL, 2 * NKB>(sRed, w, sl, sd);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) { sacc[kb] = sd[kb]; dpacc[kb] = sd[NKB + kb]; }
     }
     F uf[NKB][2];
     grads(k0, full, sacc, dpacc, uf);
@@ -610,11 +674,17 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   // With the head dimension in chunks and LDS to spare, the Q^T and dO^T
   // chunks of an item all stay in LDS: staged with Q and dO (the same global
   // lines, loaded back to back) instead of read again for the gradient stages.
-  constexpr bool QTALL = !ONE && (2 * BNK * RS + 2 * BMQ * RS + 2 * NCH * DC * TS) * sizeof(T) <= 150 * 1024;
+  // the slices of a key group split each chunk's contraction for S and dP
+  constexpr bool SPLIT = !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
+                         (2 * BNK * RS + 2 * BMQ * RS + 2 * DC * TS) * (int)sizeof(T) + NW * 2 * 4096 <= kLdsBudget;
+  constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;
+  constexpr int RED = SPLIT ? NW * 2 * 4096 : 0;
+  constexpr bool QTALL = !ONE && (2 * BNK * RS + 2 * BMQ * RS + 2 * NCH * DC * TS) * (int)sizeof(T) + RED <= 150 * 1024;
   __shared__ __attribute__((aligned(16))) T sQt[(QTALL ? NCH : 1) * DC * TS];
   __shared__ __attribute__((aligned(16))) T sOt[(QTALL ? NCH : 1) * DC * TS];
   __shared__ __attribute__((aligned(16))) float sL[BMQ];
   __shared__ __attribute__((aligned(16))) float sDl[BMQ];
+  __shared__ __attribute__((aligned(16))) float sRed[SPLIT ? NW * 2 * 1024 : 4];
 
   // XCD-aware numbering: neighbouring key blocks of a KV head, which see mostly
   // the same query tiles, run on one XCD and share them through its L2
@@ -685,7 +755,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       sacc[r] = pv;
       dpacc[r] = du;
       if constexpr (BIAS) {
-        if (dbbase && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
+        if (dbbase && sl == 0 && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
       }
     }
     pf[0] = to_frag(sacc, 0, (T*)nullptr);
@@ -814,7 +884,8 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
         load_t(it, 0);
       }
 #pragma unroll
-      for (int cc = 0; cc < DC / 16; ++cc) {
+      for (int ci = 0; ci < CPW; ++ci) {
+        const int cc = SPLIT ? ci * NSL + sl : ci;
         const F aq = lds_frag<T>(sQ + n * RS + cc * 16 + 8 * h);
         const F bk = lds_frag<T>(sK + (kg * 32 + n) * RS + cc * 16 + 8 * h);
         mma(sacc, aq, bk);
@@ -822,6 +893,12 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
         const F bv = lds_frag<T>(sV + (kg * 32 + n) * RS + cc * 16 + 8 * h);
         mma(dpacc, ao, bv);
       }
+    }
+    if constexpr (SPLIT) {
+      f32x16 sd[2] = {sacc, dpacc};
+      slice_sum<NSL, 2>(sRed, w, sl, sd);
+      sacc = sd[0];
+      dpacc = sd[1];
     }
     F pf[2], uf[2];
     grads(hq, q0, full, sacc, dpacc, pf, uf);
