@@ -155,15 +155,20 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   static_assert(ONE || DO % DC == 0, "a chunk must not straddle two slices");
   using F = typename Frag<T>::type;
 
-  __shared__ __attribute__((aligned(16))) T sQ[BM * QS];
-  __shared__ __attribute__((aligned(16))) T sK[BN * KS];
-  __shared__ __attribute__((aligned(16))) T sV[DC * VS];
   // the slices of a row group split each chunk's contraction for S
   // (fp32 only: with bf16 the partial sums cost the forward more than the
   // MFMA work they save)
   constexpr bool SPLIT = sizeof(T) == 4 && !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
                          (BM * QS + BN * KS + DC * VS) * (int)sizeof(T) + NW * NKB * 4096 <= kLdsBudget;
   constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;   // 16-column steps per wave and chunk
+  constexpr int RED = SPLIT ? NW * NKB * 4096 : 0;
+  // with the head dimension in chunks, all chunks of the Q tile stay in LDS
+  // for the whole key sweep where they fit (instead of being staged again
+  // for every key tile)
+  constexpr bool QRES = !ONE && (NCH * BM * QS + BN * KS + DC * VS) * (int)sizeof(T) + RED <= 150 * 1024;
+  __shared__ __attribute__((aligned(16))) T sQ[(QRES ? NCH : 1) * BM * QS];
+  __shared__ __attribute__((aligned(16))) T sK[BN * KS];
+  __shared__ __attribute__((aligned(16))) T sV[DC * VS];
   __shared__ __attribute__((aligned(16))) float sRed[SPLIT ? NW * NKB * 1024 : 4];
 
   // XCD-aware, longest-first numbering: the query tiles of a head share its K/V
@@ -315,8 +320,12 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   RowPairChunks<T, BN, DC, NT> rvt;
   auto load_s = [&](int t, int c) {
     rk.load(kbase, kstride, kbeg + t * BN, Sk, c * DC);
-    rq.load(qbase, qstride, q0, Sq, c * DC);
+    if constexpr (!QRES) rq.load(qbase, qstride, q0, Sq, c * DC);
   };
+  if constexpr (QRES) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) stage_rows<T, BM, DC, QS, false, NT>(sQ + c * BM * QS, qbase, qstride, q0, Sq, c * DC);
+  }
   auto load_v = [&](int t, int c) { rvt.load(vbase, kstride, kbeg + t * BN, Sk, c * DC); };
   if (ntile > 0) load_s(0, 0);
   for (int t = 0; t < ntile; ++t) {
@@ -329,14 +338,15 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
     for (int c = 0; c < NCH; ++c) {
       __syncthreads();
       rk.template store<KS, true>(sK);
-      rq.template store<QS, false>(sQ);
+      if constexpr (!QRES) rq.template store<QS, false>(sQ);
       __syncthreads();
       if (c + 1 < NCH) load_s(t, c + 1);
       else load_v(t, 0);
+      const T* tQ = sQ + (QRES ? c * BM * QS : 0);
 #pragma unroll
       for (int ci = 0; ci < CPW; ++ci) {
         const int cc = SPLIT ? ci * NSL + sl : ci;
-        const F bq = lds_frag<T>(sQ + (qg * 32 + n) * QS + cc * 16 + 8 * h);
+        const F bq = lds_frag<T>(tQ + (qg * 32 + n) * QS + cc * 16 + 8 * h);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const F ak = lds_frag<T>(sK + (kb * 32 + n) * KS + cc * 16 + 8 * h);
@@ -667,19 +677,21 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   static_assert(ONE || DO % DC == 0, "a chunk must not straddle two slices");
   using F = typename Frag<T>::type;
 
-  __shared__ __attribute__((aligned(16))) T sK[BNK * RS];
-  __shared__ __attribute__((aligned(16))) T sV[BNK * RS];
-  __shared__ __attribute__((aligned(16))) T sQ[BMQ * RS];
-  __shared__ __attribute__((aligned(16))) T sO[BMQ * RS];
-  // With the head dimension in chunks and LDS to spare, the Q^T and dO^T
-  // chunks of an item all stay in LDS: staged with Q and dO (the same global
-  // lines, loaded back to back) instead of read again for the gradient stages.
   // the slices of a key group split each chunk's contraction for S and dP
   constexpr bool SPLIT = !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
                          (2 * BNK * RS + 2 * BMQ * RS + 2 * DC * TS) * (int)sizeof(T) + NW * 2 * 4096 <= kLdsBudget;
   constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;
   constexpr int RED = SPLIT ? NW * 2 * 4096 : 0;
+  // With the head dimension in chunks and LDS to spare, the Q^T and dO^T
+  // chunks of an item all stay in LDS: staged with Q and dO (the same global
+  // lines, loaded back to back) instead of read again for the gradient stages.
+  // (Keeping the key block's K and V chunks in LDS instead, where only one of
+  // the two fits, was slower.)
   constexpr bool QTALL = !ONE && (2 * BNK * RS + 2 * BMQ * RS + 2 * NCH * DC * TS) * (int)sizeof(T) + RED <= 150 * 1024;
+  __shared__ __attribute__((aligned(16))) T sK[BNK * RS];
+  __shared__ __attribute__((aligned(16))) T sV[BNK * RS];
+  __shared__ __attribute__((aligned(16))) T sQ[BMQ * RS];
+  __shared__ __attribute__((aligned(16))) T sO[BMQ * RS];
   __shared__ __attribute__((aligned(16))) T sQt[(QTALL ? NCH : 1) * DC * TS];
   __shared__ __attribute__((aligned(16))) T sOt[(QTALL ? NCH : 1) * DC * TS];
   __shared__ __attribute__((aligned(16))) float sL[BMQ];
