@@ -682,6 +682,10 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
                          (2 * BNK * RS + 2 * BMQ * RS + 2 * DC * TS) * (int)sizeof(T) + NW * 2 * 4096 <= kLdsBudget;
   constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;
   constexpr int RED = SPLIT ? NW * 2 * 4096 : 0;
+  // bf16 with split logits: a wave needs only its share of the columns of K
+  // and V (NCH * CPW fragments of each, 4 registers apiece), which it keeps
+  // in registers for the whole sweep instead of staging K and V per item
+  constexpr bool KVREG = SPLIT && sizeof(T) == 2;
   // With the head dimension in chunks and LDS to spare, the Q^T and dO^T
   // chunks of an item all stay in LDS: staged with Q and dO (the same global
   // lines, loaded back to back) instead of read again for the gradient stages.
@@ -861,8 +865,10 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       rqt.load(qb_of(hq), qstride, q0, Sq, c * DC);
       rot.load(ob_of(hq), qstride, q0, Sq, c * DC);
     }
-    rk.load(kbase, kstride, k0, Sk, c * DC);
-    rv.load(vbase, kstride, k0, Sk, c * DC);
+    if constexpr (!KVREG) {
+      rk.load(kbase, kstride, k0, Sk, c * DC);
+      rv.load(vbase, kstride, k0, Sk, c * DC);
+    }
     if (c == 0) get_stats(hq, q0, nl, ndl);
   };
   auto load_t = [&](int it, int c) {   // stage c of dV / dK
@@ -870,6 +876,19 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
     rqt.load(qb_of(hq), qstride, q0, Sq, c * DC);
     rot.load(ob_of(hq), qstride, q0, Sq, c * DC);
   };
+  F kf[KVREG ? NCH * CPW : 1], vf[KVREG ? NCH * CPW : 1];
+  if constexpr (KVREG) {
+    // lane (n, h) holds K, V row j, columns c DC + (ci NSL + sl) 16 + 8 h .. + 8
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int ci = 0; ci < CPW; ++ci) {
+        const long off = (long)j * kstride + c * DC + (ci * NSL + sl) * 16 + 8 * h;
+        kf[c * CPW + ci] = j < Sk ? *reinterpret_cast<const F*>(kbase + off) : F{};
+        vf[c * CPW + ci] = j < Sk ? *reinterpret_cast<const F*>(vbase + off) : F{};
+      }
+    }
+  }
   if (nitems > 0) load_s(0, 0);
   for (int it = 0; it < nitems; ++it) {
     const int hq = head_of(it), q0 = q0_of(it);
@@ -880,8 +899,10 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       __syncthreads();
       rq.template store<RS, true>(sQ);
       ro.template store<RS, true>(sO);
-      rk.template store<RS, false>(sK);
-      rv.template store<RS, false>(sV);
+      if constexpr (!KVREG) {
+        rk.template store<RS, false>(sK);
+        rv.template store<RS, false>(sV);
+      }
       if constexpr (QTALL) {
         rqt.template store<TS, true>(sQt + c * DC * TS);
         rot.template store<TS, true>(sOt + c * DC * TS);
@@ -899,10 +920,10 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       for (int ci = 0; ci < CPW; ++ci) {
         const int cc = SPLIT ? ci * NSL + sl : ci;
         const F aq = lds_frag<T>(sQ + n * RS + cc * 16 + 8 * h);
-        const F bk = lds_frag<T>(sK + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+        const F bk = KVREG ? kf[KVREG ? c * CPW + ci : 0] : lds_frag<T>(sK + (kg * 32 + n) * RS + cc * 16 + 8 * h);
         mma(sacc, aq, bk);
         const F ao = lds_frag<T>(sO + n * RS + cc * 16 + 8 * h);
-        const F bv = lds_frag<T>(sV + (kg * 32 + n) * RS + cc * 16 + 8 * h);
+        const F bv = KVREG ? vf[KVREG ? c * CPW + ci : 0] : lds_frag<T>(sV + (kg * 32 + n) * RS + cc * 16 + 8 * h);
         mma(dpacc, ao, bv);
       }
     }
