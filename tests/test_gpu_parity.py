@@ -67,7 +67,7 @@ FEATURES = {
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("bf16", 256), ("fp32", 64),
-                                     ("fp32", 256), ("bf16", 512)])
+                                     ("fp32", 256), ("bf16", 512), ("fp32", 512)])
 @pytest.mark.parametrize("feat", list(FEATURES))
 def test_feature_matrix(dtype, D, feat):
     kw = dict(dtype=dtype, D=D, B=2, S=203, Hq=4, Hkv=2)
