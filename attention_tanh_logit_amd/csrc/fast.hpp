@@ -888,7 +888,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
 template <int D, bool CAP, bool BIAS, int NW, int BMQ>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   // D = 256: waves w and w + 1 share 16 keys and split dK^T, dV^T by columns
-  // (each recomputes S, dP and the gradients of the pair's keys)
+  // (and the query blocks of S, dP and dU between them: see QSPLIT)
   constexpr int NSL = D > 128 ? 2 : 1;
   constexpr int NT = 64 * NW;
   constexpr int BNK = 16 * NW / NSL;
