@@ -2,6 +2,7 @@
 // closed: a requested cap or sink is never dropped), workspace layout and the
 // launch sequence on the caller's stream.
 #include <cmath>
+#include <cstdint>
 #include <cstdlib>
 #include <cstdio>
 #include <string>
@@ -85,6 +86,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool has_segments(const attn_args* a) { return a->segment_ids != nullptr || a->cu_seqlens != nullptr; }
 
+// The kernels move rows 16 bytes at a time (vector loads, LDS DMA).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 attn_status validate(const attn_args* a) {
   if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
   if (a->dtype != ATTN_BF16 && a->dtype != ATTN_FP32) return fail(ATTN_INVALID_ARGUMENT, "dtype must be ATTN_BF16 or ATTN_FP32");
@@ -115,6 +119,8 @@ attn_status validate(const attn_args* a) {
     return fail(ATTN_UNSUPPORTED, "B*S must fit in int32");
   const size_t elems = (size_t)a->B * (a->Sq + a->Sk);
   if (elems != 0 && (!a->q || !a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "q, k and v must not be NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->bias))
+    return fail(ATTN_INVALID_ARGUMENT, "q, k, v and bias must be 16-byte aligned");
   return ATTN_OK;
 }
 
@@ -264,6 +270,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* workspace,
     return fail(ATTN_INVALID_ARGUMENT, "workspace smaller than attn_fwd_workspace_size");
   if ((size_t)a->B * a->Sq * a->Hq == 0) return ATTN_OK;
   if (!out || !lse) return fail(ATTN_INVALID_ARGUMENT, "out and lse must not be NULL");
+  if (!aligned16(out)) return fail(ATTN_INVALID_ARGUMENT, "out must be 16-byte aligned");
   if (a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -317,6 +324,8 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
   if ((phases & kPhasePre) && !out) return fail(ATTN_INVALID_ARGUMENT, "out must not be NULL");
   if ((phases & kPhaseDq) && !dq) return fail(ATTN_INVALID_ARGUMENT, "dq must not be NULL");
   if ((phases & kPhaseDkdv) && (!dk || !dv)) return fail(ATTN_INVALID_ARGUMENT, "dk and dv must not be NULL");
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbias))
+    return fail(ATTN_INVALID_ARGUMENT, "out, dout, dq, dk, dv and dbias must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   BwdParams p;

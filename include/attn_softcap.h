@@ -81,6 +81,9 @@ typedef enum attn_sink_mode {
   ATTN_SINK_LEARNABLE = 2
 } attn_sink_mode;
 
+/* Every tensor pointer (q, k, v, bias, out, dout, dq, dk, dv, dbias) must be
+ * 16-byte aligned: the kernels move rows 16 bytes at a time.  A misaligned
+ * pointer is rejected with ATTN_INVALID_ARGUMENT before anything is launched. */
 typedef struct attn_args {
   int dtype;                   /* attn_dtype of q, k, v, bias, out, dout, dq, dk, dv, dbias */
   int B, Sq, Sk, Hq, Hkv, D;   /* D in {64, 128, 256, 512}; Hq % Hkv == 0 */

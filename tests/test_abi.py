@@ -72,6 +72,8 @@ BAD = {
     "null_q": (dict(q=None), 1, "NULL"),
     "negative_scale": (dict(scale=-0.1), 1, "scale"),
     "zero_heads": (dict(Hkv=0), 1, "Hkv"),
+    "misaligned_q": (dict(q=0x1002), 1, "aligned"),
+    "misaligned_bias": (dict(bias=0x2008), 1, "aligned"),
 }
 
 
@@ -103,6 +105,15 @@ def test_fwd_rejects_before_any_launch():
     a = _args(sink_mode=2, sink=0x2000)
     s = L.attn_bwd(ctypes.byref(a), 0x10, 0x20, 0x30, 0x40, 0x50, 0x60, None, None, None, 1 << 30, None)
     assert s == 1 and "dsink" in L.attn_last_error().decode()
+
+
+def test_misaligned_outputs_rejected_before_any_launch():
+    L = A.lib()
+    a = _args()
+    assert L.attn_fwd(ctypes.byref(a), 0x1004, 0x2000, None, 0, None) == 1
+    assert "aligned" in L.attn_last_error().decode()
+    s = L.attn_bwd(ctypes.byref(a), 0x1000, 0x2000, 0x3000, 0x4002, 0x5000, 0x6000, None, None, 0x7000, 1 << 30, None)
+    assert s == 1 and "aligned" in L.attn_last_error().decode()
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
