@@ -27,31 +27,72 @@ __global__ __launch_bounds__(256) void dsink_final_kernel(const float* part, flo
   if (threadIdx.x == 0) dsink[hq] = red[0];
 }
 
-// Per-token run [start, end) of packed segment ids (non-decreasing per row):
-// lower and upper bound of the token's id in its row.
-__global__ __launch_bounds__(256) void seg_from_ids_kernel(const int* ids, int* seg_lo, int* seg_hi, int S) {
-  const int b = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= S) return;
-  const int* row = ids + (long)b * S;
-  const int id = row[t];
-  int lo = 0, hi = S;
-  while (lo < hi) {  // first index with row[x] >= id
-    const int mid = (lo + hi) >> 1;
-    if (row[mid] < id) lo = mid + 1; else hi = mid;
+// Per-token run [start, end) of packed segment ids: the maximal stretch of
+// equal adjacent ids around the token.  One workgroup per batch row sweeps
+// the row in chunks of 1024 tokens with a running maximum of run starts
+// (forwards) and a running minimum of run ends (backwards), so that the runs
+// of any id sequence are consistent (j lies in t's run iff t lies in j's);
+// for ids that do not decrease along the row they are exactly the tokens of
+// equal id.
+__device__ __forceinline__ int wave_scan_max(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x = max(x, y);
   }
-  const int start = lo;
-  lo = t;
-  hi = S;
-  while (lo < hi) {  // first index with row[x] > id
-    const int mid = (lo + hi) >> 1;
-    if (row[mid] <= id) lo = mid + 1; else hi = mid;
-  }
-  seg_lo[(long)b * S + t] = min(start, t);
-  seg_hi[(long)b * S + t] = max(lo, t + 1);
+  return x;
 }
 
-// Per-token run from cumulative sequence lengths (THD layout, one row)
+__global__ __launch_bounds__(1024) void seg_from_ids_kernel(const int* ids, int* seg_lo, int* seg_hi, int S) {
+  __shared__ int wtot[16];
+  const int b = blockIdx.x;
+  const int* row = ids + (long)b * S;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // starts: inclusive prefix maximum of the boundary positions
+  int carry = 0;
+  for (int c0 = 0; c0 < S; c0 += 1024) {
+    const int t = c0 + tid;
+    int f = 0;
+    if (t < S) f = (t == 0 || row[t] != row[t - 1]) ? t : 0;
+    f = wave_scan_max(f);
+    if (lane == 63) wtot[w] = f;
+    __syncthreads();
+    int pre = carry;
+    for (int x = 0; x < w; ++x) pre = max(pre, wtot[x]);
+    const int st = max(f, pre);
+    if (t < S) seg_lo[(long)b * S + t] = st;
+    int last = carry;
+    for (int x = 0; x < 16; ++x) last = max(last, wtot[x]);
+    __syncthreads();
+    carry = last;
+  }
+  // ends: suffix minimum of the run ends, as a prefix maximum over -end
+  // walking the row from its end
+  carry = -S;
+  for (int c0 = 0; c0 < S; c0 += 1024) {
+    const int t = S - 1 - (c0 + tid);
+    int f = -S;
+    if (t >= 0) f = (t + 1 == S || row[t + 1] != row[t]) ? -(t + 1) : -S;
+    f = wave_scan_max(f);
+    if (lane == 63) wtot[w] = f;
+    __syncthreads();
+    int pre = carry;
+    for (int x = 0; x < w; ++x) pre = max(pre, wtot[x]);
+    const int en = -max(f, pre);
+    if (t >= 0) seg_hi[(long)b * S + t] = en;
+    int last = carry;
+    for (int x = 0; x < 16; ++x) last = max(last, wtot[x]);
+    __syncthreads();
+    carry = last;
+  }
+}
+
+// Per-token run from cumulative sequence lengths (THD layout, one row):
+// [cu[s], cu[s+1]) for the sequence s holding the token; tokens before cu[0]
+// form one run [0, cu[0]) and tokens at or past cu[nseq] one run
+// [cu[nseq], T), so that the runs stay consistent for such inputs too
+// (cu non-decreasing is required; the binary search assumes it).
 __global__ __launch_bounds__(256) void seg_from_cu_kernel(const int* cu, int nseq, int* seg_lo, int* seg_hi, int T) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
@@ -60,9 +101,19 @@ __global__ __launch_bounds__(256) void seg_from_cu_kernel(const int* cu, int nse
     const int mid = (lo + hi) >> 1;
     if (cu[mid] <= t) lo = mid + 1; else hi = mid;
   }
-  const int s = max(lo - 1, 0);
-  seg_lo[t] = max(min(cu[s], t), 0);
-  seg_hi[t] = max(min(cu[min(s + 1, nseq)], T), t + 1);
+  int a, e;
+  if (lo == 0) {
+    a = 0;
+    e = cu[0];
+  } else if (lo > nseq) {
+    a = cu[nseq];
+    e = T;
+  } else {
+    a = cu[lo - 1];
+    e = cu[lo];
+  }
+  seg_lo[t] = max(min(a, t), 0);
+  seg_hi[t] = max(min(e, T), t + 1);
 }
 
 }  // namespace atl
@@ -88,6 +139,10 @@ bool has_segments(const attn_args* a) { return a->segment_ids != nullptr || a->c
 
 // The kernels move rows 16 bytes at a time (vector loads, LDS DMA).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool du_supported(const attn_args* a) {
+  return fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr);
+}
 
 attn_status validate(const attn_args* a) {
   if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
@@ -117,6 +172,11 @@ attn_status validate(const attn_args* a) {
   const long long maxi = 2147483647LL;
   if ((long long)a->B * a->Sq > maxi || (long long)a->B * a->Sk > maxi)
     return fail(ATTN_UNSUPPORTED, "B*S must fit in int32");
+  if (a->dq_mode != ATTN_DQ_AUTO && a->dq_mode != ATTN_DQ_DU_BLOCKS && a->dq_mode != ATTN_DQ_RECOMPUTE)
+    return fail(ATTN_INVALID_ARGUMENT, "dq_mode must be ATTN_DQ_AUTO, ATTN_DQ_DU_BLOCKS or ATTN_DQ_RECOMPUTE");
+  if (a->dq_mode == ATTN_DQ_DU_BLOCKS && !du_supported(a))
+    return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs bf16 with D = 64, 128 or 256 (and, with a bias, Sk % 8 == 0)");
+  if ((long long)a->B * a->Sq > 0 && a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
   const size_t elems = (size_t)a->B * (a->Sq + a->Sk);
   if (elems != 0 && (!a->q || !a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "q, k and v must not be NULL");
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->bias))
@@ -130,29 +190,20 @@ size_t pre_blocks(const attn_args* a) { return ((size_t)a->Sq + kPreRows - 1) / 
 
 size_t fwd_ws(const attn_args* a) { return seg_bytes(a); }
 
-// The bf16 kernels for head dims 64/128 hand dU from the dk/dv kernel to the
-// dq kernel through the workspace (bf16, 32-key x 32-query blocks), so that
-// dq needs neither exponentials nor a second pass over the logits; the
-// buffer holds every block of [B, Hq, Sq, Sk] and is used only while it
-// stays within a limit (else dq recomputes the probabilities): 16 GiB, or
-// the byte count in the environment variable ATTN_SOFTCAP_DU_MAX_BYTES.
-size_t du_max_bytes() {
-  const char* e = std::getenv("ATTN_SOFTCAP_DU_MAX_BYTES");
-  if (e && *e) {
-    char* end = nullptr;
-    const unsigned long long v = std::strtoull(e, &end, 10);
-    if (end && *end == '\0') return (size_t)v;
-  }
-  return (size_t)16 << 30;
-}
+// The bf16 kernels for head dims 64/128/256 can hand dU from the dk/dv
+// kernel to the dq kernel through the workspace (bf16, 32-key x 32-query
+// blocks), so that dq needs neither exponentials nor a second pass over the
+// logits.  The buffer holds every block of [B, Hq, Sq, Sk]; ATTN_DQ_AUTO
+// takes it while it stays within kDuAutoBytes, else dq recomputes.
+constexpr size_t kDuAutoBytes = (size_t)16 << 30;
 
 size_t du_raw_bytes(const attn_args* a) {
   return (size_t)a->B * a->Hq * (((size_t)a->Sk + 31) / 32) * (((size_t)a->Sq + 31) / 32) * 2048;
 }
 
 bool du_path(const attn_args* a) {
-  return fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr) &&
-         du_raw_bytes(a) <= du_max_bytes();
+  if (!du_supported(a) || a->dq_mode == ATTN_DQ_RECOMPUTE) return false;
+  return a->dq_mode == ATTN_DQ_DU_BLOCKS || du_raw_bytes(a) <= kDuAutoBytes;
 }
 
 // With a bias, the bf16 dk/dv kernel of D = 128 and 256 writes the whole of
@@ -203,8 +254,7 @@ hipError_t prep_segments(const attn_args* a, char*& ws, Mask& m, hipStream_t s) 
   int* hi = reinterpret_cast<int*>(ws);
   ws += align_up(n * sizeof(int));
   if (a->segment_ids) {
-    const dim3 grid((a->Sq + 255) / 256, a->B);
-    seg_from_ids_kernel<<<grid, 256, 0, s>>>(a->segment_ids, lo, hi, a->Sq);
+    seg_from_ids_kernel<<<a->B, 1024, 0, s>>>(a->segment_ids, lo, hi, a->Sq);
   } else {
     seg_from_cu_kernel<<<(a->Sq + 255) / 256, 256, 0, s>>>(a->cu_seqlens, a->nseq, lo, hi, a->Sq);
   }
@@ -260,8 +310,8 @@ size_t attn_bwd_workspace_size(const attn_args* a) {
 
 const char* attn_last_error(void) { return g_err.c_str(); }
 
-attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   g_err.clear();
   attn_status st = validate(a);
   if (st != ATTN_OK) return st;
@@ -270,8 +320,8 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* workspace,
     return fail(ATTN_INVALID_ARGUMENT, "workspace smaller than attn_fwd_workspace_size");
   if ((size_t)a->B * a->Sq * a->Hq == 0) return ATTN_OK;
   if (!out || !lse) return fail(ATTN_INVALID_ARGUMENT, "out and lse must not be NULL");
-  if (!aligned16(out)) return fail(ATTN_INVALID_ARGUMENT, "out must be 16-byte aligned");
-  if (a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
+  if (!aligned16(out) || !aligned16(out_lo)) return fail(ATTN_INVALID_ARGUMENT, "out and out_lo must be 16-byte aligned");
+  if (out_lo && a->dtype != ATTN_BF16) return fail(ATTN_INVALID_ARGUMENT, "out_lo is for bf16 outputs only");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   FwdParams p;
@@ -281,6 +331,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* workspace,
   p.bias = a->bias;
   p.out = out;
   p.lse = lse;
+  p.out_lo = out_lo;
   p.mask = base_mask(a);
   hipError_t e = prep_segments(a, ws, p.mask, s);
   if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
@@ -303,7 +354,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* workspace,
 // dq and dk/dv kernels.
 enum { kPhasePre = 1, kPhaseDq = 2, kPhaseDkdv = 4 };
 
-static attn_status bwd_impl(const attn_args* a, const void* out, const float* lse, const void* dout, void* dq,
+static attn_status bwd_impl(const attn_args* a, const void* out, const void* out_lo, const float* lse, const void* dout, void* dq,
                             void* dk, void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes,
                             void* stream, int phases) {
   g_err.clear();
@@ -324,8 +375,10 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
   if ((phases & kPhasePre) && !out) return fail(ATTN_INVALID_ARGUMENT, "out must not be NULL");
   if ((phases & kPhaseDq) && !dq) return fail(ATTN_INVALID_ARGUMENT, "dq must not be NULL");
   if ((phases & kPhaseDkdv) && (!dk || !dv)) return fail(ATTN_INVALID_ARGUMENT, "dk and dv must not be NULL");
-  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbias))
-    return fail(ATTN_INVALID_ARGUMENT, "out, dout, dq, dk, dv and dbias must be 16-byte aligned");
+  if (!aligned16(out) || !aligned16(out_lo) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(dbias))
+    return fail(ATTN_INVALID_ARGUMENT, "out, out_lo, dout, dq, dk, dv and dbias must be 16-byte aligned");
+  if (out_lo && a->dtype != ATTN_BF16) return fail(ATTN_INVALID_ARGUMENT, "out_lo is for bf16 outputs only");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   BwdParams p;
@@ -377,7 +430,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
   const bool cap = a->softcap > 0.0f, bias = a->bias != nullptr;
   if (phases & kPhasePre) {
     if (a->Sq > 0) {
-      e = o.pre(a->D, out, dout, lse, delta, part, a->sink, a->sink_mode, a->Hq, kPreRows, l);
+      e = o.pre(a->D, out, out_lo, dout, lse, delta, part, a->sink, a->sink_mode, a->Hq, kPreRows, l);
       if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
     }
     if (part) {
@@ -402,28 +455,30 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const float* ls
   return ATTN_OK;
 }
 
-attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, const void* dout, void* dq, void* dk,
-                     void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(a, out, lse, dout, dq, dk, dv, dbias, dsink, workspace, workspace_bytes, stream,
+attn_status attn_bwd(const attn_args* a, const void* out, const void* out_lo, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return bwd_impl(a, out, out_lo, lse, dout, dq, dk, dv, dbias, dsink, workspace, workspace_bytes, stream,
                   kPhasePre | kPhaseDq | kPhaseDkdv);
 }
 
-attn_status attn_bwd_pre(const attn_args* a, const void* out, const float* lse, const void* dout, void* dbias,
-                         float* dsink, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(a, out, lse, dout, nullptr, nullptr, nullptr, dbias, dsink, workspace, workspace_bytes, stream,
-                  kPhasePre);
+attn_status attn_bwd_pre(const attn_args* a, const void* out, const void* out_lo, const float* lse,
+                         const void* dout, void* dbias, float* dsink, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return bwd_impl(a, out, out_lo, lse, dout, nullptr, nullptr, nullptr, dbias, dsink, workspace, workspace_bytes,
+                  stream, kPhasePre);
 }
 
 attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, void* dq, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return bwd_impl(a, nullptr, lse, dout, dq, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
-                  kPhaseDq);
+  return bwd_impl(a, nullptr, nullptr, lse, dout, dq, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                  stream, kPhaseDq);
 }
 
 attn_status attn_bwd_dkdv(const attn_args* a, const float* lse, const void* dout, void* dk, void* dv, void* dbias,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(a, nullptr, lse, dout, nullptr, dk, dv, dbias, nullptr, workspace, workspace_bytes, stream,
-                  kPhaseDkdv);
+  return bwd_impl(a, nullptr, nullptr, lse, dout, nullptr, dk, dv, dbias, nullptr, workspace, workspace_bytes,
+                  stream, kPhaseDkdv);
 }
 
 }  // extern "C"

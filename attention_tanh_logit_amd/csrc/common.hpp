@@ -112,6 +112,15 @@ template <> __device__ __forceinline__ void store8<float>(float* p, const float*
   reinterpret_cast<f32x4*>(p)[1] = b;
 }
 
+// The part of 8 fp32 values that their bf16 rounding drops, v - bf16(v),
+// itself rounded to bf16 (together the two carry v to about 16 bits)
+__device__ __forceinline__ void store8_lo(bf16* p, const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)(v[i] - (float)(bf16)v[i]);
+  *reinterpret_cast<bf16x8*>(p) = r;
+}
+
 // 8 consecutive values from global memory into fp32 (16-byte aligned for bf16,
 // 32-byte for fp32)
 __device__ __forceinline__ void load8(const bf16* p, float* v) {

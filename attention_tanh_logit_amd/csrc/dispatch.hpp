@@ -166,10 +166,10 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
 }
 
 template <typename T, int D>
-hipError_t launch_pre(const T* out, const T* dout, const float* lse, float* delta, float* dsink_part,
+hipError_t launch_pre(const T* out, const T* out_lo, const T* dout, const float* lse, float* delta, float* dsink_part,
                       const float* sink, int sink_mode, int Hq, int rows_per_block, const Launch& l) {
   const dim3 grid((l.Sq + rows_per_block - 1) / rows_per_block, Hq, l.B);
-  bwd_pre_kernel<T, D><<<grid, 256, 0, l.stream>>>(out, dout, lse, delta, dsink_part, sink, sink_mode, l.Sq, Hq,
+  bwd_pre_kernel<T, D><<<grid, 256, 0, l.stream>>>(out, out_lo, dout, lse, delta, dsink_part, sink, sink_mode, l.Sq, Hq,
                                                    rows_per_block);
   return hipGetLastError();
 }
@@ -179,7 +179,8 @@ struct TypeOps {
   hipError_t (*fwd)(int D, bool cap, bool bias, const FwdParams&, const Launch&);
   hipError_t (*dq)(int D, bool cap, bool bias, const BwdParams&, const Launch&);
   hipError_t (*dkdv)(int D, bool cap, bool bias, const BwdParams&, const Launch&);
-  hipError_t (*pre)(int D, const void* out, const void* dout, const float* lse, float* delta, float* dsink_part,
+  hipError_t (*pre)(int D, const void* out, const void* out_lo, const void* dout, const float* lse, float* delta,
+                    float* dsink_part,
                     const float* sink, int sink_mode, int Hq, int rows_per_block, const Launch&);
   hipError_t (*dbias_fill)(void* dbias, const Mask&, int Hq, int rows_per_block, const Launch&);
 };
@@ -235,15 +236,17 @@ const TypeOps& ops_f32();
     }                                                                                                       \
     return hipErrorInvalidValue;                                                                            \
   }                                                                                                         \
-  hipError_t pre_any(int D, const void* out, const void* dout, const float* lse, float* delta,              \
-                     float* part, const float* sink, int sink_mode, int Hq, int rpb, const Launch& l) {     \
+  hipError_t pre_any(int D, const void* out, const void* out_lo, const void* dout, const float* lse,        \
+                     float* delta, float* part, const float* sink, int sink_mode, int Hq, int rpb,          \
+                     const Launch& l) {                                                                     \
     const T* o = static_cast<const T*>(out);                                                                \
+    const T* lo = static_cast<const T*>(out_lo);                                                            \
     const T* g = static_cast<const T*>(dout);                                                               \
     switch (D) {                                                                                            \
-      case 64: return launch_pre<T, 64>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);               \
-      case 128: return launch_pre<T, 128>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
-      case 256: return launch_pre<T, 256>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
-      case 512: return launch_pre<T, 512>(o, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
+      case 64: return launch_pre<T, 64>(o, lo, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);               \
+      case 128: return launch_pre<T, 128>(o, lo, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
+      case 256: return launch_pre<T, 256>(o, lo, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
+      case 512: return launch_pre<T, 512>(o, lo, g, lse, delta, part, sink, sink_mode, Hq, rpb, l);             \
     }                                                                                                       \
     return hipErrorInvalidValue;                                                                            \
   }                                                                                                         \

@@ -591,6 +591,7 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
   const float inv = ltot > 0.0f ? oscale / ltot : 0.0f;
   if (i < Sq) {
     bf16* orow = reinterpret_cast<bf16*>(p.out) + (((long)b * Sq + i) * p.Hq + hq) * D;
+    bf16* lorow = reinterpret_cast<bf16*>(p.out_lo) + (((long)b * Sq + i) * p.Hq + hq) * D;
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
@@ -599,6 +600,7 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
 #pragma unroll
         for (int e = 0; e < 8; ++e) vals[e] = oacc[ob][8 * hf + e] * inv;
         store8<bf16>(orow + colofs + ob * 32 + 16 * hf + 8 * h, vals);
+        if (p.out_lo) store8_lo(lorow + colofs + ob * 32 + 16 * hf + 8 * h, vals);
       }
     }
     if (h == 0 && sl == 0) p.lse[((long)b * p.Hq + hq) * Sq + i] = ltot > 0.0f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;

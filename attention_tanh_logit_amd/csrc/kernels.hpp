@@ -38,6 +38,10 @@ struct FwdParams {
   const void* bias;
   void* out;
   float* lse;
+  // bf16 only, nullable: out_lo = bf16(O - bf16(O)) of the fp32 output O, so
+  // that out + out_lo carries O to about 16 bits and the backward's
+  // delta = <dO, O> does not inherit the rounding of out
+  void* out_lo;
   Mask mask;
   int Hq, Hkv, G;
   float sl2;    // scale * log2(e)            (no cap)
@@ -391,6 +395,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if (i < Sq) {
     T* orow = reinterpret_cast<T*>(p.out) + (((long)b * Sq + i) * p.Hq + hq) * D;
+    T* lorow = reinterpret_cast<T*>(p.out_lo) + (((long)b * Sq + i) * p.Hq + hq) * D;
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
@@ -399,6 +404,9 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vals[e] = oacc[ob][8 * hf + e] * inv;
         store8<T>(orow + sl * DO + ob * 32 + 16 * hf + 8 * h, vals);
+        if constexpr (sizeof(T) == 2) {
+          if (p.out_lo) store8_lo(lorow + sl * DO + ob * 32 + 16 * hf + 8 * h, vals);
+        }
       }
     }
     if (sl == 0 && h == 0) {
@@ -993,7 +1001,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
 // delta_i = <dO_i, O_i> per row; per-block partial sums of the sink gradient
 // -sum_i exp(sigma - lse_i) delta_i (summed in a fixed order afterwards).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* out, const T* dout, const float* lse, float* delta,
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* out, const T* out_lo, const T* dout, const float* lse, float* delta,
                                                       float* dsink_part, const float* sink, int sink_mode, int Sq,
                                                       int Hq, int rows_per_block) {
   constexpr int LPR = D / 8;            // lanes per row, 8 elements each
@@ -1014,6 +1022,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* out, const T* dou
       float a[8], c[8];
       load8(out + off, a);
       load8(dout + off, c);
+      if (out_lo) {
+        float lo[8];
+        load8(out_lo + off, lo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(lo[e], c[e], s);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) s = fmaf(a[e], c[e], s);
     }

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sof
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_HIP_ERROR = 0, 1, 2, 3
 ATTN_BF16, ATTN_FP32 = 0, 1
 SINK_MODES = {"none": 0, "off_by_one": 1, "learnable": 2}
+DQ_MODES = {"auto": 0, "du_blocks": 1, "recompute": 2}
 
 
 class AttnArgs(ctypes.Structure):
@@ -35,6 +36,7 @@ class AttnArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("sink_mode", ctypes.c_int),
         ("sink", ctypes.c_void_p),
+        ("dq_mode", ctypes.c_int),
     ]
 
 
@@ -66,11 +68,11 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_workspace_size.restype = sz
     L.attn_bwd_workspace_size.argtypes = [P]
     L.attn_bwd_workspace_size.restype = sz
-    L.attn_fwd.argtypes = [P, vp, vp, vp, sz, vp]
+    L.attn_fwd.argtypes = [P, vp, vp, vp, vp, sz, vp]
     L.attn_fwd.restype = ctypes.c_int
-    L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd.restype = ctypes.c_int
-    L.attn_bwd_pre.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd_pre.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd_pre.restype = ctypes.c_int
     L.attn_bwd_dq.argtypes = [P, vp, vp, vp, vp, sz, vp]
     L.attn_bwd_dq.restype = ctypes.c_int
@@ -92,19 +94,32 @@ def _check(status: int) -> None:
 
 
 def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
-              softcap=0.0, scale=0.0, sink_mode="none", sink=None) -> AttnArgs:
-    """Fill the C argument struct from tensors (BSHD, or THD with cu_seqlens)."""
+              softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto") -> AttnArgs:
+    """Fill the C argument struct from tensors (BSHD, or THD with cu_seqlens).
+
+    The C ABI sees only pointers and sizes, so every shape, dtype and device
+    check the kernels rely on happens here: k and v must match q's batch and
+    head dim, every tensor must be contiguous and on q's device, and that
+    device must be a GPU.  Violations raise ValueError / TypeError before
+    anything reaches the library.
+    """
     thd = cu_seqlens is not None
     if thd:
-        if q.dim() != 3:
+        if q.dim() != 3 or k.dim() != 3:
             raise ValueError("THD layout: q, k, v must be [T, H, D]")
         B, Sq, Hq, D = 1, q.shape[0], q.shape[1], q.shape[2]
         Sk, Hkv = k.shape[0], k.shape[1]
     else:
-        if q.dim() != 4:
+        if q.dim() != 4 or k.dim() != 4:
             raise ValueError("BSHD layout: q, k, v must be [B, S, H, D]")
         B, Sq, Hq, D = q.shape
         Sk, Hkv = k.shape[1], k.shape[2]
+        if k.shape[0] != B:
+            raise ValueError(f"k has batch {k.shape[0]}, q has {B}")
+    if k.shape[-1] != D:
+        raise ValueError(f"k has head dim {k.shape[-1]}, q has {D}")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
     if q.dtype == torch.bfloat16:
         dt = ATTN_BF16
     elif q.dtype == torch.float32:
@@ -114,12 +129,11 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
     for name, t in (("k", k), ("v", v), ("bias", bias)):
         if t is not None and t.dtype != q.dtype:
             raise TypeError(f"{name} must have q's dtype")
-    for name, t in (("q", q), ("k", k), ("v", v), ("bias", bias), ("segment_ids", segment_ids),
-                    ("cu_seqlens", cu_seqlens), ("sink", sink)):
+    tensors = (("q", q), ("k", k), ("v", v), ("bias", bias), ("segment_ids", segment_ids),
+               ("cu_seqlens", cu_seqlens), ("sink", sink))
+    for name, t in tensors:
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape")
     if bias is not None and tuple(bias.shape) != (B, Hq, Sq, Sk):
         raise ValueError(f"bias must be [B, Hq, Sq, Sk] = {(B, Hq, Sq, Sk)}")
     if segment_ids is not None and (segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) != (B, Sq)):
@@ -128,6 +142,15 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
         raise ValueError("cu_seqlens must be int32 [nseq + 1]")
     if sink is not None and (sink.dtype != torch.float32 or tuple(sink.shape) != (Hq,)):
         raise ValueError("sink must be float32 [Hq]")
+    for name, t in tensors[1:]:
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}: every tensor must be on q's device")
+    if sink_mode not in SINK_MODES:
+        raise ValueError(f"sink_mode must be one of {sorted(SINK_MODES)}")
+    if dq_mode not in DQ_MODES:
+        raise ValueError(f"dq_mode must be one of {sorted(DQ_MODES)}")
+    if q.device.type != "cuda":
+        raise ValueError(f"q is on {q.device}: the library takes GPU tensors only")
     a = AttnArgs()
     a.dtype = dt
     a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.D = B, Sq, Sk, Hq, Hkv, D
@@ -142,7 +165,14 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
     a.scale = float(scale)
     a.sink_mode = SINK_MODES[sink_mode]
     a.sink = _ptr(sink)
+    a.dq_mode = DQ_MODES[dq_mode]
     return a
+
+
+def _like(name, t, like):
+    if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous with the shape, dtype and device of {like.shape} {like.dtype}")
+    return t
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -156,31 +186,41 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0, softcap=0.0,
-             scale=0.0, sink_mode="none", sink=None, out=None, lse=None):
-    """Forward: returns (out, lse); lse is float32 [B, Hq, Sq] ([Hq, T] for THD)."""
+             scale=0.0, sink_mode="none", sink=None, out=None, lse=None, out_lo=None, residual=True):
+    """Forward: returns (out, lse, out_lo); lse is float32 [B, Hq, Sq] ([Hq, T] for THD).
+
+    out_lo (bf16 only; None for fp32 or with ``residual=False``) is the part
+    of the fp32 output that the bf16 ``out`` drops; hand it to
+    :func:`attn_bwd` so that delta = <dO, O> is taken from the fp32 output.
+    """
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink)
     _check(L.attn_validate(ctypes.byref(a)))
     shape = (a.Hq, a.Sq) if cu_seqlens is not None else (a.B, a.Hq, a.Sq)
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
-        raise ValueError("out must be contiguous with the shape, dtype and device of q")
+    out = torch.empty_like(q) if out is None else _like("out", out, q)
     if lse is None:
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     elif tuple(lse.shape) != shape or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
         raise ValueError(f"lse must be contiguous float32 {list(shape)}")
+    if a.dtype == ATTN_BF16 and (residual or out_lo is not None):
+        out_lo = torch.empty_like(q) if out_lo is None else _like("out_lo", out_lo, q)
+    elif out_lo is not None:
+        raise ValueError("out_lo is for bf16 outputs only")
     nws = L.attn_fwd_workspace_size(ctypes.byref(a))
     ws = _workspace(nws, q.device)
-    _check(L.attn_fwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(q)))
-    return out, lse
+    _check(L.attn_fwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(out_lo), _ptr(ws), nws, _stream(q)))
+    return out, lse, out_lo
 
 
-def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
-             softcap=0.0, scale=0.0, sink_mode="none", sink=None, want_dbias=None, events=None, outputs=None):
+def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None, causal=False,
+             window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", want_dbias=None,
+             events=None, outputs=None):
     """Backward: returns (dq, dk, dv, dbias or None, dsink or None).
 
+    ``out_lo`` is what :func:`attn_fwd` returned beside ``out`` (bf16; None
+    takes delta from ``out`` alone).  ``dq_mode`` picks how dq is formed:
+    "auto", "du_blocks" or "recompute" (see ``attn_dq_mode`` in the header).
     With ``events`` (four torch.cuda.Event) the three phases are launched
     through their own entry points (pre-pass, dk/dv, dq, in that order) with
     an event recorded before the pre-pass and after each phase, on the
@@ -190,13 +230,15 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
     """
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
-                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink)
+                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode)
     _check(L.attn_validate(ctypes.byref(a)))
-    for name, t in (("out", out), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must match q (shape, dtype, contiguous)")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != a.B * a.Hq * a.Sq:
-        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    _like("out", out, q)
+    _like("dout", dout, q)
+    if out_lo is not None:
+        _like("out_lo", out_lo, q)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != a.B * a.Hq * a.Sq \
+            or lse.device != q.device:
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq] on q's device")
     want_dbias = (bias is not None) if want_dbias is None else want_dbias
     given = outputs or {}
     unknown = set(given) - {"dq", "dk", "dv", "dbias"}
@@ -205,11 +247,7 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
 
     def result(name, like):
         t = given.get(name)
-        if t is None:
-            return torch.empty_like(like)
-        if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
-            raise ValueError(f"outputs[{name!r}] must be contiguous with the shape, dtype and device of its input")
-        return t
+        return torch.empty_like(like) if t is None else _like(f"outputs[{name!r}]", t, like)
 
     dq = result("dq", q)
     dk = result("dk", k)
@@ -220,12 +258,12 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
     ws = _workspace(nws, q.device)
     st = _stream(q)
     if events is None:
-        _check(L.attn_bwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                          _ptr(dbias), _ptr(dsink), _ptr(ws), nws, st))
+        _check(L.attn_bwd(ctypes.byref(a), _ptr(out), _ptr(out_lo), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(dbias), _ptr(dsink), _ptr(ws), nws, st))
     else:
         events[0].record()
-        _check(L.attn_bwd_pre(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dbias), _ptr(dsink),
-                              _ptr(ws), nws, st))
+        _check(L.attn_bwd_pre(ctypes.byref(a), _ptr(out), _ptr(out_lo), _ptr(lse), _ptr(dout), _ptr(dbias),
+                              _ptr(dsink), _ptr(ws), nws, st))
         events[1].record()
         _check(L.attn_bwd_dkdv(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv), _ptr(dbias),
                                _ptr(ws), nws, st))
@@ -233,3 +271,10 @@ def attn_bwd(q, k, v, out, lse, dout, *, bias=None, segment_ids=None, cu_seqlens
         _check(L.attn_bwd_dq(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(ws), nws, st))
         events[3].record()
     return dq, dk, dv, dbias, dsink
+
+
+def bwd_workspace_bytes(q, k, v, **kw) -> int:
+    """attn_bwd_workspace_size for these tensors and options (the bench reports it)."""
+    a = make_args(q, k, v, **kw)
+    _check(lib().attn_validate(ctypes.byref(a)))
+    return int(lib().attn_bwd_workspace_size(ctypes.byref(a)))

@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 CLOCK_PEAK_BF16 = 256 * 4096 * 2.4e9 / 1e12   # 256 CUs x 4096 flop/clk x 2.4 GHz
 
 
@@ -138,17 +139,17 @@ def run_steps(g, kw, steps, warmup):
     import torch
     import attention_tanh_logit_amd as A
     for _ in range(warmup):
-        out, lse = A.attn_fwd(g["q"], g["k"], g["v"], **kw)
-        A.attn_bwd(g["q"], g["k"], g["v"], out, lse, g["dout"], **kw)
+        out, lse, lo = A.attn_fwd(g["q"], g["k"], g["v"], **_fwd_kw(kw))
+        A.attn_bwd(g["q"], g["k"], g["v"], out, lse, g["dout"], out_lo=lo, **kw)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         e = ev[s]
         e[0].record()
-        out, lse = A.attn_fwd(g["q"], g["k"], g["v"], **kw)
+        out, lse, lo = A.attn_fwd(g["q"], g["k"], g["v"], **_fwd_kw(kw))
         e[1].record()
-        A.attn_bwd(g["q"], g["k"], g["v"], out, lse, g["dout"], events=e[2:6], **kw)
+        A.attn_bwd(g["q"], g["k"], g["v"], out, lse, g["dout"], out_lo=lo, events=e[2:6], **kw)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ph = {"fwd": 0.0, "bwd_pre": 0.0, "dq": 0.0, "dkdv": 0.0}
@@ -158,6 +159,22 @@ def run_steps(g, kw, steps, warmup):
         ph["dkdv"] += e[3].elapsed_time(e[4])
         ph["dq"] += e[4].elapsed_time(e[5])
     return wall * 1e3 / steps, {k: v / steps for k, v in ph.items()}
+
+
+def _fwd_kw(kw):
+    return {k: v for k, v in kw.items() if k != "dq_mode"}
+
+
+def dkdv_algorithmic_bytes(w, pairs) -> float:
+    """HBM bytes the dk/dv kernel must move at least: Q, dO, K, V read once, dK, dV
+    written once, lse and delta read once; with a bias its visible entries read once
+    and the dense dbias written once (the workspace hand-off to dq is not counted)."""
+    e = 2 if w.dtype == "bf16" else 4
+    tok = w.B * w.S
+    b = e * tok * w.D * (2 * w.Hq + 4 * w.Hkv) + 8 * tok * w.Hq
+    if w.bias_std > 0:
+        b += e * pairs + e * w.B * w.Hq * w.S * w.S
+    return float(b)
 
 
 def cpu_baseline(w, d, budget_s=30.0):
@@ -200,6 +217,7 @@ def main():
     ap.add_argument("--workload", default="causal_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cap-ratio", action="store_true")
+    ap.add_argument("--no-dq-modes", action="store_true", help="skip the dq_mode=recompute timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain copy of this many MiB first (to scale HBM counters)")
     args = ap.parse_args()
@@ -223,21 +241,31 @@ def main():
     flop_fwd = 4.0 * w.D * pairs
     flop_bwd = 10.0 * w.D * pairs
     flop_step = flop_fwd + flop_bwd
-    # the dq kernel recomputes S and dP (6*D per pair) unless the dk/dv kernel
-    # hands it dU through the workspace (bf16, D = 64/128): then only dQ = dU K
-    du_bytes = w.B * w.Hq * (-(-w.S // 32)) ** 2 * 2048
-    du_limit = int(os.environ.get("ATTN_SOFTCAP_DU_MAX_BYTES", 16 << 30) or 0)
-    du_path = w.dtype == "bf16" and w.D in (64, 128, 256) and du_bytes <= du_limit
+    # dq_mode "auto" takes the dU hand-off (bf16, D = 64/128/256, blocks within 16 GiB):
+    # the dq kernel then does only dQ = dU K (2*D per pair); "recompute" redoes S and
+    # dP there (6*D per pair; the extra 4*D earn nothing in the step figure)
+    ws_auto = A.ops.bwd_workspace_bytes(g["q"], g["k"], g["v"], **kw)
+    ws_rec = A.ops.bwd_workspace_bytes(g["q"], g["k"], g["v"], **dict(kw, dq_mode="recompute"))
+    du_path = ws_auto != ws_rec
     per_kernel_flop = {"fwd": 4.0 * w.D * pairs, "dq": (2.0 if du_path else 6.0) * w.D * pairs,
                        "dkdv": 8.0 * w.D * pairs}
 
-    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup (dq_mode auto, "
+        f"{'dU hand-off' if du_path else 'recompute'}, workspace {ws_auto / 2**30:.2f} GiB)")
     ms, ph = run_steps(g, kw, args.steps, args.warmup)
     log(f"[bench] {ms:.3f} ms/step  phases {ph}")
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     value = flop_step / (ms * 1e-3) / 1e12
     fwd_tflops = flop_fwd / (ph["fwd"] * 1e-3) / 1e12
     bwd_ms = ph["bwd_pre"] + ph["dq"] + ph["dkdv"]
+
+    dq_modes = {"auto": {"path": "du_blocks" if du_path else "recompute", "ms_per_step": ms,
+                         "kernel_ms": ph, "bwd_workspace_bytes": ws_auto}}
+    if du_path and not args.no_dq_modes:
+        ms_r, ph_r = run_steps(g, dict(kw, dq_mode="recompute"), args.steps, 1)
+        dq_modes["recompute"] = {"path": "recompute", "ms_per_step": ms_r, "kernel_ms": ph_r,
+                                 "bwd_workspace_bytes": ws_rec, "tflops": flop_step / (ms_r * 1e-3) / 1e12}
+        log(f"[bench] dq_mode recompute: {ms_r:.3f} ms/step, workspace {ws_rec / 2**30:.3f} GiB, phases {ph_r}")
 
     cap_ratio = None
     if not args.no_cap_ratio and w.softcap > 0:
@@ -252,10 +280,19 @@ def main():
     dom = max(("fwd", "dq", "dkdv"), key=lambda k: ph[k])
     achieved = per_kernel_flop[dom] / (ph[dom] * 1e-3) / 1e12
     traffic, traffic_src = measured_traffic(args.workload, dom)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": traffic, "traffic_source": traffic_src,
-                "traffic_gbps": None if traffic is None else traffic / (ph[dom] * 1e-3) / 1e9,
-                "flop_per_launch": per_kernel_flop[dom], "avg_launch_ms": ph[dom]}
+    mfma = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "flop_per_launch": per_kernel_flop[dom]}
+    if w.bias_std > 0 and dom == "dkdv":
+        # the dense dbias write makes the dk/dv kernel HBM-bound on the packed workload
+        nbytes = dkdv_algorithmic_bytes(w, pairs)
+        gbps = nbytes / (ph[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": gbps / PEAK_HBM_GBPS, "bytes_per_launch": nbytes, "mfma": mfma}
+    else:
+        roofline = dict(mfma)
+    roofline.update({"traffic": traffic, "traffic_source": traffic_src,
+                     "traffic_gbps": None if traffic is None else traffic / (ph[dom] * 1e-3) / 1e9,
+                     "avg_launch_ms": ph[dom]})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -274,7 +311,7 @@ def main():
         "frac_of_peak": value / peak,
         "fwd_tflops": fwd_tflops, "fwd_frac_of_peak": fwd_tflops / peak,
         "bwd_tflops": flop_bwd / (bwd_ms * 1e-3) / 1e12,
-        "kernel_ms": ph, "cap_ratio": cap_ratio,
+        "kernel_ms": ph, "cap_ratio": cap_ratio, "dq_modes": dq_modes,
         "peak_tflops": peak, "peak_tflops_from_clock": CLOCK_PEAK_BF16 if w.dtype == "bf16" else None,
         "algorithmic_flop_per_step": flop_step, "visible_pairs": pairs,
         "roofline": roofline, "cpu_baseline": cpu,

@@ -38,8 +38,10 @@
  *  - bias, dbias      : [B, Hq, Sq, Sk], same dtype as q.
  *  - lse              : [B, Hq, Sq] float32, natural log, sink included.
  *  - segment_ids      : [B, Sq] int32, non-decreasing along each row (packed
- *                       rows); a key is visible only inside its own run.
- *  - cu_seqlens       : [nseq + 1] int32, cu[0] = 0, non-decreasing, cu[nseq] = T.
+ *                       rows); a key is visible only inside its own run of
+ *                       equal adjacent ids (for non-decreasing ids: equal id).
+ *  - cu_seqlens       : [nseq + 1] int32, cu[0] = 0, non-decreasing, cu[nseq] = T
+ *                       (tokens outside [cu[0], cu[nseq]) form one run each side).
  *  - sink / dsink     : [Hq] float32.
  *
  * Ownership: the caller allocates every buffer (device memory unless noted)
@@ -72,95 +74,140 @@ typedef enum attn_status {
 
 typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype;
 
-/* Softmax sink ("softmax_type"): none (vanilla), off-by-one (a sink column
- * with its logit fixed at 0 and no gradient), learnable (logit sink[h], with
- * gradient dsink[h]). */
+/* Softmax sink ("softmax_type" on the learnable-sink page, "What changed"):
+ * none (vanilla), off-by-one (a sink column with its logit fixed at 0 and no
+ * gradient), learnable (logit sink[h], with gradient dsink[h]). */
 typedef enum attn_sink_mode {
   ATTN_SINK_NONE = 0,
   ATTN_SINK_OFF_BY_ONE = 1,
   ATTN_SINK_LEARNABLE = 2
 } attn_sink_mode;
 
-/* Every tensor pointer (q, k, v, bias, out, dout, dq, dk, dv, dbias) must be
- * 16-byte aligned: the kernels move rows 16 bytes at a time.  A misaligned
- * pointer is rejected with ATTN_INVALID_ARGUMENT before anything is launched. */
+/* How the backward forms dq (the same result either way, to rounding).
+ *  - ATTN_DQ_DU_BLOCKS: the dk/dv kernel hands dU = dS * (1 - tanh^2) to the
+ *    dq kernel through the workspace as bf16 blocks of 32 keys x 32 queries,
+ *    B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB (4 GiB at B=4, Hq=32, S=4096; only
+ *    the visible blocks are written and read).  bf16 with D = 64, 128 or 256
+ *    only (with a bias also Sk % 8 == 0); ATTN_UNSUPPORTED otherwise.
+ *  - ATTN_DQ_RECOMPUTE: the dq kernel recomputes the logits, probabilities
+ *    and dP itself; the workspace stays O(B*Hq*Sq).
+ *  - ATTN_DQ_AUTO (0): DU_BLOCKS where supported and its buffer is at most
+ *    16 GiB, else RECOMPUTE.
+ * The [b, h, q, kv] materialisation and its memory cost are what the MaxText
+ * commit quoted on "Support logits soft-capping in the Pallas-Triton
+ * attention VJP" weighs (12.5 against 3.3 GiB at 8k tokens); the blocks here
+ * are bf16 and touched only where visible. */
+typedef enum attn_dq_mode {
+  ATTN_DQ_AUTO = 0,
+  ATTN_DQ_DU_BLOCKS = 1,
+  ATTN_DQ_RECOMPUTE = 2
+} attn_dq_mode;
+
+/* The problem description shared by every entry point.
+ * Every tensor pointer (q, k, v, bias, out, out_lo, dout, dq, dk, dv, dbias)
+ * must be 16-byte aligned: the kernels move rows 16 bytes at a time.  A
+ * misaligned pointer is rejected with ATTN_INVALID_ARGUMENT before anything is
+ * launched.  A zero-initialised struct plus the sizes and q/k/v is a valid
+ * plain attention problem (no cap, no sink, no mask, scale 1/sqrt(D)). */
 typedef struct attn_args {
   int dtype;                   /* attn_dtype of q, k, v, bias, out, dout, dq, dk, dv, dbias */
-  int B, Sq, Sk, Hq, Hkv, D;   /* D in {64, 128, 256, 512}; Hq % Hkv == 0 */
+  int B, Sq, Sk, Hq, Hkv, D;   /* D in {64, 128, 256, 512}; Hq % Hkv == 0 (MaxText commit: native GQA/MQA;
+                                  head_dim above 256) */
   const void* q;
   const void* k;
   const void* v;
-  const void* bias;            /* nullable: additive bias after the scale, before the cap */
-  const int32_t* segment_ids;  /* nullable: packed rows (needs Sq == Sk) */
+  const void* bias;            /* nullable: additive bias after the scale, before the cap (tokamax PR
+                                  description; post_scale_bias in the learnable-sink page's review) */
+  const int32_t* segment_ids;  /* nullable: packed rows (needs Sq == Sk; MaxText commit: packing) */
   const int32_t* cu_seqlens;   /* nullable: THD varlen (needs B == 1, Sq == Sk); not with segment_ids */
   int nseq;                    /* number of sequences in cu_seqlens */
   int causal;                  /* nonzero: key j visible only for j <= i (needs Sq == Sk) */
-  int window;                  /* <= 0: none; else causal: 0 <= i-j < window, non-causal: |i-j| < window */
-  float softcap;               /* 0: off; > 0: s = softcap * tanh(u / softcap) */
+  int window;                  /* <= 0: none; else causal: 0 <= i-j < window, non-causal: |i-j| < window
+                                  (MaxText commit: sliding window) */
+  float softcap;               /* 0: off; > 0: s = softcap * tanh(u / softcap) (TE softcap page, intro and
+                                  "What changed": the softcap kwarg, 0 = off) */
   float scale;                 /* 0: 1/sqrt(D) */
   int sink_mode;               /* attn_sink_mode */
   const float* sink;           /* [Hq] sink logits; required iff sink_mode == ATTN_SINK_LEARNABLE */
+  int dq_mode;                 /* attn_dq_mode (backward only; the forward ignores it) */
 } attn_args;
 
 /* Host-only check of `a` (no device access, nothing launched).  Returns the
- * status attn_fwd would return for these arguments before launching. */
+ * status that attn_fwd and attn_bwd would return for `a` before looking at
+ * their own pointer arguments (output pointers, workspace).  Fail closed as
+ * on "Thread tanh logit softcapping through FlashAttention", "What changed":
+ * a requested cap, sink or mask is never dropped; an unsupported combination
+ * is ATTN_UNSUPPORTED, never a silent fallback. */
 attn_status attn_validate(const attn_args* a);
 
-/* Device workspace (bytes) that attn_fwd / attn_bwd need for `a`
- * (0 if none).  Returns (size_t)-1 if `a` is invalid.  For bf16 with D = 64
- * or 128 the backward workspace includes B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB
- * for dU (bf16) while that stays within 16 GiB (or within the byte count
- * in the environment variable ATTN_SOFTCAP_DU_MAX_BYTES), e.g. 4 GiB at
- * B=4, Hq=32, S=4096; beyond that dq recomputes the probabilities instead.
- * The choice is made again on every call: keep the variable unchanged
- * between attn_bwd_workspace_size and the backward calls it sizes.
- * For the same bf16 cases, when B*Hkv*ceil(Sk/128) < 1024 the dk/dv kernel
- * splits each GQA group's query heads over s workgroups (s the smallest
- * divisor of Hq/Hkv reaching 1024 workgroups, else the largest) and the
- * workspace also holds 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial dK/dV, summed
- * in a fixed order (the results stay deterministic). */
+/* Device workspace (bytes) that attn_fwd / attn_bwd need for `a` (0 if
+ * none); (size_t)-1 if `a` is invalid.  The size depends only on `a`:
+ *  - forward: two int32 [B*Sq] arrays of segment runs, only with
+ *    segment_ids or cu_seqlens;
+ *  - backward: the same runs, delta [B*Hq*Sq] fp32, sink-gradient partials
+ *    with a learnable sink, the dU blocks when dq_mode resolves to
+ *    ATTN_DQ_DU_BLOCKS (see attn_dq_mode), and for bf16 with D = 64, 128 or
+ *    256 when B*Hkv*ceil(Sk/128) < 1024, 2*s*B*Sk*Hkv*D*4 bytes of fp32
+ *    partial dK/dV: the dk/dv kernel then splits each GQA group's query
+ *    heads over s workgroups (s the smallest divisor of Hq/Hkv reaching 1024
+ *    workgroups, else the largest), summed afterwards in a fixed order. */
 size_t attn_fwd_workspace_size(const attn_args* a);
 size_t attn_bwd_workspace_size(const attn_args* a);
 
-/* Forward.  Writes out [B,Sq,Hq,D] (dtype) and lse [B,Hq,Sq] (float32).
- * A query row that sees no key and has no sink gets out = 0, lse = -inf.
+/* Forward (tokamax PR description: cap after the bias add, before masking;
+ * learnable-sink page, "What changed": the sink column counted once per row,
+ * and the softmax statistics returned with the output).
+ * Writes out [B,Sq,Hq,D] (dtype) and lse [B,Hq,Sq] (float32, natural log,
+ * sink included).  A query row that sees no key and has no sink gets
+ * out = 0, lse = -inf; with a sink, out = 0 and lse = sigma.
+ * out_lo: nullable, bf16 only, [B,Sq,Hq,D] bf16: receives the part of the
+ * fp32 output that its rounding to `out` drops, out_lo = bf16(O - out).
+ * Passed on to the backward it makes delta = <dO, O> (and so dsink, which
+ * sums p_sink * delta over the query rows) exact to about 16 bits instead of
+ * inheriting out's 8; NULL keeps the bf16 `out` alone.  Must be NULL for fp32.
  * workspace: device buffer of at least attn_fwd_workspace_size(a) bytes,
  * 256-byte aligned (may be NULL when that size is 0); its contents on entry
  * do not matter. */
-attn_status attn_fwd(const attn_args* a, void* out, float* lse,
-                     void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
-/* Backward by recomputation, from the forward's out and lse and dout.
+/* Backward by recomputation, from the forward's out, out_lo and lse and
+ * dout (tokamax PR description: 1 - tanh(u/c)^2 chained into ds, taken before
+ * masking; dk and dbias are gradients with respect to the pre-cap logits;
+ * learnable-sink page, "What changed": the sink gradient is a sum over the
+ * query rows, -sum_i p_sink(i) delta(i)).
  * Writes dq, dk, dv (dk/dv per KV head: the GQA group sum is taken inside),
  * dbias (nullable; requires a->bias; written in full, exactly 0 where
  * masked) and dsink (required iff sink_mode == ATTN_SINK_LEARNABLE, else must
- * be NULL; summed over every batch row and query row).  Results are
- * deterministic (no floating-point atomics).
+ * be NULL; summed over every batch row and query row).  out_lo: nullable,
+ * what attn_fwd wrote there (bf16 only).  Results are deterministic (no
+ * floating-point atomics): the same inputs give the same bits.
  * workspace: at least attn_bwd_workspace_size(a) bytes, 256-byte aligned. */
-attn_status attn_bwd(const attn_args* a, const void* out, const float* lse, const void* dout,
-                     void* dq, void* dk, void* dv, void* dbias, float* dsink,
-                     void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_bwd(const attn_args* a, const void* out, const void* out_lo, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, void* dbias, float* dsink, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* The same backward in three phases, for callers that time them
  * (attn_bwd == pre, then dkdv, then dq).  All three take the same arguments
  * and the same workspace, which carries the pre-pass results (segment runs,
- * delta = rowsum(dout * out), sink-gradient partials) to the other two and,
- * for bf16 with D = 64, 128 or 256, the dU blocks that dkdv writes and dq
- * reads; so it must stay untouched between them and the phases must run in
- * that order (on one stream, or with the caller ordering them).
+ * delta = rowsum(dout * (out + out_lo)), sink-gradient partials) to the
+ * other two and, with ATTN_DQ_DU_BLOCKS, the dU blocks that dkdv writes and
+ * dq reads; so it must stay untouched between them and the phases must run
+ * in that order (on one stream, or with the caller ordering them).
  *  - attn_bwd_pre:  segment runs, delta, dsink (required iff LEARNABLE) and,
  *                   except for bf16 with D = 128 or 256, the zeros of dbias
  *                   on the masked pairs (dbias nullable);
- *  - attn_bwd_dq:   dq;
  *  - attn_bwd_dkdv: dk, dv and dbias on the visible pairs, and for bf16 with
  *                   D = 128 or 256 also its zeros (dbias nullable, complete
- *                   once attn_bwd_pre and attn_bwd_dkdv have both run). */
-attn_status attn_bwd_pre(const attn_args* a, const void* out, const float* lse, const void* dout,
-                         void* dbias, float* dsink, void* workspace, size_t workspace_bytes, void* stream);
-attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, void* dq,
-                        void* workspace, size_t workspace_bytes, void* stream);
+ *                   once attn_bwd_pre and attn_bwd_dkdv have both run);
+ *  - attn_bwd_dq:   dq. */
+attn_status attn_bwd_pre(const attn_args* a, const void* out, const void* out_lo, const float* lse,
+                         const void* dout, void* dbias, float* dsink, void* workspace, size_t workspace_bytes,
+                         void* stream);
 attn_status attn_bwd_dkdv(const attn_args* a, const float* lse, const void* dout, void* dk, void* dv,
                           void* dbias, void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, void* dq, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* attn_last_error(void);

@@ -70,7 +70,7 @@ def case(dtype="bf16", B=2, S=200, Hq=4, Hkv=2, D=64, causal=True, window=0, sof
                 causal=causal, window=window, softcap=softcap)
 
 
-def run_gpu(c, backward=True, thd=False):
+def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True):
     import attention_tanh_logit_amd as A
     dt = c["dtype"]
     q, k, v = (to_dev(c[n], dt) for n in ("q", "k", "v"))
@@ -88,8 +88,9 @@ def run_gpu(c, backward=True, thd=False):
     # results land in NaN-filled buffers, so an element the kernels leave unwritten shows up
     nan = float("nan")
     lse_shape = (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
-    out, lse = A.attn_fwd(q, k, v, out=torch.full_like(q, nan),
-                          lse=torch.full(lse_shape, nan, dtype=torch.float32, device=q.device), **kw)
+    out, lse, out_lo = A.attn_fwd(q, k, v, out=torch.full_like(q, nan),
+                                  lse=torch.full(lse_shape, nan, dtype=torch.float32, device=q.device),
+                                  residual=residual, **kw)
     res = {"out": out, "lse": lse}
     if backward:
         do = to_dev(c["dout"], dt)
@@ -98,7 +99,8 @@ def run_gpu(c, backward=True, thd=False):
         outs = {"dq": torch.full_like(q, nan), "dk": torch.full_like(k, nan), "dv": torch.full_like(v, nan)}
         if "bias" in kw:
             outs["dbias"] = torch.full_like(kw["bias"], nan)
-        dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, outputs=outs, **kw)
+        dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, out_lo=out_lo, outputs=outs, dq_mode=dq_mode,
+                                              **kw)
         res.update(dq=dq, dk=dk, dv=dv, dbias=dbias, dsink=dsink)
     torch.cuda.synchronize()
     res = {n: (None if t is None else t.float().cpu().numpy()) for n, t in res.items()}
@@ -123,8 +125,28 @@ def run_oracle(c, backward=True, groups=None):
     return res
 
 
-def compare(gpu, ref, dtype, names=("out", "lse", "dq", "dk", "dv", "dbias", "dsink")):
-    """Normwise errors per tensor; returns {name: err}."""
+# the head axis of each output tensor (query heads, or KV heads for dk/dv)
+HEAD_AXIS = {"out": 2, "dq": 2, "dk": 2, "dv": 2, "lse": 1, "dbias": 1}
+
+
+def per_head_errors(g, r, axis):
+    """Normwise error of every (batch row, head) slice: {(b, h): err}."""
+    out = {}
+    for b in range(r.shape[0]):
+        for h in range(r.shape[axis]):
+            idx = [b] + [slice(None)] * (r.ndim - 1)
+            idx[axis] = h
+            out[(b, h)] = rel_err(g[tuple(idx)], r[tuple(idx)])
+    return out
+
+
+def compare(gpu, ref, dtype, names=("out", "lse", "dq", "dk", "dv", "dbias", "dsink"), per_head=False):
+    """Normwise errors per tensor; returns {name: err}.
+
+    With per_head, tensors with a head axis also get one error per
+    (batch row, head) slice, reported under "name[b,h]" keys, so that a
+    single bad head shows up even when the whole tensor's error is small.
+    """
     errs = {}
     for n in names:
         if ref.get(n) is None:
@@ -134,4 +156,7 @@ def compare(gpu, ref, dtype, names=("out", "lse", "dq", "dk", "dv", "dbias", "ds
         r = ref[n]
         assert g.shape == r.shape, f"{n}: shape {g.shape} vs {r.shape}"
         errs[n] = rel_err(g, r)
+        if per_head and n in HEAD_AXIS and r.ndim >= 3:
+            for (b, h), e in per_head_errors(g, r, HEAD_AXIS[n]).items():
+                errs[f"{n}[{b},{h}]"] = e
     return errs

@@ -51,6 +51,9 @@ def test_valid_arguments_pass():
     assert _status(_args(sink_mode=1)) == (0, "")
     assert _status(_args(sink_mode=2, sink=0x2000))[0] == 0
     assert _status(_args(causal=0, Sk=300))[0] == 0
+    assert _status(_args(dq_mode=1))[0] == 0
+    assert _status(_args(dq_mode=2, dtype=1))[0] == 0
+    assert _status(_args(Sq=0, Sk=0))[0] == 0
 
 
 BAD = {
@@ -74,6 +77,11 @@ BAD = {
     "zero_heads": (dict(Hkv=0), 1, "Hkv"),
     "misaligned_q": (dict(q=0x1002), 1, "aligned"),
     "misaligned_bias": (dict(bias=0x2008), 1, "aligned"),
+    "bad_dq_mode": (dict(dq_mode=3), 1, "dq_mode"),
+    "du_blocks_fp32": (dict(dtype=1, dq_mode=1), 2, "DU_BLOCKS"),
+    "du_blocks_d512": (dict(D=512, dq_mode=1), 2, "DU_BLOCKS"),
+    "du_blocks_ragged_bias": (dict(Sq=250, Sk=250, bias=0x2000, dq_mode=1), 2, "DU_BLOCKS"),
+    "keys_empty": (dict(Sk=0, causal=0), 2, "Sk == 0"),
 }
 
 
@@ -100,19 +108,33 @@ def test_fwd_rejects_before_any_launch():
     """A failing call returns its status without touching the (bogus) pointers."""
     L = A.lib()
     a = _args(softcap=-3.0)
-    s = L.attn_fwd(ctypes.byref(a), 0x10, 0x20, None, 0, None)
+    s = L.attn_fwd(ctypes.byref(a), 0x10, 0x20, None, None, 0, None)
     assert s == 1
     a = _args(sink_mode=2, sink=0x2000)
-    s = L.attn_bwd(ctypes.byref(a), 0x10, 0x20, 0x30, 0x40, 0x50, 0x60, None, None, None, 1 << 30, None)
+    s = L.attn_bwd(ctypes.byref(a), 0x10, None, 0x20, 0x30, 0x40, 0x50, 0x60, None, None, None, 1 << 30, None)
     assert s == 1 and "dsink" in L.attn_last_error().decode()
+
+
+def test_out_lo_is_bf16_only():
+    L = A.lib()
+    a = _args(dtype=1)
+    assert L.attn_fwd(ctypes.byref(a), 0x1000, 0x2000, 0x3000, None, 0, None) == 1
+    assert "bf16" in L.attn_last_error().decode()
+    s = L.attn_bwd(ctypes.byref(a), 0x1000, 0x3000, 0x2000, 0x4000, 0x5000, 0x6000, 0x7000, None, None, 0x8000,
+                   1 << 30, None)
+    assert s == 1 and "bf16" in L.attn_last_error().decode()
+    a = _args()
+    assert L.attn_fwd(ctypes.byref(a), 0x1000, 0x2000, 0x3008, None, 0, None) == 1
+    assert "aligned" in L.attn_last_error().decode()
 
 
 def test_misaligned_outputs_rejected_before_any_launch():
     L = A.lib()
     a = _args()
-    assert L.attn_fwd(ctypes.byref(a), 0x1004, 0x2000, None, 0, None) == 1
+    assert L.attn_fwd(ctypes.byref(a), 0x1004, 0x2000, None, None, 0, None) == 1
     assert "aligned" in L.attn_last_error().decode()
-    s = L.attn_bwd(ctypes.byref(a), 0x1000, 0x2000, 0x3000, 0x4002, 0x5000, 0x6000, None, None, 0x7000, 1 << 30, None)
+    s = L.attn_bwd(ctypes.byref(a), 0x1000, None, 0x2000, 0x3000, 0x4002, 0x5000, 0x6000, None, None, 0x7000,
+                   1 << 30, None)
     assert s == 1 and "aligned" in L.attn_last_error().decode()
 
 
@@ -124,20 +146,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         ops.lib()
 
 
-def test_bwd_workspace_carries_du_blocks_for_bf16_d64_d128(monkeypatch):
-    """bf16 with D = 64/128: B*Hq*ceil(Sk/32)*ceil(Sq/32) blocks of 2 KiB for dU, unless the limit is lower."""
+def test_bwd_workspace_carries_du_blocks_by_dq_mode():
+    """bf16 with D = 64/128/256: B*Hq*ceil(Sk/32)*ceil(Sq/32) blocks of 2 KiB for dU with
+    dq_mode auto (while that stays within 16 GiB) or du_blocks; none with recompute."""
     L = A.lib()
-    monkeypatch.delenv("ATTN_SOFTCAP_DU_MAX_BYTES", raising=False)
-    a = _args()                       # bf16, B=2, Hq=8, S=256, D=128
+    a = _args()                       # bf16, B=2, Hq=8, S=256, D=128, dq_mode auto
     with_du = L.attn_bwd_workspace_size(ctypes.byref(a))
-    monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", "0")
-    without = L.attn_bwd_workspace_size(ctypes.byref(a))
+    without = L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2)))
     assert with_du - without == 2 * 8 * 8 * 8 * 2048
-    monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", str(2 * 8 * 8 * 8 * 2048))
-    assert L.attn_bwd_workspace_size(ctypes.byref(a)) == with_du
+    assert L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=1))) == with_du
     a = _args(Sq=250, Sk=250)         # ragged: still 8 blocks per side
     assert L.attn_bwd_workspace_size(ctypes.byref(a)) - without <= 2 * 8 * 8 * 8 * 2048 + 256
-    monkeypatch.delenv("ATTN_SOFTCAP_DU_MAX_BYTES", raising=False)
+    # auto leaves the hand-off once the blocks pass 16 GiB: B=8, Hq=64, S=16384 needs 32 GiB
+    big = dict(B=8, Hq=64, Hkv=8, Sq=16384, Sk=16384)
+    auto = L.attn_bwd_workspace_size(ctypes.byref(_args(**big)))
+    rec = L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **big)))
+    forced = L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=1, **big)))
+    assert auto == rec and forced - rec == 8 * 64 * 512 * 512 * 2048
     f32 = _args(dtype=1)
     g32 = _args(dtype=1, D=256)
     # the bf16 run also carries the fp32 dK/dV partials of its head split
@@ -162,15 +187,47 @@ def _split_partials(a):
     return (n + 255) // 256 * 256
 
 
-def test_bwd_workspace_carries_split_partials_only_for_small_grids(monkeypatch):
+def test_bwd_workspace_carries_split_partials_only_for_small_grids():
     """bf16 dk/dv splits a GQA group's query heads over workgroups when the grid is small:
     fp32 partial dK/dV for each split in the workspace; none for a grid of >= 1024 workgroups."""
     L = A.lib()
-    monkeypatch.setenv("ATTN_SOFTCAP_DU_MAX_BYTES", "0")
     for B, S, Hq, Hkv, D, hs in ((2, 256, 8, 2, 128, 4), (1, 4096, 64, 8, 64, 4), (4, 4096, 32, 8, 128, 1),
                                  (1, 4096, 24, 8, 128, 3)):
         assert _head_split(B, S, Hq, Hkv) == hs
-        bf = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D)
+        bf = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D, dq_mode=2)
         fp = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D, dtype=1)
         diff = L.attn_bwd_workspace_size(ctypes.byref(bf)) - L.attn_bwd_workspace_size(ctypes.byref(fp))
         assert diff == _split_partials(bf), (B, S, Hq, Hkv, D)
+
+
+# ---- the binding's own checks: the C ABI sees only pointers, so shapes and devices are checked here
+
+def _t(*shape, dtype=None, device="cpu"):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16, device=device)
+
+
+MAKE_ARGS_BAD = {
+    "k_batch": (lambda: (_t(2, 64, 4, 128), _t(1, 64, 2, 128), _t(1, 64, 2, 128)), {}, "batch"),
+    "k_head_dim": (lambda: (_t(2, 64, 4, 128), _t(2, 64, 2, 64), _t(2, 64, 2, 64)), {}, "head dim"),
+    "thd_head_dim": (lambda: (_t(64, 4, 128), _t(64, 2, 64), _t(64, 2, 64)),
+                     dict(cu_seqlens=_t(3, dtype=__import__("torch").int32)), "head dim"),
+    "v_shape": (lambda: (_t(2, 64, 4, 128), _t(2, 64, 2, 128), _t(2, 32, 2, 128)), {}, "same shape"),
+    "k_rank": (lambda: (_t(2, 64, 4, 128), _t(64, 2, 128), _t(64, 2, 128)), {}, "BSHD"),
+    "sink_on_other_device": (lambda: (_t(2, 64, 4, 128), _t(2, 64, 2, 128), _t(2, 64, 2, 128)),
+                             dict(sink_mode="learnable", sink=_t(4, dtype=__import__("torch").float32,
+                                                                 device="meta")), "device"),
+    "bias_on_other_device": (lambda: (_t(2, 64, 4, 128), _t(2, 64, 2, 128), _t(2, 64, 2, 128)),
+                             dict(bias=_t(2, 4, 64, 64, device="meta")), "device"),
+    "host_tensors": (lambda: (_t(2, 64, 4, 128), _t(2, 64, 2, 128), _t(2, 64, 2, 128)), {}, "GPU"),
+    "bad_dq_mode": (lambda: (_t(2, 64, 4, 128), _t(2, 64, 2, 128), _t(2, 64, 2, 128)),
+                    dict(dq_mode="fast"), "dq_mode"),
+}
+
+
+@pytest.mark.parametrize("name", list(MAKE_ARGS_BAD))
+def test_make_args_rejects_mismatched_tensors(name):
+    mk, kw, word = MAKE_ARGS_BAD[name]
+    q, k, v = mk()
+    with pytest.raises(ValueError, match=word):
+        A.make_args(q, k, v, **kw)

@@ -1,0 +1,95 @@
+"""Bitwise repeatability and the consistency of packed-segment runs.
+
+* The backward uses no floating-point atomics (head-split partials and the
+  sink gradient are summed in a fixed order), so two runs on the same inputs
+  must give the same bits in every output, on every kernel path.
+* Segment runs: a key is visible only inside its query's run of equal
+  adjacent segment ids (for ids that do not decrease along the row: equal
+  id), and THD tokens outside [cu[0], cu[nseq]) form one run on each side.
+  The forward and every backward kernel must agree on these runs; the oracle
+  (visibility = equal id) is fed ids renumbered by run, which it must then
+  match.
+"""
+import numpy as np
+import pytest
+import torch
+
+from harness import TOL, case, compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+REPEAT = {
+    "bf16_d64_split_du": dict(dtype="bf16", D=64, B=2, S=203, Hq=8, Hkv=2, sink_mode="learnable"),
+    "bf16_d64_nosplit": dict(dtype="bf16", D=64, B=8, S=1024, Hq=16, Hkv=16, q_scale=2.0),
+    "bf16_d128_bias": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0,
+                           segments=[[45, 70, 190], [128]]),
+    "bf16_d128_recompute": dict(dtype="bf16", D=128, B=2, S=203, Hq=4, Hkv=2, window=37),
+    "bf16_d256": dict(dtype="bf16", D=256, B=1, S=203, Hq=4, Hkv=2, sink_mode="learnable"),
+    "bf16_d512": dict(dtype="bf16", D=512, B=1, S=203, Hq=4, Hkv=2, bias=True),
+    "fp32_d64": dict(dtype="fp32", D=64, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable"),
+    "fp32_d512": dict(dtype="fp32", D=512, B=1, S=130, Hq=2, Hkv=1),
+}
+
+
+@pytest.mark.parametrize("name", list(REPEAT))
+def test_two_runs_give_the_same_bits(name):
+    c = case(**REPEAT[name])
+    mode = "recompute" if name.endswith("recompute") else "auto"
+    print(f"repeat {name}: dq_mode={mode}", flush=True)
+    a = run_gpu(c, dq_mode=mode)
+    b = run_gpu(c, dq_mode=mode)
+    for n, x in a.items():
+        if x is None:
+            assert b[n] is None
+            continue
+        assert x.tobytes() == b[n].tobytes(), f"{name}: {n} differs between two runs"
+
+
+def _run_ids(seg):
+    """Renumber segment ids by run of equal adjacent ids (row by row)."""
+    out = np.zeros_like(seg)
+    for b in range(seg.shape[0]):
+        out[b, 1:] = np.cumsum(seg[b, 1:] != seg[b, :-1])
+    return out
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("fp32", 64), ("bf16", 512)])
+def test_repeated_segment_ids_form_separate_runs(dtype, D):
+    """Ids that come back (0, 1, 0, 2): each run is its own segment, in forward and backward."""
+    c = case(dtype=dtype, D=D, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable")
+    seg = np.zeros((2, 203), dtype=np.int32)
+    seg[0, 40:70] = 1
+    seg[0, 120:] = 2
+    seg[1, 13:100] = 3
+    seg[1, 100:150] = 1
+    seg[1, 150:] = 3
+    c["segment_ids"] = seg
+    gpu = run_gpu(c)
+    ref = run_oracle(dict(c, segment_ids=_run_ids(seg)))
+    errs = compare(gpu, ref, dtype)
+    print("errors:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL[dtype] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("cu", [[0, 50, 120], [10, 50, 203], [7, 7, 90, 140]])
+def test_thd_tokens_outside_cu_seqlens_form_one_run_each_side(cu):
+    import attention_tanh_logit_amd as A
+    T = 203
+    c = case(dtype="bf16", D=128, B=1, S=T, Hq=4, Hkv=2, sink_mode="learnable")
+    ids = np.zeros((1, T), dtype=np.int32)
+    for x in cu:
+        ids[0, x:] += 1
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x[0])).to("cuda", torch.bfloat16)  # noqa: E731
+    q, k, v, do = (dev(c[n]) for n in ("q", "k", "v", "dout"))
+    kw = dict(causal=True, softcap=c["softcap"], sink_mode="learnable", sink=torch.from_numpy(c["sink"]).cuda(),
+              cu_seqlens=torch.tensor(cu, dtype=torch.int32, device="cuda"))
+    out, lse, out_lo = A.attn_fwd(q, k, v, **kw)
+    dq, dk, dv, _, dsink = A.attn_bwd(q, k, v, out, lse, do, out_lo=out_lo, **kw)
+    torch.cuda.synchronize()
+    gpu = {"out": out.float().cpu().numpy()[None], "lse": lse.cpu().numpy()[None],
+           "dq": dq.float().cpu().numpy()[None], "dk": dk.float().cpu().numpy()[None],
+           "dv": dv.float().cpu().numpy()[None], "dbias": None, "dsink": dsink.cpu().numpy()}
+    ref = run_oracle(dict(c, segment_ids=_run_ids(ids)))
+    errs = compare(gpu, ref, "bf16")
+    print(f"cu={cu} errors:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs

@@ -5,8 +5,9 @@ The GPU runs the whole problem; the fp64 oracle recomputes whole
 (batch row, KV head) groups -- every query row, key and head of the group --
 and the two are compared element by element on those groups (normwise error
 max|x - ref| / max|ref| per tensor, 1e-5 for the fp32 path, 1e-2 for bf16).
-The sink gradient is checked where the sampled groups cover every batch row
-of a head (B = 1 workloads).
+The learnable-sink workloads (B = 1) are checked on every group, so the sink
+gradient, a sum over all query rows of a head, is compared on every query
+head, per group and over all heads at once.
 """
 import numpy as np
 import pytest
@@ -22,7 +23,11 @@ SUBRUNS = {w.name: w for w in W.all_workloads()}
 
 
 def _groups(w):
-    """Sampled (b, kv_head) groups: the last one (longest causal rows) and the first."""
+    """Checked (b, kv_head) groups: every group of the learnable-sink workloads (so that
+    dsink, a sum over all query rows of a head, is checked on all query heads), else a
+    sample: the last group (longest causal rows) and the first."""
+    if w.sink_mode == "learnable":
+        return [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     last = (w.B - 1, w.Hkv - 1)
     return [last] if last == (0, 0) else [last, (0, 0)]
 
@@ -54,11 +59,12 @@ def test_workload_matches_oracle_on_sampled_groups(name):
                     slabs[(b, h)] = s
         kw["bias"] = bias
     print(f"workload {name}: GPU forward + backward", flush=True)
-    out, lse = A.attn_fwd(q, k, v, **kw)
-    dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, **kw)
+    out, lse, out_lo = A.attn_fwd(q, k, v, **kw)
+    dq, dk, dv, dbias, dsink = A.attn_bwd(q, k, v, out, lse, do, out_lo=out_lo, **kw)
     torch.cuda.synchronize()
     tol = TOL[w.dtype]
     G = w.G
+    dsink_ref = np.full(w.Hq, np.nan)
     for (b, hk) in groups:
         hs = slice(hk * G, (hk + 1) * G)
         print(f"workload {name}: oracle on group b={b} kv_head={hk}", flush=True)
@@ -86,7 +92,12 @@ def test_workload_matches_oracle_on_sampled_groups(name):
             assert np.all(gb[:, ~vis] == 0.0), f"{name}: nonzero dbias on masked pairs"
         if dsink is not None and w.B == 1:
             errs["dsink"] = rel_err(dsink[hs].cpu().numpy(), rs)
+            dsink_ref[hs] = rs
         print(f"workload {name} group ({b},{hk}) errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()),
               flush=True)
         bad = {k: v for k, v in errs.items() if not v <= tol}
         assert not bad, f"{name}: over tolerance {tol}: {bad}"
+    if dsink is not None and w.B == 1 and len(groups) == w.Hkv:
+        e = rel_err(dsink.cpu().numpy(), dsink_ref)
+        print(f"workload {name}: dsink over all {w.Hq} query heads {e:.2e}", flush=True)
+        assert e <= tol, f"{name}: dsink over all heads {e:.2e}"
