@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "attn_softcap.h"
@@ -115,6 +116,14 @@ __global__ __launch_bounds__(256) void seg_from_cu_kernel(const int* cu, int nse
   seg_lo[t] = max(min(a, t), 0);
   seg_hi[t] = max(min(e, T), t + 1);
 }
+
+// Scratch of attn_bwd_noalloc: the backward's workspace (segment runs,
+// delta, sink-gradient partials, split partials, dU blocks when they fit) for
+// callers that cannot allocate.  One copy per GPU the library runs on, held
+// until the process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 }  // namespace atl
 
@@ -287,6 +296,34 @@ void fill_consts(const attn_args* a, float& scale, float& sl2, float& xc, float&
 
 attn_status hip_fail(hipError_t e, const char* what) {
   return fail(ATTN_HIP_ERROR, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Device address of `scratch` on the stream's device (which must be the
+// current device), looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+attn_status scratch_for(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev) return fail(ATTN_INVALID_ARGUMENT, "the stream must belong to the current device");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -479,6 +516,31 @@ attn_status attn_bwd_dkdv(const attn_args* a, const float* lse, const void* dout
                           void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(a, nullptr, nullptr, lse, dout, nullptr, dk, dv, dbias, nullptr, workspace, workspace_bytes,
                   stream, kPhaseDkdv);
+}
+
+attn_status attn_bwd_noalloc(const attn_args* a, const void* out, const void* out_lo, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, void* dbias, float* dsink,
+                             void* stream) {
+  g_err.clear();
+  attn_status st = validate(a);
+  if (st != ATTN_OK) return st;
+  attn_args r = *a;
+  if (r.dq_mode == ATTN_DQ_AUTO) {
+    r.dq_mode = ATTN_DQ_DU_BLOCKS;
+    if (!du_supported(&r) || bwd_ws(&r) > kScratchBytes) r.dq_mode = ATTN_DQ_RECOMPUTE;
+  }
+  const size_t need = bwd_ws(&r);
+  if (need > kScratchBytes)
+    return fail(ATTN_UNSUPPORTED, "attn_bwd_noalloc: this problem needs " + std::to_string(need) +
+                                      " bytes of scratch, more than its " + std::to_string(kScratchBytes) +
+                                      " (use attn_bwd with a workspace)");
+  if ((size_t)r.B * (r.Sq + r.Sk) == 0) return bwd_impl(&r, out, out_lo, lse, dout, dq, dk, dv, dbias, dsink,
+                                                         nullptr, 0, stream, kPhasePre | kPhaseDq | kPhaseDkdv);
+  void* ws = nullptr;
+  st = scratch_for(stream, &ws);
+  if (st != ATTN_OK) return st;
+  return bwd_impl(&r, out, out_lo, lse, dout, dq, dk, dv, dbias, dsink, ws, kScratchBytes, stream,
+                  kPhasePre | kPhaseDq | kPhaseDkdv);
 }
 
 }  // extern "C"

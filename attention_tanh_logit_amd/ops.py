@@ -41,7 +41,8 @@ class AttnArgs(ctypes.Structure):
 
 
 EXPORTS = ("attn_validate", "attn_fwd_workspace_size", "attn_bwd_workspace_size",
-           "attn_fwd", "attn_bwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv", "attn_last_error")
+           "attn_fwd", "attn_bwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_noalloc",
+           "attn_last_error")
 
 _lib = None
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dq.restype = ctypes.c_int
     L.attn_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd_dkdv.restype = ctypes.c_int
+    L.attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_bwd_noalloc.restype = ctypes.c_int
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -270,6 +273,40 @@ def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=Non
         events[2].record()
         _check(L.attn_bwd_dq(ctypes.byref(a), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(ws), nws, st))
         events[3].record()
+    return dq, dk, dv, dbias, dsink
+
+
+def attn_bwd_noalloc(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None,
+                     causal=False, window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto",
+                     outputs):
+    """The backward through ``attn_bwd_noalloc``: no workspace, the library's own
+    static scratch instead.  ``outputs`` must hold preallocated "dq", "dk", "dv"
+    (and "dbias" with a bias, "dsink" with a learnable sink) tensors, each
+    contiguous with the shape, dtype and device of its input; this function
+    allocates nothing on the device.  Returns (dq, dk, dv, dbias, dsink)."""
+    L = lib()
+    a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
+                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode)
+    _check(L.attn_validate(ctypes.byref(a)))
+    _like("out", out, q)
+    _like("dout", dout, q)
+    if out_lo is not None:
+        _like("out_lo", out_lo, q)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != a.B * a.Hq * a.Sq \
+            or lse.device != q.device:
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq] on q's device")
+    dq = _like("outputs['dq']", outputs["dq"], q)
+    dk = _like("outputs['dk']", outputs["dk"], k)
+    dv = _like("outputs['dv']", outputs["dv"], v)
+    dbias = _like("outputs['dbias']", outputs["dbias"], bias) if outputs.get("dbias") is not None else None
+    dsink = None
+    if sink_mode == "learnable":
+        dsink = outputs["dsink"]
+        if tuple(dsink.shape) != (a.Hq,) or dsink.dtype != torch.float32 or dsink.device != q.device \
+                or not dsink.is_contiguous():
+            raise ValueError("outputs['dsink'] must be contiguous float32 [Hq] on q's device")
+    _check(L.attn_bwd_noalloc(ctypes.byref(a), _ptr(out), _ptr(out_lo), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(dbias), _ptr(dsink), _stream(q)))
     return dq, dk, dv, dbias, dsink
 
 

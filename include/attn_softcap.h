@@ -209,6 +209,23 @@ attn_status attn_bwd_dkdv(const attn_args* a, const float* lse, const void* dout
 attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, void* dq, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace lives in a static device array of
+ * 128 MiB inside the library, one per GPU (held until the process ends);
+ * dq_mode ATTN_DQ_AUTO takes the dU blocks only where the whole workspace
+ * then fits in it, else recomputes.  A problem whose workspace exceeds
+ * 128 MiB is rejected with ATTN_UNSUPPORTED before anything is launched
+ * (e.g. an explicit ATTN_DQ_DU_BLOCKS at B=4, Hq=32, S=4096).  The stream
+ * must belong to the current device.  Outputs and their meaning are those of
+ * attn_bwd, bit for bit when both resolve to the same dq_mode.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams or host threads without ordering between them)
+ * race and give wrong results.  No call allocates or frees memory. */
+attn_status attn_bwd_noalloc(const attn_args* a, const void* out, const void* out_lo, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, void* dbias, float* dsink,
+                             void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* attn_last_error(void);
 

@@ -231,3 +231,15 @@ def test_make_args_rejects_mismatched_tensors(name):
     q, k, v = mk()
     with pytest.raises(ValueError, match=word):
         A.make_args(q, k, v, **kw)
+
+
+def test_noalloc_rejects_oversize_before_any_launch():
+    """attn_bwd_noalloc checks the workspace its problem needs against its 128 MiB
+    scratch on the host: explicit dU blocks of 4 GiB are refused with no device call."""
+    L = A.lib()
+    a = _args(B=4, Sq=4096, Sk=4096, Hq=32, Hkv=8, dq_mode=1)
+    s = L.attn_bwd_noalloc(ctypes.byref(a), 0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, None, None)
+    assert s == 2 and "scratch" in L.attn_last_error().decode()
+    a = _args(dq_mode=7)
+    assert L.attn_bwd_noalloc(ctypes.byref(a), 0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, None,
+                              None) == 1
