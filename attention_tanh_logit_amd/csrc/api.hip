@@ -150,7 +150,8 @@ bool has_segments(const attn_args* a) { return a->segment_ids != nullptr || a->c
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 bool du_supported(const attn_args* a) {
-  return fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr);
+  return fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr) ||
+         wide_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->bias != nullptr);
 }
 
 attn_status validate(const attn_args* a) {
@@ -228,8 +229,11 @@ bool dkdv_writes_dbias_zeros(const attn_args* a) {
 // (four per CU), so that a small batch with a wide GQA group does not leave
 // the GPU to a few long workgroups; 1 when there are enough already.
 int head_split(const attn_args* a) {
-  if (!fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr)) return 1;
-  const long wgs = (long)((a->Sk + 127) / 128) * a->Hkv * a->B;
+  const bool bf = a->dtype == ATTN_BF16, bias = a->bias != nullptr;
+  const bool wide = wide_ok(bf, a->D, a->Hq, a->Hkv, bias);
+  if (!fast_ok(bf, a->D, a->Hq, a->Hkv, a->Sk, bias) && !wide) return 1;
+  const int bnk = wide ? 32 : 128;   // keys per dk/dv workgroup (as counted here)
+  const long wgs = (long)((a->Sk + bnk - 1) / bnk) * a->Hkv * a->B;
   const int G = a->Hq / a->Hkv;
   int hs = 1;
   for (int s = 2; s <= G && wgs * hs < 1024; ++s)

@@ -11,7 +11,7 @@
 
 #include <type_traits>
 
-#include "fast.hpp"
+#include "wide.hpp"
 
 namespace atl {
 
@@ -81,6 +81,16 @@ inline bool fast_ok(bool bf16_input, int D, int Hq, int Hkv, int Sk, bool bias) 
   return bf16_input && (D == 64 || D == 128 || D == 256) && 128L * stride * 2 < (1L << 31) &&
          (!bias || (Sk % 8 == 0 && Sk >= 8));
 }
+// bf16 with D = 512 and no bias takes the kernels of wide.hpp (same 32-bit
+// buffer offsets as the fast kernels)
+inline bool wide_ok(bool bf16_input, int D, int Hq, int Hkv, bool bias) {
+  const long stride = (long)(Hq > Hkv ? Hq : Hkv) * D;
+  return bf16_input && D == 512 && !bias && 128L * stride * 2 < (1L << 31);
+}
+template <typename T, int D, bool BIAS> constexpr bool use_wide() {
+  return std::is_same<T, bf16>::value && D == 512 && !BIAS;
+}
+
 template <int D, class Params>
 bool fast_fits(const Params& p, const Launch& l, bool bias) {
   return fast_ok(true, D, p.Hq, p.Hkv, l.Sk, bias);
@@ -96,6 +106,14 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
       // capped logits with 2 c log2(e) <= 120 keep a fixed reference maximum
       if (CAP && p.cl2 <= 60.0f) fwd_fast_kernel<D, CAP, BIAS, CAP><<<grid, NT, 0, l.stream>>>(p);
       else fwd_fast_kernel<D, CAP, BIAS, false><<<grid, NT, 0, l.stream>>>(p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (use_wide<T, D, BIAS>()) {
+    if (wide_ok(true, D, p.Hq, p.Hkv, false)) {
+      const dim3 grid((l.Sq + 63) / 64, p.Hq, l.B);
+      if (CAP && p.cl2 <= 60.0f) fwd512_kernel<CAP, CAP><<<grid, 512, 0, l.stream>>>(p);
+      else fwd512_kernel<CAP, false><<<grid, 512, 0, l.stream>>>(p);
       return hipGetLastError();
     }
   }
@@ -125,6 +143,14 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
       }
     }
   }
+  if constexpr (std::is_same<T, bf16>::value && D == 512) {
+    // the dU blocks exist only where the wide dk/dv kernel wrote them
+    if (p.du) {
+      const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
+      dq_du_kernel<D, CAP, 32, 2, 2><<<grid, 512, 0, l.stream>>>(p);
+      return hipGetLastError();
+    }
+  }
   using C = DqCfg<T, D>;
   constexpr int BM = 32 * C::NQG;
   const dim3 grid((l.Sq + BM - 1) / BM, p.Hq, l.B);
@@ -148,6 +174,19 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
         const dim3 grid((l.Sk + 127) / 128, p.Hkv * p.hsplit, l.B);
         dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
       }
+      if (p.hsplit > 1) {
+        const long nel = (long)l.B * l.Sk * p.Hkv * D;
+        const float kscale = p.scale * (CAP ? 4.0f : 1.0f);
+        dkv_reduce_kernel<bf16><<<(unsigned)((nel / 4 + 255) / 256), 256, 0, l.stream>>>(
+            p.dkv_part, p.hsplit, nel, kscale, reinterpret_cast<bf16*>(p.dk), reinterpret_cast<bf16*>(p.dv));
+      }
+      return hipGetLastError();
+    }
+  }
+  if constexpr (use_wide<T, D, BIAS>()) {
+    if (wide_ok(true, D, p.Hq, p.Hkv, false)) {
+      const dim3 grid((l.Sk + 31) / 32, p.Hkv * p.hsplit, l.B);
+      dkdv512_kernel<CAP><<<grid, 512, 0, l.stream>>>(p);
       if (p.hsplit > 1) {
         const long nel = (long)l.B * l.Sk * p.Hkv * D;
         const float kscale = p.scale * (CAP ? 4.0f : 1.0f);

@@ -195,7 +195,7 @@ struct FragOfs {
 //    s + 16g points at row 4g + s/4 (+16), columns 16 ob + 4(s%4) .. + 3.
 template <int D>
 struct Frag16Ofs {
-  static_assert(D == 128 || D == 256, "laid out for 256- or 512-byte rows");
+  static_assert(D == 128 || D == 256 || D == 512, "laid out for 256-, 512- or 1024-byte rows");
   int pbase, pxor, tbase, txor;
   __device__ __forceinline__ explicit Frag16Ofs(int lane) {
     const int r = lane & 15, g = lane >> 4;
@@ -1322,14 +1322,18 @@ __device__ __forceinline__ bf16x8 du_frag16(const bf16* blk, int lane, int sb) {
 // transposing LDS reads.  No exponentials and no masks: the dk/dv kernel
 // stored masked pairs as zeros, and it wrote every block that holds a
 // visible pair (blocks no query of the wave sees are skipped, never read).
-template <int D, bool CAP, int BN, int NST>
-__global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams p) {
-  constexpr int NT = 256;
+// With NSL > 1 (D = 512) the output columns split over NSL waves per 32-query
+// group: they share the group's dU blocks (loaded by the first of them) and
+// each accumulates D / NSL columns of dQ.
+template <int D, bool CAP, int BN, int NST, int NSL = 1>
+__global__ __launch_bounds__(256 * NSL, NSL > 1 ? 1 : (NST >= 3 ? 3 : 2)) void dq_du_kernel(BwdParams p) {
+  constexpr int NT = 256 * NSL;
   constexpr int BM = 128;
   constexpr int NKB = BN / 32;
-  constexpr int NOB = D / 32;
-  constexpr bool DU16 = D >= 128;   // blocks written by dkdv16_kernel
+  constexpr int NOB = D / 32 / NSL;
+  constexpr bool DU16 = D >= 128;   // blocks written by 16-key dk/dv waves
   static_assert(NST == 2 || NST == 3, "two or three tile stages");
+  static_assert(NSL == 1 || NST == 2, "uneven load counts per thread need full waits");
 
   // NST stages of (K tile, this workgroup's dU blocks), distinct objects so
   // that the compiler sees a read of one never alias the DMA into another
@@ -1352,7 +1356,8 @@ __global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams 
   const int hk = hq / p.G;
   const int Sq = p.mask.Sq, Sk = p.mask.Sk;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = (threadIdx.x >> 6) / NSL;   // 32-query group
+  const int sl = (threadIdx.x >> 6) % NSL;  // column slice
   const int n = lane & 31;
   const int h = lane >> 5;
   const int q0 = qt * BM;
@@ -1391,6 +1396,7 @@ __global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams 
   // memory), so the loads of a later tile can be left in flight by count
   auto fetch = [&](int k0, bf16* tK, bf16* tU) {
     load_tile<BN, D, NT, true>(tK, kbase, kstride, k0, Sk);
+    if (sl != 0) return;
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
       const bool vis = visible(k0 + 32 * kk);
@@ -1428,7 +1434,7 @@ __global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams 
         for (int sb = 0; sb < 2; ++sb) {
           const bf16x8 uf = DU16 ? du_frag16(blk, lane, sb) : du_frag(blk, lane, sb);
 #pragma unroll
-          for (int ob = 0; ob < NOB; ++ob) mma(qacc[ob], fo.frag_tr(tK, 32 * kk + 16 * sb, ob), uf);
+          for (int ob = 0; ob < NOB; ++ob) mma(qacc[ob], fo.frag_tr(tK, 32 * kk + 16 * sb, sl * NOB + ob), uf);
         }
       }
     }
@@ -1459,7 +1465,7 @@ __global__ __launch_bounds__(256, NST >= 3 ? 3 : 2) void dq_du_kernel(BwdParams 
         float vals[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vals[e] = qacc[ob][8 * hf + e] * (p.scale * kGrad4<CAP>);
-        store8<bf16>(drow + ob * 32 + 16 * hf + 8 * h, vals);
+        store8<bf16>(drow + (sl * NOB + ob) * 32 + 16 * hf + 8 * h, vals);
       }
     }
   }

@@ -1,0 +1,453 @@
+// bf16 kernels for head dim 512 (no bias): forward, dk/dv (which hands dU to
+// the dq kernel through the workspace) on the fast path's tiles and
+// fragments.
+//
+// A workgroup is 8 waves: two row (or key) groups x four column slices of
+// 128.  A wave keeps only its slice of the fixed operand (Q columns in the
+// forward, K and V columns in dk/dv) and of the output accumulators, so that
+// two waves fit a SIMD.  Each wave contracts its 128 columns into a partial
+// logit block; the four partials of a group are exchanged through LDS and
+// summed by every wave in the same slice order (bit-identical totals), after
+// which every wave of the group holds the whole logits and computes the
+// probabilities itself (MaxText commit quoted on "Support logits soft-capping
+// in the Pallas-Triton attention VJP": head_dim above 256 accumulated in
+// chunks).  Streamed tiles (K/V in the forward, Q/dO in dk/dv; 32 rows of
+// 1 KiB) go HBM -> LDS by buffer DMA, double-buffered, swizzled per row as
+// on the fast path (the swizzles permute 16-byte slots inside 128-column
+// groups, so a slice is a plain column offset).  LDS: 4 x 32 KiB of tiles +
+// 32 KiB of partials = 160 KiB, one workgroup per CU.
+#pragma once
+
+#include "fast.hpp"
+
+namespace atl {
+
+// The four partial accumulators of this wave's group, summed in slice order.
+// sX holds [wave][quantity][lane] f32x4; NQ quantities per wave.
+template <int NQ>
+__device__ __forceinline__ void group_sum4(f32x4* sX, int w, int lane, f32x4* acc) {
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) sX[(w * NQ + q) * 64 + lane] = acc[q];
+  __syncthreads();
+  const int w0 = w & ~3;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    f32x4 s = sX[(w0 * NQ + q) * 64 + lane];
+#pragma unroll
+    for (int x = 1; x < 4; ++x) s += sX[((w0 + x) * NQ + q) * 64 + lane];
+    acc[q] = s;
+  }
+}
+
+// ============================================================== forward (D = 512)
+
+// One workgroup = 64 query rows of one head; wave w = 4 rg + sl holds rows
+// q0 + 32 rg .. + 31 and columns 128 sl .. + 127 of Q (as Q^T fragments)
+// and of O.  Per 32-key tile: partial S^T = K Q^T over the slice's columns,
+// summed across the row group, then the capped logits, masking, online
+// softmax (running or, for caps with 2 c log2(e) <= 120, fixed reference
+// maximum; see fwd_fast_kernel) and O^T += V^T P^T over the slice's columns.
+template <bool CAP, bool FIXM>
+__global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
+  static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
+  constexpr int D = 512, NT = 512, BM = 64, BN = 32;
+  constexpr int NCW = 8;   // 16-column contraction steps per slice
+  constexpr int NOB = 4;   // 32-column output blocks per slice
+
+  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
+  __shared__ __attribute__((aligned(16))) f32x4 sX[8 * 4 * 64];
+
+  int qt, hq, b;
+  {
+    int x, grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, x, grp);
+    qt = p.reverse ? gridDim.x - 1 - x : x;
+    hq = grp % gridDim.y;
+    b = grp / gridDim.y;
+  }
+  const int hk = hq / p.G;
+  const int Sq = p.mask.Sq, Sk = p.mask.Sk;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int rg = w >> 2;
+  const int sl = w & 3;
+  const int colofs = 128 * sl;
+  const int q0 = qt * BM;
+  const int i = q0 + rg * 32 + n;
+  const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
+  const FragOfs<D, false> fo(lane);
+
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
+  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
+  const long kstride = (long)p.Hkv * D;
+
+  int lo_i = 0, hi_i = 0;
+  if (i < Sq) keys_of(p.mask, b, i, lo_i, hi_i);
+  const int ilast = min(q0 + BM, Sq) - 1;
+  int lo_first, hi_first, lo_last, hi_last;
+  keys_of(p.mask, b, q0, lo_first, hi_first);
+  keys_of(p.mask, b, ilast, lo_last, hi_last);
+  const bool rows_full = (q0 + BM <= Sq);
+
+  bf16x8 qf[NCW];
+  {
+    const bf16* qrow =
+        reinterpret_cast<const bf16*>(p.q) + (((long)b * Sq + min(i, Sq - 1)) * p.Hq + hq) * D + colofs;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h);
+  }
+
+  const bool has_sink = p.sink_mode != 0;
+  const float sink2 = p.sink_mode == 2 ? p.sink[hq] * kLog2e : 0.0f;
+  float m = FIXM ? lk.c2 : (has_sink ? sink2 : -INFINITY);
+  const float kfix = -0.5f / lk.c2;
+  float lsum = 0.0f;
+  f32x16 oacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) oacc[ob] = f32x16{};
+
+  const int kbeg = (lo_first / BN) * BN;
+  const int ntiles = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
+  if (ntiles > 0) {
+    load_tile<BN, D, NT, true>(sK0, kbase, kstride, kbeg, Sk);
+    load_tile<BN, D, NT, false>(sV0, vbase, kstride, kbeg, Sk);
+  }
+  wait_loads();
+  __syncthreads();
+
+  auto step = [&](const bf16* tK, const bf16* tV, bf16* wK, bf16* wV, int t) {
+    const int k0 = kbeg + t * BN;
+    if (t + 1 < ntiles) {
+      load_tile<BN, D, NT, true>(wK, kbase, kstride, k0 + BN, Sk);
+      load_tile<BN, D, NT, false>(wV, vbase, kstride, k0 + BN, Sk);
+    }
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) mma(s, fo.frag(tK, 0, 8 * sl + c), qf[c]);
+    {
+      f32x4 a[4];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) a[x >> 2][x & 3] = s[x];
+      group_sum4<4>(sX, w, lane, a);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) s[x] = a[x >> 2][x & 3];
+    }
+    // logits: CAP keeps r = 1/(1+2^y) (masked: +inf), else y (masked: -inf)
+    float ext = CAP ? INFINITY : -INFINITY;
+    auto logits = [&](auto masked) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float y = s[jj] * lk.a;
+        float v;
+        if constexpr (FIXM) v = __builtin_amdgcn_rcpf(fmaf(fast_exp2(y), kfix, kfix));
+        else if constexpr (CAP) v = __builtin_amdgcn_rcpf(1.0f + fast_exp2(y));
+        else v = y;
+        if constexpr (decltype(masked)::value) {
+          const int key = k0 + acc_row(h, jj);
+          v = (key >= lo_i && key < hi_i) ? v : ((CAP && !FIXM) ? INFINITY : -INFINITY);
+        }
+        s[jj] = v;
+        if constexpr (!FIXM) ext = CAP ? fminf(ext, v) : fmaxf(ext, v);
+      }
+    };
+    if (rows_full && k0 >= lo_last && k0 + BN <= hi_first) logits(bool_c<false>{});
+    else logits(bool_c<true>{});
+    float base = 0.0f;
+    if constexpr (!FIXM) {
+      ext = CAP ? fminf(ext, xor32(ext)) : fmaxf(ext, xor32(ext));
+      const float mx = CAP ? fmaf(ext, -2.0f * lk.c2, lk.c2) : ext;
+      const bool grow = mx > m + 8.0f;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m;
+        const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2(m - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int ob = 0; ob < NOB; ++ob) oacc[ob] *= alpha;
+        m = m_new;
+      }
+      base = (m == -INFINITY) ? 0.0f : m;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      s[jj] = FIXM  ? fast_exp2(s[jj])
+              : CAP ? fast_exp2(fmaf(s[jj], -2.0f * lk.c2, lk.c2 - base))
+                    : fast_exp2(s[jj] - base);
+    }
+    bf16x8 pf[2];
+    pf[0] = to_frag(s, 0, (bf16*)nullptr);
+    pf[1] = to_frag(s, 8, (bf16*)nullptr);
+    lsum = sum_bf16x8(pf[1], sum_bf16x8(pf[0], lsum));
+    bf16x8 tv[NOB][2];
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) tv[ob][sb] = fo.frag_tr(tV + colofs, 16 * sb, ob);
+    }
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) mma(oacc[ob], tv[ob][sb], pf[sb]);
+    }
+    wait_loads();
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(sK0, sV0, sK1, sV1, t);
+    if (t + 1 < ntiles) step(sK1, sV1, sK0, sV0, t + 1);
+  }
+
+  float ltot = lsum + xor32(lsum);
+  float oscale = 1.0f;
+  if constexpr (FIXM) {
+    if (has_sink && sink2 > m) {
+      oscale = fast_exp2(m - sink2);
+      ltot *= oscale;
+      m = sink2;
+    }
+  }
+  if (has_sink) ltot += fast_exp2(sink2 - m);
+  const float inv = ltot > 0.0f ? oscale / ltot : 0.0f;
+  if (i < Sq) {
+    const long orow_off = (((long)b * Sq + i) * p.Hq + hq) * D + colofs;
+    bf16* orow = reinterpret_cast<bf16*>(p.out) + orow_off;
+    bf16* lorow = reinterpret_cast<bf16*>(p.out_lo) + orow_off;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float vals[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = oacc[ob][8 * hf + e] * inv;
+        store8<bf16>(orow + ob * 32 + 16 * hf + 8 * h, vals);
+        if (p.out_lo) store8_lo(lorow + ob * 32 + 16 * hf + 8 * h, vals);
+      }
+    }
+    if (h == 0 && sl == 0) p.lse[((long)b * p.Hq + hq) * Sq + i] = ltot > 0.0f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ============================================================== dk, dv (D = 512)
+
+// One workgroup = 32 keys of one KV head; wave w = 4 kg + sl holds keys
+// k0 + 16 kg .. + 15 and columns 128 sl .. + 127.  Per 32-query item (one
+// query head): partial S = Q K^T and dP = dO V^T over the slice's columns on
+// v_mfma_f32_16x16x32_bf16 (lane: key r, queries 16 qb + 4g + e), summed
+// across the group, P and dU = P (dP - delta) (1 - t^2) / 4, then
+// dV^T += dO^T P and dK^T += Q^T dU over the slice's columns with Q^T, dO^T
+// from transposing reads.  Slice 0 writes the dU block halves for dq.
+template <bool CAP>
+__global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
+  constexpr int D = 512, NT = 512, BNK = 32, BMQ = 32;
+  constexpr int NCW = 4;   // 32-column contraction steps per slice
+  constexpr int NOB = 8;   // 16-column output blocks per slice
+
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sQ1[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sO0[BMQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 sO1[BMQ * D];
+  __shared__ __attribute__((aligned(16))) f32x4 sX[8 * 4 * 64];
+
+  int kb, hk, b, split;
+  {
+    int grp;
+    xcd_order(gridDim.x, gridDim.y * gridDim.z, kb, grp);
+    const int y = grp % gridDim.y;   // the splits of one KV head are adjacent
+    hk = y / p.hsplit;
+    split = y % p.hsplit;
+    b = grp / gridDim.y;
+  }
+  const int GS = p.G / p.hsplit;
+  const int Sq = p.mask.Sq, Sk = p.mask.Sk;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int kg = w >> 2;
+  const int sl = w & 3;
+  const int colofs = 128 * sl;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int k0 = kb * BNK;
+  const int kw = k0 + 16 * kg;
+  const int j = kw + r;
+  const int jc = min(j, Sk - 1);
+  const long qstride = (long)p.Hq * D;
+  const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
+  const Frag16Ofs<D> fo(lane);
+
+  // this wave's columns of its keys' K and V rows (B operand of S, dP)
+  bf16x8 kf[NCW], vf[NCW];
+  {
+    const long off = (((long)b * Sk + jc) * p.Hkv + hk) * D + colofs;
+    const bf16* krow = reinterpret_cast<const bf16*>(p.k) + off;
+    const bf16* vrow = reinterpret_cast<const bf16*>(p.v) + off;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) {
+      kf[c] = *reinterpret_cast<const bf16x8*>(krow + 8 * c + 32 * g);
+      vf[c] = *reinterpret_cast<const bf16x8*>(vrow + 8 * c + 32 * g);
+    }
+  }
+
+  int lo_j = 0, hi_j = 0;
+  if (j < Sk) queries_of(p.mask, b, j, lo_j, hi_j);
+  const int jlast = min(k0 + BNK, Sk) - 1;
+  int lo_first, hi_first, lo_last, hi_last;
+  queries_of(p.mask, b, k0, lo_first, hi_first);
+  queries_of(p.mask, b, jlast, lo_last, hi_last);
+  const bool keys_full = (k0 + BNK <= Sk);
+  const int qbeg = (lo_first / BMQ) * BMQ;
+  const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
+  const int nitems = GS * nqt;
+
+  f32x4 kacc[NOB], vacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) { kacc[ob] = f32x4{}; vacc[ob] = f32x4{}; }
+
+  auto head_of = [&](int it) { return hk * p.G + split * GS + it % GS; };
+  auto q0_of = [&](int it) { return qbeg + (nqt - 1 - it / GS) * BMQ; };
+  auto fetch = [&](int it, bf16* nQ, bf16* nO) {
+    const long hoff = ((long)b * Sq * p.Hq + head_of(it)) * D;
+    const int q0 = q0_of(it);
+    load_tile<BMQ, D, NT, false, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
+    load_tile<BMQ, D, NT, false, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
+  };
+  // lse and delta of this lane's queries 16 qb + 4g + e of item it, raw
+  float nl[8], nd[8];
+  auto get_stats = [&](int it) {
+    const long row = ((long)b * p.Hq + head_of(it)) * Sq;
+    const int q0 = q0_of(it);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int q = q0 + 16 * (x >> 2) + 4 * g + (x & 3);
+      const long li = row + min(q, Sq - 1);
+      nl[x] = q < Sq ? p.lse[li] : -INFINITY;
+      nd[x] = p.delta[li];
+    }
+  };
+
+  if (nitems > 0) {
+    fetch(0, sQ0, sO0);
+    get_stats(0);
+  }
+  wait_loads();
+  __syncthreads();
+
+  auto step = [&](const bf16* tQ, const bf16* tO, bf16* nQ, bf16* nO, int it) {
+    const bool more = it + 1 < nitems;
+    const int hq = head_of(it);
+    const int q0 = q0_of(it);
+    // this item's stats (log2 units, folded with the cap's constant), then
+    // the next item's loads
+    float lc[8], md[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      lc[x] = nl[x] != -INFINITY ? (CAP ? p.cl2 : 0.0f) - nl[x] * kLog2e : -INFINITY;
+      md[x] = -nd[x];
+    }
+    if (more) {
+      fetch(it + 1, nQ, nO);
+      get_stats(it + 1);
+    }
+
+    // partial S and dP over this slice's columns
+    f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};   // S qb 0, 1; dP qb 0, 1
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        mma16(acc[qb], fo.frag(tQ, 16 * qb, 4 * sl + c), kf[c]);
+        mma16(acc[2 + qb], fo.frag(tO, 16 * qb, 4 * sl + c), vf[c]);
+      }
+    }
+    ATL_READ_AHEAD(8, 1, 4 * NCW);
+    group_sum4<4>(sX, w, lane, acc);
+
+    auto grads = [&](auto masked) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 4 * qb + e;
+          float l = lc[x];
+          if constexpr (decltype(masked)::value) {
+            const int qi = q0 + 16 * qb + 4 * g + e;
+            l = (qi >= lo_j && qi < hi_j) ? l : -INFINITY;
+          }
+          float gg;
+          const float pv = prob_fast<CAP, false>(acc[qb][e], 0.0f, lk, l, gg);
+          acc[qb][e] = pv;
+          acc[2 + qb][e] = pv * (acc[2 + qb][e] + md[x]) * gg;
+        }
+      }
+    };
+    if (keys_full && q0 >= lo_last && q0 + BMQ <= hi_first) grads(bool_c<false>{});
+    else grads(bool_c<true>{});
+    const bf16x8 pf = pack8(acc[0], acc[1]);
+    const bf16x8 uf = pack8(acc[2], acc[3]);
+    // this key group's half of the dU block (32-key block k0, query block q0)
+    if (p.du && sl == 0) {
+      bf16* blk = reinterpret_cast<bf16*>(p.du) +
+                  ((((long)b * p.Hq + hq) * p.nkb32 + (k0 >> 5)) * p.nqb32 + (q0 >> 5)) * 1024 + kg * 512 + lane * 8;
+      __builtin_nontemporal_store(uf, reinterpret_cast<bf16x8*>(blk));
+    }
+
+    // dV^T += dO^T P, dK^T += Q^T dU over this slice's columns, transposing
+    // reads two column blocks ahead of their MFMAs
+    constexpr int TRA = 2;
+    bf16x8 tro[TRA + 1], trq[TRA + 1];
+#pragma unroll
+    for (int a = 0; a < TRA; ++a) {
+      tro[a] = fo.frag_tr(tO + colofs, 0, a);
+      trq[a] = fo.frag_tr(tQ + colofs, 0, a);
+    }
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      if (ob + TRA < NOB) {
+        tro[(ob + TRA) % (TRA + 1)] = fo.frag_tr(tO + colofs, 0, ob + TRA);
+        trq[(ob + TRA) % (TRA + 1)] = fo.frag_tr(tQ + colofs, 0, ob + TRA);
+      }
+      mma16(vacc[ob], tro[ob % (TRA + 1)], pf);
+      mma16(kacc[ob], trq[ob % (TRA + 1)], uf);
+    }
+
+    wait_loads();
+    __syncthreads();
+  };
+  for (int it = 0; it < nitems; it += 2) {
+    step(sQ0, sO0, sQ1, sO1, it);
+    if (it + 1 < nitems) step(sQ1, sO1, sQ0, sO0, it + 1);
+  }
+
+  if (j < Sk && p.hsplit > 1) {
+    const long nel = (long)gridDim.z * Sk * p.Hkv * D;
+    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    float* kp = p.dkv_part + (long)split * nel + off;
+    float* vp = p.dkv_part + (long)(p.hsplit + split) * nel + off;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      *reinterpret_cast<f32x4*>(kp + colofs + 16 * ob + 4 * g) = kacc[ob];
+      *reinterpret_cast<f32x4*>(vp + colofs + 16 * ob + 4 * g) = vacc[ob];
+    }
+  } else if (j < Sk) {
+    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    bf16* krow = reinterpret_cast<bf16*>(p.dk) + off;
+    bf16* vrow = reinterpret_cast<bf16*>(p.dv) + off;
+    const float ks = p.scale * kGrad4<CAP>;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+      bf16x4 kv, vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[e] = (bf16)(kacc[ob][e] * ks);
+        vv[e] = (bf16)vacc[ob][e];
+      }
+      *reinterpret_cast<bf16x4*>(krow + colofs + 16 * ob + 4 * g) = kv;
+      *reinterpret_cast<bf16x4*>(vrow + colofs + 16 * ob + 4 * g) = vv;
+    }
+  }
+}
+
+}  // namespace atl
