@@ -200,11 +200,14 @@ size_t pre_blocks(const attn_args* a) { return ((size_t)a->Sq + kPreRows - 1) / 
 
 size_t fwd_ws(const attn_args* a) { return seg_bytes(a); }
 
-// The bf16 kernels for head dims 64/128/256 can hand dU from the dk/dv
+// The bf16 kernels for head dims 64/128/256/512 can hand dU from the dk/dv
 // kernel to the dq kernel through the workspace (bf16, 32-key x 32-query
 // blocks), so that dq needs neither exponentials nor a second pass over the
 // logits.  The buffer holds every block of [B, Hq, Sq, Sk]; ATTN_DQ_AUTO
-// takes it while it stays within kDuAutoBytes, else dq recomputes.
+// takes it for D >= 128 while it stays within kDuAutoBytes, else dq
+// recomputes (at D = 64 the round trip of 2 bytes per pair costs more than
+// recomputing 4 * 64 flop of it: measured 1.15 against 1.10 ms per step on
+// B=1, Hq=64, Hkv=8, S=4096 with a learnable sink).
 constexpr size_t kDuAutoBytes = (size_t)16 << 30;
 
 size_t du_raw_bytes(const attn_args* a) {
@@ -213,7 +216,7 @@ size_t du_raw_bytes(const attn_args* a) {
 
 bool du_path(const attn_args* a) {
   if (!du_supported(a) || a->dq_mode == ATTN_DQ_RECOMPUTE) return false;
-  return a->dq_mode == ATTN_DQ_DU_BLOCKS || du_raw_bytes(a) <= kDuAutoBytes;
+  return a->dq_mode == ATTN_DQ_DU_BLOCKS || (a->D >= 128 && du_raw_bytes(a) <= kDuAutoBytes);
 }
 
 // With a bias, the bf16 dk/dv kernel of D = 128 and 256 writes the whole of

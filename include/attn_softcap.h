@@ -88,11 +88,12 @@ typedef enum attn_sink_mode {
  *    dq kernel through the workspace as bf16 blocks of 32 keys x 32 queries,
  *    B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB (4 GiB at B=4, Hq=32, S=4096; only
  *    the visible blocks are written and read).  bf16 with D = 64, 128 or 256
- *    only (with a bias also Sk % 8 == 0); ATTN_UNSUPPORTED otherwise.
+ *    (with a bias also Sk % 8 == 0), or D = 512 without a bias;
+ *    ATTN_UNSUPPORTED otherwise.
  *  - ATTN_DQ_RECOMPUTE: the dq kernel recomputes the logits, probabilities
  *    and dP itself; the workspace stays O(B*Hq*Sq).
- *  - ATTN_DQ_AUTO (0): DU_BLOCKS where supported and its buffer is at most
- *    16 GiB, else RECOMPUTE.
+ *  - ATTN_DQ_AUTO (0): DU_BLOCKS where supported, D >= 128 and its buffer
+ *    is at most 16 GiB, else RECOMPUTE (at D = 64 recomputing is faster).
  * The [b, h, q, kv] materialisation and its memory cost are what the MaxText
  * commit quoted on "Support logits soft-capping in the Pallas-Triton
  * attention VJP" weighs (12.5 against 3.3 GiB at 8k tokens); the blocks here

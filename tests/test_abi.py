@@ -79,7 +79,7 @@ BAD = {
     "misaligned_bias": (dict(bias=0x2008), 1, "aligned"),
     "bad_dq_mode": (dict(dq_mode=3), 1, "dq_mode"),
     "du_blocks_fp32": (dict(dtype=1, dq_mode=1), 2, "DU_BLOCKS"),
-    "du_blocks_d512": (dict(D=512, dq_mode=1), 2, "DU_BLOCKS"),
+    "du_blocks_d512_bias": (dict(D=512, dq_mode=1, bias=0x2000), 2, "DU_BLOCKS"),
     "du_blocks_ragged_bias": (dict(Sq=250, Sk=250, bias=0x2000, dq_mode=1), 2, "DU_BLOCKS"),
     "keys_empty": (dict(Sk=0, causal=0), 2, "Sk == 0"),
 }
@@ -147,8 +147,8 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 
 def test_bwd_workspace_carries_du_blocks_by_dq_mode():
-    """bf16 with D = 64/128/256: B*Hq*ceil(Sk/32)*ceil(Sq/32) blocks of 2 KiB for dU with
-    dq_mode auto (while that stays within 16 GiB) or du_blocks; none with recompute."""
+    """bf16: B*Hq*ceil(Sk/32)*ceil(Sq/32) blocks of 2 KiB for dU with dq_mode du_blocks, and
+    with auto at D >= 128 while that stays within 16 GiB; none with recompute."""
     L = A.lib()
     a = _args()                       # bf16, B=2, Hq=8, S=256, D=128, dq_mode auto
     with_du = L.attn_bwd_workspace_size(ctypes.byref(a))
@@ -163,6 +163,14 @@ def test_bwd_workspace_carries_du_blocks_by_dq_mode():
     rec = L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **big)))
     forced = L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=1, **big)))
     assert auto == rec and forced - rec == 8 * 64 * 512 * 512 * 2048
+    d64 = dict(D=64)
+    assert L.attn_bwd_workspace_size(ctypes.byref(_args(**d64))) == \
+        L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **d64)))
+    assert L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=1, **d64))) - \
+        L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **d64))) == 2 * 8 * 8 * 8 * 2048
+    d512 = dict(D=512)
+    assert L.attn_bwd_workspace_size(ctypes.byref(_args(**d512))) - \
+        L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **d512))) == 2 * 8 * 8 * 8 * 2048
     f32 = _args(dtype=1)
     g32 = _args(dtype=1, D=256)
     # the bf16 run also carries the fp32 dK/dV partials of its head split

@@ -74,22 +74,29 @@ BIAS_FAST = {
 }
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D,dq_mode", [(64, "auto"), (64, "du_blocks"), (128, "auto"), (256, "auto")])
 @pytest.mark.parametrize("feat", list(BIAS_FAST))
-def test_bias_on_the_fast_path(D, feat):
+def test_bias_on_the_fast_path(D, dq_mode, feat):
     kw = dict(dtype="bf16", D=D, B=2, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0)
     kw.update(BIAS_FAST[feat])
-    _check(case(**kw))
+    _check(case(**kw), dq_mode=dq_mode)
 
 
-@pytest.mark.parametrize("D", [128, 64, 256])
+# dq_mode "auto" takes the dU hand-off at D >= 128 and recomputes at D = 64;
+# each D also runs the other way here (D = 256 and 512 recompute through the
+# generic dq kernel)
+OTHER_DQ_MODE = {64: "du_blocks", 128: "recompute", 256: "recompute", 512: "recompute"}
+
+
+@pytest.mark.parametrize("D", [128, 64, 256, 512])
 @pytest.mark.parametrize("feat", list(FEATURES))
-def test_feature_matrix_dq_recomputed(D, feat):
-    """bf16 with dq_mode "recompute": dq recomputes the probabilities instead of
-    reading the dU blocks (D = 256 through the generic dq kernel)."""
+def test_feature_matrix_other_dq_mode(D, feat):
     kw = dict(dtype="bf16", D=D, B=2, S=203, Hq=4, Hkv=2)
     kw.update(FEATURES[feat])
-    _check(case(**kw), dq_mode="recompute")
+    mode = OTHER_DQ_MODE[D]
+    if mode == "du_blocks" and kw.get("bias"):
+        pytest.skip("the dU hand-off needs Sk % 8 == 0 with a bias (S = 203 here); see the fast-path bias tests")
+    _check(case(**kw), dq_mode=mode)
 
 
 @pytest.mark.parametrize("D", [64, 128, 256, 512])

@@ -34,7 +34,7 @@ REPEAT = {
 @pytest.mark.parametrize("name", list(REPEAT))
 def test_two_runs_give_the_same_bits(name):
     c = case(**REPEAT[name])
-    mode = "recompute" if name.endswith("recompute") else "auto"
+    mode = "recompute" if name.endswith("recompute") else ("du_blocks" if name.endswith("_du") else "auto")
     print(f"repeat {name}: dq_mode={mode}", flush=True)
     a = run_gpu(c, dq_mode=mode)
     b = run_gpu(c, dq_mode=mode)
