@@ -27,13 +27,20 @@ each line can be checked against the sources by eye:
   query rows.  Off-by-one softmax is that column with its logit fixed at 0.
 * The bias is added after the ``1/sqrt(D)`` scale (``post_scale_bias`` in
   the Greptile review "Offset Corrupts Bias Gradient Shape" on that page).
+* "Support logits soft-capping in the Pallas-Triton attention VJP", PR
+  description: besides segment ids, a packed batch can be given as
+  ``k_start`` (per query, the first key it may see) or as a dense boolean
+  mask; both only remove pairs, on top of the other masks.
 
 Readings taken where the pages are silent (each one also listed in the
 design notes):  scale ``tau = 1/sqrt(D)`` unless given; the sink logit is
 neither scaled nor capped; one sink logit per *query* head; a causal
 sliding window of ``W`` keeps ``0 <= i-j < W`` (``|i-j| < W`` without
-causal); segment visibility is equality of segment ids; a row that sees no
-key and has no sink gets ``out = 0``, ``lse = -inf`` and zero gradients.
+causal); segment visibility is equality of segment ids; ``k_start[i]`` is
+the first key query ``i`` may see (keys ``j >= k_start[i]``) and a dense
+mask entry True means visible, both intersected with the other masks; a row
+that sees no key and has no sink gets ``out = 0``, ``lse = -inf`` and zero
+gradients.
 """
 from __future__ import annotations
 
@@ -47,11 +54,13 @@ _f64 = np.float64
 
 def visibility(Sq: int, Sk: int, causal: bool, window: int,
                seg_q: Optional[np.ndarray] = None, seg_k: Optional[np.ndarray] = None,
-               rows: Optional[slice] = None) -> np.ndarray:
+               rows: Optional[slice] = None, k_start: Optional[np.ndarray] = None,
+               dense: Optional[np.ndarray] = None) -> np.ndarray:
     """Boolean [rows, Sk]: may query ``i`` see key ``j``?
 
     visible = same segment  and  (not causal or j <= i)  and
-              (W <= 0 or (0 <= i-j < W if causal else |i-j| < W)).
+              (W <= 0 or (0 <= i-j < W if causal else |i-j| < W))  and
+              (no k_start or j >= k_start[i])  and  (no dense mask or dense[i, j]).
     """
     rows = rows if rows is not None else slice(0, Sq)
     i = np.arange(Sq)[rows][:, None]
@@ -65,6 +74,10 @@ def visibility(Sq: int, Sk: int, causal: bool, window: int,
         vis &= (i - j < window) if causal else (np.abs(i - j) < window)
     if seg_q is not None:
         vis &= seg_q[rows][:, None] == seg_k[None, :]
+    if k_start is not None:
+        vis &= j >= np.asarray(k_start)[rows][:, None]
+    if dense is not None:
+        vis &= np.asarray(dense, dtype=bool)[rows]
     return vis
 
 
@@ -105,11 +118,12 @@ def _softmax_rows(s, vis, sink_logit):
 
 
 def group_forward(q, k, v, *, scale=None, softcap=0.0, causal=False, window=0,
-                  bias=None, seg=None, sink=None, row_block=1024):
+                  bias=None, seg=None, sink=None, k_start=None, dense=None, row_block=1024):
     """Forward pass of one (batch row, KV head) group.
 
     q [Sq,G,D]; k, v [Sk,D]; bias [G,Sq,Sk] or None; seg [S] segment ids or
-    None; sink [G] sink logits (off-by-one: zeros) or None.
+    None; sink [G] sink logits (off-by-one: zeros) or None; k_start [Sq] or
+    None; dense [Sq,Sk] boolean mask or None.
     Returns out [Sq,G,D] and lse [G,Sq] in fp64.
     """
     q, k, v = (np.asarray(x, dtype=_f64) for x in (q, k, v))
@@ -120,7 +134,7 @@ def group_forward(q, k, v, *, scale=None, softcap=0.0, causal=False, window=0,
     lse = np.zeros((G, Sq), dtype=_f64)
     for r0 in range(0, Sq, row_block):
         rows = slice(r0, min(Sq, r0 + row_block))
-        vis = visibility(Sq, Sk, causal, window, seg, seg, rows)
+        vis = visibility(Sq, Sk, causal, window, seg, seg, rows, k_start, dense)
         for g in range(G):
             brow = None if bias is None else np.asarray(bias[g, rows], dtype=_f64)
             s, _ = _logits(q[rows, g], k, scale, brow, softcap)
@@ -131,7 +145,8 @@ def group_forward(q, k, v, *, scale=None, softcap=0.0, causal=False, window=0,
 
 
 def group_backward(q, k, v, dout, *, scale=None, softcap=0.0, causal=False, window=0,
-                   bias=None, seg=None, sink=None, want_dbias=None, row_block=1024):
+                   bias=None, seg=None, sink=None, k_start=None, dense=None, want_dbias=None,
+                   row_block=1024):
     """Backward pass of one (batch row, KV head) group, by recomputation.
 
     Returns dq [Sq,G,D], dk [Sk,D], dv [Sk,D], dbias [G,Sq,Sk] (or None) and
@@ -150,7 +165,7 @@ def group_backward(q, k, v, dout, *, scale=None, softcap=0.0, causal=False, wind
     dsink = np.zeros(G, dtype=_f64) if sink is not None else None
     for r0 in range(0, Sq, row_block):
         rows = slice(r0, min(Sq, r0 + row_block))
-        vis = visibility(Sq, Sk, causal, window, seg, seg, rows)
+        vis = visibility(Sq, Sk, causal, window, seg, seg, rows, k_start, dense)
         for g in range(G):
             brow = None if bias is None else np.asarray(bias[g, rows], dtype=_f64)
             s, f = _logits(q[rows, g], k, scale, brow, softcap)
@@ -181,7 +196,7 @@ def segments_from_cu_seqlens(cu_seqlens, total: int) -> np.ndarray:
     return seg
 
 
-def _prepare(q, k, v, bias, segment_ids, cu_seqlens):
+def _prepare(q, k, v, bias, segment_ids, cu_seqlens, k_start=None, mask=None):
     if cu_seqlens is not None:
         if segment_ids is not None:
             raise ValueError("give segment_ids or cu_seqlens, not both")
@@ -190,8 +205,10 @@ def _prepare(q, k, v, bias, segment_ids, cu_seqlens):
         q, k, v = q[None], k[None], v[None]
         if bias is not None:
             bias = bias[None]
-        return q, k, v, bias, segment_ids, True
-    return q, k, v, bias, segment_ids, False
+        k_start = None if k_start is None else np.asarray(k_start)[None]
+        mask = None if mask is None else np.asarray(mask)[None]
+        return q, k, v, bias, segment_ids, k_start, mask, True
+    return q, k, v, bias, segment_ids, k_start, mask, False
 
 
 def _groups(B, Hkv, groups):
@@ -199,15 +216,18 @@ def _groups(B, Hkv, groups):
 
 
 def attention_forward(q, k, v, *, softcap=0.0, causal=False, window=0, scale=None,
-                      bias=None, segment_ids=None, cu_seqlens=None, sink=None, groups=None):
+                      bias=None, segment_ids=None, cu_seqlens=None, sink=None, k_start=None,
+                      mask=None, groups=None):
     """Whole forward in BSHD layout (THD when ``cu_seqlens`` is given).
 
     q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (THD: [T,H,D]); bias [B,Hq,Sq,Sk];
-    segment_ids [B,S]; sink [Hq] (zeros for off-by-one).  ``groups`` limits
-    the work to a list of (b, kv_head) pairs; other entries stay NaN.
-    Returns out (as q's shape) and lse [B,Hq,Sq] ([Hq,T] for THD), fp64.
+    segment_ids [B,S]; sink [Hq] (zeros for off-by-one); k_start [B,Sq]
+    (THD: [T]); mask [B,Sq,Sk] boolean, True = visible (THD: [T,T]).
+    ``groups`` limits the work to a list of (b, kv_head) pairs; other entries
+    stay NaN.  Returns out (as q's shape) and lse [B,Hq,Sq] ([Hq,T] for
+    THD), fp64.
     """
-    q, k, v, bias, seg, thd = _prepare(q, k, v, bias, segment_ids, cu_seqlens)
+    q, k, v, bias, seg, k_start, mask, thd = _prepare(q, k, v, bias, segment_ids, cu_seqlens, k_start, mask)
     B, Sq, Hq, D = q.shape
     Hkv = k.shape[2]
     if Hq % Hkv:
@@ -221,7 +241,9 @@ def attention_forward(q, k, v, *, softcap=0.0, causal=False, window=0, scale=Non
                              causal=causal, window=window,
                              bias=None if bias is None else bias[b, hs],
                              seg=None if seg is None else seg[b],
-                             sink=None if sink is None else sink[hs])
+                             sink=None if sink is None else sink[hs],
+                             k_start=None if k_start is None else k_start[b],
+                             dense=None if mask is None else mask[b])
         out[b, :, hs] = o
         lse[b, hs] = l
     if thd:
@@ -230,14 +252,14 @@ def attention_forward(q, k, v, *, softcap=0.0, causal=False, window=0, scale=Non
 
 
 def attention_backward(q, k, v, dout, *, softcap=0.0, causal=False, window=0, scale=None,
-                       bias=None, segment_ids=None, cu_seqlens=None, sink=None,
-                       want_dbias=None, groups=None):
+                       bias=None, segment_ids=None, cu_seqlens=None, sink=None, k_start=None,
+                       mask=None, want_dbias=None, groups=None):
     """Whole backward: dq, dk, dv, dbias (or None), dsink (or None), fp64.
 
     dsink sums over every batch row and query row that ``groups`` covers.
     """
     thd = cu_seqlens is not None
-    q, k, v, bias, seg, _ = _prepare(q, k, v, bias, segment_ids, cu_seqlens)
+    q, k, v, bias, seg, k_start, mask, _ = _prepare(q, k, v, bias, segment_ids, cu_seqlens, k_start, mask)
     if thd:
         dout = dout[None]
     B, Sq, Hq, D = q.shape
@@ -255,7 +277,9 @@ def attention_backward(q, k, v, dout, *, softcap=0.0, causal=False, window=0, sc
                            softcap=softcap, causal=causal, window=window,
                            bias=None if bias is None else bias[b, hs],
                            seg=None if seg is None else seg[b],
-                           sink=None if sink is None else sink[hs], want_dbias=want_dbias)
+                           sink=None if sink is None else sink[hs],
+                           k_start=None if k_start is None else k_start[b],
+                           dense=None if mask is None else mask[b], want_dbias=want_dbias)
         dq[b, :, hs], dk[b, :, h], dv[b, :, h] = r[0], r[1], r[2]
         if dbias is not None:
             dbias[b, hs] = r[3]

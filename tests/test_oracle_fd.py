@@ -15,7 +15,8 @@ import pytest
 from oracle import attention_backward, attention_forward
 
 
-def _case(causal=True, window=5, segments=True, bias=True, sink="learnable", softcap=3.0, seed=0):
+def _case(causal=True, window=5, segments=True, bias=True, sink="learnable", softcap=3.0, seed=0,
+          k_start=False, dense=False):
     rng = np.random.default_rng(seed)
     B, S, Hq, Hkv, D = 2, 11, 4, 2, 6
     q = rng.standard_normal((B, S, Hq, D)) * 3.0
@@ -27,6 +28,12 @@ def _case(causal=True, window=5, segments=True, bias=True, sink="learnable", sof
         kw["segment_ids"] = np.array([[0] * 4 + [1] * 7, [0] * 6 + [1] * 3 + [2] * 2])
     if bias:
         kw["bias"] = rng.standard_normal((B, Hq, S, S)) * 0.7
+    if k_start:
+        kw["k_start"] = np.array([[0, 0, 1, 1, 3, 3, 3, 5, 6, 6, 8], [0, 1, 1, 2, 2, 4, 4, 4, 7, 9, 9]])
+    if dense:
+        m = rng.random((B, S, S)) < 0.5
+        m[:, np.arange(S), np.arange(S)] = True
+        kw["mask"] = m
     if sink == "learnable":
         kw["sink"] = rng.standard_normal(Hq) * 2.0
     elif sink == "off_by_one":
@@ -63,6 +70,8 @@ CASES = {
     "plain_causal_cap": dict(window=0, segments=False, bias=False, sink=None),
     "nocausal_window_offbyone": dict(causal=False, window=4, segments=False, sink="off_by_one"),
     "nocap_sink_bias": dict(softcap=0.0, window=0),
+    "k_start_cap_bias_sink": dict(window=0, segments=False, k_start=True),
+    "dense_mask_cap_bias_sink": dict(causal=False, window=0, segments=False, dense=True),
 }
 
 

@@ -145,3 +145,80 @@ def test_custom_scale_is_used():
     ref = _sdpa(q, k, v, mask, scale=0.3)
     out, _ = attention_forward(q, k, v, causal=True, scale=0.3)
     assert _rel(out, ref) < 1e-12
+
+
+# ---- the two packed variants of the tokamax PR description: k_start and a dense boolean mask
+
+def _kstart_loop_mask(S, causal, k_start):
+    """Visibility from k_start written with loops: key j visible to query i iff j >= k_start[i]."""
+    B = k_start.shape[0]
+    m = np.zeros((B, 1, S, S), dtype=bool)
+    for b in range(B):
+        for i in range(S):
+            for j in range(S):
+                m[b, 0, i, j] = (j >= k_start[b, i]) and (not causal or j <= i)
+    return m
+
+
+def test_k_start_equals_sdpa_with_its_loop_mask():
+    q, k, v, do, rng = _inputs()
+    S = q.shape[1]
+    k_start = np.sort(rng.integers(0, S, size=(2, S)), axis=1)      # non-decreasing, one row per batch
+    got = attention_backward(q, k, v, do, causal=True, k_start=k_start)
+    out, _ = attention_forward(q, k, v, causal=True, k_start=k_start)
+    ref = _sdpa(q, k, v, _kstart_loop_mask(S, True, k_start), grad=True, do=do)
+    # rows with no visible key are NaN in SDPA; compare the rows that see something
+    ok = np.array([[k_start[b, i] <= i for i in range(S)] for b in range(2)])
+    for b in range(2):
+        r = ok[b]
+        assert _rel(out[b, r], ref[0][b, r]) < 1e-12
+        assert _rel(got[0][b, r], ref[1][b, r]) < 1e-12
+    assert _rel(got[1], ref[2]) < 1e-12 and _rel(got[2], ref[3]) < 1e-12
+
+
+def test_dense_mask_equals_sdpa_with_the_same_boolean_mask():
+    q, k, v, do, rng = _inputs(S=29)
+    S = q.shape[1]
+    dense = rng.random((2, S, S)) < 0.6
+    dense[:, np.arange(S), np.arange(S)] = True          # every row sees at least its own key
+    got = attention_backward(q, k, v, do, mask=dense)
+    out, _ = attention_forward(q, k, v, mask=dense)
+    ref = _sdpa(q, k, v, dense[:, None], grad=True, do=do)
+    assert _rel(out, ref[0]) < 1e-12
+    for a, b in zip(got[:3], ref[1:4]):
+        assert _rel(a, b) < 1e-12
+
+
+def _packings(S, rng, n=4):
+    """One packing (segment starts per row) written three ways: ids, k_start, dense."""
+    B = 2
+    seg = np.zeros((B, S), dtype=np.int64)
+    for b in range(B):
+        for c in np.sort(rng.choice(np.arange(1, S), n - 1, replace=False)):
+            seg[b, c:] += 1
+    # k_start: the first token of each token's segment, found by scanning back
+    k_start = np.zeros((B, S), dtype=np.int64)
+    for b in range(B):
+        for i in range(S):
+            x = i
+            while x > 0 and seg[b, x - 1] == seg[b, i]:
+                x -= 1
+            k_start[b, i] = x
+    dense = seg[:, :, None] == seg[:, None, :]
+    return seg, k_start, dense
+
+
+@pytest.mark.parametrize("softcap", [0.0, 5.0])
+def test_segment_ids_k_start_and_dense_mask_agree_to_every_digit(softcap):
+    """Causal packing as segment ids, as k_start and as a dense mask: the same outputs
+    and gradients, bit for bit (the PR description's 'agree to every digit')."""
+    q, k, v, do, rng = _inputs(S=41, seed=3)
+    seg, k_start, dense = _packings(41, rng)
+    kw = dict(causal=True, softcap=softcap, sink=rng.standard_normal(6))
+    a = attention_forward(q, k, v, segment_ids=seg, **kw) + attention_backward(q, k, v, do, segment_ids=seg, **kw)
+    b = attention_forward(q, k, v, k_start=k_start, **kw) + attention_backward(q, k, v, do, k_start=k_start, **kw)
+    c = attention_forward(q, k, v, mask=dense, **kw) + attention_backward(q, k, v, do, mask=dense, **kw)
+    for x, y, z in zip(a, b, c):
+        if x is None:
+            continue
+        assert np.array_equal(x, y) and np.array_equal(x, z)
