@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <climits>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -117,6 +118,52 @@ __global__ __launch_bounds__(256) void seg_from_cu_kernel(const int* cu, int nse
   seg_hi[t] = max(min(e, T), t + 1);
 }
 
+// k_start (first visible key per query, non-decreasing along a row): q_lo =
+// its running maximum along the row (so that the bounds stay non-decreasing
+// for any input; equal to k_start where it does not decrease), raised to the
+// segment-run start where segments are given.  One workgroup per batch row.
+__global__ __launch_bounds__(1024) void kstart_lo_kernel(const int* k_start, const int* seg_lo, int* q_lo, int Sq) {
+  __shared__ int wtot[16];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int carry = INT_MIN;
+  for (int c0 = 0; c0 < Sq; c0 += 1024) {
+    const int t = c0 + tid;
+    int f = INT_MIN;
+    if (t < Sq) f = k_start[(long)b * Sq + t];
+    f = wave_scan_max(f);
+    if (lane == 63) wtot[w] = f;
+    __syncthreads();
+    int pre = carry;
+    for (int x = 0; x < w; ++x) pre = max(pre, wtot[x]);
+    int lo = max(f, pre);
+    if (t < Sq) {
+      if (seg_lo) lo = max(lo, seg_lo[(long)b * Sq + t]);
+      q_lo[(long)b * Sq + t] = lo;
+    }
+    int last = carry;
+    for (int x = 0; x < 16; ++x) last = max(last, wtot[x]);
+    __syncthreads();
+    carry = last;
+  }
+}
+
+// With k_start: the queries that see key j end at the first query whose
+// (non-decreasing) q_lo passes j, cut to the segment run's end.
+__global__ __launch_bounds__(256) void kstart_hi_kernel(const int* q_lo, const int* seg_hi, int* k_hi, int Sq, int Sk) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= Sk) return;
+  const int* row = q_lo + (long)b * Sq;
+  int lo = 0, hi = Sq;
+  while (lo < hi) {  // first query with q_lo > j
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] <= j) lo = mid + 1; else hi = mid;
+  }
+  if (seg_hi) lo = min(lo, seg_hi[(long)b * Sk + j]);
+  k_hi[(long)b * Sk + j] = lo;
+}
+
 // Scratch of attn_bwd_noalloc: the backward's workspace (segment runs,
 // delta, sink-gradient partials, split partials, dU blocks when they fit) for
 // callers that cannot allocate.  One copy per GPU the library runs on, held
@@ -178,6 +225,7 @@ attn_status validate(const attn_args* a) {
     if (a->nseq < 1) return fail(ATTN_INVALID_ARGUMENT, "cu_seqlens needs nseq >= 1");
   }
   if (has_segments(a) && a->Sq != a->Sk) return fail(ATTN_INVALID_ARGUMENT, "packed segments need Sq == Sk");
+  if (a->mask && ((uintptr_t)a->mask & 15) != 0) return fail(ATTN_INVALID_ARGUMENT, "mask must be 16-byte aligned");
   if (a->causal && a->Sq != a->Sk) return fail(ATTN_UNSUPPORTED, "causal masking needs Sq == Sk");
   const long long maxi = 2147483647LL;
   if ((long long)a->B * a->Sq > maxi || (long long)a->B * a->Sk > maxi)
@@ -194,7 +242,13 @@ attn_status validate(const attn_args* a) {
   return ATTN_OK;
 }
 
-size_t seg_bytes(const attn_args* a) { return has_segments(a) ? 2 * align_up((size_t)a->B * a->Sq * sizeof(int)) : 0; }
+// Per-token visibility bounds in the workspace: the segment runs (two
+// [B*Sq] arrays) and, with k_start, q_lo [B*Sq] and k_hi [B*Sk].
+size_t seg_bytes(const attn_args* a) {
+  size_t n = has_segments(a) ? 2 * align_up((size_t)a->B * a->Sq * sizeof(int)) : 0;
+  if (a->k_start) n += align_up((size_t)a->B * a->Sq * sizeof(int)) + align_up((size_t)a->B * a->Sk * sizeof(int));
+  return n;
+}
 
 size_t pre_blocks(const attn_args* a) { return ((size_t)a->Sq + kPreRows - 1) / kPreRows; }
 
@@ -260,28 +314,42 @@ size_t bwd_ws(const attn_args* a) {
 
 const TypeOps& ops(const attn_args* a) { return a->dtype == ATTN_BF16 ? ops_bf16() : ops_f32(); }
 
-hipError_t prep_segments(const attn_args* a, char*& ws, Mask& m, hipStream_t s) {
-  m.seg_lo = nullptr;
-  m.seg_hi = nullptr;
-  if (!has_segments(a)) return hipSuccess;
-  const size_t n = (size_t)a->B * a->Sq;
-  int* lo = reinterpret_cast<int*>(ws);
-  ws += align_up(n * sizeof(int));
-  int* hi = reinterpret_cast<int*>(ws);
-  ws += align_up(n * sizeof(int));
-  if (a->segment_ids) {
-    seg_from_ids_kernel<<<a->B, 1024, 0, s>>>(a->segment_ids, lo, hi, a->Sq);
-  } else {
-    seg_from_cu_kernel<<<(a->Sq + 255) / 256, 256, 0, s>>>(a->cu_seqlens, a->nseq, lo, hi, a->Sq);
+// Lays the bounds out in the workspace (advancing ws) and, with launch,
+// computes them on stream s.
+hipError_t prep_bounds(const attn_args* a, char*& ws, Mask& m, hipStream_t s, bool launch) {
+  m.q_lo = m.q_hi = m.k_lo = m.k_hi = nullptr;
+  const size_t nq = align_up((size_t)a->B * a->Sq * sizeof(int)), nk = align_up((size_t)a->B * a->Sk * sizeof(int));
+  int* seg_lo = nullptr;
+  int* seg_hi = nullptr;
+  if (has_segments(a)) {
+    seg_lo = reinterpret_cast<int*>(ws);
+    seg_hi = reinterpret_cast<int*>(ws + nq);
+    ws += 2 * nq;
+    if (launch) {
+      if (a->segment_ids) seg_from_ids_kernel<<<a->B, 1024, 0, s>>>(a->segment_ids, seg_lo, seg_hi, a->Sq);
+      else seg_from_cu_kernel<<<(a->Sq + 255) / 256, 256, 0, s>>>(a->cu_seqlens, a->nseq, seg_lo, seg_hi, a->Sq);
+    }
+    m.q_lo = m.k_lo = seg_lo;
+    m.q_hi = m.k_hi = seg_hi;
   }
-  m.seg_lo = lo;
-  m.seg_hi = hi;
-  return hipGetLastError();
+  if (a->k_start) {
+    int* q_lo = reinterpret_cast<int*>(ws);
+    int* k_hi = reinterpret_cast<int*>(ws + nq);
+    ws += nq + nk;
+    if (launch) {
+      kstart_lo_kernel<<<a->B, 1024, 0, s>>>(a->k_start, seg_lo, q_lo, a->Sq);
+      if (a->Sk > 0) kstart_hi_kernel<<<dim3((a->Sk + 255) / 256, a->B), 256, 0, s>>>(q_lo, seg_hi, k_hi, a->Sq, a->Sk);
+    }
+    m.q_lo = q_lo;
+    m.k_hi = k_hi;
+  }
+  return launch ? hipGetLastError() : hipSuccess;
 }
 
 Mask base_mask(const attn_args* a) {
   Mask m;
-  m.seg_lo = m.seg_hi = nullptr;
+  m.q_lo = m.q_hi = m.k_lo = m.k_hi = nullptr;
+  m.dense = a->mask;
   m.Sq = a->Sq;
   m.Sk = a->Sk;
   m.causal = a->causal ? 1 : 0;
@@ -377,7 +445,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
   p.lse = lse;
   p.out_lo = out_lo;
   p.mask = base_mask(a);
-  hipError_t e = prep_segments(a, ws, p.mask, s);
+  hipError_t e = prep_bounds(a, ws, p.mask, s, true);
   if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;
@@ -438,15 +506,9 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   p.dbias = dbias;
   p.mask = base_mask(a);
   hipError_t e = hipSuccess;
-  if (phases & kPhasePre) {
-    e = prep_segments(a, ws, p.mask, s);
-    if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
-  } else if (has_segments(a)) {
-    const size_t n = align_up((size_t)a->B * a->Sq * sizeof(int));
-    p.mask.seg_lo = reinterpret_cast<int*>(ws);
-    p.mask.seg_hi = reinterpret_cast<int*>(ws + n);
-    ws += 2 * n;
-  }
+  // the pre-pass computes the bounds; the other phases find them in the workspace
+  e = prep_bounds(a, ws, p.mask, s, (phases & kPhasePre) != 0);
+  if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
   float* delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));
   float* part = nullptr;
@@ -533,8 +595,9 @@ attn_status attn_bwd_noalloc(const attn_args* a, const void* out, const void* ou
   if (st != ATTN_OK) return st;
   attn_args r = *a;
   if (r.dq_mode == ATTN_DQ_AUTO) {
-    r.dq_mode = ATTN_DQ_DU_BLOCKS;
-    if (!du_supported(&r) || bwd_ws(&r) > kScratchBytes) r.dq_mode = ATTN_DQ_RECOMPUTE;
+    // attn_bwd's choice, as long as the workspace then fits the scratch
+    r.dq_mode = du_path(&r) ? ATTN_DQ_DU_BLOCKS : ATTN_DQ_RECOMPUTE;
+    if (r.dq_mode == ATTN_DQ_DU_BLOCKS && bwd_ws(&r) > kScratchBytes) r.dq_mode = ATTN_DQ_RECOMPUTE;
   }
   const size_t need = bwd_ws(&r);
   if (need > kScratchBytes)

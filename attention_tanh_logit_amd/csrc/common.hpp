@@ -317,15 +317,20 @@ __device__ __forceinline__ void xcd_order(int ntile, int ngroup, int& tile, int&
 
 // ---------------------------------------------------------------- visibility
 //
-// Packed segments are contiguous runs; seg_lo[t] / seg_hi[t] are the first and
-// one-past-last token of t's run (absent: the whole row).  With the run, the
-// causal flag and the window, the keys a query sees and the queries a key is
-// seen by are both one contiguous range, and the range ends are
-// non-decreasing in the token index.
+// The keys a query sees and the queries a key is seen by are each one
+// contiguous range, cut down by the causal flag and the window from bounds
+// prepared per token: q_lo / q_hi (first visible key and one past the last,
+// per query: packed segment runs, k_start) and k_lo / k_hi (first query that
+// sees the key and one past the last, per key); absent arrays do not
+// restrict.  All range ends are non-decreasing in the token index.  A dense
+// boolean mask, where given, removes further pairs inside those ranges.
 
 struct Mask {
-  const int* seg_lo;   // [B * S] or null
-  const int* seg_hi;
+  const int* q_lo;     // [B * Sq] or null
+  const int* q_hi;
+  const int* k_lo;     // [B * Sk] or null
+  const int* k_hi;
+  const unsigned char* dense;   // [B, Sq, Sk] or null: nonzero = visible
   int Sq, Sk;
   int causal, window;
 };
@@ -334,10 +339,8 @@ struct Mask {
 __device__ __forceinline__ void keys_of(const Mask& m, int b, int i, int& lo, int& hi) {
   lo = 0;
   hi = m.Sk;
-  if (m.seg_lo) {
-    lo = max(m.seg_lo[(long)b * m.Sq + i], 0);
-    hi = min(m.seg_hi[(long)b * m.Sq + i], m.Sk);
-  }
+  if (m.q_lo) lo = max(m.q_lo[(long)b * m.Sq + i], 0);
+  if (m.q_hi) hi = min(m.q_hi[(long)b * m.Sq + i], m.Sk);
   if (m.causal) hi = min(hi, i + 1);
   if (m.window > 0) {
     lo = max(lo, i - m.window + 1);
@@ -351,10 +354,8 @@ __device__ __forceinline__ void keys_of(const Mask& m, int b, int i, int& lo, in
 __device__ __forceinline__ void queries_of(const Mask& m, int b, int j, int& lo, int& hi) {
   lo = 0;
   hi = m.Sq;
-  if (m.seg_lo) {
-    lo = max(m.seg_lo[(long)b * m.Sk + j], 0);
-    hi = min(m.seg_hi[(long)b * m.Sk + j], m.Sq);
-  }
+  if (m.k_lo) lo = max(m.k_lo[(long)b * m.Sk + j], 0);
+  if (m.k_hi) hi = min(m.k_hi[(long)b * m.Sk + j], m.Sq);
   if (m.causal) lo = max(lo, j);
   if (m.window > 0) {
     hi = min(hi, j + m.window);
@@ -362,6 +363,12 @@ __device__ __forceinline__ void queries_of(const Mask& m, int b, int j, int& lo,
   }
   lo = min(lo, m.Sq);  // keeps both ends non-decreasing in j and within [0, Sq]
   hi = max(hi, lo);
+}
+
+// the dense mask at (query i, key j) of batch row b (true without one); only
+// called for pairs inside the ranges above, so i < Sq and j < Sk
+__device__ __forceinline__ bool dense_ok(const Mask& m, int b, int i, int j) {
+  return !m.dense || m.dense[((long)b * m.Sq + i) * m.Sk + j] != 0;
 }
 
 // shuffle with the partner lane l ^ 32 (the other half of a 32x32 column)

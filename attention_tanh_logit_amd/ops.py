@@ -37,6 +37,8 @@ class AttnArgs(ctypes.Structure):
         ("sink_mode", ctypes.c_int),
         ("sink", ctypes.c_void_p),
         ("dq_mode", ctypes.c_int),
+        ("k_start", ctypes.c_void_p),
+        ("mask", ctypes.c_void_p),
     ]
 
 
@@ -97,7 +99,8 @@ def _check(status: int) -> None:
 
 
 def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
-              softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto") -> AttnArgs:
+              softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", k_start=None,
+              mask=None) -> AttnArgs:
     """Fill the C argument struct from tensors (BSHD, or THD with cu_seqlens).
 
     The C ABI sees only pointers and sizes, so every shape, dtype and device
@@ -133,7 +136,7 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
         if t is not None and t.dtype != q.dtype:
             raise TypeError(f"{name} must have q's dtype")
     tensors = (("q", q), ("k", k), ("v", v), ("bias", bias), ("segment_ids", segment_ids),
-               ("cu_seqlens", cu_seqlens), ("sink", sink))
+               ("cu_seqlens", cu_seqlens), ("sink", sink), ("k_start", k_start), ("mask", mask))
     for name, t in tensors:
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -145,6 +148,12 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
         raise ValueError("cu_seqlens must be int32 [nseq + 1]")
     if sink is not None and (sink.dtype != torch.float32 or tuple(sink.shape) != (Hq,)):
         raise ValueError("sink must be float32 [Hq]")
+    if k_start is not None and (k_start.dtype != torch.int32 or
+                                tuple(k_start.shape) != ((Sq,) if thd else (B, Sq))):
+        raise ValueError("k_start must be int32 [B, Sq] ([T] for THD)")
+    if mask is not None and (mask.dtype not in (torch.bool, torch.uint8) or
+                             tuple(mask.shape) != ((Sq, Sk) if thd else (B, Sq, Sk))):
+        raise ValueError("mask must be bool or uint8 [B, Sq, Sk] ([T, T] for THD)")
     for name, t in tensors[1:]:
         if t is not None and t.device != q.device:
             raise ValueError(f"{name} is on {t.device}, q on {q.device}: every tensor must be on q's device")
@@ -169,6 +178,8 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
     a.sink_mode = SINK_MODES[sink_mode]
     a.sink = _ptr(sink)
     a.dq_mode = DQ_MODES[dq_mode]
+    a.k_start = _ptr(k_start)
+    a.mask = _ptr(mask)
     return a
 
 
@@ -189,7 +200,8 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0, softcap=0.0,
-             scale=0.0, sink_mode="none", sink=None, out=None, lse=None, out_lo=None, residual=True):
+             scale=0.0, sink_mode="none", sink=None, k_start=None, mask=None, out=None, lse=None, out_lo=None,
+             residual=True):
     """Forward: returns (out, lse, out_lo); lse is float32 [B, Hq, Sq] ([Hq, T] for THD).
 
     out_lo (bf16 only; None for fp32 or with ``residual=False``) is the part
@@ -198,7 +210,8 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
     """
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
-                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink)
+                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, k_start=k_start,
+                  mask=mask)
     _check(L.attn_validate(ctypes.byref(a)))
     shape = (a.Hq, a.Sq) if cu_seqlens is not None else (a.B, a.Hq, a.Sq)
     out = torch.empty_like(q) if out is None else _like("out", out, q)
@@ -217,8 +230,8 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
 
 
 def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None, causal=False,
-             window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", want_dbias=None,
-             events=None, outputs=None):
+             window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", k_start=None, mask=None,
+             want_dbias=None, events=None, outputs=None):
     """Backward: returns (dq, dk, dv, dbias or None, dsink or None).
 
     ``out_lo`` is what :func:`attn_fwd` returned beside ``out`` (bf16; None
@@ -233,7 +246,8 @@ def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=Non
     """
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
-                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode)
+                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode,
+                  k_start=k_start, mask=mask)
     _check(L.attn_validate(ctypes.byref(a)))
     _like("out", out, q)
     _like("dout", dout, q)
@@ -278,7 +292,7 @@ def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=Non
 
 def attn_bwd_noalloc(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None,
                      causal=False, window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto",
-                     outputs):
+                     k_start=None, mask=None, outputs):
     """The backward through ``attn_bwd_noalloc``: no workspace, the library's own
     static scratch instead.  ``outputs`` must hold preallocated "dq", "dk", "dv"
     (and "dbias" with a bias, "dsink" with a learnable sink) tensors, each
@@ -286,7 +300,8 @@ def attn_bwd_noalloc(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment
     allocates nothing on the device.  Returns (dq, dk, dv, dbias, dsink)."""
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
-                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode)
+                  window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode,
+                  k_start=k_start, mask=mask)
     _check(L.attn_validate(ctypes.byref(a)))
     _like("out", out, q)
     _like("dout", dout, q)

@@ -131,6 +131,15 @@ typedef struct attn_args {
   int sink_mode;               /* attn_sink_mode */
   const float* sink;           /* [Hq] sink logits; required iff sink_mode == ATTN_SINK_LEARNABLE */
   int dq_mode;                 /* attn_dq_mode (backward only; the forward ignores it) */
+  /* The other two packed forms of "Support logits soft-capping in the
+   * Pallas-Triton attention VJP" (PR description: k_start and a dense boolean
+   * mask, agreeing to every digit with segment ids); each only removes pairs,
+   * on top of causal, window and segments. */
+  const int32_t* k_start;      /* nullable: [B, Sq] int32 (THD: [T]), the first key query i may see (keys
+                                  j >= k_start[i]); non-decreasing along a row (the library uses its running
+                                  maximum, which equals it then) */
+  const uint8_t* mask;         /* nullable: [B, Sq, Sk] bytes (THD: [T, T]), nonzero = visible; 16-byte
+                                  aligned.  Every tile then takes the per-pair masked path (slower) */
 } attn_args;
 
 /* Host-only check of `a` (no device access, nothing launched).  Returns the
@@ -144,7 +153,8 @@ attn_status attn_validate(const attn_args* a);
 /* Device workspace (bytes) that attn_fwd / attn_bwd need for `a` (0 if
  * none); (size_t)-1 if `a` is invalid.  The size depends only on `a`:
  *  - forward: two int32 [B*Sq] arrays of segment runs, only with
- *    segment_ids or cu_seqlens;
+ *    segment_ids or cu_seqlens, and with k_start one int32 [B*Sq] and one
+ *    int32 [B*Sk] array of visibility bounds;
  *  - backward: the same runs, delta [B*Hq*Sq] fp32, sink-gradient partials
  *    with a learnable sink, the dU blocks when dq_mode resolves to
  *    ATTN_DQ_DU_BLOCKS (see attn_dq_mode), and for bf16 with D = 64, 128 or
@@ -214,7 +224,7 @@ attn_status attn_bwd_dq(const attn_args* a, const float* lse, const void* dout, 
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  The workspace lives in a static device array of
  * 128 MiB inside the library, one per GPU (held until the process ends);
- * dq_mode ATTN_DQ_AUTO takes the dU blocks only where the whole workspace
+ * dq_mode ATTN_DQ_AUTO makes attn_bwd's choice where the whole workspace
  * then fits in it, else recomputes.  A problem whose workspace exceeds
  * 128 MiB is rejected with ATTN_UNSUPPORTED before anything is launched
  * (e.g. an explicit ATTN_DQ_DU_BLOCKS at B=4, Hq=32, S=4096).  The stream

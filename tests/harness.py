@@ -67,7 +67,24 @@ def case(dtype="bf16", B=2, S=200, Hq=4, Hkv=2, D=64, causal=True, window=0, sof
         if b is not None:
             b = W.round_to_bf16(b)
     return dict(dtype=dtype, q=q, k=k, v=v, dout=do, sink=sink, sink_mode=sink_mode, bias=b, segment_ids=seg,
-                causal=causal, window=window, softcap=softcap)
+                causal=causal, window=window, softcap=softcap, k_start=None, mask=None)
+
+
+def as_k_start(c):
+    """The case's packing written as k_start (first key of each token's segment) instead of ids."""
+    seg = c["segment_ids"]
+    ks = np.zeros(seg.shape, dtype=np.int32)
+    for b in range(seg.shape[0]):
+        starts = np.concatenate([[0], np.nonzero(np.diff(seg[b]))[0] + 1])
+        for a, e in zip(starts, list(starts[1:]) + [seg.shape[1]]):
+            ks[b, a:e] = a
+    return dict(c, segment_ids=None, k_start=ks)
+
+
+def as_dense_mask(c):
+    """The case's packing written as a dense boolean mask (same segment) instead of ids."""
+    seg = c["segment_ids"]
+    return dict(c, segment_ids=None, mask=seg[:, :, None] == seg[:, None, :])
 
 
 def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True):
@@ -80,11 +97,18 @@ def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True):
     if c["bias"] is not None:
         kw["bias"] = to_dev(c["bias"], dt)
     if thd:
+        assert c["segment_ids"] is not None and c["segment_ids"].shape[0] == 1 or c.get("k_start") is None
         cu = W.cu_seqlens_from_segments(c["segment_ids"])
         kw["cu_seqlens"] = torch.from_numpy(cu).cuda()
         q, k, v = (x.reshape(-1, *x.shape[2:]) for x in (q, k, v))
     elif c["segment_ids"] is not None:
         kw["segment_ids"] = torch.from_numpy(c["segment_ids"]).cuda()
+    if c.get("k_start") is not None:
+        ks = torch.from_numpy(np.ascontiguousarray(c["k_start"], dtype=np.int32)).cuda()
+        kw["k_start"] = ks.reshape(-1) if thd else ks
+    if c.get("mask") is not None:
+        mk = torch.from_numpy(np.ascontiguousarray(c["mask"], dtype=bool)).cuda()
+        kw["mask"] = mk[0] if thd else mk
     # results land in NaN-filled buffers, so an element the kernels leave unwritten shows up
     nan = float("nan")
     lse_shape = (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
@@ -116,7 +140,8 @@ def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True):
 def run_oracle(c, backward=True, groups=None):
     kw = dict(causal=c["causal"], window=c["window"], softcap=c["softcap"], bias=c["bias"],
               segment_ids=c["segment_ids"], sink=c["sink"] if c["sink_mode"] == "learnable"
-              else (np.zeros(c["q"].shape[2]) if c["sink_mode"] == "off_by_one" else None), groups=groups)
+              else (np.zeros(c["q"].shape[2]) if c["sink_mode"] == "off_by_one" else None), groups=groups,
+              k_start=c.get("k_start"), mask=c.get("mask"))
     out, lse = attention_forward(c["q"], c["k"], c["v"], **kw)
     res = {"out": out, "lse": lse}
     if backward:

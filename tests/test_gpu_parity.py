@@ -8,7 +8,7 @@ the bar is the normwise error max|x - ref| / max|ref| <= 1e-5 (fp32 path) or
 import numpy as np
 import pytest
 
-from harness import TOL, case, compare, run_gpu, run_oracle
+from harness import TOL, as_dense_mask, as_k_start, case, compare, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -164,3 +164,51 @@ def test_fully_masked_rows_give_zero_and_minus_inf(dtype, D):
     assert np.all(np.isneginf(gpu["lse"][0, :, 72:]))
     errs = compare(gpu, ref, dtype)
     assert all(v <= TOL[dtype] for v in errs.values()), errs
+
+
+# ---- the two other packed forms of the tokamax PR description: k_start and a dense boolean mask
+
+PACKED = {
+    "causal": dict(segments=[[45, 70, 190], [128]]),
+    "window_gqa_sink": dict(Hq=6, Hkv=2, segments=[[13, 100], [77, 78, 150]], window=50, sink_mode="learnable"),
+    "bias": dict(segments=[[60, 61, 131], [33]], bias=True, softcap=50.0),
+}
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 512), ("fp32", 64),
+                                     ("fp32", 512)])
+@pytest.mark.parametrize("form", ["k_start", "dense_mask"])
+@pytest.mark.parametrize("feat", list(PACKED))
+def test_packed_forms_match_oracle(dtype, D, form, feat):
+    kw = dict(dtype=dtype, D=D, B=2, S=200, Hq=4, Hkv=2)
+    kw.update(PACKED[feat])
+    c = case(**kw)
+    _check(as_k_start(c) if form == "k_start" else as_dense_mask(c))
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 512), ("fp32", 128)])
+def test_segment_ids_k_start_and_dense_mask_agree_bitwise(dtype, D):
+    """One causal packing given as segment ids, as k_start and as a dense mask: the
+    kernels agree to every bit (the dense mask adds only exact zeros from pairs it removes)."""
+    c = case(dtype=dtype, D=D, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]], sink_mode="learnable")
+    a = run_gpu(c)
+    b = run_gpu(as_k_start(c))
+    m = run_gpu(as_dense_mask(c))
+    for n, x in a.items():
+        if x is None:
+            continue
+        assert x.tobytes() == b[n].tobytes(), f"{n}: k_start differs from segment ids"
+        assert x.tobytes() == m[n].tobytes(), f"{n}: dense mask differs from segment ids"
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64), ("bf16", 512)])
+def test_random_dense_mask_and_k_start_without_causal(dtype, D):
+    """A dense mask that is not a packing (random pairs, some rows empty), and a
+    non-decreasing k_start without causal masking, on cross attention (Sq != Sk)."""
+    rng = np.random.default_rng(5)
+    c = case(dtype=dtype, D=D, B=2, S=97, Sk=150, causal=False, Hq=4, Hkv=2, sink_mode="learnable")
+    m = rng.random((2, 97, 150)) < 0.3
+    m[0, 10] = False                                      # a row that sees nothing: only the sink
+    _check(dict(c, mask=m))
+    ks = np.sort(rng.integers(0, 160, size=(2, 97)), axis=1).astype(np.int32)   # some rows past Sk: empty
+    _check(dict(c, k_start=ks))
