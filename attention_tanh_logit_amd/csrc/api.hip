@@ -203,7 +203,8 @@ bool du_supported(const attn_args* a) {
 
 attn_status validate(const attn_args* a) {
   if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
-  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_FP32) return fail(ATTN_INVALID_ARGUMENT, "dtype must be ATTN_BF16 or ATTN_FP32");
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_FP32 && a->dtype != ATTN_FP16)
+    return fail(ATTN_INVALID_ARGUMENT, "dtype must be ATTN_BF16, ATTN_FP16 or ATTN_FP32");
   if (a->B < 0 || a->Sq < 0 || a->Sk < 0) return fail(ATTN_INVALID_ARGUMENT, "B, Sq and Sk must be >= 0");
   if (a->Hq < 1 || a->Hkv < 1) return fail(ATTN_INVALID_ARGUMENT, "Hq and Hkv must be >= 1");
   if (a->Hq % a->Hkv != 0) return fail(ATTN_INVALID_ARGUMENT, "Hq must be a multiple of Hkv (GQA groups)");
@@ -312,7 +313,9 @@ size_t bwd_ws(const attn_args* a) {
   return s;
 }
 
-const TypeOps& ops(const attn_args* a) { return a->dtype == ATTN_BF16 ? ops_bf16() : ops_f32(); }
+const TypeOps& ops(const attn_args* a) {
+  return a->dtype == ATTN_BF16 ? ops_bf16() : a->dtype == ATTN_FP16 ? ops_f16() : ops_f32();
+}
 
 // Lays the bounds out in the workspace (advancing ws) and, with launch,
 // computes them on stream s.
@@ -433,7 +436,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
   if ((size_t)a->B * a->Sq * a->Hq == 0) return ATTN_OK;
   if (!out || !lse) return fail(ATTN_INVALID_ARGUMENT, "out and lse must not be NULL");
   if (!aligned16(out) || !aligned16(out_lo)) return fail(ATTN_INVALID_ARGUMENT, "out and out_lo must be 16-byte aligned");
-  if (out_lo && a->dtype != ATTN_BF16) return fail(ATTN_INVALID_ARGUMENT, "out_lo is for bf16 outputs only");
+  if (out_lo && a->dtype == ATTN_FP32) return fail(ATTN_INVALID_ARGUMENT, "out_lo is for bf16 and fp16 outputs only");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   FwdParams p;
@@ -490,7 +493,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   if (!aligned16(out) || !aligned16(out_lo) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(dbias))
     return fail(ATTN_INVALID_ARGUMENT, "out, out_lo, dout, dq, dk, dv and dbias must be 16-byte aligned");
-  if (out_lo && a->dtype != ATTN_BF16) return fail(ATTN_INVALID_ARGUMENT, "out_lo is for bf16 outputs only");
+  if (out_lo && a->dtype == ATTN_FP32) return fail(ATTN_INVALID_ARGUMENT, "out_lo is for bf16 and fp16 outputs only");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   BwdParams p;

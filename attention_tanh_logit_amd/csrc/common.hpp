@@ -10,6 +10,8 @@ namespace atl {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -37,10 +39,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { using type = bf16x8; };
+template <> struct Frag<f16> { using type = f16x8; };
 template <> struct Frag<float> { using type = f32x8; };
 
 __device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
 #pragma unroll
@@ -56,6 +62,8 @@ template <typename T>
 __device__ __forceinline__ typename Frag<T>::type lds_frag(const T* p);
 template <>
 __device__ __forceinline__ bf16x8 lds_frag<bf16>(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+template <>
+__device__ __forceinline__ f16x8 lds_frag<f16>(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
 template <>
 __device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
   f32x4 a = *reinterpret_cast<const f32x4*>(p);
@@ -73,6 +81,12 @@ __device__ __forceinline__ bf16x8 to_frag(const f32x16& c, int base, bf16*) {
   for (int i = 0; i < 8; ++i) r[i] = (bf16)c[base + i];
   return r;
 }
+__device__ __forceinline__ f16x8 to_frag(const f32x16& c, int base, f16*) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (f16)c[base + i];
+  return r;
+}
 __device__ __forceinline__ f32x8 to_frag(const f32x16& c, int base, float*) {
   f32x8 r;
 #pragma unroll
@@ -83,18 +97,20 @@ __device__ __forceinline__ f32x8 to_frag(const f32x16& c, int base, float*) {
 // ---------------------------------------------------------------- scalar helpers
 
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// tanh for the soft-cap.  The bf16 path uses 1 - 2/(1 + e^{2x}) (one exp2,
-// one reciprocal; exact limits +-1 at overflow/underflow, absolute error a
-// few fp32 ulps, far below bf16 rounding).  The fp32 path keeps the device
+// tanh for the soft-cap.  The bf16 and fp16 paths use 1 - 2/(1 + e^{2x})
+// (one exp2, one reciprocal; exact limits +-1 at overflow/underflow,
+// absolute error a few fp32 ulps, far below bf16 or fp16 rounding).  The fp32 path keeps the device
 // library's tanhf, which stays accurate to a few ulps relative near 0.
 __device__ __forceinline__ float cap_tanh(float x, bf16*) {
   float e = fast_exp2(x * (2.0f * kLog2e));
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
 }
+__device__ __forceinline__ float cap_tanh(float x, f16*) { return cap_tanh(x, (bf16*)nullptr); }
 __device__ __forceinline__ float cap_tanh(float x, float*) { return tanhf(x); }
 
 template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
@@ -103,6 +119,12 @@ template <> __device__ __forceinline__ void store8<bf16>(bf16* p, const float* v
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = (bf16)v[i];
   *reinterpret_cast<bf16x8*>(p) = r;
+}
+template <> __device__ __forceinline__ void store8<f16>(f16* p, const float* v) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (f16)v[i];
+  *reinterpret_cast<f16x8*>(p) = r;
 }
 template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
   f32x4 a, b;
@@ -120,11 +142,22 @@ __device__ __forceinline__ void store8_lo(bf16* p, const float* v) {
   for (int i = 0; i < 8; ++i) r[i] = (bf16)(v[i] - (float)(bf16)v[i]);
   *reinterpret_cast<bf16x8*>(p) = r;
 }
+__device__ __forceinline__ void store8_lo(f16* p, const float* v) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (f16)(v[i] - (float)(f16)v[i]);
+  *reinterpret_cast<f16x8*>(p) = r;
+}
 
 // 8 consecutive values from global memory into fp32 (16-byte aligned for bf16,
 // 32-byte for fp32)
 __device__ __forceinline__ void load8(const bf16* p, float* v) {
   bf16x8 r = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)r[i];
+}
+__device__ __forceinline__ void load8(const f16* p, float* v) {
+  f16x8 r = *reinterpret_cast<const f16x8*>(p);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = (float)r[i];
 }

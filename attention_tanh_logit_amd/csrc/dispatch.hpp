@@ -55,6 +55,20 @@ ATL_DKDV(float, 128, 128, 2, 128)
 ATL_DKDV(float, 256, 64, 1, 64)
 ATL_DKDV(float, 512, 128, 1, 128)
 
+// fp16 takes the generic kernels with the bf16 shapes (same element size)
+ATL_FWD(f16, 64, 64, 4, 64, 64)
+ATL_FWD(f16, 128, 128, 4, 64, 128)
+ATL_FWD(f16, 256, 256, 2, 32, 256)
+ATL_FWD(f16, 512, 128, 2, 64, 128)
+ATL_DQ(f16, 64, 64, 4, 64, 64)
+ATL_DQ(f16, 128, 128, 4, 32, 128)
+ATL_DQ(f16, 256, 256, 2, 32, 256)
+ATL_DQ(f16, 512, 256, 2, 64, 128)
+ATL_DKDV(f16, 64, 64, 4, 64)
+ATL_DKDV(f16, 128, 128, 4, 128)
+ATL_DKDV(f16, 256, 128, 2, 256)
+ATL_DKDV(f16, 512, 128, 1, 128)
+
 #undef ATL_FWD
 #undef ATL_DQ
 #undef ATL_DKDV
@@ -225,6 +239,7 @@ struct TypeOps {
 };
 
 const TypeOps& ops_bf16();
+const TypeOps& ops_f16();
 const TypeOps& ops_f32();
 
 }  // namespace atl

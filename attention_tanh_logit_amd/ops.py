@@ -15,7 +15,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_softcap.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_HIP_ERROR = 0, 1, 2, 3
-ATTN_BF16, ATTN_FP32 = 0, 1
+ATTN_BF16, ATTN_FP32, ATTN_FP16 = 0, 1, 2
 SINK_MODES = {"none": 0, "off_by_one": 1, "learnable": 2}
 DQ_MODES = {"auto": 0, "du_blocks": 1, "recompute": 2}
 
@@ -128,10 +128,12 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
         raise ValueError("k and v must have the same shape")
     if q.dtype == torch.bfloat16:
         dt = ATTN_BF16
+    elif q.dtype == torch.float16:
+        dt = ATTN_FP16
     elif q.dtype == torch.float32:
         dt = ATTN_FP32
     else:
-        raise TypeError("q must be bfloat16 or float32")
+        raise TypeError("q must be bfloat16, float16 or float32")
     for name, t in (("k", k), ("v", v), ("bias", bias)):
         if t is not None and t.dtype != q.dtype:
             raise TypeError(f"{name} must have q's dtype")
@@ -204,8 +206,8 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
              residual=True):
     """Forward: returns (out, lse, out_lo); lse is float32 [B, Hq, Sq] ([Hq, T] for THD).
 
-    out_lo (bf16 only; None for fp32 or with ``residual=False``) is the part
-    of the fp32 output that the bf16 ``out`` drops; hand it to
+    out_lo (bf16 and fp16; None for fp32 or with ``residual=False``) is the
+    part of the fp32 output that ``out`` drops in its rounding; hand it to
     :func:`attn_bwd` so that delta = <dO, O> is taken from the fp32 output.
     """
     L = lib()
@@ -219,10 +221,10 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     elif tuple(lse.shape) != shape or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
         raise ValueError(f"lse must be contiguous float32 {list(shape)}")
-    if a.dtype == ATTN_BF16 and (residual or out_lo is not None):
+    if a.dtype != ATTN_FP32 and (residual or out_lo is not None):
         out_lo = torch.empty_like(q) if out_lo is None else _like("out_lo", out_lo, q)
     elif out_lo is not None:
-        raise ValueError("out_lo is for bf16 outputs only")
+        raise ValueError("out_lo is for bf16 and fp16 outputs only")
     nws = L.attn_fwd_workspace_size(ctypes.byref(a))
     ws = _workspace(nws, q.device)
     _check(L.attn_fwd(ctypes.byref(a), _ptr(out), _ptr(lse), _ptr(out_lo), _ptr(ws), nws, _stream(q)))

@@ -72,7 +72,11 @@ typedef enum attn_status {
   ATTN_HIP_ERROR = 3         /* a launch failed; nothing further was enqueued */
 } attn_status;
 
-typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype;
+/* Element type of q, k, v, bias, out, dout, dq, dk, dv, dbias.  bf16 and fp16
+ * contract on the matrix cores with fp32 accumulation; fp32 on the fp32
+ * matrix instructions.  (fp16 is listed as not covered on the learnable-sink
+ * page, "Not covered"; here it runs the generic kernels.) */
+typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1, ATTN_FP16 = 2 } attn_dtype;
 
 /* Softmax sink ("softmax_type" on the learnable-sink page, "What changed"):
  * none (vanilla), off-by-one (a sink column with its logit fixed at 0 and no
@@ -171,11 +175,13 @@ size_t attn_bwd_workspace_size(const attn_args* a);
  * Writes out [B,Sq,Hq,D] (dtype) and lse [B,Hq,Sq] (float32, natural log,
  * sink included).  A query row that sees no key and has no sink gets
  * out = 0, lse = -inf; with a sink, out = 0 and lse = sigma.
- * out_lo: nullable, bf16 only, [B,Sq,Hq,D] bf16: receives the part of the
- * fp32 output that its rounding to `out` drops, out_lo = bf16(O - out).
+ * out_lo: nullable, bf16 or fp16 only, [B,Sq,Hq,D] in that type: receives the
+ * part of the fp32 output that its rounding to `out` drops, out_lo = O - out
+ * rounded to the type.
  * Passed on to the backward it makes delta = <dO, O> (and so dsink, which
  * sums p_sink * delta over the query rows) exact to about 16 bits instead of
- * inheriting out's 8; NULL keeps the bf16 `out` alone.  Must be NULL for fp32.
+ * inheriting out's 8 (bf16) or 11 (fp16); NULL keeps `out` alone.  Must be NULL
+ * for fp32.
  * workspace: device buffer of at least attn_fwd_workspace_size(a) bytes,
  * 256-byte aligned (may be NULL when that size is 0); its contents on entry
  * do not matter. */
@@ -191,7 +197,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
  * dbias (nullable; requires a->bias; written in full, exactly 0 where
  * masked) and dsink (required iff sink_mode == ATTN_SINK_LEARNABLE, else must
  * be NULL; summed over every batch row and query row).  out_lo: nullable,
- * what attn_fwd wrote there (bf16 only).  Results are deterministic (no
+ * what attn_fwd wrote there (bf16 or fp16).  Results are deterministic (no
  * floating-point atomics): the same inputs give the same bits.
  * workspace: at least attn_bwd_workspace_size(a) bytes, 256-byte aligned. */
 attn_status attn_bwd(const attn_args* a, const void* out, const void* out_lo, const float* lse, const void* dout,

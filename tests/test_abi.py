@@ -54,6 +54,7 @@ def test_valid_arguments_pass():
     assert _status(_args(dq_mode=1))[0] == 0
     assert _status(_args(dq_mode=2, dtype=1))[0] == 0
     assert _status(_args(Sq=0, Sk=0))[0] == 0
+    assert _status(_args(dtype=2))[0] == 0
 
 
 BAD = {
@@ -119,10 +120,10 @@ def test_out_lo_is_bf16_only():
     L = A.lib()
     a = _args(dtype=1)
     assert L.attn_fwd(ctypes.byref(a), 0x1000, 0x2000, 0x3000, None, 0, None) == 1
-    assert "bf16" in L.attn_last_error().decode()
+    assert "fp16" in L.attn_last_error().decode()
     s = L.attn_bwd(ctypes.byref(a), 0x1000, 0x3000, 0x2000, 0x4000, 0x5000, 0x6000, 0x7000, None, None, 0x8000,
                    1 << 30, None)
-    assert s == 1 and "bf16" in L.attn_last_error().decode()
+    assert s == 1 and "fp16" in L.attn_last_error().decode()
     a = _args()
     assert L.attn_fwd(ctypes.byref(a), 0x1000, 0x2000, 0x3008, None, 0, None) == 1
     assert "aligned" in L.attn_last_error().decode()

@@ -28,6 +28,7 @@ REPEAT = {
     "bf16_d512": dict(dtype="bf16", D=512, B=1, S=203, Hq=4, Hkv=2, bias=True),
     "fp32_d64": dict(dtype="fp32", D=64, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable"),
     "fp32_d512": dict(dtype="fp32", D=512, B=1, S=130, Hq=2, Hkv=1),
+    "fp16_d128_bias": dict(dtype="fp16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True, sink_mode="learnable"),
 }
 
 
