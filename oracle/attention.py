@@ -27,6 +27,9 @@ each line can be checked against the sources by eye:
   query rows.  Off-by-one softmax is that column with its logit fixed at 0.
 * The bias is added after the ``1/sqrt(D)`` scale (``post_scale_bias`` in
   the Greptile review "Offset Corrupts Bias Gradient Shape" on that page).
+* The same review: the bias gradient has the bias's own shape, so a bias
+  broadcast over batch rows or heads ([1 or B, 1 or Hq, Sq, Sk]) gets the
+  full gradient summed over the broadcast dimensions.
 * "Support logits soft-capping in the Pallas-Triton attention VJP", PR
   description: besides segment ids, a packed batch can be given as
   ``k_start`` (per query, the first key it may see) or as a dense boolean
@@ -229,6 +232,8 @@ def attention_forward(q, k, v, *, softcap=0.0, causal=False, window=0, scale=Non
     """
     q, k, v, bias, seg, k_start, mask, thd = _prepare(q, k, v, bias, segment_ids, cu_seqlens, k_start, mask)
     B, Sq, Hq, D = q.shape
+    if bias is not None:
+        bias = np.broadcast_to(bias, (B, Hq, Sq, k.shape[1]))
     Hkv = k.shape[2]
     if Hq % Hkv:
         raise ValueError("query heads must be a multiple of KV heads")
@@ -263,6 +268,10 @@ def attention_backward(q, k, v, dout, *, softcap=0.0, causal=False, window=0, sc
     if thd:
         dout = dout[None]
     B, Sq, Hq, D = q.shape
+    bias_shape = None
+    if bias is not None:
+        bias_shape = np.shape(bias)
+        bias = np.broadcast_to(bias, (B, Hq, Sq, k.shape[1]))
     Hkv = k.shape[2]
     G = Hq // Hkv
     want_dbias = (bias is not None) if want_dbias is None else want_dbias
@@ -285,6 +294,10 @@ def attention_backward(q, k, v, dout, *, softcap=0.0, causal=False, window=0, sc
             dbias[b, hs] = r[3]
         if dsink is not None:
             dsink[hs] += r[4]
+    if dbias is not None and tuple(bias_shape) != dbias.shape:
+        # the gradient of a broadcast bias: summed over the dimensions it was broadcast along
+        axes = tuple(a for a in (0, 1) if bias_shape[a] == 1 and dbias.shape[a] != 1)
+        dbias = dbias.sum(axis=axes, keepdims=True)
     if thd:
         return dq[0], dk[0], dv[0], (None if dbias is None else dbias[0]), dsink
     return dq, dk, dv, dbias, dsink

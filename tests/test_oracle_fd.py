@@ -120,3 +120,16 @@ def test_gradients_where_the_cap_saturates():
     loss = lambda: _loss(q, k, v, do, kw)  # noqa: E731
     for grad, x in ((dq, q), (dk, k), (dv, v)):
         assert _rel(grad, _fd(loss, x, h=1e-6)) < 1e-6
+
+
+@pytest.mark.parametrize("shape", [(1, 4), (2, 1), (1, 1)])
+def test_broadcast_bias_gradient_matches_central_differences(shape):
+    """A bias broadcast over batch rows and/or heads: its gradient, of the bias's own
+    shape, against central differences taken on that small tensor."""
+    q, k, v, do, kw = _case()
+    rng = np.random.default_rng(7)
+    kw["bias"] = rng.standard_normal(shape + (11, 11)) * 0.7
+    dbias = attention_backward(q, k, v, do, **kw)[3]
+    assert dbias.shape == kw["bias"].shape
+    loss = lambda: _loss(q, k, v, do, kw)  # noqa: E731
+    assert _rel(dbias, _fd(loss, kw["bias"])) < 1e-7
