@@ -227,6 +227,9 @@ attn_status validate(const attn_args* a) {
   }
   if (has_segments(a) && a->Sq != a->Sk) return fail(ATTN_INVALID_ARGUMENT, "packed segments need Sq == Sk");
   if (a->mask && ((uintptr_t)a->mask & 15) != 0) return fail(ATTN_INVALID_ARGUMENT, "mask must be 16-byte aligned");
+  if (a->bias_bcast < 0 || a->bias_bcast > 3)
+    return fail(ATTN_INVALID_ARGUMENT, "bias_bcast must be a combination of ATTN_BIAS_BCAST_BATCH and _HEADS");
+  if (a->bias_bcast && !a->bias) return fail(ATTN_INVALID_ARGUMENT, "bias_bcast given without a bias");
   if (a->causal && a->Sq != a->Sk) return fail(ATTN_UNSUPPORTED, "causal masking needs Sq == Sk");
   const long long maxi = 2147483647LL;
   if ((long long)a->B * a->Sq > maxi || (long long)a->B * a->Sk > maxi)
@@ -304,8 +307,16 @@ size_t dkv_part_bytes(const attn_args* a) {
   return hs > 1 ? (size_t)2 * hs * a->B * a->Sk * a->Hkv * a->D * sizeof(float) : 0;
 }
 
+size_t elem_bytes(const attn_args* a) { return a->dtype == ATTN_FP32 ? 4 : 2; }
+
+// A broadcast bias: the kernels write the full [B, Hq, Sq, Sk] dbias here,
+// reduced into the caller's dbias afterwards.
+size_t dbias_full_bytes(const attn_args* a) {
+  return a->bias && a->bias_bcast ? align_up((size_t)a->B * a->Hq * a->Sq * a->Sk * elem_bytes(a)) : 0;
+}
+
 size_t bwd_ws(const attn_args* a) {
-  size_t s = seg_bytes(a);
+  size_t s = seg_bytes(a) + dbias_full_bytes(a);
   s += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));  // delta
   if (a->sink_mode == ATTN_SINK_LEARNABLE) s += align_up((size_t)a->Hq * a->B * pre_blocks(a) * sizeof(float));
   if (du_path(a)) s += align_up(du_raw_bytes(a));
@@ -347,6 +358,13 @@ hipError_t prep_bounds(const attn_args* a, char*& ws, Mask& m, hipStream_t s, bo
     m.k_hi = k_hi;
   }
   return launch ? hipGetLastError() : hipSuccess;
+}
+
+// Element strides of the bias over batch rows and query heads (0 where broadcast)
+void bias_strides(const attn_args* a, long& bs, long& hs) {
+  const long SS = (long)a->Sq * a->Sk;
+  hs = (a->bias_bcast & ATTN_BIAS_BCAST_HEADS) ? 0 : SS;
+  bs = (a->bias_bcast & ATTN_BIAS_BCAST_BATCH) ? 0 : ((a->bias_bcast & ATTN_BIAS_BCAST_HEADS) ? 1 : a->Hq) * SS;
 }
 
 Mask base_mask(const attn_args* a) {
@@ -444,6 +462,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
   p.k = a->k;
   p.v = a->v;
   p.bias = a->bias;
+  bias_strides(a, p.bias_bs, p.bias_hs);
   p.out = out;
   p.lse = lse;
   p.out_lo = out_lo;
@@ -501,6 +520,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   p.k = a->k;
   p.v = a->v;
   p.bias = a->bias;
+  bias_strides(a, p.bias_bs, p.bias_hs);
   p.dout = dout;
   p.lse = lse;
   p.dq = dq;
@@ -512,6 +532,13 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   // the pre-pass computes the bounds; the other phases find them in the workspace
   e = prep_bounds(a, ws, p.mask, s, (phases & kPhasePre) != 0);
   if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
+  // with a broadcast bias the kernels write the full gradient to the workspace
+  void* dbias_user = dbias;
+  if (dbias && a->bias_bcast) {
+    dbias = ws;
+    p.dbias = ws;
+  }
+  ws += dbias_full_bytes(a);
   float* delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));
   float* part = nullptr;
@@ -556,6 +583,10 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   if ((phases & kPhaseDkdv) && a->Sk > 0) {
     e = o.dkdv(a->D, cap, bias, p, l);
     if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
+    if (dbias_user && a->bias_bcast && a->Sq > 0) {
+      e = o.dbias_reduce(dbias, dbias_user, a->Hq, a->bias_bcast, l);
+      if (e != hipSuccess) return hip_fail(e, "dbias reduction launch");
+    }
   }
   if ((phases & kPhaseDq) && a->Sq > 0) {
     e = o.dq(a->D, cap, bias, p, l);

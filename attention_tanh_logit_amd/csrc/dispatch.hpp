@@ -236,6 +236,7 @@ struct TypeOps {
                     float* dsink_part,
                     const float* sink, int sink_mode, int Hq, int rows_per_block, const Launch&);
   hipError_t (*dbias_fill)(void* dbias, const Mask&, int Hq, int rows_per_block, const Launch&);
+  hipError_t (*dbias_reduce)(const void* full, void* out, int Hq, int bcast, const Launch&);
 };
 
 const TypeOps& ops_bf16();
@@ -309,9 +310,16 @@ const TypeOps& ops_f32();
     dbias_fill_kernel<T><<<grid, 256, 0, l.stream>>>(static_cast<T*>(dbias), m, Hq, rpb);                    \
     return hipGetLastError();                                                                               \
   }                                                                                                         \
+  hipError_t reduce_any(const void* full, void* out, int Hq, int bcast, const Launch& l) {                  \
+    const long SS = (long)l.Sq * l.Sk;                                                                      \
+    const long n = (long)((bcast & 1) ? 1 : l.B) * ((bcast & 2) ? 1 : Hq) * SS;                             \
+    dbias_reduce_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, l.stream>>>(                              \
+        static_cast<const T*>(full), static_cast<T*>(out), l.B, Hq, SS, bcast);                             \
+    return hipGetLastError();                                                                               \
+  }                                                                                                         \
   }                                                                                                         \
   const TypeOps& NAME() {                                                                                   \
-    static const TypeOps o = {fwd_any, dq_any, dkdv_any, pre_any, fill_any};                               \
+    static const TypeOps o = {fwd_any, dq_any, dkdv_any, pre_any, fill_any, reduce_any};                   \
     return o;                                                                                               \
   }                                                                                                         \
   }

@@ -416,7 +416,7 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
     for (int cc = 0; cc < NCC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + 16 * cc + 8 * h);
   }
   const bf16* brow = nullptr;
-  if constexpr (BIAS) brow = reinterpret_cast<const bf16*>(p.bias) + (((long)b * p.Hq + hq) * Sq + min(i, Sq - 1)) * Sk;
+  if constexpr (BIAS) brow = reinterpret_cast<const bf16*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + (long)min(i, Sq - 1) * Sk;
 
   const bool has_sink = p.sink_mode != 0;
   const float sink2 = p.sink_mode == 2 ? p.sink[hq] * kLog2e : 0.0f;
@@ -749,9 +749,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
     const bf16* bcol = nullptr;
     bf16* dbcol = nullptr;
     if constexpr (BIAS) {
-      const long boff = (((long)b * p.Hq + hq) * Sq) * Sk + jc;
-      bcol = reinterpret_cast<const bf16*>(p.bias) + boff;
-      if (p.dbias) dbcol = reinterpret_cast<bf16*>(p.dbias) + boff;
+      bcol = reinterpret_cast<const bf16*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + jc;
+      if (p.dbias) dbcol = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.Hq + hq) * Sq) * Sk + jc;
     }
     auto grads = [&](auto masked) {
 #pragma unroll
@@ -1009,7 +1008,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     if constexpr (BIAS) {
       const int hq = hk * p.G + split * GS + it % GS;
       const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
-      const bf16* g0 = reinterpret_cast<const bf16*>(p.bias) + (((long)b * p.Hq + hq) * Sq) * Sk + k0;
+      const bf16* g0 = reinterpret_cast<const bf16*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + k0;
       const auto rsrc = rows_rsrc(g0, Sk, q0, Sq);
       const int w64 = threadIdx.x >> 6;
 #pragma unroll
@@ -1544,7 +1543,7 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
     }
   }
   const bf16* brow = nullptr;
-  if constexpr (BIAS) brow = reinterpret_cast<const bf16*>(p.bias) + row * Sk;
+  if constexpr (BIAS) brow = reinterpret_cast<const bf16*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + (long)min(i, Sq - 1) * Sk;
 
   f32x16 qacc[NOB];
 #pragma unroll

@@ -36,6 +36,7 @@ struct FwdParams {
   const void* k;
   const void* v;
   const void* bias;
+  long bias_bs, bias_hs;   // bias element strides over batch rows and query heads (0: broadcast)
   void* out;
   float* lse;
   // bf16 only, nullable: out_lo = bf16(O - bf16(O)) of the fp32 output O, so
@@ -58,6 +59,7 @@ struct BwdParams {
   const void* k;
   const void* v;
   const void* bias;
+  long bias_bs, bias_hs;   // bias element strides over batch rows and query heads (0: broadcast)
   const void* dout;
   const float* lse;    // [B,Hq,Sq] natural log
   const float* delta;  // [B,Hq,Sq]
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   const bool rows_full = (q0 + BM <= Sq) && !p.mask.dense;
 
   const T* brow = nullptr;
-  if constexpr (BIAS) brow = reinterpret_cast<const T*>(p.bias) + (((long)b * p.Hq + hq) * Sq + min(i, Sq - 1)) * Sk;
+  if constexpr (BIAS) brow = reinterpret_cast<const T*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + (long)min(i, Sq - 1) * Sk;
 
   const bool has_sink = p.sink_mode != 0;
   const float sink2 = p.sink_mode == 2 ? p.sink[hq] * kLog2e : 0.0f;
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   const float lse2 = (i < Sq && lse_i != -INFINITY) ? lse_i * kLog2e : INFINITY;
   const float delta_i = (i < Sq) ? p.delta[row] : 0.0f;
   const T* brow = nullptr;
-  if constexpr (BIAS) brow = reinterpret_cast<const T*>(p.bias) + row * Sk;
+  if constexpr (BIAS) brow = reinterpret_cast<const T*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + (long)min(i, Sq - 1) * Sk;
 
   f32x16 qacc[NOB];
 #pragma unroll
@@ -761,7 +763,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
     const T* bbase = nullptr;
     T* dbbase = nullptr;
     if constexpr (BIAS) {
-      bbase = reinterpret_cast<const T*>(p.bias) + lrow * Sk;
+      bbase = reinterpret_cast<const T*>(p.bias) + b * p.bias_bs + hq * p.bias_hs;
       if (p.dbias) dbbase = reinterpret_cast<T*>(p.dbias) + lrow * Sk;
     }
 #pragma unroll
@@ -1052,6 +1054,26 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* out, const T* out
     __syncthreads();
   }
   if (t == 0) dsink_part[((long)hq * gridDim.z + b) * gridDim.x + blockIdx.x] = red[0];
+}
+
+// The gradient of a bias broadcast over batch rows (bcast & 1) and/or query
+// heads (bcast & 2): the full [B, Hq, Sq*Sk] gradient summed over those
+// dimensions, in fp32 and in a fixed order, into out [Bb, Hb, Sq*Sk].
+template <typename T>
+__global__ __launch_bounds__(256) void dbias_reduce_kernel(const T* full, T* out, int B, int Hq, long SS, int bcast) {
+  const int Hb = (bcast & 2) ? 1 : Hq;
+  const int Bb = (bcast & 1) ? 1 : B;
+  const long x = (long)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (long)Bb * Hb * SS) return;
+  const long e = x % SS;
+  const int hb = (int)((x / SS) % Hb);
+  const int bb = (int)(x / SS / Hb);
+  const int b0 = (bcast & 1) ? 0 : bb, b1 = (bcast & 1) ? B : bb + 1;
+  const int h0 = (bcast & 2) ? 0 : hb, h1 = (bcast & 2) ? Hq : hb + 1;
+  float s = 0.0f;
+  for (int b = b0; b < b1; ++b)
+    for (int h = h0; h < h1; ++h) s += to_f32(full[((long)b * Hq + h) * SS + e]);
+  out[x] = (T)s;
 }
 
 // dbias = 0 on every pair that no query-key visibility covers (the dkdv

@@ -39,6 +39,7 @@ class AttnArgs(ctypes.Structure):
         ("dq_mode", ctypes.c_int),
         ("k_start", ctypes.c_void_p),
         ("mask", ctypes.c_void_p),
+        ("bias_bcast", ctypes.c_int),
     ]
 
 
@@ -142,8 +143,12 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
     for name, t in tensors:
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if bias is not None and tuple(bias.shape) != (B, Hq, Sq, Sk):
-        raise ValueError(f"bias must be [B, Hq, Sq, Sk] = {(B, Hq, Sq, Sk)}")
+    bias_bcast = 0
+    if bias is not None:
+        if bias.dim() != 4 or tuple(bias.shape[2:]) != (Sq, Sk) or bias.shape[0] not in (1, B) \
+                or bias.shape[1] not in (1, Hq):
+            raise ValueError(f"bias must be [B or 1, Hq or 1, Sq, Sk] with B, Hq, Sq, Sk = {(B, Hq, Sq, Sk)}")
+        bias_bcast = (1 if bias.shape[0] != B else 0) | (2 if bias.shape[1] != Hq else 0)
     if segment_ids is not None and (segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) != (B, Sq)):
         raise ValueError("segment_ids must be int32 [B, Sq]")
     if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
@@ -182,6 +187,7 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
     a.dq_mode = DQ_MODES[dq_mode]
     a.k_start = _ptr(k_start)
     a.mask = _ptr(mask)
+    a.bias_bcast = bias_bcast
     return a
 
 

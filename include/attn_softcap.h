@@ -35,7 +35,8 @@
  *  - k, v, dk, dv     : [B, Sk, Hkv, D]
  *  - THD (varlen): pass cu_seqlens, B = 1 and Sq = Sk = total tokens T; the
  *    tensors are then [T, H, D], which is the same memory as [1, T, H, D].
- *  - bias, dbias      : [B, Hq, Sq, Sk], same dtype as q.
+ *  - bias, dbias      : [B, Hq, Sq, Sk], same dtype as q (or broadcast: see
+ *                       attn_bias_bcast).
  *  - lse              : [B, Hq, Sq] float32, natural log, sink included.
  *  - segment_ids      : [B, Sq] int32, non-decreasing along each row (packed
  *                       rows); a key is visible only inside its own run of
@@ -86,6 +87,15 @@ typedef enum attn_sink_mode {
   ATTN_SINK_OFF_BY_ONE = 1,
   ATTN_SINK_LEARNABLE = 2
 } attn_sink_mode;
+
+/* A bias broadcast over batch rows and/or query heads: its shape is
+ * [1 or B, 1 or Hq, Sq, Sk] and dbias has the same shape, the full gradient
+ * summed over the broadcast dimensions (the learnable-sink page's review
+ * "Offset Corrupts Bias Gradient Shape": dbias follows the bias shape). */
+typedef enum attn_bias_bcast {
+  ATTN_BIAS_BCAST_BATCH = 1,
+  ATTN_BIAS_BCAST_HEADS = 2
+} attn_bias_bcast;
 
 /* How the backward forms dq (the same result either way, to rounding).
  *  - ATTN_DQ_DU_BLOCKS: the dk/dv kernel hands dU = dS * (1 - tanh^2) to the
@@ -144,6 +154,7 @@ typedef struct attn_args {
                                   maximum, which equals it then) */
   const uint8_t* mask;         /* nullable: [B, Sq, Sk] bytes (THD: [T, T]), nonzero = visible; 16-byte
                                   aligned.  Every tile then takes the per-pair masked path (slower) */
+  int bias_bcast;              /* 0: bias and dbias are [B, Hq, Sq, Sk]; else attn_bias_bcast flags */
 } attn_args;
 
 /* Host-only check of `a` (no device access, nothing launched).  Returns the
@@ -161,11 +172,13 @@ attn_status attn_validate(const attn_args* a);
  *    int32 [B*Sk] array of visibility bounds;
  *  - backward: the same runs, delta [B*Hq*Sq] fp32, sink-gradient partials
  *    with a learnable sink, the dU blocks when dq_mode resolves to
- *    ATTN_DQ_DU_BLOCKS (see attn_dq_mode), and for bf16 with D = 64, 128 or
- *    256 when B*Hkv*ceil(Sk/128) < 1024, 2*s*B*Sk*Hkv*D*4 bytes of fp32
- *    partial dK/dV: the dk/dv kernel then splits each GQA group's query
- *    heads over s workgroups (s the smallest divisor of Hq/Hkv reaching 1024
- *    workgroups, else the largest), summed afterwards in a fixed order. */
+ *    ATTN_DQ_DU_BLOCKS (see attn_dq_mode), a full [B, Hq, Sq, Sk] dbias in
+ *    the input dtype when the bias is broadcast (reduced into the caller's
+ *    dbias), and for bf16 with D = 64, 128 or 256 when B*Hkv*ceil(Sk/128) <
+ *    1024, 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial dK/dV: the dk/dv kernel
+ *    then splits each GQA group's query heads over s workgroups (s the
+ *    smallest divisor of Hq/Hkv reaching 1024 workgroups, else the largest),
+ *    summed afterwards in a fixed order. */
 size_t attn_fwd_workspace_size(const attn_args* a);
 size_t attn_bwd_workspace_size(const attn_args* a);
 
@@ -216,7 +229,8 @@ attn_status attn_bwd(const attn_args* a, const void* out, const void* out_lo, co
  *                   on the masked pairs (dbias nullable);
  *  - attn_bwd_dkdv: dk, dv and dbias on the visible pairs, and for bf16 with
  *                   D = 128 or 256 also its zeros (dbias nullable, complete
- *                   once attn_bwd_pre and attn_bwd_dkdv have both run);
+ *                   once attn_bwd_pre and attn_bwd_dkdv have both run; a
+ *                   broadcast dbias is reduced at the end of this phase);
  *  - attn_bwd_dq:   dq. */
 attn_status attn_bwd_pre(const attn_args* a, const void* out, const void* out_lo, const float* lse,
                          const void* dout, void* dbias, float* dsink, void* workspace, size_t workspace_bytes,

@@ -53,7 +53,7 @@ def to_dev(x, dtype: str, device="cuda"):
 
 
 def case(dtype="bf16", B=2, S=200, Hq=4, Hkv=2, D=64, causal=True, window=0, softcap=30.0, q_scale=4.0,
-         sink_mode="none", bias=False, segments=None, seed=0, Sk=None):
+         sink_mode="none", bias=False, segments=None, seed=0, Sk=None, bias_bcast=""):
     """Random inputs for one case (numpy fp32 values, bf16-rounded for bf16)."""
     rng = np.random.default_rng(seed)
     Sk = S if Sk is None else Sk
@@ -65,7 +65,9 @@ def case(dtype="bf16", B=2, S=200, Hq=4, Hkv=2, D=64, causal=True, window=0, sof
     sink = None
     if sink_mode == "learnable":
         sink = rng.standard_normal(Hq, dtype=f) * f(5.0)
-    b = rng.standard_normal((B, Hq, S, Sk), dtype=f) * f(0.5) if bias else None
+    # bias_bcast: "batch" and/or "heads" give the bias a 1 in that dimension (broadcast)
+    bshape = (1 if "batch" in bias_bcast else B, 1 if "heads" in bias_bcast else Hq, S, Sk)
+    b = rng.standard_normal(bshape, dtype=f) * f(0.5) if bias else None
     seg = None
     if segments is not None:
         seg = np.zeros((B, S), dtype=np.int32)

@@ -83,6 +83,9 @@ BAD = {
     "du_blocks_d512_bias": (dict(D=512, dq_mode=1, bias=0x2000), 2, "DU_BLOCKS"),
     "du_blocks_ragged_bias": (dict(Sq=250, Sk=250, bias=0x2000, dq_mode=1), 2, "DU_BLOCKS"),
     "keys_empty": (dict(Sk=0, causal=0), 2, "Sk == 0"),
+    "bias_bcast_without_bias": (dict(bias_bcast=1), 1, "bias_bcast"),
+    "bias_bcast_bad": (dict(bias=0x2000, bias_bcast=4), 1, "bias_bcast"),
+    "mask_misaligned": (dict(mask=0x3001), 1, "mask"),
 }
 
 
@@ -252,3 +255,22 @@ def test_noalloc_rejects_oversize_before_any_launch():
     a = _args(dq_mode=7)
     assert L.attn_bwd_noalloc(ctypes.byref(a), 0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, None,
                               None) == 1
+
+
+def test_broadcast_bias_workspace_holds_the_full_gradient():
+    L = A.lib()
+    full = L.attn_bwd_workspace_size(ctypes.byref(_args(bias=0x2000, dq_mode=2)))
+    for f in (1, 2, 3):
+        bc = L.attn_bwd_workspace_size(ctypes.byref(_args(bias=0x2000, bias_bcast=f, dq_mode=2)))
+        assert bc - full == 2 * 8 * 256 * 256 * 2     # B*Hq*Sq*Sk bf16
+
+
+def test_make_args_broadcast_bias_flags():
+    import torch
+    q = _t(2, 64, 4, 128)
+    k = _t(2, 64, 2, 128)
+    for shape, flags in (((2, 4, 64, 64), 0), ((1, 4, 64, 64), 1), ((2, 1, 64, 64), 2), ((1, 1, 64, 64), 3)):
+        with pytest.raises(ValueError, match="GPU"):       # shapes pass; the host tensors are then refused
+            A.make_args(q, k, k, bias=_t(*shape))
+    with pytest.raises(ValueError, match="bias must be"):
+        A.make_args(q, k, k, bias=_t(3, 4, 64, 64))

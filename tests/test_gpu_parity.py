@@ -212,3 +212,15 @@ def test_random_dense_mask_and_k_start_without_causal(dtype, D):
     _check(dict(c, mask=m))
     ks = np.sort(rng.integers(0, 160, size=(2, 97)), axis=1).astype(np.int32)   # some rows past Sk: empty
     _check(dict(c, k_start=ks))
+
+
+# ---- a bias broadcast over batch rows and/or heads: dbias of the bias's own shape
+
+@pytest.mark.parametrize("dtype,D,S", [("bf16", 64, 200), ("bf16", 128, 200), ("bf16", 256, 200),
+                                       ("bf16", 512, 203), ("fp32", 128, 203), ("fp16", 64, 200)])
+@pytest.mark.parametrize("bcast", ["batch", "heads", "batch_heads"])
+def test_broadcast_bias(dtype, D, S, bcast):
+    c = case(dtype=dtype, D=D, B=2, S=S, Hq=4, Hkv=2, bias=True, softcap=50.0, bias_bcast=bcast,
+             segments=[[45, 70, 190], [128]], sink_mode="learnable")
+    errs = _check(c)
+    assert "dbias" in errs
