@@ -196,9 +196,23 @@ bool has_segments(const attn_args* a) { return a->segment_ids != nullptr || a->c
 // The kernels move rows 16 bytes at a time (vector loads, LDS DMA).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Element strides of the q side and the k side for the layout
+struct Strides {
+  long qbs, qts, kbs, kts;
+};
+Strides strides_of(const attn_args* a) {
+  const long qh = (long)a->Hq * a->D, kh = (long)a->Hkv * a->D;
+  if (a->layout == ATTN_LAYOUT_SBHD) return {qh, qh * a->B, kh, kh * a->B};
+  return {qh * a->Sq, qh, kh * a->Sk, kh};
+}
+long max_token_stride(const attn_args* a) {
+  const Strides t = strides_of(a);
+  return t.qts > t.kts ? t.qts : t.kts;
+}
+
 bool du_supported(const attn_args* a) {
-  return fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, a->bias != nullptr) ||
-         wide_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->bias != nullptr);
+  return fast_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->Sk, a->bias != nullptr) ||
+         wide_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->bias != nullptr);
 }
 
 attn_status validate(const attn_args* a) {
@@ -227,6 +241,10 @@ attn_status validate(const attn_args* a) {
   }
   if (has_segments(a) && a->Sq != a->Sk) return fail(ATTN_INVALID_ARGUMENT, "packed segments need Sq == Sk");
   if (a->mask && ((uintptr_t)a->mask & 15) != 0) return fail(ATTN_INVALID_ARGUMENT, "mask must be 16-byte aligned");
+  if (a->layout != ATTN_LAYOUT_BSHD && a->layout != ATTN_LAYOUT_SBHD)
+    return fail(ATTN_INVALID_ARGUMENT, "layout must be ATTN_LAYOUT_BSHD or ATTN_LAYOUT_SBHD");
+  if (a->layout == ATTN_LAYOUT_SBHD && a->cu_seqlens && a->B != 1)
+    return fail(ATTN_INVALID_ARGUMENT, "cu_seqlens needs B == 1");
   if (a->bias_bcast < 0 || a->bias_bcast > 3)
     return fail(ATTN_INVALID_ARGUMENT, "bias_bcast must be a combination of ATTN_BIAS_BCAST_BATCH and _HEADS");
   if (a->bias_bcast && !a->bias) return fail(ATTN_INVALID_ARGUMENT, "bias_bcast given without a bias");
@@ -282,7 +300,7 @@ bool du_path(const attn_args* a) {
 // writes those zeros and the dk/dv kernel the visible pairs.
 bool dkdv_writes_dbias_zeros(const attn_args* a) {
   return a->bias != nullptr && (a->D == 128 || a->D == 256) &&
-         fast_ok(a->dtype == ATTN_BF16, a->D, a->Hq, a->Hkv, a->Sk, true);
+         fast_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->Sk, true);
 }
 
 // Query-head splits of the bf16 dk/dv kernels (both take 128 keys per
@@ -291,8 +309,8 @@ bool dkdv_writes_dbias_zeros(const attn_args* a) {
 // the GPU to a few long workgroups; 1 when there are enough already.
 int head_split(const attn_args* a) {
   const bool bf = a->dtype == ATTN_BF16, bias = a->bias != nullptr;
-  const bool wide = wide_ok(bf, a->D, a->Hq, a->Hkv, bias);
-  if (!fast_ok(bf, a->D, a->Hq, a->Hkv, a->Sk, bias) && !wide) return 1;
+  const bool wide = wide_ok(bf, a->D, max_token_stride(a), bias);
+  if (!fast_ok(bf, a->D, max_token_stride(a), a->Sk, bias) && !wide) return 1;
   const int bnk = wide ? 32 : 128;   // keys per dk/dv workgroup (as counted here)
   const long wgs = (long)((a->Sk + bnk - 1) / bnk) * a->Hkv * a->B;
   const int G = a->Hq / a->Hkv;
@@ -466,6 +484,11 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
   p.out = out;
   p.lse = lse;
   p.out_lo = out_lo;
+  const Strides st_ = strides_of(a);
+  p.qbs = st_.qbs;
+  p.qts = st_.qts;
+  p.kbs = st_.kbs;
+  p.kts = st_.kts;
   p.mask = base_mask(a);
   hipError_t e = prep_bounds(a, ws, p.mask, s, true);
   if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
@@ -477,7 +500,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
   p.sink = a->sink;
   p.sink_mode = a->sink_mode;
   p.reverse = a->causal ? 1 : 0;
-  const Launch l{a->B, a->Sq, a->Sk, s};
+  const Launch l{a->B, a->Sq, a->Sk, s, st_.qbs, st_.qts, st_.kbs, st_.kts};
   e = ops(a).fwd(a->D, a->softcap > 0.0f, a->bias != nullptr, p, l);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   return ATTN_OK;
@@ -527,6 +550,11 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   p.dk = dk;
   p.dv = dv;
   p.dbias = dbias;
+  const Strides st_ = strides_of(a);
+  p.qbs = st_.qbs;
+  p.qts = st_.qts;
+  p.kbs = st_.kbs;
+  p.kts = st_.kts;
   p.mask = base_mask(a);
   hipError_t e = hipSuccess;
   // the pre-pass computes the bounds; the other phases find them in the workspace
@@ -561,7 +589,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   p.G = a->Hq / a->Hkv;
   fill_consts(a, p.scale, p.sl2, p.xc, p.bc, p.cl2);
   p.reverse = a->causal ? 1 : 0;
-  const Launch l{a->B, a->Sq, a->Sk, s};
+  const Launch l{a->B, a->Sq, a->Sk, s, st_.qbs, st_.qts, st_.kbs, st_.kts};
   const TypeOps& o = ops(a);
   const bool cap = a->softcap > 0.0f, bias = a->bias != nullptr;
   if (phases & kPhasePre) {

@@ -76,6 +76,7 @@ ATL_DKDV(f16, 512, 128, 1, 128)
 struct Launch {
   int B, Sq, Sk;
   hipStream_t stream;
+  long qbs, qts, kbs, kts;   // element strides of batch rows and tokens, q side and k side
 };
 
 template <typename T, int D> constexpr int fwd_rows() { return 32 * FwdCfg<T, D>::NQG; }
@@ -88,18 +89,17 @@ template <typename T, int D> constexpr bool use_fast() {
 }
 
 // The fast kernels address a streamed tile through a buffer resource with
-// 32-bit byte offsets: 128 rows of the widest token stride must stay below
-// 2^31 bytes.  The fast path reads bias rows 8 keys at a time.
-inline bool fast_ok(bool bf16_input, int D, int Hq, int Hkv, int Sk, bool bias) {
-  const long stride = (long)(Hq > Hkv ? Hq : Hkv) * D;
-  return bf16_input && (D == 64 || D == 128 || D == 256) && 128L * stride * 2 < (1L << 31) &&
+// 32-bit byte offsets: 128 rows of the widest token stride (tstride,
+// elements) must stay below 2^31 bytes.  The fast path reads bias rows 8
+// keys at a time.
+inline bool fast_ok(bool bf16_input, int D, long tstride, int Sk, bool bias) {
+  return bf16_input && (D == 64 || D == 128 || D == 256) && 128L * tstride * 2 < (1L << 31) &&
          (!bias || (Sk % 8 == 0 && Sk >= 8));
 }
 // bf16 with D = 512 and no bias takes the kernels of wide.hpp (same 32-bit
 // buffer offsets as the fast kernels)
-inline bool wide_ok(bool bf16_input, int D, int Hq, int Hkv, bool bias) {
-  const long stride = (long)(Hq > Hkv ? Hq : Hkv) * D;
-  return bf16_input && D == 512 && !bias && 128L * stride * 2 < (1L << 31);
+inline bool wide_ok(bool bf16_input, int D, long tstride, bool bias) {
+  return bf16_input && D == 512 && !bias && 128L * tstride * 2 < (1L << 31);
 }
 template <typename T, int D, bool BIAS> constexpr bool use_wide() {
   return std::is_same<T, bf16>::value && D == 512 && !BIAS;
@@ -107,7 +107,7 @@ template <typename T, int D, bool BIAS> constexpr bool use_wide() {
 
 template <int D, class Params>
 bool fast_fits(const Params& p, const Launch& l, bool bias) {
-  return fast_ok(true, D, p.Hq, p.Hkv, l.Sk, bias);
+  return fast_ok(true, D, p.qts > p.kts ? p.qts : p.kts, l.Sk, bias);
 }
 
 
@@ -124,7 +124,7 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.Hq, p.Hkv, false)) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
       const dim3 grid((l.Sq + 63) / 64, p.Hq, l.B);
       if (CAP && p.cl2 <= 60.0f) fwd512_kernel<CAP, CAP><<<grid, 512, 0, l.stream>>>(p);
       else fwd512_kernel<CAP, false><<<grid, 512, 0, l.stream>>>(p);
@@ -192,20 +192,22 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
         const long nel = (long)l.B * l.Sk * p.Hkv * D;
         const float kscale = p.scale * (CAP ? 4.0f : 1.0f);
         dkv_reduce_kernel<bf16><<<(unsigned)((nel / 4 + 255) / 256), 256, 0, l.stream>>>(
-            p.dkv_part, p.hsplit, nel, kscale, reinterpret_cast<bf16*>(p.dk), reinterpret_cast<bf16*>(p.dv));
+            p.dkv_part, p.hsplit, nel, kscale, reinterpret_cast<bf16*>(p.dk), reinterpret_cast<bf16*>(p.dv), l.Sk,
+            (long)p.Hkv * D, p.kbs, p.kts);
       }
       return hipGetLastError();
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.Hq, p.Hkv, false)) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
       const dim3 grid((l.Sk + 31) / 32, p.Hkv * p.hsplit, l.B);
       dkdv512_kernel<CAP><<<grid, 512, 0, l.stream>>>(p);
       if (p.hsplit > 1) {
         const long nel = (long)l.B * l.Sk * p.Hkv * D;
         const float kscale = p.scale * (CAP ? 4.0f : 1.0f);
         dkv_reduce_kernel<bf16><<<(unsigned)((nel / 4 + 255) / 256), 256, 0, l.stream>>>(
-            p.dkv_part, p.hsplit, nel, kscale, reinterpret_cast<bf16*>(p.dk), reinterpret_cast<bf16*>(p.dv));
+            p.dkv_part, p.hsplit, nel, kscale, reinterpret_cast<bf16*>(p.dk), reinterpret_cast<bf16*>(p.dv), l.Sk,
+            (long)p.Hkv * D, p.kbs, p.kts);
       }
       return hipGetLastError();
     }
@@ -223,7 +225,7 @@ hipError_t launch_pre(const T* out, const T* out_lo, const T* dout, const float*
                       const float* sink, int sink_mode, int Hq, int rows_per_block, const Launch& l) {
   const dim3 grid((l.Sq + rows_per_block - 1) / rows_per_block, Hq, l.B);
   bwd_pre_kernel<T, D><<<grid, 256, 0, l.stream>>>(out, out_lo, dout, lse, delta, dsink_part, sink, sink_mode, l.Sq, Hq,
-                                                   rows_per_block);
+                                                   rows_per_block, l.qbs, l.qts);
   return hipGetLastError();
 }
 

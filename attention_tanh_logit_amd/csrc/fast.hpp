@@ -394,9 +394,9 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
   // slice's V^T fragments are those of column block ob at a column offset
   const int colofs = 32 * NOB * sl;
 
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
-  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
-  const long kstride = (long)p.Hkv * D;
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + koff(p, b, 0, hk, D);
+  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + koff(p, b, 0, hk, D);
+  const long kstride = p.kts;
   const TilePlan<BN, D, NT, true> kplan(kstride);
   const TilePlan<BN, D, NT, false> vplan(kstride);
 
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
   // Q^T fragments of this wave's 32 queries stay in registers
   bf16x8 qf[NCC];
   {
-    const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + (((long)b * Sq + min(i, Sq - 1)) * p.Hq + hq) * D;
+    const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + qoff(p, b, min(i, Sq - 1), hq, D);
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + 16 * cc + 8 * h);
   }
@@ -590,8 +590,8 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
   if (has_sink) ltot += fast_exp2(sink2 - m);
   const float inv = ltot > 0.0f ? oscale / ltot : 0.0f;
   if (i < Sq) {
-    bf16* orow = reinterpret_cast<bf16*>(p.out) + (((long)b * Sq + i) * p.Hq + hq) * D;
-    bf16* lorow = reinterpret_cast<bf16*>(p.out_lo) + (((long)b * Sq + i) * p.Hq + hq) * D;
+    bf16* orow = reinterpret_cast<bf16*>(p.out) + qoff(p, b, i, hq, D);
+    bf16* lorow = reinterpret_cast<bf16*>(p.out_lo) + qoff(p, b, i, hq, D);
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
@@ -656,18 +656,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   const int k0 = kb * BNK;
   const int j = k0 + w * 32 + n;
   const int jc = min(j, Sk - 1);
-  const long qstride = (long)p.Hq * D;
+  const long qstride = p.qts;
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const FragOfs<D, true> fo(lane);
 
   bf16x8 kf[NCC];
   {
-    const bf16* krow = reinterpret_cast<const bf16*>(p.k) + (((long)b * Sk + jc) * p.Hkv + hk) * D;
+    const bf16* krow = reinterpret_cast<const bf16*>(p.k) + koff(p, b, jc, hk, D);
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(krow + 16 * cc + 8 * h);
   }
-  load_tile<BNK, D, NT, false>(sVr, reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D,
-                               (long)p.Hkv * D, k0, Sk);
+  load_tile<BNK, D, NT, false>(sVr, reinterpret_cast<const bf16*>(p.v) + koff(p, b, 0, hk, D),
+                               p.kts, k0, Sk);
 
   int lo_j = 0, hi_j = 0;
   if (j < Sk) queries_of(p.mask, b, j, lo_j, hi_j);
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   auto fetch = [&](int it, bf16* nQ, bf16* nO) {
     const int hq = hk * p.G + split * GS + it % GS;
     const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
-    const long hoff = ((long)b * Sq * p.Hq + hq) * D;
+    const long hoff = qoff(p, b, 0, hq, D);
     load_tile<BMQ, D, NT, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
     load_tile<BMQ, D, NT, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
     if (threadIdx.x < BMQ) {
@@ -850,7 +850,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
       }
     }
   } else if (j < Sk) {
-    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    const long off = koff(p, b, j, hk, D);
     bf16* krow = reinterpret_cast<bf16*>(p.dk) + off;
     bf16* vrow = reinterpret_cast<bf16*>(p.dv) + off;
 #pragma unroll
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   const int kw = k0 + 16 * kgi;
   const int j = kw + r;
   const int jc = min(j, Sk - 1);
-  const long qstride = (long)p.Hq * D;
+  const long qstride = p.qts;
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const Frag16Ofs<D> fo(lane);
 
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   // 8(c + 4g) .. + 7 of key kw + r (the B operand of S = Q K^T, dP = dO V^T)
   bf16x8 kf[NC], vf[NC];
   {
-    const long off = (((long)b * Sk + jc) * p.Hkv + hk) * D;
+    const long off = koff(p, b, jc, hk, D);
     const bf16* krow = reinterpret_cast<const bf16*>(p.k) + off;
     const bf16* vrow = reinterpret_cast<const bf16*>(p.v) + off;
 #pragma unroll
@@ -983,7 +983,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   auto fetch = [&](int it, bf16* nQ, bf16* nO) {
     const int hq = hk * p.G + split * GS + it % GS;
     const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
-    const long hoff = ((long)b * Sq * p.Hq + hq) * D;
+    const long hoff = qoff(p, b, 0, hq, D);
     load_tile<BMQ, D, NT, false, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
     load_tile<BMQ, D, NT, false, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
     if (threadIdx.x < BMQ) {
@@ -1206,7 +1206,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       *reinterpret_cast<f32x4*>(vp + colofs + 16 * ob + 4 * g) = vacc[ob];
     }
   } else if (j < Sk) {
-    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    const long off = koff(p, b, j, hk, D);
     bf16* krow = reinterpret_cast<bf16*>(p.dk) + off;
     bf16* vrow = reinterpret_cast<bf16*>(p.dv) + off;
     const float ks = p.scale * kGrad4<CAP>;
@@ -1252,9 +1252,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
 // dk = kscale * sum of the dK partials, dv = sum of the dV partials, over the
 // hsplit query-head splits in a fixed order (deterministic); 4 elements per
 // thread, nel = B * Sk * Hkv * D (a multiple of 4).
+// The partials are [B, Sk, Hkv, D] contiguous; dk and dv have the k-side
+// layout's strides (kbs, kts; hd = Hkv * D elements per token).
 template <typename T>
 __global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* part, int hsplit, long nel, float kscale, T* dk,
-                                                        T* dv) {
+                                                        T* dv, int Sk, long hd, long kbs, long kts) {
   static_assert(std::is_same<T, bf16>::value, "bf16 outputs");
   const long i = 4 * ((long)blockIdx.x * 256 + threadIdx.x);
   if (i >= nel) return;
@@ -1269,8 +1271,11 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* part, int 
     ok[e] = (bf16)(sk[e] * kscale);
     ov[e] = (bf16)sv[e];
   }
-  *reinterpret_cast<bf16x4*>(dk + i) = ok;
-  *reinterpret_cast<bf16x4*>(dv + i) = ov;
+  // 4 consecutive elements share a token (hd is a multiple of 4)
+  const long tok = i / hd;
+  const long o = (tok / Sk) * kbs + (tok % Sk) * kts + i % hd;
+  *reinterpret_cast<bf16x4*>(dk + o) = ok;
+  *reinterpret_cast<bf16x4*>(dv + o) = ov;
 }
 
 // ============================================================== backward: dq from dU
@@ -1364,8 +1369,8 @@ __global__ __launch_bounds__(256 * NSL, NSL > 1 ? 1 : (NST >= 3 ? 3 : 2)) void d
   const int i = qw + n;
   const FragOfs<D, true> fo(lane);
 
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
-  const long kstride = (long)p.Hkv * D;
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + koff(p, b, 0, hk, D);
+  const long kstride = p.kts;
 
   const int ilast = min(q0 + BM, Sq) - 1;
   int lo_first, hi_first, lo_last, hi_last;
@@ -1456,7 +1461,7 @@ __global__ __launch_bounds__(256 * NSL, NSL > 1 ? 1 : (NST >= 3 ? 3 : 2)) void d
   }
 
   if (i < Sq) {
-    bf16* drow = reinterpret_cast<bf16*>(p.dq) + (((long)b * Sq + i) * p.Hq + hq) * D;
+    bf16* drow = reinterpret_cast<bf16*>(p.dq) + qoff(p, b, i, hq, D);
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
@@ -1513,9 +1518,9 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const FragOfs<D, ROWPERM_TR> fo(lane);
 
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
-  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
-  const long kstride = (long)p.Hkv * D;
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + koff(p, b, 0, hk, D);
+  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + koff(p, b, 0, hk, D);
+  const long kstride = p.kts;
 
   int lo_i = 0, hi_i = 0;
   if (i < Sq) keys_of(p.mask, b, i, lo_i, hi_i);
@@ -1533,7 +1538,7 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
 
   bf16x8 qf[NCC], of[NCC];
   {
-    const long off = (((long)b * Sq + min(i, Sq - 1)) * p.Hq + hq) * D;
+    const long off = qoff(p, b, min(i, Sq - 1), hq, D);
     const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + off;
     const bf16* orow = reinterpret_cast<const bf16*>(p.dout) + off;
 #pragma unroll
@@ -1611,7 +1616,7 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   }
 
   if (i < Sq) {
-    bf16* drow = reinterpret_cast<bf16*>(p.dq) + (((long)b * Sq + i) * p.Hq + hq) * D;
+    bf16* drow = reinterpret_cast<bf16*>(p.dq) + qoff(p, b, i, hq, D);
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll

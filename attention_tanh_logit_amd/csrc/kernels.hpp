@@ -43,6 +43,7 @@ struct FwdParams {
   // that out + out_lo carries O to about 16 bits and the backward's
   // delta = <dO, O> does not inherit the rounding of out
   void* out_lo;
+  long qbs, qts, kbs, kts;   // element strides: batch row and token, q side and k side
   Mask mask;
   int Hq, Hkv, G;
   float sl2;    // scale * log2(e)            (no cap)
@@ -71,6 +72,7 @@ struct BwdParams {
   // read by the dq kernel; null when dq recomputes the probabilities itself
   void* du;
   int nkb32, nqb32;  // blocks along keys and along queries
+  long qbs, qts, kbs, kts;   // element strides: batch row and token, q side and k side
   Mask mask;
   int Hq, Hkv, G;
   float scale;
@@ -83,6 +85,18 @@ struct BwdParams {
   int hsplit;
   float* dkv_part;
 };
+
+// Element offset of (batch row b, token t, head h) in a q-side tensor (q, out,
+// out_lo, dout, dq) or a k-side one (k, v, dk, dv): batch and token strides
+// come from the layout (BSHD or SBHD), heads and columns are contiguous.
+template <class P>
+__device__ __forceinline__ long qoff(const P& p, int b, long t, int h, int D) {
+  return b * p.qbs + t * p.qts + (long)h * D;
+}
+template <class P>
+__device__ __forceinline__ long koff(const P& p, int b, long t, int h, int D) {
+  return b * p.kbs + t * p.kts + (long)h * D;
+}
 
 template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };
 
@@ -198,11 +212,11 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   const int q0 = qt * BM;
   const int i = q0 + qg * 32 + n;
 
-  const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
-  const T* kbase = reinterpret_cast<const T*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
-  const T* vbase = reinterpret_cast<const T*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
-  const long qstride = (long)p.Hq * D;
-  const long kstride = (long)p.Hkv * D;
+  const T* qbase = reinterpret_cast<const T*>(p.q) + qoff(p, b, 0, hq, D);
+  const T* kbase = reinterpret_cast<const T*>(p.k) + koff(p, b, 0, hk, D);
+  const T* vbase = reinterpret_cast<const T*>(p.v) + koff(p, b, 0, hk, D);
+  const long qstride = p.qts;
+  const long kstride = p.kts;
 
   // visible key range of this lane's query and of the whole tile
   int lo_i = 0, hi_i = 0;
@@ -396,8 +410,8 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   if (has_sink) ltot += fast_exp2(sink2 - m);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if (i < Sq) {
-    T* orow = reinterpret_cast<T*>(p.out) + (((long)b * Sq + i) * p.Hq + hq) * D;
-    T* lorow = reinterpret_cast<T*>(p.out_lo) + (((long)b * Sq + i) * p.Hq + hq) * D;
+    T* orow = reinterpret_cast<T*>(p.out) + qoff(p, b, i, hq, D);
+    T* lorow = reinterpret_cast<T*>(p.out_lo) + qoff(p, b, i, hq, D);
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
@@ -466,12 +480,12 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   const int q0 = qt * BM;
   const int i = q0 + qg * 32 + n;
 
-  const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
-  const T* obase = reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D;
-  const T* kbase = reinterpret_cast<const T*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
-  const T* vbase = reinterpret_cast<const T*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
-  const long qstride = (long)p.Hq * D;
-  const long kstride = (long)p.Hkv * D;
+  const T* qbase = reinterpret_cast<const T*>(p.q) + qoff(p, b, 0, hq, D);
+  const T* obase = reinterpret_cast<const T*>(p.dout) + qoff(p, b, 0, hq, D);
+  const T* kbase = reinterpret_cast<const T*>(p.k) + koff(p, b, 0, hk, D);
+  const T* vbase = reinterpret_cast<const T*>(p.v) + koff(p, b, 0, hk, D);
+  const long qstride = p.qts;
+  const long kstride = p.kts;
 
   int lo_i = 0, hi_i = 0;
   if (i < Sq) keys_of(p.mask, b, i, lo_i, hi_i);
@@ -656,7 +670,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   }
 
   if (i < Sq) {
-    T* drow = reinterpret_cast<T*>(p.dq) + (((long)b * Sq + i) * p.Hq + hq) * D;
+    T* drow = reinterpret_cast<T*>(p.dq) + qoff(p, b, i, hq, D);
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
@@ -731,10 +745,10 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   const int k0 = kt * BNK;
   const int j = k0 + kg * 32 + n;
 
-  const T* kbase = reinterpret_cast<const T*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
-  const T* vbase = reinterpret_cast<const T*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
-  const long qstride = (long)p.Hq * D;
-  const long kstride = (long)p.Hkv * D;
+  const T* kbase = reinterpret_cast<const T*>(p.k) + koff(p, b, 0, hk, D);
+  const T* vbase = reinterpret_cast<const T*>(p.v) + koff(p, b, 0, hk, D);
+  const long qstride = p.qts;
+  const long kstride = p.kts;
 
   // queries that see this lane's key, and the query range of the whole tile
   int lo_j = 0, hi_j = 0;
@@ -811,8 +825,8 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   if constexpr (ONE) {
   for (int g = 0; g < p.G; ++g) {
     const int hq = hk * p.G + g;
-    const T* qbase = reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D;
-    const T* obase = reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D;
+    const T* qbase = reinterpret_cast<const T*>(p.q) + qoff(p, b, 0, hq, D);
+    const T* obase = reinterpret_cast<const T*>(p.dout) + qoff(p, b, 0, hq, D);
     for (int q0 = qbeg; q0 < hi_last; q0 += BMQ) {
       const bool full = keys_full && q0 >= lo_last && q0 + BMQ <= hi_first;
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -862,8 +876,8 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   const int nitems = p.G * nqt;
   auto head_of = [&](int it) { return hk * p.G + it / nqt; };
   auto q0_of = [&](int it) { return qbeg + (it % nqt) * BMQ; };
-  auto qb_of = [&](int hq) { return reinterpret_cast<const T*>(p.q) + ((long)b * Sq * p.Hq + hq) * D; };
-  auto ob_of = [&](int hq) { return reinterpret_cast<const T*>(p.dout) + ((long)b * Sq * p.Hq + hq) * D; };
+  auto qb_of = [&](int hq) { return reinterpret_cast<const T*>(p.q) + qoff(p, b, 0, hq, D); };
+  auto ob_of = [&](int hq) { return reinterpret_cast<const T*>(p.dout) + qoff(p, b, 0, hq, D); };
   RowChunks<T, BMQ, DC, NT> rq, ro;
   RowChunks<T, BNK, DC, NT> rk, rv;
   RowPairChunks<T, BMQ, DC, NT> rqt, rot;
@@ -979,8 +993,8 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   }
 
   if (j < Sk) {
-    T* krow = reinterpret_cast<T*>(p.dk) + (((long)b * Sk + j) * p.Hkv + hk) * D;
-    T* vrow = reinterpret_cast<T*>(p.dv) + (((long)b * Sk + j) * p.Hkv + hk) * D;
+    T* krow = reinterpret_cast<T*>(p.dk) + koff(p, b, j, hk, D);
+    T* vrow = reinterpret_cast<T*>(p.dv) + koff(p, b, j, hk, D);
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
@@ -1006,7 +1020,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* out, const T* out_lo, const T* dout, const float* lse, float* delta,
                                                       float* dsink_part, const float* sink, int sink_mode, int Sq,
-                                                      int Hq, int rows_per_block) {
+                                                      int Hq, int rows_per_block, long qbs, long qts) {
   constexpr int LPR = D / 8;            // lanes per row, 8 elements each
   constexpr int RPP = 256 / LPR;        // rows per pass
   const int hq = blockIdx.y;
@@ -1021,7 +1035,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* out, const T* out
     const int i = r0 + base + rr;
     float s = 0.0f;
     if (base + rr < rows_per_block && i < Sq) {
-      const long off = (((long)b * Sq + i) * Hq + hq) * D + sub * 8;
+      const long off = b * qbs + i * qts + (long)hq * D + sub * 8;
       float a[8], c[8];
       load8(out + off, a);
       load8(dout + off, c);

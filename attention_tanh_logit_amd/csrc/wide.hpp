@@ -82,9 +82,9 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const FragOfs<D, false> fo(lane);
 
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)b * Sk * p.Hkv + hk) * D;
-  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)b * Sk * p.Hkv + hk) * D;
-  const long kstride = (long)p.Hkv * D;
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + koff(p, b, 0, hk, D);
+  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + koff(p, b, 0, hk, D);
+  const long kstride = p.kts;
 
   int lo_i = 0, hi_i = 0;
   if (i < Sq) keys_of(p.mask, b, i, lo_i, hi_i);
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   bf16x8 qf[NCW];
   {
     const bf16* qrow =
-        reinterpret_cast<const bf16*>(p.q) + (((long)b * Sq + min(i, Sq - 1)) * p.Hq + hq) * D + colofs;
+        reinterpret_cast<const bf16*>(p.q) + qoff(p, b, min(i, Sq - 1), hq, D) + colofs;
 #pragma unroll
     for (int c = 0; c < NCW; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h);
   }
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   if (has_sink) ltot += fast_exp2(sink2 - m);
   const float inv = ltot > 0.0f ? oscale / ltot : 0.0f;
   if (i < Sq) {
-    const long orow_off = (((long)b * Sq + i) * p.Hq + hq) * D + colofs;
+    const long orow_off = qoff(p, b, i, hq, D) + colofs;
     bf16* orow = reinterpret_cast<bf16*>(p.out) + orow_off;
     bf16* lorow = reinterpret_cast<bf16*>(p.out_lo) + orow_off;
 #pragma unroll
@@ -274,14 +274,14 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   const int kw = k0 + 16 * kg;
   const int j = kw + r;
   const int jc = min(j, Sk - 1);
-  const long qstride = (long)p.Hq * D;
+  const long qstride = p.qts;
   const LogitK lk(p.sl2, p.xc, p.bc, p.cl2, CAP);
   const Frag16Ofs<D> fo(lane);
 
   // this wave's columns of its keys' K and V rows (B operand of S, dP)
   bf16x8 kf[NCW], vf[NCW];
   {
-    const long off = (((long)b * Sk + jc) * p.Hkv + hk) * D + colofs;
+    const long off = koff(p, b, jc, hk, D) + colofs;
     const bf16* krow = reinterpret_cast<const bf16*>(p.k) + off;
     const bf16* vrow = reinterpret_cast<const bf16*>(p.v) + off;
 #pragma unroll
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   auto head_of = [&](int it) { return hk * p.G + split * GS + it % GS; };
   auto q0_of = [&](int it) { return qbeg + (nqt - 1 - it / GS) * BMQ; };
   auto fetch = [&](int it, bf16* nQ, bf16* nO) {
-    const long hoff = ((long)b * Sq * p.Hq + head_of(it)) * D;
+    const long hoff = qoff(p, b, 0, head_of(it), D);
     const int q0 = q0_of(it);
     load_tile<BMQ, D, NT, false, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
     load_tile<BMQ, D, NT, false, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
       *reinterpret_cast<f32x4*>(vp + colofs + 16 * ob + 4 * g) = vacc[ob];
     }
   } else if (j < Sk) {
-    const long off = (((long)b * Sk + j) * p.Hkv + hk) * D;
+    const long off = koff(p, b, j, hk, D);
     bf16* krow = reinterpret_cast<bf16*>(p.dk) + off;
     bf16* vrow = reinterpret_cast<bf16*>(p.dv) + off;
     const float ks = p.scale * kGrad4<CAP>;

@@ -18,6 +18,7 @@ ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_HIP_ERROR = 0, 1, 2, 3
 ATTN_BF16, ATTN_FP32, ATTN_FP16 = 0, 1, 2
 SINK_MODES = {"none": 0, "off_by_one": 1, "learnable": 2}
 DQ_MODES = {"auto": 0, "du_blocks": 1, "recompute": 2}
+LAYOUTS = {"bshd": 0, "sbhd": 1}
 
 
 class AttnArgs(ctypes.Structure):
@@ -40,6 +41,7 @@ class AttnArgs(ctypes.Structure):
         ("k_start", ctypes.c_void_p),
         ("mask", ctypes.c_void_p),
         ("bias_bcast", ctypes.c_int),
+        ("layout", ctypes.c_int),
     ]
 
 
@@ -101,8 +103,8 @@ def _check(status: int) -> None:
 
 def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
               softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", k_start=None,
-              mask=None) -> AttnArgs:
-    """Fill the C argument struct from tensors (BSHD, or THD with cu_seqlens).
+              mask=None, layout="bshd") -> AttnArgs:
+    """Fill the C argument struct from tensors (BSHD or SBHD, or THD with cu_seqlens).
 
     The C ABI sees only pointers and sizes, so every shape, dtype and device
     check the kernels rely on happens here: k and v must match q's batch and
@@ -116,6 +118,13 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
             raise ValueError("THD layout: q, k, v must be [T, H, D]")
         B, Sq, Hq, D = 1, q.shape[0], q.shape[1], q.shape[2]
         Sk, Hkv = k.shape[0], k.shape[1]
+    elif layout == "sbhd":
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("SBHD layout: q, k, v must be [S, B, H, D]")
+        Sq, B, Hq, D = q.shape
+        Sk, Hkv = k.shape[0], k.shape[2]
+        if k.shape[1] != B:
+            raise ValueError(f"k has batch {k.shape[1]}, q has {B}")
     else:
         if q.dim() != 4 or k.dim() != 4:
             raise ValueError("BSHD layout: q, k, v must be [B, S, H, D]")
@@ -123,6 +132,8 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
         Sk, Hkv = k.shape[1], k.shape[2]
         if k.shape[0] != B:
             raise ValueError(f"k has batch {k.shape[0]}, q has {B}")
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
     if k.shape[-1] != D:
         raise ValueError(f"k has head dim {k.shape[-1]}, q has {D}")
     if k.shape != v.shape:
@@ -188,6 +199,7 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
     a.k_start = _ptr(k_start)
     a.mask = _ptr(mask)
     a.bias_bcast = bias_bcast
+    a.layout = LAYOUTS[layout]
     return a
 
 
@@ -208,8 +220,8 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0, softcap=0.0,
-             scale=0.0, sink_mode="none", sink=None, k_start=None, mask=None, out=None, lse=None, out_lo=None,
-             residual=True):
+             scale=0.0, sink_mode="none", sink=None, k_start=None, mask=None, layout="bshd", out=None, lse=None,
+             out_lo=None, residual=True):
     """Forward: returns (out, lse, out_lo); lse is float32 [B, Hq, Sq] ([Hq, T] for THD).
 
     out_lo (bf16 and fp16; None for fp32 or with ``residual=False``) is the
@@ -219,7 +231,7 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, k_start=k_start,
-                  mask=mask)
+                  mask=mask, layout=layout)
     _check(L.attn_validate(ctypes.byref(a)))
     shape = (a.Hq, a.Sq) if cu_seqlens is not None else (a.B, a.Hq, a.Sq)
     out = torch.empty_like(q) if out is None else _like("out", out, q)
@@ -239,7 +251,7 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
 
 def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None, causal=False,
              window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", k_start=None, mask=None,
-             want_dbias=None, events=None, outputs=None):
+             layout="bshd", want_dbias=None, events=None, outputs=None):
     """Backward: returns (dq, dk, dv, dbias or None, dsink or None).
 
     ``out_lo`` is what :func:`attn_fwd` returned beside ``out`` (bf16; None
@@ -255,7 +267,7 @@ def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=Non
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode,
-                  k_start=k_start, mask=mask)
+                  k_start=k_start, mask=mask, layout=layout)
     _check(L.attn_validate(ctypes.byref(a)))
     _like("out", out, q)
     _like("dout", dout, q)
@@ -300,7 +312,7 @@ def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=Non
 
 def attn_bwd_noalloc(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None,
                      causal=False, window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto",
-                     k_start=None, mask=None, outputs):
+                     k_start=None, mask=None, layout="bshd", outputs):
     """The backward through ``attn_bwd_noalloc``: no workspace, the library's own
     static scratch instead.  ``outputs`` must hold preallocated "dq", "dk", "dv"
     (and "dbias" with a bias, "dsink" with a learnable sink) tensors, each
@@ -309,7 +321,7 @@ def attn_bwd_noalloc(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode,
-                  k_start=k_start, mask=mask)
+                  k_start=k_start, mask=mask, layout=layout)
     _check(L.attn_validate(ctypes.byref(a)))
     _like("out", out, q)
     _like("dout", dout, q)

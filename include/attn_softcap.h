@@ -31,8 +31,8 @@
  *    query row, and its gradient summed over the query rows.
  *
  * Layouts (all contiguous, row-major):
- *  - q, out, dout, dq : [B, Sq, Hq, D]   (BSHD)
- *  - k, v, dk, dv     : [B, Sk, Hkv, D]
+ *  - q, out, dout, dq : [B, Sq, Hq, D]   (BSHD; SBHD [Sq, B, Hq, D]: attn_layout)
+ *  - k, v, dk, dv     : [B, Sk, Hkv, D]  (SBHD [Sk, B, Hkv, D])
  *  - THD (varlen): pass cu_seqlens, B = 1 and Sq = Sk = total tokens T; the
  *    tensors are then [T, H, D], which is the same memory as [1, T, H, D].
  *  - bias, dbias      : [B, Hq, Sq, Sk], same dtype as q (or broadcast: see
@@ -87,6 +87,12 @@ typedef enum attn_sink_mode {
   ATTN_SINK_OFF_BY_ONE = 1,
   ATTN_SINK_LEARNABLE = 2
 } attn_sink_mode;
+
+/* Memory layout of q, k, v, out, out_lo, dout, dq, dk, dv (heads and the
+ * head dimension contiguous in both): BSHD [B, S, H, D] or SBHD [S, B, H, D]
+ * (the bshd and sbhd formats of the learnable-sink page's "Verification"
+ * table).  THD (cu_seqlens) is BSHD with B = 1. */
+typedef enum attn_layout { ATTN_LAYOUT_BSHD = 0, ATTN_LAYOUT_SBHD = 1 } attn_layout;
 
 /* A bias broadcast over batch rows and/or query heads: its shape is
  * [1 or B, 1 or Hq, Sq, Sk] and dbias has the same shape, the full gradient
@@ -155,6 +161,7 @@ typedef struct attn_args {
   const uint8_t* mask;         /* nullable: [B, Sq, Sk] bytes (THD: [T, T]), nonzero = visible; 16-byte
                                   aligned.  Every tile then takes the per-pair masked path (slower) */
   int bias_bcast;              /* 0: bias and dbias are [B, Hq, Sq, Sk]; else attn_bias_bcast flags */
+  int layout;                  /* attn_layout of the q- and k-side tensors (0: BSHD) */
 } attn_args;
 
 /* Host-only check of `a` (no device access, nothing launched).  Returns the

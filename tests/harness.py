@@ -100,11 +100,17 @@ def as_dense_mask(c):
     return dict(c, segment_ids=None, mask=seg[:, :, None] == seg[:, None, :])
 
 
-def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True):
+def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True, layout="bshd"):
+    """The case through the C ABI; results as numpy in BSHD order.  layout="sbhd"
+    hands the library [S, B, H, D] tensors (and transposes the results back)."""
     import attention_tanh_logit_amd as A
     dt = c["dtype"]
-    q, k, v = (to_dev(c[n], dt) for n in ("q", "k", "v"))
+    sb = layout == "sbhd"
+    lay = (lambda x: x.transpose(0, 1).contiguous()) if sb else (lambda x: x)  # noqa: E731
+    q, k, v = (lay(to_dev(c[n], dt)) for n in ("q", "k", "v"))
     kw = dict(causal=c["causal"], window=c["window"], softcap=c["softcap"], sink_mode=c["sink_mode"])
+    if sb:
+        kw["layout"] = "sbhd"
     if c["sink"] is not None:
         kw["sink"] = torch.from_numpy(c["sink"]).cuda()
     if c["bias"] is not None:
@@ -124,13 +130,14 @@ def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True):
         kw["mask"] = mk[0] if thd else mk
     # results land in NaN-filled buffers, so an element the kernels leave unwritten shows up
     nan = float("nan")
-    lse_shape = (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
+    B_, S_ = c["q"].shape[:2]
+    lse_shape = (q.shape[1], q.shape[0]) if thd else (B_, q.shape[2], S_)
     out, lse, out_lo = A.attn_fwd(q, k, v, out=torch.full_like(q, nan),
                                   lse=torch.full(lse_shape, nan, dtype=torch.float32, device=q.device),
                                   residual=residual, **kw)
     res = {"out": out, "lse": lse}
     if backward:
-        do = to_dev(c["dout"], dt)
+        do = lay(to_dev(c["dout"], dt))
         if thd:
             do = do.reshape(-1, *do.shape[2:])
         outs = {"dq": torch.full_like(q, nan), "dk": torch.full_like(k, nan), "dv": torch.full_like(v, nan)}
@@ -140,6 +147,10 @@ def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True):
                                               **kw)
         res.update(dq=dq, dk=dk, dv=dv, dbias=dbias, dsink=dsink)
     torch.cuda.synchronize()
+    if sb:
+        for n in ("out", "dq", "dk", "dv"):
+            if res.get(n) is not None:
+                res[n] = res[n].transpose(0, 1)
     res = {n: (None if t is None else t.float().cpu().numpy()) for n, t in res.items()}
     if thd:  # back to the BSHD view of the same rows
         B, S = c["q"].shape[:2]

@@ -13,12 +13,13 @@ from harness import TOL, as_dense_mask, as_k_start, case, compare, run_gpu, run_
 pytestmark = pytest.mark.gpu
 
 
-def _check(c, thd=False, backward=True, dq_mode="auto", residual=True, per_head=True):
+def _check(c, thd=False, backward=True, dq_mode="auto", residual=True, per_head=True, layout="bshd"):
     """Every tensor, and (per_head) every (batch row, head) slice of it, must meet the bar."""
     print(f"case: dtype={c['dtype']} q={c['q'].shape} k={c['k'].shape} causal={c['causal']} window={c['window']} "
           f"cap={c['softcap']} sink={c['sink_mode']} bias={c['bias'] is not None} "
-          f"seg={c['segment_ids'] is not None} thd={thd} dq_mode={dq_mode} residual={residual}", flush=True)
-    gpu = run_gpu(c, backward=backward, thd=thd, dq_mode=dq_mode, residual=residual)
+          f"seg={c['segment_ids'] is not None} thd={thd} dq_mode={dq_mode} residual={residual} layout={layout}",
+          flush=True)
+    gpu = run_gpu(c, backward=backward, thd=thd, dq_mode=dq_mode, residual=residual, layout=layout)
     ref = run_oracle(c, backward=backward)
     errs = compare(gpu, ref, c["dtype"], per_head=per_head)
     whole = {k: v for k, v in errs.items() if "[" not in k}
@@ -224,3 +225,32 @@ def test_broadcast_bias(dtype, D, S, bcast):
              segments=[[45, 70, 190], [128]], sink_mode="learnable")
     errs = _check(c)
     assert "dbias" in errs
+
+
+# ---- SBHD layout ([S, B, H, D], the sbhd rows of the learnable-sink page's verification table)
+
+SBHD = {
+    "bf16_d64_split": (dict(dtype="bf16", D=64, B=2, S=203, Hq=8, Hkv=2, sink_mode="learnable"), "auto"),
+    "bf16_d64_du": (dict(dtype="bf16", D=64, B=2, S=200, Hq=4, Hkv=2, bias=True, segments=[[45, 70], [128]]),
+                    "du_blocks"),
+    "bf16_d128_bias": (dict(dtype="bf16", D=128, B=3, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0,
+                            segments=[[45, 70, 190], [128], [5]]), "auto"),
+    "bf16_d128_recompute": (dict(dtype="bf16", D=128, B=2, S=203, Hq=4, Hkv=1, window=37), "recompute"),
+    "bf16_d256": (dict(dtype="bf16", D=256, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable"), "auto"),
+    "bf16_d512": (dict(dtype="bf16", D=512, B=2, S=150, Hq=2, Hkv=1, sink_mode="learnable"), "auto"),
+    "bf16_d512_bias": (dict(dtype="bf16", D=512, B=2, S=150, Hq=2, Hkv=1, bias=True), "auto"),
+    "fp32_d128": (dict(dtype="fp32", D=128, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable", window=50), "auto"),
+    "fp16_d64": (dict(dtype="fp16", D=64, B=2, S=203, Hq=4, Hkv=2, causal=False), "auto"),
+}
+
+
+@pytest.mark.parametrize("name", list(SBHD))
+def test_sbhd_layout_matches_oracle_and_bshd(name):
+    kw, mode = SBHD[name]
+    c = case(**kw)
+    _check(c, dq_mode=mode, layout="sbhd")
+    a = run_gpu(c, dq_mode=mode)
+    b = run_gpu(c, dq_mode=mode, layout="sbhd")
+    for n, x in a.items():
+        if x is not None:
+            assert x.tobytes() == b[n].tobytes(), f"{name}: {n} differs between BSHD and SBHD"
