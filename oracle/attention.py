@@ -30,6 +30,15 @@ each line can be checked against the sources by eye:
 * The same review: the bias gradient has the bias's own shape, so a bias
   broadcast over batch rows or heads ([1 or B, 1 or Hq, Sq, Sk]) gets the
   full gradient summed over the broadcast dimensions.
+* Dropout inside the fused kernel: the tokamax PR description keeps
+  ``dropout_mask`` out of its cases and the MaxText commit quoted there
+  rejects packing with dropout where the fallback kernels have none; the
+  learnable-sink page ("What changed") carries the rng state among the
+  forward's auxiliary outputs.  Read here as the usual attention dropout:
+  after the softmax, each probability is kept with probability 1 - p and
+  scaled by 1/(1 - p); lse is that of the softmax before dropout.  The keep
+  decisions come from a counter-based generator (``oracle/philox.py``) keyed
+  by the caller's seed and offset.
 * "Support logits soft-capping in the Pallas-Triton attention VJP", PR
   description: besides segment ids, a packed batch can be given as
   ``k_start`` (per query, the first key it may see) or as a dense boolean
@@ -121,12 +130,13 @@ def _softmax_rows(s, vis, sink_logit):
 
 
 def group_forward(q, k, v, *, scale=None, softcap=0.0, causal=False, window=0,
-                  bias=None, seg=None, sink=None, k_start=None, dense=None, row_block=1024):
+                  bias=None, seg=None, sink=None, k_start=None, dense=None, dropout=None, row_block=1024):
     """Forward pass of one (batch row, KV head) group.
 
     q [Sq,G,D]; k, v [Sk,D]; bias [G,Sq,Sk] or None; seg [S] segment ids or
     None; sink [G] sink logits (off-by-one: zeros) or None; k_start [Sq] or
-    None; dense [Sq,Sk] boolean mask or None.
+    None; dense [Sq,Sk] boolean mask or None; dropout (p, keep) with
+    keep(g, rows) the boolean keep decisions [rows, Sk] of head g, or None.
     Returns out [Sq,G,D] and lse [G,Sq] in fp64.
     """
     q, k, v = (np.asarray(x, dtype=_f64) for x in (q, k, v))
@@ -142,13 +152,15 @@ def group_forward(q, k, v, *, scale=None, softcap=0.0, causal=False, window=0,
             brow = None if bias is None else np.asarray(bias[g, rows], dtype=_f64)
             s, _ = _logits(q[rows, g], k, scale, brow, softcap)
             P, _, l = _softmax_rows(s, vis, None if sink is None else float(sink[g]))
+            if dropout is not None:
+                P = P * dropout[1](g, rows) / (1.0 - dropout[0])
             out[rows, g] = P @ v
             lse[g, rows] = l
     return out, lse
 
 
 def group_backward(q, k, v, dout, *, scale=None, softcap=0.0, causal=False, window=0,
-                   bias=None, seg=None, sink=None, k_start=None, dense=None, want_dbias=None,
+                   bias=None, seg=None, sink=None, k_start=None, dense=None, dropout=None, want_dbias=None,
                    row_block=1024):
     """Backward pass of one (batch row, KV head) group, by recomputation.
 
@@ -175,6 +187,11 @@ def group_backward(q, k, v, dout, *, scale=None, softcap=0.0, causal=False, wind
             P, p_sink, _ = _softmax_rows(s, vis, None if sink is None else float(sink[g]))
             do = dout[rows, g]
             dP = do @ v.T                              # dL/dP
+            Pd = P                                     # the probabilities that multiply V
+            if dropout is not None:
+                kd = dropout[1](g, rows) / (1.0 - dropout[0])
+                Pd = P * kd
+                dP = dP * kd                           # through the kept, rescaled probabilities
             delta = (P * dP).sum(axis=1)               # sum_j P_ij dP_ij (sink column has no value)
             dS = P * (dP - delta[:, None])             # softmax Jacobian, sink column included
             dU = dS * f if f is not None else dS       # chain through the cap: 1 - tanh(u/c)^2
@@ -182,7 +199,7 @@ def group_backward(q, k, v, dout, *, scale=None, softcap=0.0, causal=False, wind
                 dbias[g, rows] = dU
             dq[rows, g] = scale * (dU @ k)
             dk += scale * (dU.T @ q[rows, g])
-            dv += P.T @ do
+            dv += Pd.T @ do
             if dsink is not None:
                 dsink[g] -= float((p_sink * delta).sum())   # dL/dsigma = -sum_i p_i delta_i
     return dq, dk, dv, dbias, dsink
@@ -214,13 +231,25 @@ def _prepare(q, k, v, bias, segment_ids, cu_seqlens, k_start=None, mask=None):
     return q, k, v, bias, segment_ids, k_start, mask, False
 
 
+def _dropout(p, seed, offset, b, hq0, Hq, Sk):
+    """(p, keep) for the group whose first query head is hq0, or None without dropout."""
+    if not p:
+        return None
+    from .philox import dropout_keep
+
+    def keep(g, rows):
+        r = np.arange(rows.start, rows.stop) if isinstance(rows, slice) else np.asarray(rows)
+        return dropout_keep(b, hq0 + g, Hq, r, Sk, p, seed, offset)
+    return (float(p), keep)
+
+
 def _groups(B, Hkv, groups):
     return [(b, h) for b in range(B) for h in range(Hkv)] if groups is None else list(groups)
 
 
 def attention_forward(q, k, v, *, softcap=0.0, causal=False, window=0, scale=None,
                       bias=None, segment_ids=None, cu_seqlens=None, sink=None, k_start=None,
-                      mask=None, groups=None):
+                      mask=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0, groups=None):
     """Whole forward in BSHD layout (THD when ``cu_seqlens`` is given).
 
     q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (THD: [T,H,D]); bias [B,Hq,Sq,Sk];
@@ -248,7 +277,8 @@ def attention_forward(q, k, v, *, softcap=0.0, causal=False, window=0, scale=Non
                              seg=None if seg is None else seg[b],
                              sink=None if sink is None else sink[hs],
                              k_start=None if k_start is None else k_start[b],
-                             dense=None if mask is None else mask[b])
+                             dense=None if mask is None else mask[b],
+                             dropout=_dropout(dropout_p, dropout_seed, dropout_offset, b, h * G, Hq, k.shape[1]))
         out[b, :, hs] = o
         lse[b, hs] = l
     if thd:
@@ -258,7 +288,7 @@ def attention_forward(q, k, v, *, softcap=0.0, causal=False, window=0, scale=Non
 
 def attention_backward(q, k, v, dout, *, softcap=0.0, causal=False, window=0, scale=None,
                        bias=None, segment_ids=None, cu_seqlens=None, sink=None, k_start=None,
-                       mask=None, want_dbias=None, groups=None):
+                       mask=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0, want_dbias=None, groups=None):
     """Whole backward: dq, dk, dv, dbias (or None), dsink (or None), fp64.
 
     dsink sums over every batch row and query row that ``groups`` covers.
@@ -288,7 +318,9 @@ def attention_backward(q, k, v, dout, *, softcap=0.0, causal=False, window=0, sc
                            seg=None if seg is None else seg[b],
                            sink=None if sink is None else sink[hs],
                            k_start=None if k_start is None else k_start[b],
-                           dense=None if mask is None else mask[b], want_dbias=want_dbias)
+                           dense=None if mask is None else mask[b],
+                           dropout=_dropout(dropout_p, dropout_seed, dropout_offset, b, h * G, Hq, k.shape[1]),
+                           want_dbias=want_dbias)
         dq[b, :, hs], dk[b, :, h], dv[b, :, h] = r[0], r[1], r[2]
         if dbias is not None:
             dbias[b, hs] = r[3]
