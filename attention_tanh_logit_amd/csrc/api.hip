@@ -211,6 +211,7 @@ long max_token_stride(const attn_args* a) {
 }
 
 bool du_supported(const attn_args* a) {
+  if (a->dropout_p > 0.0f) return false;   // dropout runs on the generic kernels
   return fast_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->Sk, a->bias != nullptr) ||
          wide_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->bias != nullptr);
 }
@@ -241,6 +242,8 @@ attn_status validate(const attn_args* a) {
   }
   if (has_segments(a) && a->Sq != a->Sk) return fail(ATTN_INVALID_ARGUMENT, "packed segments need Sq == Sk");
   if (a->mask && ((uintptr_t)a->mask & 15) != 0) return fail(ATTN_INVALID_ARGUMENT, "mask must be 16-byte aligned");
+  if (!(a->dropout_p >= 0.0f && a->dropout_p < 1.0f))
+    return fail(ATTN_INVALID_ARGUMENT, "dropout_p must be in [0, 1)");
   if (a->layout != ATTN_LAYOUT_BSHD && a->layout != ATTN_LAYOUT_SBHD)
     return fail(ATTN_INVALID_ARGUMENT, "layout must be ATTN_LAYOUT_BSHD or ATTN_LAYOUT_SBHD");
   if (a->layout == ATTN_LAYOUT_SBHD && a->cu_seqlens && a->B != 1)
@@ -255,7 +258,8 @@ attn_status validate(const attn_args* a) {
   if (a->dq_mode != ATTN_DQ_AUTO && a->dq_mode != ATTN_DQ_DU_BLOCKS && a->dq_mode != ATTN_DQ_RECOMPUTE)
     return fail(ATTN_INVALID_ARGUMENT, "dq_mode must be ATTN_DQ_AUTO, ATTN_DQ_DU_BLOCKS or ATTN_DQ_RECOMPUTE");
   if (a->dq_mode == ATTN_DQ_DU_BLOCKS && !du_supported(a))
-    return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs bf16 with D = 64, 128 or 256 (and, with a bias, Sk % 8 == 0)");
+    return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs bf16 with D = 64, 128 or 256 (with a bias, Sk % 8 == 0) "
+                                  "or D = 512 without a bias, and no dropout");
   if ((long long)a->B * a->Sq > 0 && a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
   const size_t elems = (size_t)a->B * (a->Sq + a->Sk);
   if (elems != 0 && (!a->q || !a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "q, k and v must not be NULL");
@@ -299,7 +303,7 @@ bool du_path(const attn_args* a) {
 // dbias, the zeros of the masked pairs included; elsewhere the pre-pass
 // writes those zeros and the dk/dv kernel the visible pairs.
 bool dkdv_writes_dbias_zeros(const attn_args* a) {
-  return a->bias != nullptr && (a->D == 128 || a->D == 256) &&
+  return a->bias != nullptr && (a->D == 128 || a->D == 256) && a->dropout_p == 0.0f &&
          fast_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->Sk, true);
 }
 
@@ -308,7 +312,7 @@ bool dkdv_writes_dbias_zeros(const attn_args* a) {
 // (four per CU), so that a small batch with a wide GQA group does not leave
 // the GPU to a few long workgroups; 1 when there are enough already.
 int head_split(const attn_args* a) {
-  const bool bf = a->dtype == ATTN_BF16, bias = a->bias != nullptr;
+  const bool bf = a->dtype == ATTN_BF16 && a->dropout_p == 0.0f, bias = a->bias != nullptr;
   const bool wide = wide_ok(bf, a->D, max_token_stride(a), bias);
   if (!fast_ok(bf, a->D, max_token_stride(a), a->Sk, bias) && !wide) return 1;
   const int bnk = wide ? 32 : 128;   // keys per dk/dv workgroup (as counted here)
@@ -383,6 +387,18 @@ void bias_strides(const attn_args* a, long& bs, long& hs) {
   const long SS = (long)a->Sq * a->Sk;
   hs = (a->bias_bcast & ATTN_BIAS_BCAST_HEADS) ? 0 : SS;
   bs = (a->bias_bcast & ATTN_BIAS_BCAST_BATCH) ? 0 : ((a->bias_bcast & ATTN_BIAS_BCAST_HEADS) ? 1 : a->Hq) * SS;
+}
+
+Dropout dropout_of(const attn_args* a) {
+  Dropout d;
+  d.on = a->dropout_p > 0.0f;
+  const double t = std::floor((double)a->dropout_p * 4294967296.0);
+  d.thresh = (uint32_t)(t > 4294967295.0 ? 4294967295.0 : t);
+  d.seed_lo = (uint32_t)(a->dropout_seed & 0xFFFFFFFFu);
+  d.seed_hi = (uint32_t)(a->dropout_seed >> 32);
+  d.offset = (uint32_t)(a->dropout_offset & 0xFFFFFFFFu);
+  d.scale = (float)(1.0 / (1.0 - (double)a->dropout_p));
+  return d;
 }
 
 Mask base_mask(const attn_args* a) {
@@ -490,6 +506,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
   p.kbs = st_.kbs;
   p.kts = st_.kts;
   p.mask = base_mask(a);
+  p.drop = dropout_of(a);
   hipError_t e = prep_bounds(a, ws, p.mask, s, true);
   if (e != hipSuccess) return hip_fail(e, "segment preparation launch");
   p.Hq = a->Hq;
@@ -556,6 +573,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   p.kbs = st_.kbs;
   p.kts = st_.kts;
   p.mask = base_mask(a);
+  p.drop = dropout_of(a);
   hipError_t e = hipSuccess;
   // the pre-pass computes the bounds; the other phases find them in the workspace
   e = prep_bounds(a, ws, p.mask, s, (phases & kPhasePre) != 0);

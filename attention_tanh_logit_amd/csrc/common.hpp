@@ -404,6 +404,49 @@ __device__ __forceinline__ bool dense_ok(const Mask& m, int b, int i, int j) {
   return !m.dense || m.dense[((long)b * m.Sq + i) * m.Sk + j] != 0;
 }
 
+// ---------------------------------------------------------------- dropout
+//
+// Keep decisions from the counter-based generator Philox4x32-10 (Salmon,
+// Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC
+// 2011): ten rounds over a four-word counter and a two-word key; each round
+// forms the full 64-bit products of words 0 and 2 with 0xD2511F53 and
+// 0xCD9E8D57 and crosses their halves with words 1 and 3 and the key, which
+// grows by 0x9E3779B9 and 0xBB67AE85 between rounds.  Pair (query i, key j)
+// of batch row b, query head h uses word j % 4 at counter (j / 4, i,
+// b * Hq + h, offset) under key (seed low, seed high) and is kept iff that
+// word is at least thresh = floor(p 2^32); kept probabilities are scaled by
+// 1 / (1 - p).
+struct Dropout {
+  int on;
+  uint32_t thresh, seed_lo, seed_hi, offset;
+  float scale;   // 1 / (1 - p)
+};
+
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// the four keep decisions of keys j4 .. j4 + 3 (j4 a multiple of 4), bit e for key j4 + e
+__device__ __forceinline__ unsigned keep4(const Dropout& d, int i, int j4, int bh) {
+  uint32_t c[4] = {(uint32_t)j4 >> 2, (uint32_t)i, (uint32_t)bh, d.offset};
+  philox4x32_10(c, d.seed_lo, d.seed_hi);
+  return (c[0] >= d.thresh ? 1u : 0u) | (c[1] >= d.thresh ? 2u : 0u) | (c[2] >= d.thresh ? 4u : 0u) |
+         (c[3] >= d.thresh ? 8u : 0u);
+}
+
 // shuffle with the partner lane l ^ 32 (the other half of a 32x32 column)
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -83,7 +83,8 @@ template <typename T, int D> constexpr int fwd_rows() { return 32 * FwdCfg<T, D>
 template <typename T, int D> constexpr int dq_rows() { return 32 * DqCfg<T, D>::NQG; }
 template <typename T, int D> constexpr int dkdv_keys() { return 32 * DkdvCfg<T, D>::NKG; }
 
-// bf16 with D <= 128 takes the pipelined kernels of fast.hpp
+// bf16 with D <= 256 takes the pipelined kernels of fast.hpp (dropout runs
+// on the generic kernels)
 template <typename T, int D> constexpr bool use_fast() {
   return std::is_same<T, bf16>::value && (D == 64 || D == 128 || D == 256);
 }
@@ -114,7 +115,7 @@ bool fast_fits(const Params& p, const Launch& l, bool bias) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS)) {
+    if (fast_fits<D>(p, l, BIAS) && !p.drop.on) {
       constexpr int NT = D > 128 ? 512 : 256;
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // capped logits with 2 c log2(e) <= 120 keep a fixed reference maximum
@@ -124,7 +125,7 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false) && !p.drop.on) {
       const dim3 grid((l.Sq + 63) / 64, p.Hq, l.B);
       if (CAP && p.cl2 <= 60.0f) fwd512_kernel<CAP, CAP><<<grid, 512, 0, l.stream>>>(p);
       else fwd512_kernel<CAP, false><<<grid, 512, 0, l.stream>>>(p);
@@ -142,7 +143,7 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dq(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS)) {
+    if (fast_fits<D>(p, l, BIAS) && !p.drop.on) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // 32-key tiles, two stages, four workgroups per CU (measured against
       // 64-key tiles and against three stages)
@@ -176,7 +177,7 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS)) {
+    if (fast_fits<D>(p, l, BIAS) && !p.drop.on) {
       if constexpr (D >= 128) {
         // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64
         // queries); at D = 256 two waves per 16 keys and 32-query items
@@ -199,7 +200,7 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false) && !p.drop.on) {
       const dim3 grid((l.Sk + 31) / 32, p.Hkv * p.hsplit, l.B);
       dkdv512_kernel<CAP><<<grid, 512, 0, l.stream>>>(p);
       if (p.hsplit > 1) {

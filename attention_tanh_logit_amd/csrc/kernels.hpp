@@ -44,6 +44,7 @@ struct FwdParams {
   // delta = <dO, O> does not inherit the rounding of out
   void* out_lo;
   long qbs, qts, kbs, kts;   // element strides: batch row and token, q side and k side
+  Dropout drop;              // generic kernels only (the host routes dropout there)
   Mask mask;
   int Hq, Hkv, G;
   float sl2;    // scale * log2(e)            (no cap)
@@ -73,6 +74,7 @@ struct BwdParams {
   void* du;
   int nkb32, nqb32;  // blocks along keys and along queries
   long qbs, qts, kbs, kts;   // element strides: batch row and token, q side and k side
+  Dropout drop;              // generic kernels only (the host routes dropout there)
   Mask mask;
   int Hq, Hkv, G;
   float scale;
@@ -283,6 +285,17 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
         sacc[kb][j] = pv;
         ps += pv;
       }
+      if (p.drop.on) {
+        // the row sum (lse) is that of the undropped softmax; V sees the kept
+        // probabilities, scaled by 1 / (1 - p) in the epilogue
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const unsigned kp = keep4(p.drop, i, k0 + kb * 32 + acc_row(h, 4 * j4), b * p.Hq + hq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!((kp >> e) & 1u)) sacc[kb][4 * j4 + e] = 0.0f;
+        }
+      }
       pf[kb][0] = to_frag(sacc[kb], 0, (T*)nullptr);
       pf[kb][1] = to_frag(sacc[kb], 8, (T*)nullptr);
     }
@@ -408,7 +421,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   // ---- epilogue: normalise (the sink joins the sum once) and write
   float ltot = lsum + xor32(lsum);
   if (has_sink) ltot += fast_exp2(sink2 - m);
-  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  const float inv = ltot > 0.0f ? (p.drop.on ? p.drop.scale : 1.0f) / ltot : 0.0f;
   if (i < Sq) {
     T* orow = reinterpret_cast<T*>(p.out) + qoff(p, b, i, hq, D);
     T* lorow = reinterpret_cast<T*>(p.out_lo) + qoff(p, b, i, hq, D);
@@ -535,7 +548,14 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
           const int key = k0 + kb * 32 + acc_row(h, j);
           if (key < lo_i || key >= hi_i || !dense_ok(p.mask, b, i, key)) pv = 0.0f;
         }
-        sacc[kb][j] = pv * (dpacc[kb][j] - delta_i) * f;
+        float dp = dpacc[kb][j];
+        if (p.drop.on) {
+          // dP reaches the softmax through the kept, rescaled probabilities
+          const int key = k0 + kb * 32 + acc_row(h, j);
+          const unsigned kp = keep4(p.drop, i, key & ~3, b * p.Hq + hq);
+          dp = ((kp >> (key & 3)) & 1u) ? dp * p.drop.scale : 0.0f;
+        }
+        sacc[kb][j] = pv * (dp - delta_i) * f;
       }
       uf[kb][0] = to_frag(sacc[kb], 0, (T*)nullptr);
       uf[kb][1] = to_frag(sacc[kb], 8, (T*)nullptr);
@@ -773,6 +793,14 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   // ---- P, dU of one (query head, 32-query tile) item from S and dP
   // (lane: key j; register r: query q0 + acc_row(h, r)), as operand fragments
   auto grads = [&](int hq, int q0, bool full, f32x16& sacc, f32x16& dpacc, F* pf, F* uf) {
+    // Explicit wait states between the last MFMA of the S / dP chains and
+    // the reads of their results: on the branch that skips the visibility
+    // test (a fully visible item) the compiler left about 8 after a 16-pass
+    // fp32 MFMA, and that instantiation (fp32, D = 64, no cap, no bias)
+    // read stale dP values under dropout (dk off by 0.2; exact with these).
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     const long lrow = ((long)b * p.Hq + hq) * Sq;
     const T* bbase = nullptr;
     T* dbbase = nullptr;
@@ -792,8 +820,16 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       if (!full) vis = (qi >= lo_j && qi < hi_j);
       // a pair the dense mask removes inside the range gets P = 0 and a dbias of 0
       if (!vis || (!full && !dense_ok(p.mask, b, qi, j))) pv = 0.0f;
-      const float du = pv * (dpacc[r] - sDl[acc_row(h, r)]) * f;
-      sacc[r] = pv;
+      float dp = dpacc[r], pd = pv;
+      if (p.drop.on) {
+        // V and dP see the kept probabilities, scaled by 1 / (1 - p)
+        const unsigned kp = keep4(p.drop, qi, j & ~3, b * p.Hq + hq);
+        const float kd = ((kp >> (j & 3)) & 1u) ? p.drop.scale : 0.0f;
+        dp *= kd;
+        pd *= kd;
+      }
+      const float du = pv * (dp - sDl[acc_row(h, r)]) * f;
+      sacc[r] = pd;
       dpacc[r] = du;
       if constexpr (BIAS) {
         if (dbbase && sl == 0 && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;

@@ -42,6 +42,9 @@ class AttnArgs(ctypes.Structure):
         ("mask", ctypes.c_void_p),
         ("bias_bcast", ctypes.c_int),
         ("layout", ctypes.c_int),
+        ("dropout_p", ctypes.c_float),
+        ("dropout_seed", ctypes.c_uint64),
+        ("dropout_offset", ctypes.c_uint64),
     ]
 
 
@@ -103,7 +106,7 @@ def _check(status: int) -> None:
 
 def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0,
               softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", k_start=None,
-              mask=None, layout="bshd") -> AttnArgs:
+              mask=None, layout="bshd", dropout_p=0.0, dropout_seed=0, dropout_offset=0) -> AttnArgs:
     """Fill the C argument struct from tensors (BSHD or SBHD, or THD with cu_seqlens).
 
     The C ABI sees only pointers and sizes, so every shape, dtype and device
@@ -200,6 +203,9 @@ def make_args(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=F
     a.mask = _ptr(mask)
     a.bias_bcast = bias_bcast
     a.layout = LAYOUTS[layout]
+    a.dropout_p = float(dropout_p)
+    a.dropout_seed = int(dropout_seed) & 0xFFFFFFFFFFFFFFFF
+    a.dropout_offset = int(dropout_offset) & 0xFFFFFFFFFFFFFFFF
     return a
 
 
@@ -220,8 +226,8 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=False, window=0, softcap=0.0,
-             scale=0.0, sink_mode="none", sink=None, k_start=None, mask=None, layout="bshd", out=None, lse=None,
-             out_lo=None, residual=True):
+             scale=0.0, sink_mode="none", sink=None, k_start=None, mask=None, layout="bshd", dropout_p=0.0,
+             dropout_seed=0, dropout_offset=0, out=None, lse=None, out_lo=None, residual=True):
     """Forward: returns (out, lse, out_lo); lse is float32 [B, Hq, Sq] ([Hq, T] for THD).
 
     out_lo (bf16 and fp16; None for fp32 or with ``residual=False``) is the
@@ -231,7 +237,8 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, k_start=k_start,
-                  mask=mask, layout=layout)
+                  mask=mask, layout=layout,
+                  dropout_p=dropout_p, dropout_seed=dropout_seed, dropout_offset=dropout_offset)
     _check(L.attn_validate(ctypes.byref(a)))
     shape = (a.Hq, a.Sq) if cu_seqlens is not None else (a.B, a.Hq, a.Sq)
     out = torch.empty_like(q) if out is None else _like("out", out, q)
@@ -251,7 +258,8 @@ def attn_fwd(q, k, v, *, bias=None, segment_ids=None, cu_seqlens=None, causal=Fa
 
 def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None, causal=False,
              window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto", k_start=None, mask=None,
-             layout="bshd", want_dbias=None, events=None, outputs=None):
+             layout="bshd", dropout_p=0.0, dropout_seed=0, dropout_offset=0, want_dbias=None, events=None,
+             outputs=None):
     """Backward: returns (dq, dk, dv, dbias or None, dsink or None).
 
     ``out_lo`` is what :func:`attn_fwd` returned beside ``out`` (bf16; None
@@ -267,7 +275,8 @@ def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=Non
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode,
-                  k_start=k_start, mask=mask, layout=layout)
+                  k_start=k_start, mask=mask, layout=layout,
+                  dropout_p=dropout_p, dropout_seed=dropout_seed, dropout_offset=dropout_offset)
     _check(L.attn_validate(ctypes.byref(a)))
     _like("out", out, q)
     _like("dout", dout, q)
@@ -312,7 +321,8 @@ def attn_bwd(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=Non
 
 def attn_bwd_noalloc(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment_ids=None, cu_seqlens=None,
                      causal=False, window=0, softcap=0.0, scale=0.0, sink_mode="none", sink=None, dq_mode="auto",
-                     k_start=None, mask=None, layout="bshd", outputs):
+                     k_start=None, mask=None, layout="bshd", dropout_p=0.0, dropout_seed=0, dropout_offset=0,
+                     outputs):
     """The backward through ``attn_bwd_noalloc``: no workspace, the library's own
     static scratch instead.  ``outputs`` must hold preallocated "dq", "dk", "dv"
     (and "dbias" with a bias, "dsink" with a learnable sink) tensors, each
@@ -321,7 +331,8 @@ def attn_bwd_noalloc(q, k, v, out, lse, dout, *, out_lo=None, bias=None, segment
     L = lib()
     a = make_args(q, k, v, bias=bias, segment_ids=segment_ids, cu_seqlens=cu_seqlens, causal=causal,
                   window=window, softcap=softcap, scale=scale, sink_mode=sink_mode, sink=sink, dq_mode=dq_mode,
-                  k_start=k_start, mask=mask, layout=layout)
+                  k_start=k_start, mask=mask, layout=layout,
+                  dropout_p=dropout_p, dropout_seed=dropout_seed, dropout_offset=dropout_offset)
     _check(L.attn_validate(ctypes.byref(a)))
     _like("out", out, q)
     _like("dout", dout, q)

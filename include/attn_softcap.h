@@ -162,6 +162,20 @@ typedef struct attn_args {
                                   aligned.  Every tile then takes the per-pair masked path (slower) */
   int bias_bcast;              /* 0: bias and dbias are [B, Hq, Sq, Sk]; else attn_bias_bcast flags */
   int layout;                  /* attn_layout of the q- and k-side tensors (0: BSHD) */
+  /* Dropout on the attention probabilities inside the kernels (the pages
+   * exclude it or reject it with packing: tokamax PR description, MaxText
+   * commit; the learnable-sink page's "What changed" carries the rng state
+   * among the forward's outputs).  After the softmax each probability is kept
+   * with probability 1 - p and scaled by 1 / (1 - p); lse is that of the
+   * undropped softmax.  Pair (query i, key j) of batch row b, query head h is
+   * kept iff word j % 4 of Philox4x32-10 at counter (j / 4, i, b * Hq + h,
+   * offset % 2^32) under key (seed % 2^32, seed / 2^32) is at least
+   * floor(p * 2^32).  The backward must get the same p, seed and offset.
+   * Runs on the generic (slower) kernels; ATTN_DQ_DU_BLOCKS is unsupported
+   * with it. */
+  float dropout_p;             /* 0: off; in [0, 1) */
+  uint64_t dropout_seed;
+  uint64_t dropout_offset;
 } attn_args;
 
 /* Host-only check of `a` (no device access, nothing launched).  Returns the

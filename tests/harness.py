@@ -53,7 +53,7 @@ def to_dev(x, dtype: str, device="cuda"):
 
 
 def case(dtype="bf16", B=2, S=200, Hq=4, Hkv=2, D=64, causal=True, window=0, softcap=30.0, q_scale=4.0,
-         sink_mode="none", bias=False, segments=None, seed=0, Sk=None, bias_bcast=""):
+         sink_mode="none", bias=False, segments=None, seed=0, Sk=None, bias_bcast="", dropout_p=0.0):
     """Random inputs for one case (numpy fp32 values, bf16-rounded for bf16)."""
     rng = np.random.default_rng(seed)
     Sk = S if Sk is None else Sk
@@ -80,7 +80,8 @@ def case(dtype="bf16", B=2, S=200, Hq=4, Hkv=2, D=64, causal=True, window=0, sof
         if b is not None:
             b = rnd(b)
     return dict(dtype=dtype, q=q, k=k, v=v, dout=do, sink=sink, sink_mode=sink_mode, bias=b, segment_ids=seg,
-                causal=causal, window=window, softcap=softcap, k_start=None, mask=None)
+                causal=causal, window=window, softcap=softcap, k_start=None, mask=None,
+                dropout=(dropout_p, 0x1234_5678_9ABC_DEF0 + seed, 3 + seed) if dropout_p else None)
 
 
 def as_k_start(c):
@@ -111,6 +112,8 @@ def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True, layout="
     kw = dict(causal=c["causal"], window=c["window"], softcap=c["softcap"], sink_mode=c["sink_mode"])
     if sb:
         kw["layout"] = "sbhd"
+    if c.get("dropout"):
+        kw.update(dropout_p=c["dropout"][0], dropout_seed=c["dropout"][1], dropout_offset=c["dropout"][2])
     if c["sink"] is not None:
         kw["sink"] = torch.from_numpy(c["sink"]).cuda()
     if c["bias"] is not None:
@@ -166,6 +169,8 @@ def run_oracle(c, backward=True, groups=None):
               segment_ids=c["segment_ids"], sink=c["sink"] if c["sink_mode"] == "learnable"
               else (np.zeros(c["q"].shape[2]) if c["sink_mode"] == "off_by_one" else None), groups=groups,
               k_start=c.get("k_start"), mask=c.get("mask"))
+    if c.get("dropout"):
+        kw.update(dropout_p=c["dropout"][0], dropout_seed=c["dropout"][1], dropout_offset=c["dropout"][2])
     out, lse = attention_forward(c["q"], c["k"], c["v"], **kw)
     res = {"out": out, "lse": lse}
     if backward:

@@ -86,6 +86,10 @@ BAD = {
     "bias_bcast_without_bias": (dict(bias_bcast=1), 1, "bias_bcast"),
     "bias_bcast_bad": (dict(bias=0x2000, bias_bcast=4), 1, "bias_bcast"),
     "mask_misaligned": (dict(mask=0x3001), 1, "mask"),
+    "dropout_one": (dict(dropout_p=1.0), 1, "dropout_p"),
+    "dropout_negative": (dict(dropout_p=-0.1), 1, "dropout_p"),
+    "dropout_with_du_blocks": (dict(dropout_p=0.1, dq_mode=1), 2, "DU_BLOCKS"),
+    "bad_layout": (dict(layout=2), 1, "layout"),
 }
 
 
@@ -274,3 +278,18 @@ def test_make_args_broadcast_bias_flags():
             A.make_args(q, k, k, bias=_t(*shape))
     with pytest.raises(ValueError, match="bias must be"):
         A.make_args(q, k, k, bias=_t(3, 4, 64, 64))
+
+
+def test_ctypes_struct_matches_the_c_header(tmp_path):
+    """attn_args as the C compiler lays it out (gcc on the header) equals the binding's ctypes struct."""
+    import subprocess
+    names = [f[0] for f in AttnArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "attn_softcap.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(attn_args));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(attn_args, {n}));\n' for n in names) + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    out = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    assert out[0] == ctypes.sizeof(AttnArgs)
+    assert out[1:] == [getattr(AttnArgs, n).offset for n in names]

@@ -254,3 +254,23 @@ def test_sbhd_layout_matches_oracle_and_bshd(name):
     for n, x in a.items():
         if x is not None:
             assert x.tobytes() == b[n].tobytes(), f"{name}: {n} differs between BSHD and SBHD"
+
+
+# ---- dropout inside the kernels: the same Philox4x32-10 keep decisions as the oracle's
+
+DROPOUT = {
+    "causal": dict(),
+    "sink_bias": dict(sink_mode="learnable", bias=True, softcap=50.0),
+    "segments_window": dict(segments=[[45, 70, 190], [128]], window=60, Hq=6, Hkv=2),
+    "no_causal_cross": dict(causal=False, Sk=150, softcap=0.0),
+}
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 512), ("fp16", 128), ("fp32", 64),
+                                     ("fp32", 256)])
+@pytest.mark.parametrize("p", [0.1, 0.5])
+@pytest.mark.parametrize("feat", list(DROPOUT))
+def test_dropout_matches_oracle(dtype, D, p, feat):
+    kw = dict(dtype=dtype, D=D, B=2, S=203, Hq=4, Hkv=2, dropout_p=p)
+    kw.update(DROPOUT[feat])
+    _check(case(**kw))
