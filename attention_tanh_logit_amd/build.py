@@ -38,10 +38,11 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (needs ROCm)")
 
 
-# Per-unit extra flags.  The bf16 unit keeps MFMA accumulators in VGPR form:
+# Per-unit extra flags.  The 16-bit units keep MFMA accumulators in VGPR form:
 # its dk/dv kernel holds two 32x128 fp32 accumulators and, left to the
 # default heuristic, round-trips them through AGPRs on every tile.
-UNIT_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+UNIT_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "attn_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, obj: str, verbose: bool) -> None:

@@ -174,9 +174,44 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 }  // namespace atl
 
+// The fp16 unit's entry points (its argument structs have the layout of ours)
+namespace atl_f16_bridge {
+hipError_t fwd(int D, bool cap, bool bias, const void* p, const void* l);
+hipError_t dq(int D, bool cap, bool bias, const void* p, const void* l);
+hipError_t dkdv(int D, bool cap, bool bias, const void* p, const void* l);
+hipError_t pre(int D, const void* out, const void* out_lo, const void* dout, const float* lse, float* delta,
+               float* part, const float* sink, int sink_mode, int Hq, int rpb, const void* l);
+hipError_t dbias_fill(void* dbias, const void* m, int Hq, int rpb, const void* l);
+hipError_t dbias_reduce(const void* full, void* out, int Hq, int bcast, const void* l);
+}  // namespace atl_f16_bridge
+
 using namespace atl;
 
 namespace {
+
+hipError_t f16_fwd(int D, bool c, bool b, const FwdParams& p, const Launch& l) {
+  return atl_f16_bridge::fwd(D, c, b, &p, &l);
+}
+hipError_t f16_dq(int D, bool c, bool b, const BwdParams& p, const Launch& l) {
+  return atl_f16_bridge::dq(D, c, b, &p, &l);
+}
+hipError_t f16_dkdv(int D, bool c, bool b, const BwdParams& p, const Launch& l) {
+  return atl_f16_bridge::dkdv(D, c, b, &p, &l);
+}
+hipError_t f16_pre(int D, const void* out, const void* out_lo, const void* dout, const float* lse, float* delta,
+                   float* part, const float* sink, int sink_mode, int Hq, int rpb, const Launch& l) {
+  return atl_f16_bridge::pre(D, out, out_lo, dout, lse, delta, part, sink, sink_mode, Hq, rpb, &l);
+}
+hipError_t f16_fill(void* dbias, const Mask& m, int Hq, int rpb, const Launch& l) {
+  return atl_f16_bridge::dbias_fill(dbias, &m, Hq, rpb, &l);
+}
+hipError_t f16_reduce(const void* full, void* out, int Hq, int bcast, const Launch& l) {
+  return atl_f16_bridge::dbias_reduce(full, out, Hq, bcast, &l);
+}
+const TypeOps& ops_fp16() {
+  static const TypeOps o = {f16_fwd, f16_dq, f16_dkdv, f16_pre, f16_fill, f16_reduce};
+  return o;
+}
 
 thread_local std::string g_err;
 
@@ -196,6 +231,9 @@ bool has_segments(const attn_args* a) { return a->segment_ids != nullptr || a->c
 // The kernels move rows 16 bytes at a time (vector loads, LDS DMA).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// bf16 and fp16 run the same kernels (the 16-bit fast paths)
+bool is16(const attn_args* a) { return a->dtype == ATTN_BF16 || a->dtype == ATTN_FP16; }
+
 // Element strides of the q side and the k side for the layout
 struct Strides {
   long qbs, qts, kbs, kts;
@@ -212,8 +250,8 @@ long max_token_stride(const attn_args* a) {
 
 bool du_supported(const attn_args* a) {
   if (a->dropout_p > 0.0f) return false;   // dropout runs on the generic kernels
-  return fast_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->Sk, a->bias != nullptr) ||
-         wide_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->bias != nullptr);
+  return fast_ok(is16(a), a->D, max_token_stride(a), a->Sk, a->bias != nullptr) ||
+         wide_ok(is16(a), a->D, max_token_stride(a), a->bias != nullptr);
 }
 
 attn_status validate(const attn_args* a) {
@@ -304,7 +342,7 @@ bool du_path(const attn_args* a) {
 // writes those zeros and the dk/dv kernel the visible pairs.
 bool dkdv_writes_dbias_zeros(const attn_args* a) {
   return a->bias != nullptr && (a->D == 128 || a->D == 256) && a->dropout_p == 0.0f &&
-         fast_ok(a->dtype == ATTN_BF16, a->D, max_token_stride(a), a->Sk, true);
+         fast_ok(is16(a), a->D, max_token_stride(a), a->Sk, true);
 }
 
 // Query-head splits of the bf16 dk/dv kernels (both take 128 keys per
@@ -312,7 +350,7 @@ bool dkdv_writes_dbias_zeros(const attn_args* a) {
 // (four per CU), so that a small batch with a wide GQA group does not leave
 // the GPU to a few long workgroups; 1 when there are enough already.
 int head_split(const attn_args* a) {
-  const bool bf = a->dtype == ATTN_BF16 && a->dropout_p == 0.0f, bias = a->bias != nullptr;
+  const bool bf = is16(a) && a->dropout_p == 0.0f, bias = a->bias != nullptr;
   const bool wide = wide_ok(bf, a->D, max_token_stride(a), bias);
   if (!fast_ok(bf, a->D, max_token_stride(a), a->Sk, bias) && !wide) return 1;
   const int bnk = wide ? 32 : 128;   // keys per dk/dv workgroup (as counted here)
@@ -347,7 +385,7 @@ size_t bwd_ws(const attn_args* a) {
 }
 
 const TypeOps& ops(const attn_args* a) {
-  return a->dtype == ATTN_BF16 ? ops_bf16() : a->dtype == ATTN_FP16 ? ops_f16() : ops_f32();
+  return a->dtype == ATTN_BF16 ? ops_bf16() : a->dtype == ATTN_FP16 ? ops_fp16() : ops_f32();
 }
 
 // Lays the bounds out in the workspace (advancing ws) and, with launch,

@@ -6,12 +6,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace atl {
+// The kernels live in namespace ATL_NS (atl).  The fp16 unit compiles the
+// same sources a second time with ATL_FAST_F16 set and ATL_NS renamed: there
+// the 16-bit element type `bf16` is IEEE fp16 (_Float16), with the fp16 MFMA
+// and dot instructions, so that fp16 inputs run the same kernels.
+#ifndef ATL_NS
+#define ATL_NS atl
+#endif
+#ifndef ATL_FAST_F16
+#define ATL_FAST_F16 0
+#endif
 
+namespace ATL_NS {
+
+#if ATL_FAST_F16
+typedef _Float16 bf16;
+typedef _Float16 bf16x8 __attribute__((ext_vector_type(8)));
+#else
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16;
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+#endif
+// the 16-bit element type has fp16's exponent range (2^-24 .. 65504)
+constexpr bool kNarrow16 = ATL_FAST_F16 != 0;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -39,14 +55,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { using type = bf16x8; };
-template <> struct Frag<f16> { using type = f16x8; };
 template <> struct Frag<float> { using type = f32x8; };
 
 __device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void mma(f32x16& c, const f16x8& a, const f16x8& b) {
+#if ATL_FAST_F16
   c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+#else
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+#endif
 }
 __device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
 #pragma unroll
@@ -62,8 +78,7 @@ template <typename T>
 __device__ __forceinline__ typename Frag<T>::type lds_frag(const T* p);
 template <>
 __device__ __forceinline__ bf16x8 lds_frag<bf16>(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-template <>
-__device__ __forceinline__ f16x8 lds_frag<f16>(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
+
 template <>
 __device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
   f32x4 a = *reinterpret_cast<const f32x4*>(p);
@@ -81,12 +96,6 @@ __device__ __forceinline__ bf16x8 to_frag(const f32x16& c, int base, bf16*) {
   for (int i = 0; i < 8; ++i) r[i] = (bf16)c[base + i];
   return r;
 }
-__device__ __forceinline__ f16x8 to_frag(const f32x16& c, int base, f16*) {
-  f16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (f16)c[base + i];
-  return r;
-}
 __device__ __forceinline__ f32x8 to_frag(const f32x16& c, int base, float*) {
   f32x8 r;
 #pragma unroll
@@ -97,20 +106,18 @@ __device__ __forceinline__ f32x8 to_frag(const f32x16& c, int base, float*) {
 // ---------------------------------------------------------------- scalar helpers
 
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
-__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// tanh for the soft-cap.  The bf16 and fp16 paths use 1 - 2/(1 + e^{2x})
-// (one exp2, one reciprocal; exact limits +-1 at overflow/underflow,
-// absolute error a few fp32 ulps, far below bf16 or fp16 rounding).  The fp32 path keeps the device
+// tanh for the soft-cap.  The 16-bit paths use 1 - 2/(1 + e^{2x}) (one
+// exp2, one reciprocal; exact limits +-1 at overflow/underflow, absolute
+// error a few fp32 ulps, far below bf16 or fp16 rounding).  The fp32 path keeps the device
 // library's tanhf, which stays accurate to a few ulps relative near 0.
 __device__ __forceinline__ float cap_tanh(float x, bf16*) {
   float e = fast_exp2(x * (2.0f * kLog2e));
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
 }
-__device__ __forceinline__ float cap_tanh(float x, f16*) { return cap_tanh(x, (bf16*)nullptr); }
 __device__ __forceinline__ float cap_tanh(float x, float*) { return tanhf(x); }
 
 template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
@@ -119,12 +126,6 @@ template <> __device__ __forceinline__ void store8<bf16>(bf16* p, const float* v
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = (bf16)v[i];
   *reinterpret_cast<bf16x8*>(p) = r;
-}
-template <> __device__ __forceinline__ void store8<f16>(f16* p, const float* v) {
-  f16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (f16)v[i];
-  *reinterpret_cast<f16x8*>(p) = r;
 }
 template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
   f32x4 a, b;
@@ -142,22 +143,12 @@ __device__ __forceinline__ void store8_lo(bf16* p, const float* v) {
   for (int i = 0; i < 8; ++i) r[i] = (bf16)(v[i] - (float)(bf16)v[i]);
   *reinterpret_cast<bf16x8*>(p) = r;
 }
-__device__ __forceinline__ void store8_lo(f16* p, const float* v) {
-  f16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (f16)(v[i] - (float)(f16)v[i]);
-  *reinterpret_cast<f16x8*>(p) = r;
-}
+
 
 // 8 consecutive values from global memory into fp32 (16-byte aligned for bf16,
 // 32-byte for fp32)
 __device__ __forceinline__ void load8(const bf16* p, float* v) {
   bf16x8 r = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (float)r[i];
-}
-__device__ __forceinline__ void load8(const f16* p, float* v) {
-  f16x8 r = *reinterpret_cast<const f16x8*>(p);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = (float)r[i];
 }
@@ -450,4 +441,4 @@ __device__ __forceinline__ unsigned keep4(const Dropout& d, int i, int j4, int b
 // shuffle with the partner lane l ^ 32 (the other half of a 32x32 column)
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-}  // namespace atl
+}  // namespace ATL_NS

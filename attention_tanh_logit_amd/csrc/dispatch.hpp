@@ -13,7 +13,7 @@
 
 #include "wide.hpp"
 
-namespace atl {
+namespace ATL_NS {
 
 template <typename T, int D> struct FwdCfg;
 template <typename T, int D> struct DqCfg;
@@ -54,20 +54,6 @@ ATL_DKDV(float, 64, 64, 4, 64)
 ATL_DKDV(float, 128, 128, 2, 128)
 ATL_DKDV(float, 256, 64, 1, 64)
 ATL_DKDV(float, 512, 128, 1, 128)
-
-// fp16 takes the generic kernels with the bf16 shapes (same element size)
-ATL_FWD(f16, 64, 64, 4, 64, 64)
-ATL_FWD(f16, 128, 128, 4, 64, 128)
-ATL_FWD(f16, 256, 256, 2, 32, 256)
-ATL_FWD(f16, 512, 128, 2, 64, 128)
-ATL_DQ(f16, 64, 64, 4, 64, 64)
-ATL_DQ(f16, 128, 128, 4, 32, 128)
-ATL_DQ(f16, 256, 256, 2, 32, 256)
-ATL_DQ(f16, 512, 256, 2, 64, 128)
-ATL_DKDV(f16, 64, 64, 4, 64)
-ATL_DKDV(f16, 128, 128, 4, 128)
-ATL_DKDV(f16, 256, 128, 2, 256)
-ATL_DKDV(f16, 512, 128, 1, 128)
 
 #undef ATL_FWD
 #undef ATL_DQ
@@ -119,7 +105,9 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
       constexpr int NT = D > 128 ? 512 : 256;
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // capped logits with 2 c log2(e) <= 120 keep a fixed reference maximum
-      if (CAP && p.cl2 <= 60.0f) fwd_fast_kernel<D, CAP, BIAS, CAP><<<grid, NT, 0, l.stream>>>(p);
+      // (not with fp16 elements: probabilities relative to the cap would
+      // leave fp16's exponent range)
+      if (CAP && p.cl2 <= 60.0f && !kNarrow16) fwd_fast_kernel<D, CAP, BIAS, CAP><<<grid, NT, 0, l.stream>>>(p);
       else fwd_fast_kernel<D, CAP, BIAS, false><<<grid, NT, 0, l.stream>>>(p);
       return hipGetLastError();
     }
@@ -127,7 +115,7 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
   if constexpr (use_wide<T, D, BIAS>()) {
     if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false) && !p.drop.on) {
       const dim3 grid((l.Sq + 63) / 64, p.Hq, l.B);
-      if (CAP && p.cl2 <= 60.0f) fwd512_kernel<CAP, CAP><<<grid, 512, 0, l.stream>>>(p);
+      if (CAP && p.cl2 <= 60.0f && !kNarrow16) fwd512_kernel<CAP, CAP><<<grid, 512, 0, l.stream>>>(p);
       else fwd512_kernel<CAP, false><<<grid, 512, 0, l.stream>>>(p);
       return hipGetLastError();
     }
@@ -246,11 +234,11 @@ const TypeOps& ops_bf16();
 const TypeOps& ops_f16();
 const TypeOps& ops_f32();
 
-}  // namespace atl
+}  // namespace ATL_NS
 
 // Instantiates the TypeOps of one element type.
 #define ATL_DEFINE_TYPE_OPS(T, NAME)                                                                        \
-  namespace atl {                                                                                           \
+  namespace ATL_NS {                                                                                           \
   namespace {                                                                                               \
   template <int D>                                                                                          \
   hipError_t fwd_d(bool cap, bool bias, const FwdParams& p, const Launch& l) {                              \

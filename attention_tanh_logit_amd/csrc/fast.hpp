@@ -29,10 +29,10 @@
 
 #include "kernels.hpp"
 
-namespace atl {
+namespace ATL_NS {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // swap the two bits of a 2-bit index
 __device__ __forceinline__ int swp2(int a) { return ((a & 1) << 1) | ((a >> 1) & 1); }
@@ -224,7 +224,11 @@ struct Frag16Ofs {
 };
 
 __device__ __forceinline__ void mma16(f32x4& c, const bf16x8& a, const bf16x8& b) {
+#if ATL_FAST_F16
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+#else
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+#endif
 }
 
 // Two 16x16 accumulators (query blocks 2kc, 2kc+1) -> one operand fragment
@@ -244,11 +248,17 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4& a, const f32x4& b) {
 // probabilities its P V products use, so that each output row is normalised
 // by its own numerator's weights (an fp32 sum would scale the row by the
 // rounding of its largest probability, up to 2^-9).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float sum_bf16x8(const bf16x8& f, float acc) {
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[2 * e], f[2 * e + 1]}, one, acc, false);
+  for (int e = 0; e < 4; ++e) {
+#if ATL_FAST_F16
+    acc = __builtin_amdgcn_fdot2(bf16x2{f[2 * e], f[2 * e + 1]}, one, acc, false);
+#else
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[2 * e], f[2 * e + 1]}, one, acc, false);
+#endif
+  }
   return acc;
 }
 
@@ -1630,4 +1640,4 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   }
 }
 
-}  // namespace atl
+}  // namespace ATL_NS

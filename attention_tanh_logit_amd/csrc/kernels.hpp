@@ -29,7 +29,7 @@
 
 #include "common.hpp"
 
-namespace atl {
+namespace ATL_NS {
 
 struct FwdParams {
   const void* q;
@@ -1146,4 +1146,4 @@ __global__ __launch_bounds__(256) void dbias_fill_kernel(T* dbias, Mask mask, in
   }
 }
 
-}  // namespace atl
+}  // namespace ATL_NS

@@ -20,7 +20,7 @@
 
 #include "fast.hpp"
 
-namespace atl {
+namespace ATL_NS {
 
 // The four partial accumulators of this wave's group, summed in slice order.
 // sX holds [wave][quantity][lane] f32x4; NQ quantities per wave.
@@ -450,4 +450,4 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   }
 }
 
-}  // namespace atl
+}  // namespace ATL_NS

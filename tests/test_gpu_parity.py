@@ -54,7 +54,8 @@ FEATURES = {
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("bf16", 256), ("fp32", 64),
-                                     ("fp32", 256), ("bf16", 512), ("fp32", 512), ("fp16", 128), ("fp16", 512)])
+                                     ("fp32", 256), ("bf16", 512), ("fp32", 512), ("fp16", 64), ("fp16", 128),
+                                     ("fp16", 256), ("fp16", 512)])
 @pytest.mark.parametrize("feat", list(FEATURES))
 def test_feature_matrix(dtype, D, feat):
     kw = dict(dtype=dtype, D=D, B=2, S=203, Hq=4, Hkv=2)
@@ -75,10 +76,11 @@ BIAS_FAST = {
 }
 
 
-@pytest.mark.parametrize("D,dq_mode", [(64, "auto"), (64, "du_blocks"), (128, "auto"), (256, "auto")])
+@pytest.mark.parametrize("dtype,D,dq_mode", [("bf16", 64, "auto"), ("bf16", 64, "du_blocks"), ("bf16", 128, "auto"),
+                                             ("bf16", 256, "auto"), ("fp16", 128, "auto"), ("fp16", 64, "du_blocks")])
 @pytest.mark.parametrize("feat", list(BIAS_FAST))
-def test_bias_on_the_fast_path(D, dq_mode, feat):
-    kw = dict(dtype="bf16", D=D, B=2, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0)
+def test_bias_on_the_fast_path(dtype, D, dq_mode, feat):
+    kw = dict(dtype=dtype, D=D, B=2, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0)
     kw.update(BIAS_FAST[feat])
     _check(case(**kw), dq_mode=dq_mode)
 
