@@ -108,27 +108,55 @@ def workload(name):
         "window_d256_fp32": W.window_large_d(256, "fp32"),
         "window_d512_fp32": W.window_large_d(512, "fp32"),
         "packed_varlen": W.packed_varlen(),
+        "packed_varlen_k_start": W.packed_varlen(),
+        "packed_varlen_dense_mask": W.packed_varlen(),
+        "packed_varlen_bias_heads": W.packed_varlen().with_(name="packed_varlen_bias_heads_bf16_cap50", bias_heads=1),
+        "causal_gqa_fp16": W.causal_gqa(30.0).with_(name="causal_gqa_fp16_cap30", dtype="fp16"),
+        "causal_gqa_sbhd": W.causal_gqa(30.0).with_(name="causal_gqa_sbhd_bf16_cap30", layout="sbhd"),
+        "causal_gqa_dropout": W.causal_gqa(30.0).with_(name="causal_gqa_dropout0.1_bf16_cap30", dropout_p=0.1),
         "tiny": W.tiny_fp32(),
     }
     return table[name]
 
 
-def to_gpu(w, d):
+# the packed workload's segments given in the other two packed forms
+PACKED_FORMS = {"packed_varlen_k_start": "k_start", "packed_varlen_dense_mask": "dense_mask"}
+
+
+def to_gpu(w, d, form=None):
     import numpy as np
     import torch
     import workloads as W
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)  # noqa: E731
-    g = {"q": t(d["q"]), "k": t(d["k"]), "v": t(d["v"]), "dout": t(d["dout"])}
+    lay = (lambda x: x.transpose(0, 1).contiguous()) if w.layout == "sbhd" else (lambda x: x)  # noqa: E731
+    g = {"q": lay(t(d["q"])), "k": lay(t(d["k"])), "v": lay(t(d["v"])), "dout": lay(t(d["dout"]))}
     kw = dict(causal=w.causal, window=w.window, softcap=w.softcap, sink_mode=w.sink_mode)
+    if w.layout != "bshd":
+        kw["layout"] = w.layout
+    if w.dropout_p > 0:
+        kw.update(dropout_p=w.dropout_p, dropout_seed=w.seed, dropout_offset=0)
     if d["sink"] is not None and w.sink_mode == "learnable":
         kw["sink"] = torch.from_numpy(d["sink"]).cuda()
-    if d["segment_ids"] is not None:
-        kw["segment_ids"] = torch.from_numpy(d["segment_ids"]).cuda()
+    seg = d["segment_ids"]
+    if seg is not None and form == "k_start":
+        # the first token of each token's segment
+        ks = np.zeros(seg.shape, dtype=np.int32)
+        for b in range(seg.shape[0]):
+            starts = np.concatenate([[0], np.nonzero(np.diff(seg[b]))[0] + 1])
+            for a, e in zip(starts, list(starts[1:]) + [seg.shape[1]]):
+                ks[b, a:e] = a
+        kw["k_start"] = torch.from_numpy(ks).cuda()
+    elif seg is not None and form == "dense_mask":
+        s = torch.from_numpy(seg).cuda()
+        kw["mask"] = (s[:, :, None] == s[:, None, :]).contiguous()
+    elif seg is not None:
+        kw["segment_ids"] = torch.from_numpy(seg).cuda()
     if w.bias_std > 0:
-        bias = torch.empty((w.B, w.Hq, w.S, w.S), dtype=dt, device="cuda")
+        nh = 1 if w.bias_heads else w.Hq
+        bias = torch.empty((w.B, nh, w.S, w.S), dtype=dt, device="cuda")
         for b in range(w.B):
-            for h in range(w.Hq):
+            for h in range(nh):
                 bias[b, h] = t(W.bias_slab(w, b, h))
         kw["bias"] = bias
     return g, kw
@@ -169,11 +197,12 @@ def dkdv_algorithmic_bytes(w, pairs) -> float:
     """HBM bytes the dk/dv kernel must move at least: Q, dO, K, V read once, dK, dV
     written once, lse and delta read once; with a bias its visible entries read once
     and the dense dbias written once (the workspace hand-off to dq is not counted)."""
-    e = 2 if w.dtype == "bf16" else 4
+    e = 4 if w.dtype == "fp32" else 2
     tok = w.B * w.S
     b = e * tok * w.D * (2 * w.Hq + 4 * w.Hkv) + 8 * tok * w.Hq
     if w.bias_std > 0:
-        b += e * pairs + e * w.B * w.Hq * w.S * w.S
+        nh = 1 if w.bias_heads else w.Hq    # a head-broadcast bias (and its dbias) is one slab per batch row
+        b += e * pairs * nh // w.Hq + e * w.B * nh * w.S * w.S
     return float(b)
 
 
@@ -236,7 +265,7 @@ def main():
         calibration_copy(args.calib_copy_mib)
     log(f"[bench] workload {w.name}: drawing inputs")
     d = W.draw(w)
-    g, kw = to_gpu(w, d)
+    g, kw = to_gpu(w, d, PACKED_FORMS.get(args.workload))
     pairs = visible_pairs(w, d["segment_ids"]) * w.Hq
     flop_fwd = 4.0 * w.D * pairs
     flop_bwd = 10.0 * w.D * pairs
@@ -254,7 +283,7 @@ def main():
         f"{'dU hand-off' if du_path else 'recompute'}, workspace {ws_auto / 2**30:.2f} GiB)")
     ms, ph = run_steps(g, kw, args.steps, args.warmup)
     log(f"[bench] {ms:.3f} ms/step  phases {ph}")
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    peak = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS   # fp16 dense MFMA peak = bf16
     value = flop_step / (ms * 1e-3) / 1e12
     fwd_tflops = flop_fwd / (ph["fwd"] * 1e-3) / 1e12
     bwd_ms = ph["bwd_pre"] + ph["dq"] + ph["dkdv"]
@@ -304,15 +333,17 @@ def main():
         "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak; capped/uncapped time ratio",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "fp32", "data": "synthetic (seeded, workloads.py)",
+        "dtype": w.dtype, "data": "synthetic (seeded, workloads.py)",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "causal": w.causal, "window": w.window, "softcap": w.softcap, "sink": w.sink_mode,
-                   "bias": w.bias_std > 0, "packed": w.n_segments is not None},
+                   "bias": w.bias_std > 0, "packed": w.n_segments is not None,
+                   "packed_form": PACKED_FORMS.get(args.workload, "segment_ids") if w.n_segments else None,
+                   "layout": w.layout, "dropout_p": w.dropout_p, "bias_broadcast_heads": bool(w.bias_heads)},
         "frac_of_peak": value / peak,
         "fwd_tflops": fwd_tflops, "fwd_frac_of_peak": fwd_tflops / peak,
         "bwd_tflops": flop_bwd / (bwd_ms * 1e-3) / 1e12,
         "kernel_ms": ph, "cap_ratio": cap_ratio, "dq_modes": dq_modes,
-        "peak_tflops": peak, "peak_tflops_from_clock": CLOCK_PEAK_BF16 if w.dtype == "bf16" else None,
+        "peak_tflops": peak, "peak_tflops_from_clock": CLOCK_PEAK_BF16 if w.dtype != "fp32" else None,
         "algorithmic_flop_per_step": flop_step, "visible_pairs": pairs,
         "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -10,9 +10,9 @@ workload is drawn per (batch row, query head) slab from
 ``default_rng([seed, 7919, b, h])`` so that a single slab can be rebuilt
 without drawing the whole 4.3 GB tensor.
 
-bf16 workloads draw in fp32 and round to nearest-even bf16; the arrays
-returned here already hold the rounded values (as float32), so the GPU gets
-exactly those bf16 numbers and the oracle gets them widened to fp64.
+bf16 (fp16) workloads draw in fp32 and round to nearest-even bf16 (fp16); the
+arrays returned here already hold the rounded values (as float32), so the
+GPU gets exactly those numbers and the oracle gets them widened to fp64.
 """
 from __future__ import annotations
 
@@ -20,6 +20,11 @@ import dataclasses
 from typing import Optional
 
 import numpy as np
+
+
+def round_to_fp16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest fp16 (ties to even); returns float32."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -52,6 +57,9 @@ class Workload:
     bias_std: float = 0.0       # > 0: dense additive bias [B,Hq,S,S]
     n_segments: Optional[tuple] = None  # (min, max) segments per row: packed rows
     seed: int = 0
+    layout: str = "bshd"        # "bshd" or "sbhd" memory layout of q/k/v and their gradients
+    dropout_p: float = 0.0      # > 0: attention dropout with seed `seed` and offset 0
+    bias_heads: int = 0         # 1: the bias is one [S,S] slab per batch row, broadcast over heads
 
     @property
     def G(self) -> int:
@@ -82,10 +90,11 @@ def draw(w: Workload, need_dout: bool = True) -> dict:
     seg = None
     if w.n_segments is not None:
         seg = _draw_segments(rng, w.B, w.S, *w.n_segments)
-    if w.dtype == "bf16":
-        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    if w.dtype in ("bf16", "fp16"):
+        rnd = round_to_bf16 if w.dtype == "bf16" else round_to_fp16
+        q, k, v = rnd(q), rnd(k), rnd(v)
         if do is not None:
-            do = round_to_bf16(do)
+            do = rnd(do)
     return {"q": q, "k": k, "v": v, "dout": do, "sink": sink, "segment_ids": seg}
 
 
@@ -117,7 +126,7 @@ def bias_slab(w: Workload, b: int, h: int) -> np.ndarray:
     """The [S,S] additive-bias slab of batch row ``b`` and query head ``h``."""
     rng = np.random.default_rng([w.seed, 7919, b, h])
     x = rng.standard_normal((w.S, w.S), dtype=np.float32) * np.float32(w.bias_std)
-    return round_to_bf16(x) if w.dtype == "bf16" else x
+    return round_to_bf16(x) if w.dtype == "bf16" else (round_to_fp16(x) if w.dtype == "fp16" else x)
 
 
 def bias_full(w: Workload) -> np.ndarray:
