@@ -1,4 +1,6 @@
-// Pipelined bf16 kernels for head dims 64 and 128.
+// Pipelined kernels for 16-bit elements (bf16; fp16 in the second build of
+// these sources) at head dims 64, 128 and 256, and the dq kernel that reads
+// the dU blocks (also at head dim 512, after the kernels of wide.hpp).
 //
 // Same arithmetic and masking as the kernels in kernels.hpp, arranged for
 // gfx950 throughput:
@@ -12,10 +14,11 @@
 //    swizzled per row, and read both ways: plain 16-byte fragment reads for
 //    one contraction and ds_read_b64_tr_b16 transposing reads for the other
 //    (no transposed copies in LDS), both free of bank conflicts;
-//  * loads are branch-free: rows past the end repeat the last row, whose
-//    pairs the mask removes (their probabilities are exactly 0), and the mask
-//    itself is evaluated only on tiles that are partly visible, chosen once
-//    per tile rather than per element;
+//  * loads are branch-free: the buffer resource's range check returns zeros
+//    for rows past the end of a head's rows, whose pairs the mask removes
+//    (their probabilities are exactly 0), and the mask itself is evaluated
+//    only on tiles that are partly visible, chosen once per tile rather than
+//    per element;
 //  * the output accumulator is rescaled only when some row's running
 //    maximum grows by more than 2^8 (probabilities stay bounded by 256 in
 //    between, well inside fp32 and bf16 range).

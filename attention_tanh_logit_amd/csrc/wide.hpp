@@ -1,6 +1,6 @@
-// bf16 kernels for head dim 512 (no bias): forward, dk/dv (which hands dU to
-// the dq kernel through the workspace) on the fast path's tiles and
-// fragments.
+// 16-bit kernels (bf16; fp16 in the second build of these sources) for head
+// dim 512 without a bias: forward, and dk/dv, which hands dU to the dq kernel
+// through the workspace, on the fast path's tiles and fragments.
 //
 // A workgroup is 8 waves: two row (or key) groups x four column slices of
 // 128.  A wave keeps only its slice of the fixed operand (Q columns in the

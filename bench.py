@@ -35,14 +35,20 @@ def log(*a):
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and the C header (what the counters were taken on)."""
+    """sha256 over the code of the HIP sources and the C header (what the counters were
+    taken on), with comments and whitespace removed so that a documentation change
+    does not retire the counters."""
     import hashlib
+    import re
     hsh = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_tanh_logit_amd", "csrc")
     files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))] + [os.path.join(ROOT, "include", "attn_softcap.h")]
     for f in files:
-        with open(f, "rb") as fh:
-            hsh.update(os.path.basename(f).encode() + b"\0" + fh.read())
+        with open(f, encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = " ".join(code.split())
+        hsh.update(os.path.basename(f).encode() + b"\0" + code.encode())
     return hsh.hexdigest()
 
 

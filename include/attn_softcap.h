@@ -76,7 +76,10 @@ typedef enum attn_status {
 /* Element type of q, k, v, bias, out, dout, dq, dk, dv, dbias.  bf16 and fp16
  * contract on the matrix cores with fp32 accumulation; fp32 on the fp32
  * matrix instructions.  (fp16 is listed as not covered on the learnable-sink
- * page, "Not covered"; here it runs the generic kernels.) */
+ * page, "Not covered"; here it takes the same kernels as bf16, built a
+ * second time for fp16 elements, except that the forward keeps a running
+ * maximum: probabilities relative to a fixed reference at the cap could
+ * leave fp16's exponent range.) */
 typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1, ATTN_FP16 = 2 } attn_dtype;
 
 /* Softmax sink ("softmax_type" on the learnable-sink page, "What changed"):
