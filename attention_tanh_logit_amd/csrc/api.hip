@@ -164,6 +164,147 @@ __global__ __launch_bounds__(256) void kstart_hi_kernel(const int* q_lo, const i
   k_hi[(long)b * Sk + j] = lo;
 }
 
+// Dense mask, first pass: per query row, the first visible key a, one past
+// the last e (a = Sk, e = 0 for a row that sees none) and whether the row's
+// visible keys are all of [a, e).  One wave per row; rows are read 16 bytes
+// per lane when Sk is a multiple of 16 (the mask is 16-byte aligned), else a
+// byte per lane.
+__device__ __forceinline__ unsigned nonzero_bytes(unsigned w) {
+  // bit 7 of each byte set iff that byte is nonzero
+  return (((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u;
+}
+__global__ __launch_bounds__(256) void dense_rows_kernel(const unsigned char* mask, int Sq, int Sk, int* ra, int* re,
+                                                         int* rc) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= Sq) return;
+  const unsigned char* row = mask + ((long)b * Sq + i) * Sk;
+  int first = INT_MAX, last = -1, cnt = 0;
+  if ((Sk & 15) == 0) {
+    const uint4* row16 = reinterpret_cast<const uint4*>(row);
+    for (int c = lane; c < Sk / 16; c += 64) {
+      const uint4 v = row16[c];
+      const unsigned wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const unsigned m = nonzero_bytes(wd[q]);
+        if (m) {
+          const int j0 = 16 * c + 4 * q;
+          first = min(first, j0 + (__builtin_ctz(m) >> 3));
+          last = max(last, j0 + ((31 - __builtin_clz(m)) >> 3));
+          cnt += __builtin_popcount(m);
+        }
+      }
+    }
+  } else {
+    for (int j = lane; j < Sk; j += 64) {
+      if (row[j]) {
+        first = min(first, j);
+        last = max(last, j);
+        ++cnt;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    first = min(first, __shfl_xor(first, o, 64));
+    last = max(last, __shfl_xor(last, o, 64));
+    cnt += __shfl_xor(cnt, o, 64);
+  }
+  if (lane == 0) {
+    const long t = (long)b * Sq + i;
+    ra[t] = cnt ? first : Sk;
+    re[t] = cnt ? last + 1 : 0;
+    rc[t] = (cnt == 0 || cnt == last + 1 - first) ? 1 : 0;
+  }
+}
+
+// Dense mask, second pass (one workgroup per batch row): non-decreasing
+// envelopes A_i = min over rows i' >= i of a_i' and E_i = max over rows
+// i' <= i of e_i', cut by the bounds of segments / k_start (lo_in, hi_in,
+// nullable) into q_lo, q_hi.  The batch row is exact when every row's final
+// range [q_lo, q_hi) is empty or lies inside its own [a, e) with all of
+// [a, e) visible: the ranges then say everything the mask says.
+__global__ __launch_bounds__(1024) void dense_bounds_kernel(const int* ra, const int* re, const int* rc,
+                                                            const int* lo_in, const int* hi_in, int* q_lo, int* q_hi,
+                                                            int* exact, int Sq, int Sk) {
+  __shared__ int wtot[16];
+  const int b = blockIdx.x;
+  const long base = (long)b * Sq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // A: running maximum of -a from the last row backwards
+  int carry = INT_MIN;
+  for (int c0 = ((Sq - 1) / 1024) * 1024; c0 >= 0; c0 -= 1024) {
+    const int t = c0 + 1023 - tid;
+    int f = INT_MIN;
+    if (t < Sq) f = -ra[base + t];
+    f = wave_scan_max(f);
+    if (lane == 63) wtot[w] = f;
+    __syncthreads();
+    int pre = carry;
+    for (int x = 0; x < w; ++x) pre = max(pre, wtot[x]);
+    if (t < Sq) q_lo[base + t] = -max(f, pre);
+    int lastv = carry;
+    for (int x = 0; x < 16; ++x) lastv = max(lastv, wtot[x]);
+    __syncthreads();
+    carry = lastv;
+  }
+  // E: running maximum of e; then the final ranges and their exactness
+  carry = INT_MIN;
+  int ok = 1;
+  for (int c0 = 0; c0 < Sq; c0 += 1024) {
+    const int t = c0 + tid;
+    int f = INT_MIN;
+    if (t < Sq) f = re[base + t];
+    f = wave_scan_max(f);
+    if (lane == 63) wtot[w] = f;
+    __syncthreads();
+    int pre = carry;
+    for (int x = 0; x < w; ++x) pre = max(pre, wtot[x]);
+    if (t < Sq) {
+      int lo = q_lo[base + t];   // A_t, written by this workgroup above
+      int hi = max(f, pre);      // E_t
+      if (lo_in) lo = max(lo, lo_in[base + t]);
+      hi = min(hi, hi_in ? hi_in[base + t] : Sk);
+      q_lo[base + t] = lo;
+      q_hi[base + t] = hi;
+      ok &= rc[base + t] != 0 && (lo >= hi || (lo >= ra[base + t] && hi <= re[base + t]));
+    }
+    int lastv = carry;
+    for (int x = 0; x < 16; ++x) lastv = max(lastv, wtot[x]);
+    __syncthreads();
+    carry = lastv;
+  }
+  ok = __syncthreads_and(ok);
+  if (tid == 0) exact[b] = ok;
+}
+
+// Per key, the queries whose (non-decreasing) ranges [q_lo, q_hi) hold it:
+// from the first query with q_hi > j to the first with q_lo > j.
+__global__ __launch_bounds__(256) void rows_to_keys_kernel(const int* q_lo, const int* q_hi, int* k_lo, int* k_hi,
+                                                           int Sq, int Sk) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= Sk) return;
+  const int* rl = q_lo + (long)b * Sq;
+  const int* rh = q_hi + (long)b * Sq;
+  int lo = 0, hi = Sq;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rh[mid] <= j) lo = mid + 1; else hi = mid;
+  }
+  const int first = lo;
+  lo = first;
+  hi = Sq;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rl[mid] <= j) lo = mid + 1; else hi = mid;
+  }
+  k_lo[(long)b * Sk + j] = first;
+  k_hi[(long)b * Sk + j] = lo;
+}
+
 // Scratch of attn_bwd_noalloc: the backward's workspace (segment runs,
 // delta, sink-gradient partials, split partials, dU blocks when they fit) for
 // callers that cannot allocate.  One copy per GPU the library runs on, held
@@ -307,10 +448,14 @@ attn_status validate(const attn_args* a) {
 }
 
 // Per-token visibility bounds in the workspace: the segment runs (two
-// [B*Sq] arrays) and, with k_start, q_lo [B*Sq] and k_hi [B*Sk].
+// [B*Sq] arrays), with k_start q_lo [B*Sq] and k_hi [B*Sk], and with a dense
+// mask the per-row scan (three [B*Sq] arrays), the final q_lo, q_hi [B*Sq],
+// k_lo, k_hi [B*Sk] and one exactness flag per batch row.
 size_t seg_bytes(const attn_args* a) {
-  size_t n = has_segments(a) ? 2 * align_up((size_t)a->B * a->Sq * sizeof(int)) : 0;
-  if (a->k_start) n += align_up((size_t)a->B * a->Sq * sizeof(int)) + align_up((size_t)a->B * a->Sk * sizeof(int));
+  const size_t nq = align_up((size_t)a->B * a->Sq * sizeof(int)), nk = align_up((size_t)a->B * a->Sk * sizeof(int));
+  size_t n = has_segments(a) ? 2 * nq : 0;
+  if (a->k_start) n += nq + nk;
+  if (a->mask) n += 5 * nq + 2 * nk + align_up((size_t)a->B * sizeof(int));
   return n;
 }
 
@@ -417,6 +562,29 @@ hipError_t prep_bounds(const attn_args* a, char*& ws, Mask& m, hipStream_t s, bo
     m.q_lo = q_lo;
     m.k_hi = k_hi;
   }
+  if (a->mask) {
+    // ranges from the mask itself, cut by the bounds above; where they say
+    // all the mask says, the kernels skip its per-pair reads
+    int* ra = reinterpret_cast<int*>(ws);
+    int* re = reinterpret_cast<int*>(ws + nq);
+    int* rc = reinterpret_cast<int*>(ws + 2 * nq);
+    int* q_lo = reinterpret_cast<int*>(ws + 3 * nq);
+    int* q_hi = reinterpret_cast<int*>(ws + 4 * nq);
+    int* k_lo = reinterpret_cast<int*>(ws + 5 * nq);
+    int* k_hi = reinterpret_cast<int*>(ws + 5 * nq + nk);
+    int* exact = reinterpret_cast<int*>(ws + 5 * nq + 2 * nk);
+    ws += 5 * nq + 2 * nk + align_up((size_t)a->B * sizeof(int));
+    if (launch && a->Sq > 0) {
+      dense_rows_kernel<<<dim3((a->Sq + 3) / 4, a->B), 256, 0, s>>>(a->mask, a->Sq, a->Sk, ra, re, rc);
+      dense_bounds_kernel<<<a->B, 1024, 0, s>>>(ra, re, rc, m.q_lo, m.q_hi, q_lo, q_hi, exact, a->Sq, a->Sk);
+      rows_to_keys_kernel<<<dim3((a->Sk + 255) / 256, a->B), 256, 0, s>>>(q_lo, q_hi, k_lo, k_hi, a->Sq, a->Sk);
+    }
+    m.q_lo = q_lo;
+    m.q_hi = q_hi;
+    m.k_lo = k_lo;
+    m.k_hi = k_hi;
+    m.exact = exact;
+  }
   return launch ? hipGetLastError() : hipSuccess;
 }
 
@@ -443,6 +611,7 @@ Mask base_mask(const attn_args* a) {
   Mask m;
   m.q_lo = m.q_hi = m.k_lo = m.k_hi = nullptr;
   m.dense = a->mask;
+  m.exact = nullptr;
   m.Sq = a->Sq;
   m.Sk = a->Sk;
   m.causal = a->causal ? 1 : 0;

@@ -347,7 +347,9 @@ __device__ __forceinline__ void xcd_order(int ntile, int ngroup, int& tile, int&
 // per query: packed segment runs, k_start) and k_lo / k_hi (first query that
 // sees the key and one past the last, per key); absent arrays do not
 // restrict.  All range ends are non-decreasing in the token index.  A dense
-// boolean mask, where given, removes further pairs inside those ranges.
+// boolean mask, where given, removes further pairs inside those ranges,
+// unless its batch row is marked exact (the ranges, prepared from the mask
+// itself, then hold exactly its visible pairs).
 
 struct Mask {
   const int* q_lo;     // [B * Sq] or null
@@ -355,6 +357,7 @@ struct Mask {
   const int* k_lo;     // [B * Sk] or null
   const int* k_hi;
   const unsigned char* dense;   // [B, Sq, Sk] or null: nonzero = visible
+  const int* exact;    // [B] or null: 1 where the bounds already say all the dense mask says
   int Sq, Sk;
   int causal, window;
 };
@@ -389,10 +392,17 @@ __device__ __forceinline__ void queries_of(const Mask& m, int b, int j, int& lo,
   hi = max(hi, lo);
 }
 
-// the dense mask at (query i, key j) of batch row b (true without one); only
-// called for pairs inside the ranges above, so i < Sq and j < Sk
-__device__ __forceinline__ bool dense_ok(const Mask& m, int b, int i, int j) {
-  return !m.dense || m.dense[((long)b * m.Sq + i) * m.Sk + j] != 0;
+// whether batch row b needs the dense mask read pair by pair: it has one and
+// the bounds above do not already describe it exactly
+__device__ __forceinline__ bool dense_row(const Mask& m, int b) {
+  return m.dense != nullptr && !(m.exact != nullptr && m.exact[b] != 0);
+}
+
+// the dense mask at (query i, key j) of batch row b, where chk = dense_row(m,
+// b) (true otherwise); only called for pairs inside the ranges above, so
+// i < Sq and j < Sk
+__device__ __forceinline__ bool dense_ok(const Mask& m, bool chk, int b, int i, int j) {
+  return !chk || m.dense[((long)b * m.Sq + i) * m.Sk + j] != 0;
 }
 
 // ---------------------------------------------------------------- dropout

@@ -419,7 +419,8 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
   int lo_first, hi_first, lo_last, hi_last;
   keys_of(p.mask, b, q0, lo_first, hi_first);
   keys_of(p.mask, b, ilast, lo_last, hi_last);
-  const bool rows_full = (q0 + BM <= Sq) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool rows_full = (q0 + BM <= Sq) && !dchk;
 
   // Q^T fragments of this wave's 32 queries stay in registers
   bf16x8 qf[NCC];
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
           else v = y;
           if constexpr (decltype(masked)::value) {
             const int key = k0 + kb * 32 + acc_row(h, j);
-            v = (key >= lo_i && key < hi_i && dense_ok(p.mask, b, i, key)) ? v : ((CAP && !FIXM) ? INFINITY : -INFINITY);
+            v = (key >= lo_i && key < hi_i && dense_ok(p.mask, dchk, b, i, key)) ? v : ((CAP && !FIXM) ? INFINITY : -INFINITY);
           }
           scur[kb][j] = v;
           if constexpr (!FIXM) ext = CAP ? fminf(ext, v) : fmaxf(ext, v);
@@ -688,7 +689,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   int lo_first, hi_first, lo_last, hi_last;
   queries_of(p.mask, b, k0, lo_first, hi_first);
   queries_of(p.mask, b, jlast, lo_last, hi_last);
-  const bool keys_full = (k0 + BNK <= Sk) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool keys_full = (k0 + BNK <= Sk) && !dchk;
   const int qbeg = (lo_first / BMQ) * BMQ;
   const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
   const int nitems = GS * nqt;
@@ -771,7 +773,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
         const int qi = q0 + acc_row(h, r);
         float lc = L4[4 * (r >> 3) + 2 * h + ((r >> 2) & 1)][r & 3];
         // a masked pair gets Lc = -inf, hence P = 0, without a branch
-        if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, b, qi, j)) ? lc : -INFINITY;
+        if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, dchk, b, qi, j)) ? lc : -INFINITY;
         float bvv = 0.0f;
         if constexpr (BIAS) bvv = (float)bcol[(long)min(qi, Sq - 1) * Sk];
         float g;
@@ -982,7 +984,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   int lo_first, hi_first, lo_last, hi_last;
   queries_of(p.mask, b, k0, lo_first, hi_first);
   queries_of(p.mask, b, jlast, lo_last, hi_last);
-  const bool keys_full = (k0 + BNK <= Sk) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool keys_full = (k0 + BNK <= Sk) && !dchk;
   const int qbeg = (lo_first / BMQ) * BMQ;
   const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
   const int nitems = GS * nqt;
@@ -1109,7 +1112,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
         for (int e = 0; e < 4; ++e) {
           const int qi = q0 + 16 * qb + 4 * g + e;
           float lc = l4[e];
-          if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, b, qi, j)) ? lc : -INFINITY;
+          if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, dchk, b, qi, j)) ? lc : -INFINITY;
           float bvv = 0.0f;
           if constexpr (BIAS) bvv = (float)tB[bidx(16 * qb + 4 * g + e, bcol)];
           float gg;
@@ -1541,7 +1544,8 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
   int lo_first, hi_first, lo_last, hi_last;
   keys_of(p.mask, b, q0, lo_first, hi_first);
   keys_of(p.mask, b, ilast, lo_last, hi_last);
-  const bool rows_full = (q0 + BM <= Sq) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool rows_full = (q0 + BM <= Sq) && !dchk;
 
   const long row = ((long)b * p.Hq + hq) * Sq + min(i, Sq - 1);
   const float lse_i = p.lse[row];
@@ -1602,7 +1606,7 @@ __global__ __launch_bounds__(256, 2) void dq_fast_kernel(BwdParams p) {
         float pv = prob_fast<CAP, BIAS>(sacc[r], BIAS ? bv[r] : 0.0f, lk, lc_i, g);
         if constexpr (decltype(masked)::value) {
           const int key = k0 + acc_row(h, r);
-          pv = (key >= lo_i && key < hi_i && dense_ok(p.mask, b, i, key)) ? pv : 0.0f;
+          pv = (key >= lo_i && key < hi_i && dense_ok(p.mask, dchk, b, i, key)) ? pv : 0.0f;
         }
         sacc[r] = pv * (dpacc[r] - delta_i) * g;
       }

@@ -227,7 +227,8 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   int lo_first, hi_first, lo_last, hi_last;
   keys_of(p.mask, b, q0, lo_first, hi_first);
   keys_of(p.mask, b, ilast, lo_last, hi_last);
-  const bool rows_full = (q0 + BM <= Sq) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool rows_full = (q0 + BM <= Sq) && !dchk;
 
   const T* brow = nullptr;
   if constexpr (BIAS) brow = reinterpret_cast<const T*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + (long)min(i, Sq - 1) * Sk;
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
         float s2 = logit2<T, CAP, BIAS>(sacc[kb][j], BIAS ? bv[j] : 0.0f, p.sl2, p.xc, p.bc, p.cl2, f);
         if (!full) {
           const int key = k0 + kb * 32 + acc_row(h, j);
-          if (key < lo_i || key >= hi_i || !dense_ok(p.mask, b, i, key)) s2 = -INFINITY;
+          if (key < lo_i || key >= hi_i || !dense_ok(p.mask, dchk, b, i, key)) s2 = -INFINITY;
         }
         sacc[kb][j] = s2;
         mx = fmaxf(mx, s2);
@@ -506,7 +507,8 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   int lo_first, hi_first, lo_last, hi_last;
   keys_of(p.mask, b, q0, lo_first, hi_first);
   keys_of(p.mask, b, ilast, lo_last, hi_last);
-  const bool rows_full = (q0 + BM <= Sq) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool rows_full = (q0 + BM <= Sq) && !dchk;
 
   const long row = ((long)b * p.Hq + hq) * Sq + min(i, Sq - 1);
   const float lse_i = p.lse[row];
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
         float pv = fast_exp2(s2 - lse2);
         if (!full) {
           const int key = k0 + kb * 32 + acc_row(h, j);
-          if (key < lo_i || key >= hi_i || !dense_ok(p.mask, b, i, key)) pv = 0.0f;
+          if (key < lo_i || key >= hi_i || !dense_ok(p.mask, dchk, b, i, key)) pv = 0.0f;
         }
         float dp = dpacc[kb][j];
         if (p.drop.on) {
@@ -777,7 +779,8 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   int lo_first, hi_first, lo_last, hi_last;
   queries_of(p.mask, b, k0, lo_first, hi_first);
   queries_of(p.mask, b, jlast, lo_last, hi_last);
-  const bool keys_full = (k0 + BNK <= Sk) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool keys_full = (k0 + BNK <= Sk) && !dchk;
 
   f32x16 kacc[NOB], vacc[NOB];
 #pragma unroll
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       bool vis = true;
       if (!full) vis = (qi >= lo_j && qi < hi_j);
       // a pair the dense mask removes inside the range gets P = 0 and a dbias of 0
-      if (!vis || (!full && !dense_ok(p.mask, b, qi, j))) pv = 0.0f;
+      if (!vis || (!full && !dense_ok(p.mask, dchk, b, qi, j))) pv = 0.0f;
       float dp = dpacc[r], pd = pv;
       if (p.drop.on) {
         // V and dP see the kept probabilities, scaled by 1 / (1 - p)

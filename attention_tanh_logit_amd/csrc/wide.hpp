@@ -92,7 +92,8 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   int lo_first, hi_first, lo_last, hi_last;
   keys_of(p.mask, b, q0, lo_first, hi_first);
   keys_of(p.mask, b, ilast, lo_last, hi_last);
-  const bool rows_full = (q0 + BM <= Sq) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool rows_full = (q0 + BM <= Sq) && !dchk;
 
   bf16x8 qf[NCW];
   {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
         else v = y;
         if constexpr (decltype(masked)::value) {
           const int key = k0 + acc_row(h, jj);
-          v = (key >= lo_i && key < hi_i && dense_ok(p.mask, b, i, key)) ? v : ((CAP && !FIXM) ? INFINITY : -INFINITY);
+          v = (key >= lo_i && key < hi_i && dense_ok(p.mask, dchk, b, i, key)) ? v : ((CAP && !FIXM) ? INFINITY : -INFINITY);
         }
         s[jj] = v;
         if constexpr (!FIXM) ext = CAP ? fminf(ext, v) : fmaxf(ext, v);
@@ -297,7 +298,8 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   int lo_first, hi_first, lo_last, hi_last;
   queries_of(p.mask, b, k0, lo_first, hi_first);
   queries_of(p.mask, b, jlast, lo_last, hi_last);
-  const bool keys_full = (k0 + BNK <= Sk) && !p.mask.dense;
+  const bool dchk = dense_row(p.mask, b);
+  const bool keys_full = (k0 + BNK <= Sk) && !dchk;
   const int qbeg = (lo_first / BMQ) * BMQ;
   const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
   const int nitems = GS * nqt;
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
           float l = lc[x];
           if constexpr (decltype(masked)::value) {
             const int qi = q0 + 16 * qb + 4 * g + e;
-            l = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, b, qi, j)) ? l : -INFINITY;
+            l = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, dchk, b, qi, j)) ? l : -INFINITY;
           }
           float gg;
           const float pv = prob_fast<CAP, false>(acc[qb][e], 0.0f, lk, l, gg);

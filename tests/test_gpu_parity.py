@@ -217,6 +217,50 @@ def test_random_dense_mask_and_k_start_without_causal(dtype, D):
     _check(dict(c, k_start=ks))
 
 
+def _interval_mask(a, e, Sk):
+    j = np.arange(Sk)[None, None, :]
+    return (j >= a[:, :, None]) & (j < e[:, :, None])
+
+
+DENSE_INTERVALS = ["monotone", "not_monotone", "mixed_rows", "causal_band_with_segments"]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 512), ("fp32", 64),
+                                     ("fp16", 128)])
+@pytest.mark.parametrize("kind", DENSE_INTERVALS)
+def test_dense_masks_of_key_intervals(dtype, D, kind):
+    """Dense masks whose rows are key intervals.  Where the intervals' ends do not
+    decrease down the rows the library describes the mask by per-row ranges alone
+    (no per-pair mask reads); otherwise, and in a batch row with a gap inside a row,
+    it reads the mask pair by pair inside wider ranges.  Both against the oracle."""
+    rng = np.random.default_rng(11)
+    B, S, Sk = 2, 203, 203
+    causal = kind == "causal_band_with_segments"
+    kw = dict(dtype=dtype, D=D, B=B, S=S, Hq=4, Hkv=2, causal=causal, sink_mode="learnable")
+    if causal:
+        kw["segments"] = [[45, 70, 190], [128]]
+    c = case(**kw)
+    if kind == "monotone":
+        a = np.sort(rng.integers(0, Sk, size=(B, S)), axis=1)
+        e = np.maximum(a + 1, np.sort(rng.integers(0, Sk + 1, size=(B, S)), axis=1))
+        m = _interval_mask(a, e, Sk)
+    elif kind == "not_monotone":
+        a = rng.integers(0, Sk, size=(B, S))
+        e = np.minimum(a + rng.integers(1, 90, size=(B, S)), Sk)
+        m = _interval_mask(a, e, Sk)
+    elif kind == "mixed_rows":
+        a = np.sort(rng.integers(0, Sk, size=(B, S)), axis=1)
+        e = np.maximum(a + 1, np.sort(rng.integers(0, Sk + 1, size=(B, S)), axis=1))
+        m = _interval_mask(a, e, Sk)
+        m[1, 100, (a[1, 100] + e[1, 100]) // 2] = False   # a gap inside one row of batch row 1
+        m[1, 150] = False                                   # and a row that sees nothing
+    else:
+        i = np.arange(S)[:, None]
+        j = np.arange(Sk)[None, :]
+        m = np.broadcast_to((i - j < 37) & (j <= i + 5), (B, S, Sk)).copy()   # a band, cut by causal
+    _check(dict(c, mask=m))
+
+
 # ---- a bias broadcast over batch rows and/or heads: dbias of the bias's own shape
 
 @pytest.mark.parametrize("dtype,D,S", [("bf16", 64, 200), ("bf16", 128, 200), ("bf16", 256, 200),
