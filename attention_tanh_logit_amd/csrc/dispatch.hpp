@@ -69,8 +69,9 @@ template <typename T, int D> constexpr int fwd_rows() { return 32 * FwdCfg<T, D>
 template <typename T, int D> constexpr int dq_rows() { return 32 * DqCfg<T, D>::NQG; }
 template <typename T, int D> constexpr int dkdv_keys() { return 32 * DkdvCfg<T, D>::NKG; }
 
-// bf16 with D <= 256 takes the pipelined kernels of fast.hpp (dropout runs
-// on the generic kernels)
+// bf16 with D <= 256 takes the pipelined kernels of fast.hpp (with dropout
+// the forward at every such D, dk/dv at D = 128 and 256, dq from their dU
+// blocks; the rest of dropout runs on the generic kernels)
 template <typename T, int D> constexpr bool use_fast() {
   return std::is_same<T, bf16>::value && (D == 64 || D == 128 || D == 256);
 }
@@ -101,14 +102,20 @@ bool fast_fits(const Params& p, const Launch& l, bool bias) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS) && !p.drop.on) {
+    if (fast_fits<D>(p, l, BIAS)) {
       constexpr int NT = D > 128 ? 512 : 256;
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // capped logits with 2 c log2(e) <= 120 keep a fixed reference maximum
       // (not with fp16 elements: probabilities relative to the cap would
       // leave fp16's exponent range)
-      if (CAP && p.cl2 <= 60.0f && !kNarrow16) fwd_fast_kernel<D, CAP, BIAS, CAP><<<grid, NT, 0, l.stream>>>(p);
-      else fwd_fast_kernel<D, CAP, BIAS, false><<<grid, NT, 0, l.stream>>>(p);
+      const bool fixm = CAP && p.cl2 <= 60.0f && !kNarrow16;
+      if (p.drop.on) {
+        if (fixm) fwd_fast_kernel<D, CAP, BIAS, CAP, true><<<grid, NT, 0, l.stream>>>(p);
+        else fwd_fast_kernel<D, CAP, BIAS, false, true><<<grid, NT, 0, l.stream>>>(p);
+      } else {
+        if (fixm) fwd_fast_kernel<D, CAP, BIAS, CAP, false><<<grid, NT, 0, l.stream>>>(p);
+        else fwd_fast_kernel<D, CAP, BIAS, false, false><<<grid, NT, 0, l.stream>>>(p);
+      }
       return hipGetLastError();
     }
   }
@@ -131,18 +138,21 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dq(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS) && !p.drop.on) {
+    if (fast_fits<D>(p, l, BIAS)) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       // 32-key tiles, two stages, four workgroups per CU (measured against
-      // 64-key tiles and against three stages)
+      // 64-key tiles and against three stages); the dU blocks carry any
+      // dropout already
       if (p.du) {
         dq_du_kernel<D, CAP, 32, 2><<<grid, 256, 0, l.stream>>>(p);
         return hipGetLastError();
       }
       // the recomputing dq kernel holds whole Q and dO rows: D <= 128 only
       if constexpr (D <= 128) {
-        dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
-        return hipGetLastError();
+        if (!p.drop.on) {
+          dq_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+          return hipGetLastError();
+        }
       }
     }
   }
@@ -165,14 +175,15 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS) && !p.drop.on) {
+    if (fast_fits<D>(p, l, BIAS) && (!p.drop.on || D >= 128)) {
       if constexpr (D >= 128) {
         // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64
         // queries); at D = 256 two waves per 16 keys and 32-query items
         // (with a bias, 32-query items: the bias and dbias tiles take registers)
         constexpr int NW = 8, BMQ = (D > 128 || BIAS) ? 32 : 64, BNK = D > 128 ? 64 : 128;
         const dim3 grid((l.Sk + BNK - 1) / BNK, p.Hkv * p.hsplit, l.B);
-        dkdv16_kernel<D, CAP, BIAS, NW, BMQ><<<grid, 64 * NW, 0, l.stream>>>(p);
+        if (p.drop.on) dkdv16_kernel<D, CAP, BIAS, NW, BMQ, true><<<grid, 64 * NW, 0, l.stream>>>(p);
+        else dkdv16_kernel<D, CAP, BIAS, NW, BMQ, false><<<grid, 64 * NW, 0, l.stream>>>(p);
       } else {
         const dim3 grid((l.Sk + 127) / 128, p.Hkv * p.hsplit, l.B);
         dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);

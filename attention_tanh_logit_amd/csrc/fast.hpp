@@ -361,7 +361,13 @@ struct TilePlan {
 // waves, 128 rows); both compute the row's logits and probabilities, each
 // accumulates its 128 columns of O, so O fits the register file beside the
 // whole row of Q^T fragments.
-template <int D, bool CAP, bool BIAS, bool FIXM>
+//
+// DROP: dropout on the probabilities.  A lane's 16 logits of a 32-key block
+// are four runs of 4 consecutive keys of its query, so one Philox4x32-10
+// evaluation gives the keep decisions of a run; the row sum (and lse) takes
+// the undropped probabilities, P.V the kept ones, and the epilogue scales O
+// by 1 / (1 - p).
+template <int D, bool CAP, bool BIAS, bool FIXM, bool DROP>
 __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast_kernel(FwdParams p) {
   static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
   constexpr int NSL = D > 128 ? 2 : 1;     // column slices of O per row group
@@ -547,6 +553,17 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
         pf[0] = to_frag(scur[kb], 0, (bf16*)nullptr);
         pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
         ps = sum_bf16x8(pf[1], sum_bf16x8(pf[0], ps));
+        if constexpr (DROP) {
+          // run q4 = keys k0 + 32 kb + acc_row(h, 4 q4 + e), e = 0..3
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const unsigned kp = keep4(p.drop, i, k0 + kb * 32 + acc_row(h, 4 * q4), b * p.Hq + hq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) scur[kb][4 * q4 + e] = ((kp >> e) & 1u) ? scur[kb][4 * q4 + e] : 0.0f;
+          }
+          pf[0] = to_frag(scur[kb], 0, (bf16*)nullptr);
+          pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
+        }
         // V^T fragments of column block ob + 2 requested before the MFMAs of block ob
         {
           constexpr int TA = D > 128 ? 1 : 2;
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
     }
   }
   if (has_sink) ltot += fast_exp2(sink2 - m);
-  const float inv = ltot > 0.0f ? oscale / ltot : 0.0f;
+  const float inv = ltot > 0.0f ? (DROP ? p.drop.scale : 1.0f) * oscale / ltot : 0.0f;
   if (i < Sq) {
     bf16* orow = reinterpret_cast<bf16*>(p.out) + qoff(p, b, i, hq, D);
     bf16* lorow = reinterpret_cast<bf16*>(p.out_lo) + qoff(p, b, i, hq, D);
@@ -901,7 +918,15 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
 // The dU hand-off block (32 keys x 32 queries, 2 KiB) takes the two waves of
 // a 32-key pair as its halves: half kh = w % 2, then chunk lane' = key
 // kappa + 16 g' holding dU(16 kh + kappa, queries sigma(g', 0..7)).
-template <int D, bool CAP, bool BIAS, int NW, int BMQ>
+//
+// DROP: dropout.  The lanes of a quad (keys 4m .. 4m + 3, one lane each)
+// hold the same four queries; lane t evaluates Philox4x32-10 once for query
+// t of the four and key run 4m, which gives the decisions of all four keys
+// at that query, and the quad exchanges them (DPP broadcasts), so a pair
+// costs a quarter of an evaluation as in the forward.  dV takes the kept
+// probabilities times 1 / (1 - p), and dS = P (m dP - delta) with m = keep /
+// (1 - p).
+template <int D, bool CAP, bool BIAS, int NW, int BMQ, bool DROP>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   // D = 256: waves w and w + 1 share 16 keys and split dK^T, dV^T by columns
   // (and the query blocks of S, dP and dU between them: see QSPLIT)
@@ -1108,6 +1133,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       for (int i = 0; i < NQL; ++i) {
         const int qb = qb0 + i;
         const f32x4 l4 = L4[4 * qb + g];
+        unsigned kq = 0xFu;   // bit e: keep (query q0 + 16 qb + 4g + e, key j)
+        f32x4 md4{};          // -delta of those queries
+        if constexpr (DROP) {
+          const int t = r & 3;
+          const int w4 = (int)keep4(p.drop, q0 + 16 * qb + 4 * g + t, j & ~3, b * p.Hq + hq);
+          const int n0 = __builtin_amdgcn_update_dpp(0, w4, 0x00, 0xF, 0xF, false);
+          const int n1 = __builtin_amdgcn_update_dpp(0, w4, 0x55, 0xF, 0xF, false);
+          const int n2 = __builtin_amdgcn_update_dpp(0, w4, 0xAA, 0xF, 0xF, false);
+          const int n3 = __builtin_amdgcn_update_dpp(0, w4, 0xFF, 0xF, 0xF, false);
+          kq = ((n0 >> t) & 1) | (((n1 >> t) & 1) << 1) | (((n2 >> t) & 1) << 2) | (((n3 >> t) & 1) << 3);
+          md4 = D4[4 * qb + g];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qi = q0 + 16 * qb + 4 * g + e;
@@ -1117,8 +1154,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
           if constexpr (BIAS) bvv = (float)tB[bidx(16 * qb + 4 * g + e, bcol)];
           float gg;
           const float pv = prob_fast<CAP, BIAS>(sacc[i][e], bvv, lk, lc, gg);
-          const float du = pv * dpacc[i][e] * gg;
-          sacc[i][e] = pv;
+          float du, pd;
+          if constexpr (DROP) {
+            // dP - delta sits on top of -delta (md4): m dP - delta = m (dP - delta) + (1 - m)(-delta)
+            const float mk = ((kq >> e) & 1u) ? p.drop.scale : 0.0f;
+            du = pv * fmaf(mk, dpacc[i][e], (1.0f - mk) * md4[e]) * gg;
+            pd = pv * mk;
+          } else {
+            du = pv * dpacc[i][e] * gg;
+            pd = pv;
+          }
+          sacc[i][e] = pd;
           dpacc[i][e] = du;
           // masked pairs have P = 0 and are written as zeros; each query block
           // by the one wave that computed it

@@ -309,14 +309,25 @@ DROPOUT = {
     "sink_bias": dict(sink_mode="learnable", bias=True, softcap=50.0),
     "segments_window": dict(segments=[[45, 70, 190], [128]], window=60, Hq=6, Hkv=2),
     "no_causal_cross": dict(causal=False, Sk=150, softcap=0.0),
+    "sink_bias_fast": dict(S=200, sink_mode="learnable", bias=True, softcap=30.0),   # Sk % 8 == 0: fast kernels
 }
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 512), ("fp16", 128), ("fp32", 64),
-                                     ("fp32", 256)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 512), ("fp16", 128),
+                                     ("fp16", 256), ("fp32", 64), ("fp32", 256)])
 @pytest.mark.parametrize("p", [0.1, 0.5])
 @pytest.mark.parametrize("feat", list(DROPOUT))
 def test_dropout_matches_oracle(dtype, D, p, feat):
     kw = dict(dtype=dtype, D=D, B=2, S=203, Hq=4, Hkv=2, dropout_p=p)
     kw.update(DROPOUT[feat])
     _check(case(**kw))
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("dq_mode", ["du_blocks", "recompute"])
+def test_dropout_on_the_fast_dkdv_kernel_both_dq_modes(D, dq_mode):
+    """The fast dk/dv kernel with dropout hands dq either its dU blocks or leaves dq to the
+    recomputing (generic) kernel; both against the oracle, over several query tiles and a
+    query-head split (B * Hkv * key blocks < 1024)."""
+    c = case(dtype="bf16", D=D, B=2, S=333, Hq=8, Hkv=2, softcap=30.0, sink_mode="learnable", dropout_p=0.2)
+    _check(c, dq_mode=dq_mode)

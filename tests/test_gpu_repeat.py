@@ -29,6 +29,8 @@ REPEAT = {
     "fp32_d64": dict(dtype="fp32", D=64, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable"),
     "fp32_d512": dict(dtype="fp32", D=512, B=1, S=130, Hq=2, Hkv=1),
     "fp16_d128_bias": dict(dtype="fp16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True, sink_mode="learnable"),
+    "bf16_d128_dropout": dict(dtype="bf16", D=128, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable", dropout_p=0.3),
+    "bf16_d64_dropout": dict(dtype="bf16", D=64, B=2, S=203, Hq=4, Hkv=2, dropout_p=0.3),
 }
 
 
