@@ -389,10 +389,10 @@ long max_token_stride(const attn_args* a) {
   return t.qts > t.kts ? t.qts : t.kts;
 }
 
-// Dropout on the fast dk/dv kernel (16-bit, D = 128 or 256); elsewhere the
-// generic kernels, which write no dU blocks.
+// Dropout on the fast dk/dv kernels (16-bit, D = 64, 128 or 256); elsewhere
+// the generic kernels, which write no dU blocks.
 bool drop_fast(const attn_args* a) {
-  return (a->D == 128 || a->D == 256) && fast_ok(is16(a), a->D, max_token_stride(a), a->Sk, a->bias != nullptr);
+  return fast_ok(is16(a), a->D, max_token_stride(a), a->Sk, a->bias != nullptr);
 }
 
 bool du_supported(const attn_args* a) {
@@ -444,7 +444,7 @@ attn_status validate(const attn_args* a) {
     return fail(ATTN_INVALID_ARGUMENT, "dq_mode must be ATTN_DQ_AUTO, ATTN_DQ_DU_BLOCKS or ATTN_DQ_RECOMPUTE");
   if (a->dq_mode == ATTN_DQ_DU_BLOCKS && !du_supported(a))
     return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs bf16 with D = 64, 128 or 256 (with a bias, Sk % 8 == 0) "
-                                  "or D = 512 without a bias; with dropout D = 128 or 256 only");
+                                  "or D = 512 without a bias (not with dropout)");
   if ((long long)a->B * a->Sq > 0 && a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
   const size_t elems = (size_t)a->B * (a->Sq + a->Sk);
   if (elems != 0 && (!a->q || !a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "q, k and v must not be NULL");
@@ -485,7 +485,10 @@ size_t du_raw_bytes(const attn_args* a) {
 
 bool du_path(const attn_args* a) {
   if (!du_supported(a) || a->dq_mode == ATTN_DQ_RECOMPUTE) return false;
-  return a->dq_mode == ATTN_DQ_DU_BLOCKS || (a->D >= 128 && du_raw_bytes(a) <= kDuAutoBytes);
+  // at D = 64 recomputing is faster, except with dropout (whose recomputing
+  // dq kernel is the generic one)
+  return a->dq_mode == ATTN_DQ_DU_BLOCKS ||
+         ((a->D >= 128 || a->dropout_p > 0.0f) && du_raw_bytes(a) <= kDuAutoBytes);
 }
 
 // With a bias, the bf16 dk/dv kernel of D = 128 and 256 writes the whole of
@@ -501,8 +504,7 @@ bool dkdv_writes_dbias_zeros(const attn_args* a) {
 // (four per CU), so that a small batch with a wide GQA group does not leave
 // the GPU to a few long workgroups; 1 when there are enough already.
 int head_split(const attn_args* a) {
-  // with dropout only the 16-bit D = 128 / 256 dk/dv kernel (which splits)
-  const bool bf = is16(a) && (a->dropout_p == 0.0f || a->D == 128 || a->D == 256), bias = a->bias != nullptr;
+  const bool bf = is16(a), bias = a->bias != nullptr;
   const bool wide = wide_ok(is16(a) && a->dropout_p == 0.0f, a->D, max_token_stride(a), bias);
   if (!fast_ok(bf, a->D, max_token_stride(a), a->Sk, bias) && !wide) return 1;
   const int bnk = wide ? 32 : 128;   // keys per dk/dv workgroup (as counted here)

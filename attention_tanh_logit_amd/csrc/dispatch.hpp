@@ -70,8 +70,8 @@ template <typename T, int D> constexpr int dq_rows() { return 32 * DqCfg<T, D>::
 template <typename T, int D> constexpr int dkdv_keys() { return 32 * DkdvCfg<T, D>::NKG; }
 
 // bf16 with D <= 256 takes the pipelined kernels of fast.hpp (with dropout
-// the forward at every such D, dk/dv at D = 128 and 256, dq from their dU
-// blocks; the rest of dropout runs on the generic kernels)
+// too: dq then reads the dk/dv kernel's dU blocks, or runs the generic
+// kernel when asked to recompute)
 template <typename T, int D> constexpr bool use_fast() {
   return std::is_same<T, bf16>::value && (D == 64 || D == 128 || D == 256);
 }
@@ -175,7 +175,7 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
-    if (fast_fits<D>(p, l, BIAS) && (!p.drop.on || D >= 128)) {
+    if (fast_fits<D>(p, l, BIAS)) {
       if constexpr (D >= 128) {
         // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64
         // queries); at D = 256 two waves per 16 keys and 32-query items
@@ -186,7 +186,8 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
         else dkdv16_kernel<D, CAP, BIAS, NW, BMQ, false><<<grid, 64 * NW, 0, l.stream>>>(p);
       } else {
         const dim3 grid((l.Sk + 127) / 128, p.Hkv * p.hsplit, l.B);
-        dkdv_fast_kernel<D, CAP, BIAS><<<grid, 256, 0, l.stream>>>(p);
+        if (p.drop.on) dkdv_fast_kernel<D, CAP, BIAS, true><<<grid, 256, 0, l.stream>>>(p);
+        else dkdv_fast_kernel<D, CAP, BIAS, false><<<grid, 256, 0, l.stream>>>(p);
       }
       if (p.hsplit > 1) {
         const long nel = (long)l.B * l.Sk * p.Hkv * D;

@@ -647,7 +647,11 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
 // query heads and their visible 32-query tiles, which stream through a
 // double-buffered LDS tile (rows stored through swp).  (D = 128 runs
 // dkdv16_kernel.)
-template <int D, bool CAP, bool BIAS>
+//
+// DROP: dropout, with the keep decisions shared in quads of lanes (keys 4m ..
+// 4m + 3) as in dkdv16_kernel: per run of four consecutive queries of a
+// lane, lane t evaluates Philox4x32-10 for query t of the run.
+template <int D, bool CAP, bool BIAS, bool DROP>
 __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   static_assert(D == 64, "32-key waves at D = 64 only");
   constexpr int NT = 256;
@@ -785,18 +789,44 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
       if (p.dbias) dbcol = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.Hq + hq) * Sq) * Sk + jc;
     }
     auto grads = [&](auto masked) {
+      // dropout: bit r of kq keeps (query q0 + acc_row(h, r), key j); run u =
+      // registers 4u .. 4u + 3 = queries q0 + acc_row(h, 4u) + 0..3
+      unsigned kq = 0;
+      if constexpr (DROP) {
+        const int t = n & 3;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int w4 = (int)keep4(p.drop, q0 + acc_row(h, 4 * u) + t, j & ~3, b * p.Hq + hq);
+          const int n0 = __builtin_amdgcn_update_dpp(0, w4, 0x00, 0xF, 0xF, false);
+          const int n1 = __builtin_amdgcn_update_dpp(0, w4, 0x55, 0xF, 0xF, false);
+          const int n2 = __builtin_amdgcn_update_dpp(0, w4, 0xAA, 0xF, 0xF, false);
+          const int n3 = __builtin_amdgcn_update_dpp(0, w4, 0xFF, 0xF, 0xF, false);
+          kq |= (unsigned)(((n0 >> t) & 1) | (((n1 >> t) & 1) << 1) | (((n2 >> t) & 1) << 2) |
+                           (((n3 >> t) & 1) << 3)) << (4 * u);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + acc_row(h, r);
-        float lc = L4[4 * (r >> 3) + 2 * h + ((r >> 2) & 1)][r & 3];
+        const int si = 4 * (r >> 3) + 2 * h + ((r >> 2) & 1);   // f32x4 of this query's stats
+        float lc = L4[si][r & 3];
         // a masked pair gets Lc = -inf, hence P = 0, without a branch
         if constexpr (decltype(masked)::value) lc = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, dchk, b, qi, j)) ? lc : -INFINITY;
         float bvv = 0.0f;
         if constexpr (BIAS) bvv = (float)bcol[(long)min(qi, Sq - 1) * Sk];
         float g;
         const float pv = prob_fast<CAP, BIAS>(sacc[r], bvv, lk, lc, g);
-        const float du = pv * dpacc[r] * g;
-        sacc[r] = pv;
+        float du, pd;
+        if constexpr (DROP) {
+          // m dP - delta = m (dP - delta) + (1 - m)(-delta), m = keep / (1 - p)
+          const float mk = ((kq >> r) & 1u) ? p.drop.scale : 0.0f;
+          du = pv * fmaf(mk, dpacc[r], (1.0f - mk) * D4[si][r & 3]) * g;
+          pd = pv * mk;
+        } else {
+          du = pv * dpacc[r] * g;
+          pd = pv;
+        }
+        sacc[r] = pd;
         dpacc[r] = du;
         if constexpr (BIAS) {
           const bool vis = decltype(masked)::value ? (qi >= lo_j && qi < hi_j) : true;

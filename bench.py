@@ -120,6 +120,8 @@ def workload(name):
         "causal_gqa_fp16": W.causal_gqa(30.0).with_(name="causal_gqa_fp16_cap30", dtype="fp16"),
         "causal_gqa_sbhd": W.causal_gqa(30.0).with_(name="causal_gqa_sbhd_bf16_cap30", layout="sbhd"),
         "causal_gqa_dropout": W.causal_gqa(30.0).with_(name="causal_gqa_dropout0.1_bf16_cap30", dropout_p=0.1),
+        "sink_gqa_dropout": W.sink_gqa("learnable", 30.0).with_(name="sink_learnable_gqa_dropout0.1_bf16_cap30",
+                                                                 dropout_p=0.1),
         "tiny": W.tiny_fp32(),
     }
     return table[name]
