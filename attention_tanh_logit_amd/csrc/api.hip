@@ -523,10 +523,21 @@ size_t dkv_part_bytes(const attn_args* a) {
 
 size_t elem_bytes(const attn_args* a) { return a->dtype == ATTN_FP32 ? 4 : 2; }
 
-// A broadcast bias: the kernels write the full [B, Hq, Sq, Sk] dbias here,
-// reduced into the caller's dbias afterwards.
+// A bias broadcast over heads on the 16-key dk/dv kernel: each workgroup
+// column (KV head and query-head split) sums its heads' dbias tiles in LDS
+// and writes one [Sq, Sk] slab per batch row; 0 otherwise.
+int dbias_partials(const attn_args* a) {
+  return a->bias && (a->bias_bcast & ATTN_BIAS_BCAST_HEADS) && dkdv_writes_dbias_zeros(a) ? a->Hkv * head_split(a)
+                                                                                             : 0;
+}
+
+// A broadcast bias: the kernels write the full [B, Hq, Sq, Sk] dbias (or the
+// [B, partials, Sq, Sk] slabs above) here, reduced into the caller's dbias
+// afterwards.
 size_t dbias_full_bytes(const attn_args* a) {
-  return a->bias && a->bias_bcast ? align_up((size_t)a->B * a->Hq * a->Sq * a->Sk * elem_bytes(a)) : 0;
+  if (!a->bias || !a->bias_bcast) return 0;
+  const int np = dbias_partials(a);
+  return align_up((size_t)a->B * (np > 0 ? np : a->Hq) * a->Sq * a->Sk * elem_bytes(a));
 }
 
 size_t bwd_ws(const attn_args* a) {
@@ -801,6 +812,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
     p.dbias = ws;
   }
   ws += dbias_full_bytes(a);
+  p.dbias_np = dbias ? dbias_partials(a) : 0;
   float* delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)a->B * a->Hq * a->Sq * sizeof(float));
   float* part = nullptr;
@@ -846,7 +858,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
     e = o.dkdv(a->D, cap, bias, p, l);
     if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
     if (dbias_user && a->bias_bcast && a->Sq > 0) {
-      e = o.dbias_reduce(dbias, dbias_user, a->Hq, a->bias_bcast, l);
+      e = o.dbias_reduce(dbias, dbias_user, p.dbias_np > 0 ? p.dbias_np : a->Hq, a->bias_bcast, l);
       if (e != hipSuccess) return hip_fail(e, "dbias reduction launch");
     }
   }

@@ -182,8 +182,14 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
         // (with a bias, 32-query items: the bias and dbias tiles take registers)
         constexpr int NW = 8, BMQ = (D > 128 || BIAS) ? 32 : 64, BNK = D > 128 ? 64 : 128;
         const dim3 grid((l.Sk + BNK - 1) / BNK, p.Hkv * p.hsplit, l.B);
-        if (p.drop.on) dkdv16_kernel<D, CAP, BIAS, NW, BMQ, true><<<grid, 64 * NW, 0, l.stream>>>(p);
-        else dkdv16_kernel<D, CAP, BIAS, NW, BMQ, false><<<grid, 64 * NW, 0, l.stream>>>(p);
+        const bool part = BIAS && p.dbias_np > 0;
+        if (part) {
+          if (p.drop.on) dkdv16_kernel<D, CAP, BIAS, NW, BMQ, true, BIAS><<<grid, 64 * NW, 0, l.stream>>>(p);
+          else dkdv16_kernel<D, CAP, BIAS, NW, BMQ, false, BIAS><<<grid, 64 * NW, 0, l.stream>>>(p);
+        } else {
+          if (p.drop.on) dkdv16_kernel<D, CAP, BIAS, NW, BMQ, true, false><<<grid, 64 * NW, 0, l.stream>>>(p);
+          else dkdv16_kernel<D, CAP, BIAS, NW, BMQ, false, false><<<grid, 64 * NW, 0, l.stream>>>(p);
+        }
       } else {
         const dim3 grid((l.Sk + 127) / 128, p.Hkv * p.hsplit, l.B);
         if (p.drop.on) dkdv_fast_kernel<D, CAP, BIAS, true><<<grid, 256, 0, l.stream>>>(p);

@@ -956,8 +956,13 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
 // costs a quarter of an evaluation as in the forward.  dV takes the kept
 // probabilities times 1 / (1 - p), and dS = P (m dP - delta) with m = keep /
 // (1 - p).
-template <int D, bool CAP, bool BIAS, int NW, int BMQ, bool DROP>
+//
+// PART (with BIAS, a bias broadcast over heads): dbias summed over the
+// workgroup's query heads in LDS, one slab per workgroup column
+// (p.dbias_np > 0).
+template <int D, bool CAP, bool BIAS, int NW, int BMQ, bool DROP, bool PART>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
+  static_assert(BIAS || !PART, "head-summed dbias needs a bias");
   // D = 256: waves w and w + 1 share 16 keys and split dK^T, dV^T by columns
   // (and the query blocks of S, dP and dU between them: see QSPLIT)
   constexpr int NSL = D > 128 ? 2 : 1;
@@ -990,6 +995,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sB1[BT];
   __shared__ __attribute__((aligned(16))) bf16 sG0[BT];
   __shared__ __attribute__((aligned(16))) bf16 sG1[BT];
+  // a bias broadcast over heads (p.dbias_np > 0): the dbias tile summed over
+  // the workgroup's query heads of one query tile, in fp32, one buffer per
+  // query tile in turn (written out during the next tile's first item)
+  constexpr int BA = PART ? BT : 4;
+  __shared__ __attribute__((aligned(16))) float sA0[BA];
+  __shared__ __attribute__((aligned(16))) float sA1[BA];
 
   // XCD-aware, longest-first numbering and a lockstep query sweep, as in
   // the 32-key kernel
@@ -1094,11 +1105,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
     }
   };
   // the dbias tile of item it, gathered in tG, to global memory as whole rows
+  // (partial mode: the sum over the query tile's heads, after its last head)
   auto store_dbias = [&](int it, const bf16* tG) {
     if constexpr (BIAS) {
       if (!p.dbias) return;
-      const int hq = hk * p.G + split * GS + it % GS;
       const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
+      if constexpr (PART) {
+        if (it % GS != GS - 1) return;
+        const float* tA = ((it / GS) & 1) ? sA1 : sA0;
+        bf16* g0 = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.dbias_np + hk * p.hsplit + split) * Sq) * Sk + k0;
+#pragma unroll
+        for (int u = 0; u < (BMQ * BCPR + NT - 1) / NT; ++u) {
+          const int pc = u * NT + threadIdx.x;
+          if (pc < BMQ * BCPR) {
+            const int R = pc / BCPR, c = pc % BCPR;
+            if (q0 + R < Sq && k0 + 8 * c < Sk) {
+              const float* src = tA + R * BNK + 8 * (c ^ bsw(R));
+              float vals[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) vals[e] = src[e];
+              store8<bf16>(g0 + (long)(q0 + R) * Sk + 8 * c, vals);
+            }
+          }
+        }
+        return;
+      }
+      const int hq = hk * p.G + split * GS + it % GS;
       bf16* g0 = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.Hq + hq) * Sq) * Sk + k0;
 #pragma unroll
       for (int u = 0; u < (BMQ * BCPR + NT - 1) / NT; ++u) {
@@ -1199,7 +1231,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
           // masked pairs have P = 0 and are written as zeros; each query block
           // by the one wave that computed it
           if constexpr (BIAS) {
-            if (QSPLIT || sl == 0) tG[bidx(16 * qb + 4 * g + e, bcol)] = (bf16)(du * kGrad4<CAP>);
+            if (QSPLIT || sl == 0) {
+              const int x = bidx(16 * qb + 4 * g + e, bcol);
+              if constexpr (PART) {
+                float* tA = ((it / GS) & 1) ? sA1 : sA0;
+                tA[x] = (it % GS == 0 ? 0.0f : tA[x]) + du * kGrad4<CAP>;
+              } else {
+                tG[x] = (bf16)(du * kGrad4<CAP>);
+              }
+            }
           }
         }
       }
@@ -1326,9 +1366,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       const int z_hi = max(z_lo, min(qbeg + nqt * BMQ, Sq));
       const int nz = z_lo + (Sq - z_hi);
       const bf16x8 zero = {};
-      for (int hh = 0; hh < GS; ++hh) {
+      const int nzh = PART ? 1 : GS;
+      for (int hh = 0; hh < nzh; ++hh) {
         const int hq = hk * p.G + split * GS + hh;
-        bf16* g0 = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.Hq + hq) * Sq) * Sk + k0;
+        bf16* g0 = reinterpret_cast<bf16*>(p.dbias) +
+                   (PART ? ((long)b * p.dbias_np + hk * p.hsplit + split) * Sq * Sk
+                         : (((long)b * p.Hq + hq) * Sq) * Sk) + k0;
         for (int u = threadIdx.x; u < nz * BCPR; u += NT) {
           const int R = u / BCPR, c = u % BCPR;
           const int i = R < z_lo ? R : z_hi + (R - z_lo);

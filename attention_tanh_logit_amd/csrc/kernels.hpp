@@ -44,7 +44,7 @@ struct FwdParams {
   // delta = <dO, O> does not inherit the rounding of out
   void* out_lo;
   long qbs, qts, kbs, kts;   // element strides: batch row and token, q side and k side
-  Dropout drop;              // generic kernels only (the host routes dropout there)
+  Dropout drop;
   Mask mask;
   int Hq, Hkv, G;
   float sl2;    // scale * log2(e)            (no cap)
@@ -69,12 +69,16 @@ struct BwdParams {
   void* dk;
   void* dv;
   void* dbias;
+  // 0: dbias is [B, Hq, Sq, Sk].  > 0 (a bias broadcast over heads, on the
+  // 16-key dk/dv kernel): dbias is [B, dbias_np, Sq, Sk] with dbias_np =
+  // grid.y = Hkv * hsplit, each workgroup column's sum over its query heads
+  int dbias_np;
   // dU^T in 32-key x 32-query blocks (bf16), written by the dk/dv kernel and
   // read by the dq kernel; null when dq recomputes the probabilities itself
   void* du;
   int nkb32, nqb32;  // blocks along keys and along queries
   long qbs, qts, kbs, kts;   // element strides: batch row and token, q side and k side
-  Dropout drop;              // generic kernels only (the host routes dropout there)
+  Dropout drop;
   Mask mask;
   int Hq, Hkv, G;
   float scale;
