@@ -120,10 +120,16 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false) && !p.drop.on) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
       const dim3 grid((l.Sq + 63) / 64, p.Hq, l.B);
-      if (CAP && p.cl2 <= 60.0f && !kNarrow16) fwd512_kernel<CAP, CAP><<<grid, 512, 0, l.stream>>>(p);
-      else fwd512_kernel<CAP, false><<<grid, 512, 0, l.stream>>>(p);
+      const bool fixm = CAP && p.cl2 <= 60.0f && !kNarrow16;
+      if (p.drop.on) {
+        if (fixm) fwd512_kernel<CAP, CAP, true><<<grid, 512, 0, l.stream>>>(p);
+        else fwd512_kernel<CAP, false, true><<<grid, 512, 0, l.stream>>>(p);
+      } else {
+        if (fixm) fwd512_kernel<CAP, CAP, false><<<grid, 512, 0, l.stream>>>(p);
+        else fwd512_kernel<CAP, false, false><<<grid, 512, 0, l.stream>>>(p);
+      }
       return hipGetLastError();
     }
   }
@@ -206,9 +212,10 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false) && !p.drop.on) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
       const dim3 grid((l.Sk + 31) / 32, p.Hkv * p.hsplit, l.B);
-      dkdv512_kernel<CAP><<<grid, 512, 0, l.stream>>>(p);
+      if (p.drop.on) dkdv512_kernel<CAP, true><<<grid, 512, 0, l.stream>>>(p);
+      else dkdv512_kernel<CAP, false><<<grid, 512, 0, l.stream>>>(p);
       if (p.hsplit > 1) {
         const long nel = (long)l.B * l.Sk * p.Hkv * D;
         const float kscale = p.scale * (CAP ? 4.0f : 1.0f);

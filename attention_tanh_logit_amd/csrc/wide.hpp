@@ -47,7 +47,9 @@ __device__ __forceinline__ void group_sum4(f32x4* sX, int w, int lane, f32x4* ac
 // summed across the row group, then the capped logits, masking, online
 // softmax (running or, for caps with 2 c log2(e) <= 120, fixed reference
 // maximum; see fwd_fast_kernel) and O^T += V^T P^T over the slice's columns.
-template <bool CAP, bool FIXM>
+// DROP: dropout as in fwd_fast_kernel (one Philox4x32-10 evaluation per run
+// of four keys of a lane's query).
+template <bool CAP, bool FIXM, bool DROP>
 __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
   constexpr int D = 512, NT = 512, BM = 64, BN = 32;
@@ -183,6 +185,16 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
     pf[0] = to_frag(s, 0, (bf16*)nullptr);
     pf[1] = to_frag(s, 8, (bf16*)nullptr);
     lsum = sum_bf16x8(pf[1], sum_bf16x8(pf[0], lsum));
+    if constexpr (DROP) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const unsigned kp = keep4(p.drop, i, k0 + acc_row(h, 4 * q4), b * p.Hq + hq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * q4 + e] = ((kp >> e) & 1u) ? s[4 * q4 + e] : 0.0f;
+      }
+      pf[0] = to_frag(s, 0, (bf16*)nullptr);
+      pf[1] = to_frag(s, 8, (bf16*)nullptr);
+    }
     bf16x8 tv[NOB][2];
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
     }
   }
   if (has_sink) ltot += fast_exp2(sink2 - m);
-  const float inv = ltot > 0.0f ? oscale / ltot : 0.0f;
+  const float inv = ltot > 0.0f ? (DROP ? p.drop.scale : 1.0f) * oscale / ltot : 0.0f;
   if (i < Sq) {
     const long orow_off = qoff(p, b, i, hq, D) + colofs;
     bf16* orow = reinterpret_cast<bf16*>(p.out) + orow_off;
@@ -241,7 +253,9 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
 // across the group, P and dU = P (dP - delta) (1 - t^2) / 4, then
 // dV^T += dO^T P and dK^T += Q^T dU over the slice's columns with Q^T, dO^T
 // from transposing reads.  Slice 0 writes the dU block halves for dq.
-template <bool CAP>
+// DROP: dropout, the keep decisions shared in quads of lanes as in
+// dkdv16_kernel (every slice of a key group evaluates them for itself).
+template <bool CAP, bool DROP>
 __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   constexpr int D = 512, NT = 512, BNK = 32, BMQ = 32;
   constexpr int NCW = 4;   // 32-column contraction steps per slice
@@ -367,6 +381,21 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
     ATL_READ_AHEAD(8, 1, 4 * NCW);
     group_sum4<4>(sX, w, lane, acc);
 
+    // dropout: bit 4 qb + e keeps (query q0 + 16 qb + 4g + e, key j)
+    unsigned kq = 0;
+    if constexpr (DROP) {
+      const int t = r & 3;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int w4 = (int)keep4(p.drop, q0 + 16 * qb + 4 * g + t, j & ~3, b * p.Hq + hq);
+        const int n0 = __builtin_amdgcn_update_dpp(0, w4, 0x00, 0xF, 0xF, false);
+        const int n1 = __builtin_amdgcn_update_dpp(0, w4, 0x55, 0xF, 0xF, false);
+        const int n2 = __builtin_amdgcn_update_dpp(0, w4, 0xAA, 0xF, 0xF, false);
+        const int n3 = __builtin_amdgcn_update_dpp(0, w4, 0xFF, 0xF, 0xF, false);
+        kq |= (unsigned)(((n0 >> t) & 1) | (((n1 >> t) & 1) << 1) | (((n2 >> t) & 1) << 2) | (((n3 >> t) & 1) << 3))
+              << (4 * qb);
+      }
+    }
     auto grads = [&](auto masked) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -380,8 +409,15 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
           }
           float gg;
           const float pv = prob_fast<CAP, false>(acc[qb][e], 0.0f, lk, l, gg);
-          acc[qb][e] = pv;
-          acc[2 + qb][e] = pv * (acc[2 + qb][e] + md[x]) * gg;
+          if constexpr (DROP) {
+            // m dP - delta with m = keep / (1 - p); md = -delta
+            const float mk = ((kq >> x) & 1u) ? p.drop.scale : 0.0f;
+            acc[qb][e] = pv * mk;
+            acc[2 + qb][e] = pv * fmaf(mk, acc[2 + qb][e], md[x]) * gg;
+          } else {
+            acc[qb][e] = pv;
+            acc[2 + qb][e] = pv * (acc[2 + qb][e] + md[x]) * gg;
+          }
         }
       }
     };

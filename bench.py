@@ -122,6 +122,8 @@ def workload(name):
         "causal_gqa_dropout": W.causal_gqa(30.0).with_(name="causal_gqa_dropout0.1_bf16_cap30", dropout_p=0.1),
         "sink_gqa_dropout": W.sink_gqa("learnable", 30.0).with_(name="sink_learnable_gqa_dropout0.1_bf16_cap30",
                                                                  dropout_p=0.1),
+        "window_d512_dropout": W.window_large_d(512, "bf16").with_(name="window1024_d512_dropout0.1_bf16_cap50",
+                                                                    dropout_p=0.1),
         "tiny": W.tiny_fp32(),
     }
     return table[name]

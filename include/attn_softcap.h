@@ -111,8 +111,8 @@ typedef enum attn_bias_bcast {
  *    dq kernel through the workspace as bf16 blocks of 32 keys x 32 queries,
  *    B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB (4 GiB at B=4, Hq=32, S=4096; only
  *    the visible blocks are written and read).  bf16 with D = 64, 128 or 256
- *    (with a bias also Sk % 8 == 0), or D = 512 without a bias (not
- *    with dropout); ATTN_UNSUPPORTED otherwise.
+ *    (with a bias also Sk % 8 == 0), or D = 512 without a bias;
+ *    ATTN_UNSUPPORTED otherwise.
  *  - ATTN_DQ_RECOMPUTE: the dq kernel recomputes the logits, probabilities
  *    and dP itself; the workspace stays O(B*Hq*Sq).
  *  - ATTN_DQ_AUTO (0): DU_BLOCKS where supported, D >= 128 (or dropout is
@@ -175,9 +175,10 @@ typedef struct attn_args {
    * kept iff word j % 4 of Philox4x32-10 at counter (j / 4, i, b * Hq + h,
    * offset % 2^32) under key (seed % 2^32, seed / 2^32) is at least
    * floor(p * 2^32).  The backward must get the same p, seed and offset.
-   * bf16 / fp16 with D = 64, 128 or 256 run it on the fast kernels (dq from
-   * the dU blocks, or on the generic kernel with ATTN_DQ_RECOMPUTE); fp32
-   * and D = 512 run the generic (slower) kernels. */
+   * bf16 / fp16 run it on the fast kernels where those take the problem (D
+   * = 64 .. 256, and 512 without a bias; dq from the dU blocks, or on the
+   * generic kernel with ATTN_DQ_RECOMPUTE); fp32 and the rest run the
+   * generic (slower) kernels. */
   float dropout_p;             /* 0: off; in [0, 1) */
   uint64_t dropout_seed;
   uint64_t dropout_offset;

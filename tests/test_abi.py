@@ -58,6 +58,7 @@ def test_valid_arguments_pass():
     assert _status(_args(dropout_p=0.1, dq_mode=1))[0] == 0          # dropout on the fast dk/dv kernel, D = 128
     assert _status(_args(dropout_p=0.1, dq_mode=1, D=256))[0] == 0
     assert _status(_args(dropout_p=0.1, dq_mode=1, D=64))[0] == 0
+    assert _status(_args(dropout_p=0.1, dq_mode=1, D=512))[0] == 0
 
 
 BAD = {
@@ -91,7 +92,7 @@ BAD = {
     "mask_misaligned": (dict(mask=0x3001), 1, "mask"),
     "dropout_one": (dict(dropout_p=1.0), 1, "dropout_p"),
     "dropout_negative": (dict(dropout_p=-0.1), 1, "dropout_p"),
-    "dropout_with_du_blocks_d512": (dict(dropout_p=0.1, dq_mode=1, D=512), 2, "DU_BLOCKS"),
+    "dropout_with_du_blocks_fp32": (dict(dropout_p=0.1, dq_mode=1, dtype=1), 2, "DU_BLOCKS"),
     "bad_layout": (dict(layout=2), 1, "layout"),
 }
 

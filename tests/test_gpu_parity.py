@@ -323,7 +323,7 @@ def test_dropout_matches_oracle(dtype, D, p, feat):
     _check(case(**kw))
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
 @pytest.mark.parametrize("dq_mode", ["du_blocks", "recompute"])
 def test_dropout_on_the_fast_dkdv_kernel_both_dq_modes(D, dq_mode):
     """The fast dk/dv kernel with dropout hands dq either its dU blocks or leaves dq to the

@@ -31,6 +31,7 @@ REPEAT = {
     "fp16_d128_bias": dict(dtype="fp16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True, sink_mode="learnable"),
     "bf16_d128_dropout": dict(dtype="bf16", D=128, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable", dropout_p=0.3),
     "bf16_d64_dropout": dict(dtype="bf16", D=64, B=2, S=203, Hq=4, Hkv=2, dropout_p=0.3),
+    "bf16_d512_dropout": dict(dtype="bf16", D=512, B=1, S=203, Hq=4, Hkv=2, dropout_p=0.3, sink_mode="learnable"),
 }
 
 
