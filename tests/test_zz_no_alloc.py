@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import attention_tanh_logit_amd as A
-from harness import TOL, case, rel_err, to_dev
+from harness import TOL, as_dense_mask, as_k_start, case, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,12 @@ def _inputs(c):
         kw["bias"] = to_dev(c["bias"], dt)
     if c["segment_ids"] is not None:
         kw["segment_ids"] = torch.from_numpy(c["segment_ids"]).cuda()
+    if c.get("k_start") is not None:
+        kw["k_start"] = torch.from_numpy(np.ascontiguousarray(c["k_start"], dtype=np.int32)).cuda()
+    if c.get("mask") is not None:
+        kw["mask"] = torch.from_numpy(np.ascontiguousarray(c["mask"], dtype=bool)).cuda()
+    if c.get("dropout"):
+        kw.update(dropout_p=c["dropout"][0], dropout_seed=c["dropout"][1], dropout_offset=c["dropout"][2])
     return q, k, v, do, kw
 
 
@@ -61,10 +67,21 @@ SMALL_AFTER = {
 }
 
 
+# packed forms and dropout: the first call with a dense mask (its prepared ranges in the
+# scratch), the second with k_start
+FORMS = {"bf16_d128_dropout_packed": ("dense_mask", "k_start")}
+SMALL_AFTER["bf16_d128_dropout_packed"] = (
+    dict(dtype="bf16", D=128, B=2, S=512, Hq=8, Hkv=2, dropout_p=0.2, sink_mode="learnable",
+         segments=[[100, 301], [64]]),
+    dict(dtype="bf16", D=128, B=1, S=203, Hq=4, Hkv=2, dropout_p=0.1, segments=[[77]]))
+
+
 @pytest.mark.parametrize("name", list(SMALL_AFTER))
 def test_noalloc_equals_attn_bwd_bitwise_on_two_calls(name):
     for i, kw in enumerate(SMALL_AFTER[name]):
         c = case(**kw)
+        if name in FORMS:
+            c = as_dense_mask(c) if FORMS[name][i] == "dense_mask" else as_k_start(c)
         print(f"noalloc {name} call {i + 1}: q={c['q'].shape}", flush=True)
         ref, got = _both(c, "auto", "auto")
         for n, r in ref.items():
