@@ -708,6 +708,7 @@ attn_status attn_fwd(const attn_args* a, void* out, float* lse, void* out_lo, vo
   const size_t need = fwd_ws(a);
   if (workspace_bytes < need || (need && !workspace))
     return fail(ATTN_INVALID_ARGUMENT, "workspace smaller than attn_fwd_workspace_size");
+  if (((uintptr_t)workspace & 255) != 0) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if ((size_t)a->B * a->Sq * a->Hq == 0) return ATTN_OK;
   if (!out || !lse) return fail(ATTN_INVALID_ARGUMENT, "out and lse must not be NULL");
   if (!aligned16(out) || !aligned16(out_lo)) return fail(ATTN_INVALID_ARGUMENT, "out and out_lo must be 16-byte aligned");
@@ -767,6 +768,7 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
   const size_t need = bwd_ws(a);
   if (workspace_bytes < need || (need && !workspace))
     return fail(ATTN_INVALID_ARGUMENT, "workspace smaller than attn_bwd_workspace_size");
+  if (((uintptr_t)workspace & 255) != 0) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if ((size_t)a->B * (a->Sq + a->Sk) == 0) return ATTN_OK;
   if (!lse || !dout) return fail(ATTN_INVALID_ARGUMENT, "lse and dout must not be NULL");
   if ((phases & kPhasePre) && !out) return fail(ATTN_INVALID_ARGUMENT, "out must not be NULL");

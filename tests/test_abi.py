@@ -150,6 +150,21 @@ def test_misaligned_outputs_rejected_before_any_launch():
     assert s == 1 and "aligned" in L.attn_last_error().decode()
 
 
+def test_misaligned_workspace_rejected_before_any_launch():
+    """The header asks for a 256-byte aligned workspace (its parts are laid out at 256-byte
+    offsets from it); a misaligned one is refused with nothing enqueued."""
+    L = A.lib()
+    a = _args(segment_ids=0x9000)                      # a forward that needs a workspace
+    need = L.attn_fwd_workspace_size(ctypes.byref(a))
+    assert need > 0
+    assert L.attn_fwd(ctypes.byref(a), 0x1000, 0x2000, None, 0x10010, need, None) == 1
+    assert "256-byte" in L.attn_last_error().decode()
+    need = L.attn_bwd_workspace_size(ctypes.byref(a))
+    s = L.attn_bwd(ctypes.byref(a), 0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, None, 0x10040,
+                   need, None)
+    assert s == 1 and "256-byte" in L.attn_last_error().decode()
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     import attention_tanh_logit_amd.ops as ops
     monkeypatch.setattr(ops, "_lib", None)
