@@ -129,6 +129,22 @@ def test_thd_varlen_matches_oracle(dtype):
     _check(c, thd=True)
 
 
+@pytest.mark.parametrize("form", ["dropout", "k_start", "dense_mask"])
+def test_thd_with_the_other_options(form):
+    """THD (cu_seqlens, one flat token axis) together with dropout, a k_start that cuts a
+    window into each sequence, or a dense band mask on top of the sequences."""
+    c = case(dtype="bf16", D=128, B=1, S=230, segments=[[7, 64, 65, 130]], sink_mode="learnable",
+             dropout_p=0.2 if form == "dropout" else 0.0)
+    seg = c["segment_ids"][0]
+    i = np.arange(230)
+    start = np.array([np.nonzero(seg == seg[t])[0][0] for t in i])
+    if form == "k_start":
+        c["k_start"] = np.maximum(start, i - 40)[None].astype(np.int32)
+    elif form == "dense_mask":
+        c["mask"] = ((i[:, None] - i[None, :]) < 50)[None]
+    _check(c, thd=True)
+
+
 def test_thd_equals_segment_ids_bitwise():
     c = case(dtype="bf16", D=64, B=2, S=192, segments=[[50, 51, 120], [64, 128]])
     a = run_gpu(c)
