@@ -1,0 +1,54 @@
+"""The kernels read no workspace they have not written in the same call.
+
+Every workspace the binding allocates is filled with 0xFF bytes first (NaN as bf16, fp16 and
+fp32, -1 as int32), and the results must be bitwise those of a run on a fresh workspace.  A
+kernel that read a part of the workspace no earlier kernel of the call wrote (the visibility
+bounds, delta, the sink partials, the dU blocks, the head-split dK/dV partials, the full or
+head-summed dbias of a broadcast bias) would turn NaN or a wrong bound into its results.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_tanh_logit_amd.ops as ops
+from harness import as_dense_mask, as_k_start, case, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "du_blocks_segments": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]],
+                               sink_mode="learnable"),
+    "head_split_d64": dict(dtype="bf16", D=64, B=1, S=203, Hq=8, Hkv=2, sink_mode="learnable"),
+    "bias_heads_partials": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True, bias_bcast="heads",
+                                softcap=50.0),
+    "bias_batch_fp32": dict(dtype="fp32", D=128, B=2, S=131, Hq=4, Hkv=2, bias=True, bias_bcast="batch"),
+    "dense_mask": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]]),
+    "k_start": dict(dtype="bf16", D=256, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]]),
+    "dropout": dict(dtype="bf16", D=128, B=2, S=203, Hq=4, Hkv=2, dropout_p=0.2, sink_mode="learnable"),
+    "wide_d512": dict(dtype="bf16", D=512, B=1, S=150, Hq=2, Hkv=1, sink_mode="learnable"),
+}
+
+
+def _poisoned(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.full((nbytes,), 255, dtype=torch.uint8, device=device)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_results_do_not_depend_on_the_workspace_contents(name, monkeypatch):
+    c = case(**CASES[name])
+    if name == "dense_mask":
+        c = as_dense_mask(c)
+    elif name == "k_start":
+        c = as_k_start(c)
+    print(f"workspace poisoning: {name}", flush=True)
+    clean = run_gpu(c)
+    monkeypatch.setattr(ops, "_workspace", _poisoned)
+    dirty = run_gpu(c)
+    for n, x in clean.items():
+        if x is None:
+            assert dirty[n] is None, n
+            continue
+        assert not np.isnan(x).any(), f"{name}: {n} has NaN on a fresh workspace"
+        assert x.tobytes() == dirty[n].tobytes(), f"{name}: {n} depends on the workspace contents"
