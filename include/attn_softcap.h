@@ -110,8 +110,8 @@ typedef enum attn_bias_bcast {
  *  - ATTN_DQ_DU_BLOCKS: the dk/dv kernel hands dU = dS * (1 - tanh^2) to the
  *    dq kernel through the workspace as bf16 blocks of 32 keys x 32 queries,
  *    B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB (4 GiB at B=4, Hq=32, S=4096; only
- *    the visible blocks are written and read).  bf16 with D = 64, 128 or 256
- *    (with a bias also Sk % 8 == 0), or D = 512 without a bias;
+ *    the visible blocks are written and read).  bf16 or fp16 with D = 64, 128
+ *    or 256 (with a bias also Sk % 8 == 0), or D = 512 without a bias;
  *    ATTN_UNSUPPORTED otherwise.
  *  - ATTN_DQ_RECOMPUTE: the dq kernel recomputes the logits, probabilities
  *    and dP itself; the workspace stays O(B*Hq*Sq).
@@ -195,14 +195,20 @@ attn_status attn_validate(const attn_args* a);
 /* Device workspace (bytes) that attn_fwd / attn_bwd need for `a` (0 if
  * none); (size_t)-1 if `a` is invalid.  The size depends only on `a`:
  *  - forward: two int32 [B*Sq] arrays of segment runs, only with
- *    segment_ids or cu_seqlens, and with k_start one int32 [B*Sq] and one
- *    int32 [B*Sk] array of visibility bounds;
- *  - backward: the same runs, delta [B*Hq*Sq] fp32, sink-gradient partials
- *    with a learnable sink, the dU blocks when dq_mode resolves to
- *    ATTN_DQ_DU_BLOCKS (see attn_dq_mode), a full [B, Hq, Sq, Sk] dbias in
- *    the input dtype when the bias is broadcast (reduced into the caller's
- *    dbias), and for bf16 with D = 64, 128 or 256 when B*Hkv*ceil(Sk/128) <
- *    1024, 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial dK/dV: the dk/dv kernel
+ *    segment_ids or cu_seqlens; with k_start one int32 [B*Sq] and one int32
+ *    [B*Sk] array of visibility bounds; with a dense mask five int32 [B*Sq]
+ *    and two int32 [B*Sk] arrays and one int32 per batch row (the key range
+ *    of each query prepared from the mask, the query range of each key, and
+ *    whether those ranges describe the mask exactly);
+ *  - backward: the same, delta [B*Hq*Sq] fp32, sink-gradient partials with
+ *    a learnable sink, the dU blocks when dq_mode resolves to
+ *    ATTN_DQ_DU_BLOCKS (see attn_dq_mode), with a broadcast bias and dbias a
+ *    full [B, Hq, Sq, Sk] dbias in the input dtype (for a bias broadcast over
+ *    heads on the 16-bit D = 128 / 256 kernels, [B, Hkv*s, Sq, Sk] slabs
+ *    already summed over each workgroup's heads; reduced into the caller's
+ *    dbias), and for bf16 / fp16 with D = 64, 128 or 256 when
+ *    B*Hkv*ceil(Sk/128) < 1024 (D = 512 without a bias: B*Hkv*ceil(Sk/32) <
+ *    1024), 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial dK/dV: the dk/dv kernel
  *    then splits each GQA group's query heads over s workgroups (s the
  *    smallest divisor of Hq/Hkv reaching 1024 workgroups, else the largest),
  *    summed afterwards in a fixed order. */
