@@ -42,7 +42,7 @@ ATL_DQ(bf16, 256, 256, 2, 32, 256)
 ATL_DQ(bf16, 512, 256, 2, 64, 128)
 ATL_DQ(float, 64, 64, 4, 32, 64)
 ATL_DQ(float, 128, 128, 2, 32, 128)
-ATL_DQ(float, 256, 128, 2, 32, 128)
+ATL_DQ(float, 256, 128, 4, 32, 64)
 ATL_DQ(float, 512, 256, 2, 32, 128)
 
 //           T      D   DO NKG  DC
