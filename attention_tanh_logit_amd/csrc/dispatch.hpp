@@ -33,8 +33,8 @@ ATL_FWD(bf16, 256, 256, 2, 32, 256)
 ATL_FWD(bf16, 512, 128, 2, 64, 128)
 ATL_FWD(float, 64, 64, 4, 32, 64)
 ATL_FWD(float, 128, 128, 2, 32, 128)
-ATL_FWD(float, 256, 256, 4, 32, 128)
-ATL_FWD(float, 512, 256, 2, 32, 128)
+ATL_FWD(float, 256, 256, 4, 64, 64)
+ATL_FWD(float, 512, 256, 4, 32, 64)
 
 ATL_DQ(bf16, 64, 64, 4, 64, 64)
 ATL_DQ(bf16, 128, 128, 4, 32, 128)
