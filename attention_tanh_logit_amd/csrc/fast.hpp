@@ -265,6 +265,20 @@ __device__ __forceinline__ float sum_bf16x8(const bf16x8& f, float acc) {
   return acc;
 }
 
+// The same for 4 values.
+__device__ __forceinline__ float sum_bf16x4(const bf16x4& f, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+#if ATL_FAST_F16
+    acc = __builtin_amdgcn_fdot2(bf16x2{f[2 * e], f[2 * e + 1]}, one, acc, false);
+#else
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[2 * e], f[2 * e + 1]}, one, acc, false);
+#endif
+  }
+  return acc;
+}
+
 // Log2-unit logit constants of the bf16 fast path (see the header comment).
 struct LogitK {
   float a;    // multiplies q.k:   2*log2e*scale/c (cap) or scale*log2e

@@ -6,49 +6,40 @@
 // 128.  A wave keeps only its slice of the fixed operand (Q columns in the
 // forward, K and V columns in dk/dv) and of the output accumulators, so that
 // two waves fit a SIMD.  Each wave contracts its 128 columns into a partial
-// logit block; the four partials of a group are exchanged through LDS and
-// summed by every wave in the same slice order (bit-identical totals), after
-// which every wave of the group holds the whole logits and computes the
-// probabilities itself (MaxText commit quoted on "Support logits soft-capping
-// in the Pallas-Triton attention VJP": head_dim above 256 accumulated in
-// chunks).  Streamed tiles (K/V in the forward, Q/dO in dk/dv; 32 rows of
-// 1 KiB) go HBM -> LDS by buffer DMA, double-buffered, swizzled per row as
-// on the fast path (the swizzles permute 16-byte slots inside 128-column
-// groups, so a slice is a plain column offset).  LDS: 4 x 32 KiB of tiles +
-// 32 KiB of partials = 160 KiB, one workgroup per CU.
+// logit block (MaxText commit quoted on "Support logits soft-capping in the
+// Pallas-Triton attention VJP": head_dim above 256 accumulated in chunks).
+// The four partials of a group are reduce-scattered through LDS: each wave
+// sums one quarter of the block's elements, in slice order, and computes the
+// probabilities (and in dk/dv the dU) of that quarter only; the quarters,
+// rounded to 16 bits as the P V, dO^T P and Q^T dU products take them, are
+// then gathered through LDS so that every wave holds the whole fragments.
+// The transcendental and elementwise work of a tile is thus done once per
+// group, not once per slice.  Streamed tiles (K/V in the forward, Q/dO in
+// dk/dv; 32 rows of 1 KiB) go HBM -> LDS by buffer DMA, double-buffered,
+// swizzled per row as on the fast path (the swizzles permute 16-byte slots
+// inside 128-column groups, so a slice is a plain column offset).  LDS:
+// 4 x 32 KiB of tiles + 24 KiB of partials + the gathered fragments (and in
+// the forward the row extremes and sums) = 156-158 KiB, one workgroup per CU.
 #pragma once
 
 #include "fast.hpp"
 
 namespace ATL_NS {
 
-// The four partial accumulators of this wave's group, summed in slice order.
-// sX holds [wave][quantity][lane] f32x4; NQ quantities per wave.
-template <int NQ>
-__device__ __forceinline__ void group_sum4(f32x4* sX, int w, int lane, f32x4* acc) {
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) sX[(w * NQ + q) * 64 + lane] = acc[q];
-  __syncthreads();
-  const int w0 = w & ~3;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    f32x4 s = sX[(w0 * NQ + q) * 64 + lane];
-#pragma unroll
-    for (int x = 1; x < 4; ++x) s += sX[((w0 + x) * NQ + q) * 64 + lane];
-    acc[q] = s;
-  }
-}
-
 // ============================================================== forward (D = 512)
 
 // One workgroup = 64 query rows of one head; wave w = 4 rg + sl holds rows
 // q0 + 32 rg .. + 31 and columns 128 sl .. + 127 of Q (as Q^T fragments)
 // and of O.  Per 32-key tile: partial S^T = K Q^T over the slice's columns,
-// summed across the row group, then the capped logits, masking, online
-// softmax (running or, for caps with 2 c log2(e) <= 120, fixed reference
-// maximum; see fwd_fast_kernel) and O^T += V^T P^T over the slice's columns.
+// reduce-scattered across the row group; wave sl takes the capped logits,
+// masking and probabilities of its quarter (keys acc_row(h, 4 sl) + 0..3 of
+// each lane's query) under the online softmax (running maximum, its extreme
+// exchanged between the quarters through LDS, or for caps with
+// 2 c log2(e) <= 120 a fixed reference maximum; see fwd_fast_kernel), keeps
+// the row sum of its quarter, and after the gather O^T += V^T P^T over the
+// slice's columns.  The quarters' row sums are added once, at the end.
 // DROP: dropout as in fwd_fast_kernel (one Philox4x32-10 evaluation per run
-// of four keys of a lane's query).
+// of four keys of a lane's query, the run of the wave's quarter).
 template <bool CAP, bool FIXM, bool DROP>
 __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
@@ -60,7 +51,12 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
-  __shared__ __attribute__((aligned(16))) f32x4 sX[8 * 4 * 64];
+  // partials for the reduce-scatter: [rg][quarter][the three other slices][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 sX[2 * 4 * 3 * 64];
+  // the gathered P fragments: [rg][key half][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 sP[2 * 2 * 64];
+  // the quarters' logit extremes (per key tile), then their row sums: [rg][slice][lane]
+  __shared__ float sE[2 * 4 * 64];
 
   int qt, hq, b;
   {
@@ -132,29 +128,37 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
     f32x16 s = f32x16{};
 #pragma unroll
     for (int c = 0; c < NCW; ++c) mma(s, fo.frag(tK, 0, 8 * sl + c), qf[c]);
-    {
-      f32x4 a[4];
+    // reduce-scatter: quarter x (elements 4x .. 4x + 3, keys acc_row(h, 4x) + 0..3)
+    // goes to slice x; each wave sums its own quarter in slice order
+    f32x4 own = f32x4{};
 #pragma unroll
-      for (int x = 0; x < 16; ++x) a[x >> 2][x & 3] = s[x];
-      group_sum4<4>(sX, w, lane, a);
-#pragma unroll
-      for (int x = 0; x < 16; ++x) s[x] = a[x >> 2][x & 3];
+    for (int x = 0; x < 4; ++x) {
+      const f32x4 v = {s[4 * x], s[4 * x + 1], s[4 * x + 2], s[4 * x + 3]};
+      if (x != sl) sX[((rg * 4 + x) * 3 + (sl < x ? sl : sl - 1)) * 64 + lane] = v;
+      else own = v;
     }
-    // logits: CAP keeps r = 1/(1+2^y) (masked: +inf), else y (masked: -inf)
+    __syncthreads();
+    f32x4 lq = f32x4{};
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      if (y == sl) lq += own;
+      else lq += sX[((rg * 4 + sl) * 3 + (y < sl ? y : y - 1)) * 64 + lane];
+    }
+    // logits of the quarter: CAP keeps r = 1/(1+2^y) (masked: +inf), else y (masked: -inf)
     float ext = CAP ? INFINITY : -INFINITY;
     auto logits = [&](auto masked) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const float y = s[jj] * lk.a;
+      for (int e = 0; e < 4; ++e) {
+        const float y = lq[e] * lk.a;
         float v;
         if constexpr (FIXM) v = __builtin_amdgcn_rcpf(fmaf(fast_exp2(y), kfix, kfix));
         else if constexpr (CAP) v = __builtin_amdgcn_rcpf(1.0f + fast_exp2(y));
         else v = y;
         if constexpr (decltype(masked)::value) {
-          const int key = k0 + acc_row(h, jj);
+          const int key = k0 + acc_row(h, 4 * sl + e);
           v = (key >= lo_i && key < hi_i && dense_ok(p.mask, dchk, b, i, key)) ? v : ((CAP && !FIXM) ? INFINITY : -INFINITY);
         }
-        s[jj] = v;
+        lq[e] = v;
         if constexpr (!FIXM) ext = CAP ? fminf(ext, v) : fmaxf(ext, v);
       }
     };
@@ -162,7 +166,15 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
     else logits(bool_c<true>{});
     float base = 0.0f;
     if constexpr (!FIXM) {
+      // the row's extreme over the four quarters
       ext = CAP ? fminf(ext, xor32(ext)) : fmaxf(ext, xor32(ext));
+      sE[(rg * 4 + sl) * 64 + lane] = ext;
+      __syncthreads();
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const float o = sE[(rg * 4 + y) * 64 + lane];
+        ext = CAP ? fminf(ext, o) : fmaxf(ext, o);
+      }
       const float mx = CAP ? fmaf(ext, -2.0f * lk.c2, lk.c2) : ext;
       const bool grow = mx > m + 8.0f;
       if (__any(grow)) {
@@ -175,26 +187,26 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
       }
       base = (m == -INFINITY) ? 0.0f : m;
     }
+    bf16x4 pq;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      s[jj] = FIXM  ? fast_exp2(s[jj])
-              : CAP ? fast_exp2(fmaf(s[jj], -2.0f * lk.c2, lk.c2 - base))
-                    : fast_exp2(s[jj] - base);
+    for (int e = 0; e < 4; ++e) {
+      pq[e] = (bf16)(FIXM  ? fast_exp2(lq[e])
+                     : CAP ? fast_exp2(fmaf(lq[e], -2.0f * lk.c2, lk.c2 - base))
+                           : fast_exp2(lq[e] - base));
     }
-    bf16x8 pf[2];
-    pf[0] = to_frag(s, 0, (bf16*)nullptr);
-    pf[1] = to_frag(s, 8, (bf16*)nullptr);
-    lsum = sum_bf16x8(pf[1], sum_bf16x8(pf[0], lsum));
+    // the quarter's share of the row sum (of the rounded probabilities, before dropout)
+    lsum = sum_bf16x4(pq, lsum);
     if constexpr (DROP) {
+      const unsigned kp = keep4(p.drop, i, k0 + acc_row(h, 4 * sl), b * p.Hq + hq);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const unsigned kp = keep4(p.drop, i, k0 + acc_row(h, 4 * q4), b * p.Hq + hq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[4 * q4 + e] = ((kp >> e) & 1u) ? s[4 * q4 + e] : 0.0f;
-      }
-      pf[0] = to_frag(s, 0, (bf16*)nullptr);
-      pf[1] = to_frag(s, 8, (bf16*)nullptr);
+      for (int e = 0; e < 4; ++e) pq[e] = ((kp >> e) & 1u) ? pq[e] : (bf16)0.0f;
     }
+    // gather the quarters: quarter sl is elements 4 (sl % 2) .. + 3 of P fragment sl / 2
+    reinterpret_cast<bf16x4*>(&sP[(rg * 2 + (sl >> 1)) * 64 + lane])[sl & 1] = pq;
+    __syncthreads();
+    bf16x8 pf[2];
+    pf[0] = sP[(rg * 2) * 64 + lane];
+    pf[1] = sP[(rg * 2 + 1) * 64 + lane];
     bf16x8 tv[NOB][2];
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
@@ -214,7 +226,13 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
     if (t + 1 < ntiles) step(sK1, sV1, sK0, sV0, t + 1);
   }
 
-  float ltot = lsum + xor32(lsum);
+  // the row sum over the four quarters, in slice order, and the two key halves
+  sE[(rg * 4 + sl) * 64 + lane] = lsum;
+  __syncthreads();
+  float lrow = 0.0f;
+#pragma unroll
+  for (int y = 0; y < 4; ++y) lrow += sE[(rg * 4 + y) * 64 + lane];
+  float ltot = lrow + xor32(lrow);
   float oscale = 1.0f;
   if constexpr (FIXM) {
     if (has_sink && sink2 > m) {
@@ -249,12 +267,16 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
 // One workgroup = 32 keys of one KV head; wave w = 4 kg + sl holds keys
 // k0 + 16 kg .. + 15 and columns 128 sl .. + 127.  Per 32-query item (one
 // query head): partial S = Q K^T and dP = dO V^T over the slice's columns on
-// v_mfma_f32_16x16x32_bf16 (lane: key r, queries 16 qb + 4g + e), summed
-// across the group, P and dU = P (dP - delta) (1 - t^2) / 4, then
-// dV^T += dO^T P and dK^T += Q^T dU over the slice's columns with Q^T, dO^T
-// from transposing reads.  Slice 0 writes the dU block halves for dq.
-// DROP: dropout, the keep decisions shared in quads of lanes as in
-// dkdv16_kernel (every slice of a key group evaluates them for itself).
+// v_mfma_f32_16x16x32_bf16 (lane: key r, queries 16 qb + 4g + e).  The
+// partials are reduce-scattered across the group: wave sl sums, in slice
+// order, only the quarter qb = sl / 2, e = 2 (sl % 2) .. + 1 of each lane's
+// eight (key, query) pairs and takes P and dU = P (dP - delta) (1 - t^2) / 4
+// for that quarter alone; the four quarters, packed to 16 bits, are then
+// gathered through LDS so that every wave of the group holds all of P and
+// dU.  Then dV^T += dO^T P and dK^T += Q^T dU over the slice's columns with
+// Q^T, dO^T from transposing reads.  Slice 0 writes the dU block halves for
+// dq.  DROP: dropout, the keep decisions shared in quads of lanes as in
+// dkdv16_kernel (each wave evaluates those of its quarter).
 template <bool CAP, bool DROP>
 __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   constexpr int D = 512, NT = 512, BNK = 32, BMQ = 32;
@@ -265,7 +287,11 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sQ1[BMQ * D];
   __shared__ __attribute__((aligned(16))) bf16 sO0[BMQ * D];
   __shared__ __attribute__((aligned(16))) bf16 sO1[BMQ * D];
-  __shared__ __attribute__((aligned(16))) f32x4 sX[8 * 4 * 64];
+  // partials for the reduce-scatter: [kg][quarter][the three other slices][lane],
+  // each (S, S, dP, dP) of the quarter's two pairs
+  __shared__ __attribute__((aligned(16))) f32x4 sX[2 * 4 * 3 * 64];
+  // the gathered P and dU fragments: [kg][P, dU][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 sPU[2 * 2 * 64];
 
   int kb, hk, b, split;
   {
@@ -285,6 +311,8 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   const int colofs = 128 * sl;
   const int r = lane & 15;
   const int g = lane >> 4;
+  const int qbw = sl >> 1;       // this wave's quarter: query block qbw,
+  const int ew = 2 * (sl & 1);   // pairs e = ew, ew + 1
   const int k0 = kb * BNK;
   const int kw = k0 + 16 * kg;
   const int j = kw + r;
@@ -330,17 +358,18 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
     load_tile<BMQ, D, NT, false, true>(nQ, reinterpret_cast<const bf16*>(p.q) + hoff, qstride, q0, Sq);
     load_tile<BMQ, D, NT, false, true>(nO, reinterpret_cast<const bf16*>(p.dout) + hoff, qstride, q0, Sq);
   };
-  // lse and delta of this lane's queries 16 qb + 4g + e of item it, raw
-  float nl[8], nd[8];
+  // lse and delta of this lane's queries of the wave's quarter of item it
+  // (16 qbw + 4g + ew + t), raw
+  float nl[2], nd[2];
   auto get_stats = [&](int it) {
     const long row = ((long)b * p.Hq + head_of(it)) * Sq;
     const int q0 = q0_of(it);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int q = q0 + 16 * (x >> 2) + 4 * g + (x & 3);
+    for (int t = 0; t < 2; ++t) {
+      const int q = q0 + 16 * qbw + 4 * g + ew + t;
       const long li = row + min(q, Sq - 1);
-      nl[x] = q < Sq ? p.lse[li] : -INFINITY;
-      nd[x] = p.delta[li];
+      nl[t] = q < Sq ? p.lse[li] : -INFINITY;
+      nd[t] = p.delta[li];
     }
   };
 
@@ -357,11 +386,11 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
     const int q0 = q0_of(it);
     // this item's stats (log2 units, folded with the cap's constant), then
     // the next item's loads
-    float lc[8], md[8];
+    float lc[2], md[2];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      lc[x] = nl[x] != -INFINITY ? (CAP ? p.cl2 : 0.0f) - nl[x] * kLog2e : -INFINITY;
-      md[x] = -nd[x];
+    for (int t = 0; t < 2; ++t) {
+      lc[t] = nl[t] != -INFINITY ? (CAP ? p.cl2 : 0.0f) - nl[t] * kLog2e : -INFINITY;
+      md[t] = -nd[t];
     }
     if (more) {
       fetch(it + 1, nQ, nO);
@@ -379,52 +408,77 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
       }
     }
     ATL_READ_AHEAD(8, 1, 4 * NCW);
-    group_sum4<4>(sX, w, lane, acc);
 
-    // dropout: bit 4 qb + e keeps (query q0 + 16 qb + 4g + e, key j)
+    // reduce-scatter: quarter x (query block x / 2, pairs 2 (x % 2) .. + 1)
+    // goes to slice x; each wave sums its own quarter in slice order
+    f32x4 own = f32x4{};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int qb = x >> 1, e = 2 * (x & 1);
+      const f32x4 v = {acc[qb][e], acc[qb][e + 1], acc[2 + qb][e], acc[2 + qb][e + 1]};
+      if (x != sl) sX[((kg * 4 + x) * 3 + (sl < x ? sl : sl - 1)) * 64 + lane] = v;
+      else own = v;
+    }
+    __syncthreads();
+    f32x4 tot = f32x4{};
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      if (y == sl) tot += own;
+      else tot += sX[((kg * 4 + sl) * 3 + (y < sl ? y : y - 1)) * 64 + lane];
+    }
+
+    // dropout: bit t keeps (query q0 + 16 qbw + 4g + ew + t, key j)
     unsigned kq = 0;
     if constexpr (DROP) {
       const int t = r & 3;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int w4 = (int)keep4(p.drop, q0 + 16 * qb + 4 * g + t, j & ~3, b * p.Hq + hq);
-        const int n0 = __builtin_amdgcn_update_dpp(0, w4, 0x00, 0xF, 0xF, false);
-        const int n1 = __builtin_amdgcn_update_dpp(0, w4, 0x55, 0xF, 0xF, false);
-        const int n2 = __builtin_amdgcn_update_dpp(0, w4, 0xAA, 0xF, 0xF, false);
-        const int n3 = __builtin_amdgcn_update_dpp(0, w4, 0xFF, 0xF, 0xF, false);
-        kq |= (unsigned)(((n0 >> t) & 1) | (((n1 >> t) & 1) << 1) | (((n2 >> t) & 1) << 2) | (((n3 >> t) & 1) << 3))
-              << (4 * qb);
+      const int w4 = (int)keep4(p.drop, q0 + 16 * qbw + 4 * g + t, j & ~3, b * p.Hq + hq);
+      int n0, n1;
+      if (ew == 0) {
+        n0 = __builtin_amdgcn_update_dpp(0, w4, 0x00, 0xF, 0xF, false);
+        n1 = __builtin_amdgcn_update_dpp(0, w4, 0x55, 0xF, 0xF, false);
+      } else {
+        n0 = __builtin_amdgcn_update_dpp(0, w4, 0xAA, 0xF, 0xF, false);
+        n1 = __builtin_amdgcn_update_dpp(0, w4, 0xFF, 0xF, 0xF, false);
       }
+      kq = (unsigned)(((n0 >> t) & 1) | (((n1 >> t) & 1) << 1));
     }
+    float pq[2], uq[2];
     auto grads = [&](auto masked) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = 4 * qb + e;
-          float l = lc[x];
-          if constexpr (decltype(masked)::value) {
-            const int qi = q0 + 16 * qb + 4 * g + e;
-            l = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, dchk, b, qi, j)) ? l : -INFINITY;
-          }
-          float gg;
-          const float pv = prob_fast<CAP, false>(acc[qb][e], 0.0f, lk, l, gg);
-          if constexpr (DROP) {
-            // m dP - delta with m = keep / (1 - p); md = -delta
-            const float mk = ((kq >> x) & 1u) ? p.drop.scale : 0.0f;
-            acc[qb][e] = pv * mk;
-            acc[2 + qb][e] = pv * fmaf(mk, acc[2 + qb][e], md[x]) * gg;
-          } else {
-            acc[qb][e] = pv;
-            acc[2 + qb][e] = pv * (acc[2 + qb][e] + md[x]) * gg;
-          }
+      for (int t = 0; t < 2; ++t) {
+        float l = lc[t];
+        if constexpr (decltype(masked)::value) {
+          const int qi = q0 + 16 * qbw + 4 * g + ew + t;
+          l = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, dchk, b, qi, j)) ? l : -INFINITY;
+        }
+        float gg;
+        const float pv = prob_fast<CAP, false>(tot[t], 0.0f, lk, l, gg);
+        if constexpr (DROP) {
+          // m dP - delta with m = keep / (1 - p); md = -delta
+          const float mk = ((kq >> t) & 1u) ? p.drop.scale : 0.0f;
+          pq[t] = pv * mk;
+          uq[t] = pv * fmaf(mk, tot[2 + t], md[t]) * gg;
+        } else {
+          pq[t] = pv;
+          uq[t] = pv * (tot[2 + t] + md[t]) * gg;
         }
       }
     };
     if (keys_full && q0 >= lo_last && q0 + BMQ <= hi_first) grads(bool_c<false>{});
     else grads(bool_c<true>{});
-    const bf16x8 pf = pack8(acc[0], acc[1]);
-    const bf16x8 uf = pack8(acc[2], acc[3]);
+    // gather the quarters: element 4 qbw + ew + t of the lane's fragments
+    {
+      bf16x2 pp, uu;
+      pp[0] = (bf16)pq[0];
+      pp[1] = (bf16)pq[1];
+      uu[0] = (bf16)uq[0];
+      uu[1] = (bf16)uq[1];
+      reinterpret_cast<bf16x2*>(&sPU[(kg * 2) * 64 + lane])[2 * qbw + (ew >> 1)] = pp;
+      reinterpret_cast<bf16x2*>(&sPU[(kg * 2 + 1) * 64 + lane])[2 * qbw + (ew >> 1)] = uu;
+    }
+    __syncthreads();
+    const bf16x8 pf = sPU[(kg * 2) * 64 + lane];
+    const bf16x8 uf = sPU[(kg * 2 + 1) * 64 + lane];
     // this key group's half of the dU block (32-key block k0, query block q0)
     if (p.du && sl == 0) {
       bf16* blk = reinterpret_cast<bf16*>(p.du) +
