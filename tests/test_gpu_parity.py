@@ -109,13 +109,32 @@ def test_without_the_output_residual(D):
     _check(case(dtype="bf16", D=D, B=2, S=203, Hq=4, Hkv=2, sink_mode="learnable"), residual=False)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
 def test_learnable_sink_above_the_cap(D):
     """Sink logits above the cap: the forward's fixed reference maximum (the
     cap) moves to the sink in the epilogue."""
     c = case(dtype="bf16", D=D, B=2, S=203, Hq=4, Hkv=2, softcap=30.0, sink_mode="learnable")
     c["sink"] = np.array([45.0, -3.0, 60.0, 29.5], dtype=np.float32)
     _check(c)
+
+
+# Without a bias, D = 512 runs on the four-slice kernels.  A cap of 50 (2 c log2 e > 60) takes the
+# running row maximum, whose per-tile extreme the slices exchange; cap 30 (the feature matrix)
+# takes the fixed reference maximum.
+WIDE_CAP50 = {
+    "plain": dict(),
+    "sink_learnable": dict(sink_mode="learnable"),
+    "sink_off_by_one": dict(sink_mode="off_by_one"),
+    "window_segments": dict(window=37, segments=[[45, 70, 190], [128]]),
+    "dropout": dict(dropout_p=0.2, sink_mode="learnable"),
+    "no_causal": dict(causal=False),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("feat", list(WIDE_CAP50))
+def test_d512_running_maximum(dtype, feat):
+    _check(case(dtype=dtype, D=512, B=2, S=203, Hq=4, Hkv=2, softcap=50.0, **WIDE_CAP50[feat]))
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 64), ("fp32", 64), ("bf16", 128), ("fp32", 256), ("bf16", 512)])
