@@ -329,6 +329,11 @@ const TypeOps& ops_f32();
   hipError_t reduce_any(const void* full, void* out, int Hq, int bcast, const Launch& l) {                  \
     const long SS = (long)l.Sq * l.Sk;                                                                      \
     const long n = (long)((bcast & 1) ? 1 : l.B) * ((bcast & 2) ? 1 : Hq) * SS;                             \
+    if (SS % 8 == 0 && ((uintptr_t)full & 15) == 0 && ((uintptr_t)out & 15) == 0) {                         \
+      dbias_reduce8_kernel<T><<<(unsigned)((n / 8 + 255) / 256), 256, 0, l.stream>>>(                       \
+          static_cast<const T*>(full), static_cast<T*>(out), l.B, Hq, SS, bcast);                           \
+      return hipGetLastError();                                                                             \
+    }                                                                                                       \
     dbias_reduce_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, l.stream>>>(                              \
         static_cast<const T*>(full), static_cast<T*>(out), l.B, Hq, SS, bcast);                             \
     return hipGetLastError();                                                                               \
