@@ -323,7 +323,7 @@ hipError_t dkdv(int D, bool cap, bool bias, const void* p, const void* l);
 hipError_t pre(int D, const void* out, const void* out_lo, const void* dout, const float* lse, float* delta,
                float* part, const float* sink, int sink_mode, int Hq, int rpb, const void* l);
 hipError_t dbias_fill(void* dbias, const void* m, int Hq, int rpb, const void* l);
-hipError_t dbias_reduce(const void* full, void* out, int Hq, int bcast, const void* l);
+hipError_t dbias_reduce(const void* full, void* out, int Hq, int bcast, const void* part, int D, const void* l);
 }  // namespace atl_f16_bridge
 
 using namespace atl;
@@ -346,8 +346,8 @@ hipError_t f16_pre(int D, const void* out, const void* out_lo, const void* dout,
 hipError_t f16_fill(void* dbias, const Mask& m, int Hq, int rpb, const Launch& l) {
   return atl_f16_bridge::dbias_fill(dbias, &m, Hq, rpb, &l);
 }
-hipError_t f16_reduce(const void* full, void* out, int Hq, int bcast, const Launch& l) {
-  return atl_f16_bridge::dbias_reduce(full, out, Hq, bcast, &l);
+hipError_t f16_reduce(const void* full, void* out, int Hq, int bcast, const Mask* part, int D, const Launch& l) {
+  return atl_f16_bridge::dbias_reduce(full, out, Hq, bcast, part, D, &l);
 }
 const TypeOps& ops_fp16() {
   static const TypeOps o = {f16_fwd, f16_dq, f16_dkdv, f16_pre, f16_fill, f16_reduce};
@@ -856,7 +856,8 @@ static attn_status bwd_impl(const attn_args* a, const void* out, const void* out
     e = o.dkdv(a->D, cap, bias, p, l);
     if (e != hipSuccess) return hip_fail(e, "dk/dv kernel launch");
     if (dbias_user && a->bias_bcast && a->Sq > 0) {
-      e = o.dbias_reduce(dbias, dbias_user, p.dbias_np > 0 ? p.dbias_np : a->Hq, a->bias_bcast, l);
+      e = p.dbias_np > 0 ? o.dbias_reduce(dbias, dbias_user, p.dbias_np, a->bias_bcast, &p.mask, a->D, l)
+                         : o.dbias_reduce(dbias, dbias_user, a->Hq, a->bias_bcast, nullptr, a->D, l);
       if (e != hipSuccess) return hip_fail(e, "dbias reduction launch");
     }
   }

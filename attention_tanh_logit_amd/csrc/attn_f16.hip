@@ -28,7 +28,8 @@ hipError_t pre(int D, const void* out, const void* out_lo, const void* dout, con
 hipError_t dbias_fill(void* dbias, const void* m, int Hq, int rpb, const void* l) {
   return ops_f16().dbias_fill(dbias, *static_cast<const Mask*>(m), Hq, rpb, *static_cast<const Launch*>(l));
 }
-hipError_t dbias_reduce(const void* full, void* out, int Hq, int bcast, const void* l) {
-  return ops_f16().dbias_reduce(full, out, Hq, bcast, *static_cast<const Launch*>(l));
+hipError_t dbias_reduce(const void* full, void* out, int Hq, int bcast, const void* part, int D, const void* l) {
+  return ops_f16().dbias_reduce(full, out, Hq, bcast, static_cast<const Mask*>(part), D,
+                                *static_cast<const Launch*>(l));
 }
 }  // namespace atl_f16_bridge

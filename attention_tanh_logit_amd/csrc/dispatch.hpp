@@ -178,15 +178,43 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
   return hipGetLastError();
 }
 
+// dk/dv tiles of dkdv16_kernel (D = 128 / 256): keys per workgroup and queries
+// per item (8 waves x 16 keys, 64-query items -- measured best of 4/8 waves x
+// 32/64 queries; at D = 256 two waves per 16 keys and 32-query items; with a
+// bias, 32-query items: the bias and dbias tiles take registers).  The
+// reduction of head-summed dbias slabs recomputes the rows they wrote from
+// the same two numbers.
+template <int D> constexpr int dkdv16_keys() { return D > 128 ? 64 : 128; }
+template <int D, bool BIAS> constexpr int dkdv16_queries() { return (D > 128 || BIAS) ? 32 : 64; }
+
+template <typename T>
+hipError_t launch_reduce_part(const void* slabs, void* out, int np, int bcast, const Mask& m, int D,
+                              const Launch& l) {
+  if constexpr (std::is_same<T, float>::value) {
+    return hipErrorInvalidValue;   // head-summed slabs come from the 16-bit kernels only
+  } else {
+    if (l.Sk % 8 != 0 || (D != 128 && D != 256)) return hipErrorInvalidValue;
+    const long n = (long)((bcast & 1) ? 1 : l.B) * l.Sq * (l.Sk / 8);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    const bool vec = ((uintptr_t)out & 15) == 0;
+    const T* s = static_cast<const T*>(slabs);
+    T* o = static_cast<T*>(out);
+    if (D == 128)
+      dbias_reduce_part_kernel<T, dkdv16_keys<128>(), dkdv16_queries<128, true>()><<<blocks, 256, 0, l.stream>>>(
+          s, o, l.B, np, bcast, m, vec);
+    else
+      dbias_reduce_part_kernel<T, dkdv16_keys<256>(), dkdv16_queries<256, true>()><<<blocks, 256, 0, l.stream>>>(
+          s, o, l.B, np, bcast, m, vec);
+    return hipGetLastError();
+  }
+}
+
 template <typename T, int D, bool CAP, bool BIAS>
 hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
   if constexpr (use_fast<T, D>()) {
     if (fast_fits<D>(p, l, BIAS)) {
       if constexpr (D >= 128) {
-        // 8 waves x 16 keys, 64-query items (measured best of 4/8 waves x 32/64
-        // queries); at D = 256 two waves per 16 keys and 32-query items
-        // (with a bias, 32-query items: the bias and dbias tiles take registers)
-        constexpr int NW = 8, BMQ = (D > 128 || BIAS) ? 32 : 64, BNK = D > 128 ? 64 : 128;
+        constexpr int NW = 8, BMQ = dkdv16_queries<D, BIAS>(), BNK = dkdv16_keys<D>();
         const dim3 grid((l.Sk + BNK - 1) / BNK, p.Hkv * p.hsplit, l.B);
         const bool part = BIAS && p.dbias_np > 0;
         if (part) {
@@ -252,7 +280,10 @@ struct TypeOps {
                     float* dsink_part,
                     const float* sink, int sink_mode, int Hq, int rows_per_block, const Launch&);
   hipError_t (*dbias_fill)(void* dbias, const Mask&, int Hq, int rows_per_block, const Launch&);
-  hipError_t (*dbias_reduce)(const void* full, void* out, int Hq, int bcast, const Launch&);
+  // part: the mask when `full` holds the head-summed slabs of the 16-bit dk/dv
+  // kernel (Hq = their number per batch row), else nullptr
+  hipError_t (*dbias_reduce)(const void* full, void* out, int Hq, int bcast, const Mask* part, int D,
+                             const Launch&);
 };
 
 const TypeOps& ops_bf16();
@@ -326,7 +357,9 @@ const TypeOps& ops_f32();
     dbias_fill_kernel<T><<<grid, 256, 0, l.stream>>>(static_cast<T*>(dbias), m, Hq, rpb);                    \
     return hipGetLastError();                                                                               \
   }                                                                                                         \
-  hipError_t reduce_any(const void* full, void* out, int Hq, int bcast, const Launch& l) {                  \
+  hipError_t reduce_any(const void* full, void* out, int Hq, int bcast, const Mask* part, int D,            \
+                        const Launch& l) {                                                                  \
+    if (part) return launch_reduce_part<T>(full, out, Hq, bcast, *part, D, l);                              \
     const long SS = (long)l.Sq * l.Sk;                                                                      \
     const long n = (long)((bcast & 1) ? 1 : l.B) * ((bcast & 2) ? 1 : Hq) * SS;                             \
     if (SS % 8 == 0 && ((uintptr_t)full & 15) == 0 && ((uintptr_t)out & 15) == 0) {                         \

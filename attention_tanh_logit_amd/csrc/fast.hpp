@@ -973,7 +973,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
 //
 // PART (with BIAS, a bias broadcast over heads): dbias summed over the
 // workgroup's query heads in LDS, one slab per workgroup column
-// (p.dbias_np > 0).
+// (p.dbias_np > 0), written only on the query rows the items cover.
 template <int D, bool CAP, bool BIAS, int NW, int BMQ, bool DROP, bool PART>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   static_assert(BIAS || !PART, "head-summed dbias needs a bias");
@@ -1373,19 +1373,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
   // [qbeg, qbeg + nqt BMQ); every other row sees none of the block's keys
   // (the visible query range of a key moves monotonically with the key), so
   // its dbias is zero.  Written here rather than by a separate pass, so that
-  // these stores stream out while other workgroups compute.
-  if constexpr (BIAS) {
+  // these stores stream out while other workgroups compute.  (PART: left
+  // unwritten in the slabs; the slab reduction recomputes the covered rows
+  // and writes the zeros of the others into the result.)
+  if constexpr (BIAS && !PART) {
     if (p.dbias) {
       const int z_lo = min(qbeg, Sq);
       const int z_hi = max(z_lo, min(qbeg + nqt * BMQ, Sq));
       const int nz = z_lo + (Sq - z_hi);
       const bf16x8 zero = {};
-      const int nzh = PART ? 1 : GS;
-      for (int hh = 0; hh < nzh; ++hh) {
+      for (int hh = 0; hh < GS; ++hh) {
         const int hq = hk * p.G + split * GS + hh;
-        bf16* g0 = reinterpret_cast<bf16*>(p.dbias) +
-                   (PART ? ((long)b * p.dbias_np + hk * p.hsplit + split) * Sq * Sk
-                         : (((long)b * p.Hq + hq) * Sq) * Sk) + k0;
+        bf16* g0 = reinterpret_cast<bf16*>(p.dbias) + (((long)b * p.Hq + hq) * Sq) * Sk + k0;
         for (int u = threadIdx.x; u < nz * BCPR; u += NT) {
           const int R = u / BCPR, c = u % BCPR;
           const int i = R < z_lo ? R : z_hi + (R - z_lo);

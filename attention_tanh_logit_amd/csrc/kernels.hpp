@@ -1160,6 +1160,54 @@ __global__ __launch_bounds__(256) void dbias_reduce8_kernel(const T* full, T* ou
   store8<T>(out + x * 8, s);
 }
 
+// Head-summed dbias slabs of the 16-bit dk/dv kernel ([B][np][Sq][Sk], one
+// per KV head and head split) into the caller's dbias ([B or 1][1][Sq][Sk]).
+// The dk/dv workgroups of a block of BNK keys write the rows
+// [qbeg, qbeg + nqt BMQ) of its columns, which the same visibility bounds
+// give here; every other row of those columns sees none of the block's keys,
+// is left unwritten in the slabs, and is zero in the result.  8 consecutive
+// keys per thread (Sk % 8 == 0 on this path).
+template <typename T, int BNK, int BMQ>
+__global__ __launch_bounds__(256) void dbias_reduce_part_kernel(const T* slabs, T* out, int B, int np, int bcast,
+                                                                Mask m, bool vec_out) {
+  const int Sq = m.Sq, Sk = m.Sk;
+  const int nc = Sk / 8;
+  const int Bb = (bcast & 1) ? 1 : B;
+  const long x = (long)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (long)Bb * Sq * nc) return;
+  const int bb = (int)(x / ((long)Sq * nc));
+  const long rem = x % ((long)Sq * nc);
+  const int i = (int)(rem / nc);
+  const int j = (int)(rem % nc) * 8;
+  const int k0 = (j / BNK) * BNK;
+  const int jlast = min(k0 + BNK, Sk) - 1;
+  const long SS = (long)Sq * Sk;
+  float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  const int b0 = (bcast & 1) ? 0 : bb, b1 = (bcast & 1) ? B : bb + 1;
+  for (int b = b0; b < b1; ++b) {
+    int lo_first, hi_first, lo_last, hi_last;
+    queries_of(m, b, k0, lo_first, hi_first);
+    queries_of(m, b, jlast, lo_last, hi_last);
+    const int qbeg = (lo_first / BMQ) * BMQ;
+    const int nqt = hi_last > qbeg ? (hi_last - qbeg + BMQ - 1) / BMQ : 0;
+    if (i < qbeg || i >= qbeg + nqt * BMQ) continue;
+    const T* src = slabs + (long)b * np * SS + (long)i * Sk + j;
+    for (int h = 0; h < np; ++h) {
+      float v[8];
+      load8(src + h * SS, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += v[e];
+    }
+  }
+  T* dst = out + ((long)bb * Sq + i) * Sk + j;
+  if (vec_out) {
+    store8<T>(dst, s);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = (T)s[e];
+  }
+}
+
 // dbias = 0 on every pair that no query-key visibility covers (the dkdv
 // kernel writes the visible pairs).  One block per (row group, head, batch).
 template <typename T>

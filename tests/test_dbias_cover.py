@@ -8,7 +8,10 @@ grounds that those rows see none of the block's keys.  This test walks that
 rule over ragged causal / windowed / packed-segment / cross-length masks and
 checks that every element of dbias is written, and that the zero rows hold
 no visible pair (which is what the monotone visible query range of a key
-guarantees).  No GPU needed.
+guarantees).  With a bias broadcast over heads the same rows split the work
+between two kernels: dk/dv writes the covered rows of its head-summed slab and
+the slab reduction, recomputing [qbeg, qbeg + nqt * BMQ) per key block, reads
+only those and writes the zeros of the others.  No GPU needed.
 """
 import numpy as np
 import pytest
