@@ -205,8 +205,9 @@ attn_status attn_validate(const attn_args* a);
  *    ATTN_DQ_DU_BLOCKS (see attn_dq_mode), with a broadcast bias and dbias a
  *    full [B, Hq, Sq, Sk] dbias in the input dtype (for a bias broadcast over
  *    heads on the 16-bit D = 128 / 256 kernels, [B, Hkv*s, Sq, Sk] slabs
- *    already summed over each workgroup's heads; reduced into the caller's
- *    dbias), and for bf16 / fp16 with D = 64, 128 or 256 when
+ *    already summed over each workgroup's heads, of which only the query
+ *    rows that see some key of a key block are written and read; reduced
+ *    into the caller's dbias), and for bf16 / fp16 with D = 64, 128 or 256 when
  *    B*Hkv*ceil(Sk/128) < 1024 (D = 512 without a bias: B*Hkv*ceil(Sk/32) <
  *    1024), 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial dK/dV: the dk/dv kernel
  *    then splits each GQA group's query heads over s workgroups (s the
