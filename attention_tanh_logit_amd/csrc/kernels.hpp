@@ -847,6 +847,101 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
     uf[0] = to_frag(dpacc, 0, (T*)nullptr);
     uf[1] = to_frag(dpacc, 8, (T*)nullptr);
   };
+  // SPLIT over four slices: the partial S and dP are reduce-scattered over the
+  // key group's slices instead of summed by each (slice_sum): slice sl adds up,
+  // in slice order (the same totals, bit for bit), only accumulator registers
+  // 4 sl .. 4 sl + 3 of each lane -- query rows acc_row(h, 4 sl) + 0..3 of its
+  // key -- and takes P and dU of those alone; the quarters (fp32, before the
+  // operand rounding) are then gathered back, so every slice holds the whole
+  // operand fragments and the elementwise work is done once per key group.
+  // sRed: [kg][quarter][the three other slices][S, dP][lane] float4 partials,
+  // then [kg][P, dU][quarter][lane] float4 gathered values (NW * 8 KiB).
+  auto grads_rs = [&](int hq, int q0, bool full, f32x16& sacc, f32x16& dpacc, F* pf, F* uf) {
+    // the same explicit wait states after the S / dP MFMAs as in grads
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    float4* r4 = reinterpret_cast<float4*>(sRed);
+    float4* g4 = r4 + NKG * 4 * 3 * 2 * 64;
+    float4 os = make_float4(0.0f, 0.0f, 0.0f, 0.0f), od = os;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float4 vs = make_float4(sacc[4 * x], sacc[4 * x + 1], sacc[4 * x + 2], sacc[4 * x + 3]);
+      const float4 vd = make_float4(dpacc[4 * x], dpacc[4 * x + 1], dpacc[4 * x + 2], dpacc[4 * x + 3]);
+      if (x != sl) {
+        const int base = ((kg * 4 + x) * 3 + (sl < x ? sl : sl - 1)) * 2;
+        r4[base * 64 + lane] = vs;
+        r4[(base + 1) * 64 + lane] = vd;
+      } else {
+        os = vs;
+        od = vd;
+      }
+    }
+    __syncthreads();
+    float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f}, td[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      float4 vs, vd;
+      if (y == sl) {
+        vs = os;
+        vd = od;
+      } else {
+        const int base = ((kg * 4 + sl) * 3 + (y < sl ? y : y - 1)) * 2;
+        vs = r4[base * 64 + lane];
+        vd = r4[(base + 1) * 64 + lane];
+      }
+      ts[0] += vs.x; ts[1] += vs.y; ts[2] += vs.z; ts[3] += vs.w;
+      td[0] += vd.x; td[1] += vd.y; td[2] += vd.z; td[3] += vd.w;
+    }
+    const long lrow = ((long)b * p.Hq + hq) * Sq;
+    const T* bbase = nullptr;
+    T* dbbase = nullptr;
+    if constexpr (BIAS) {
+      bbase = reinterpret_cast<const T*>(p.bias) + b * p.bias_bs + hq * p.bias_hs;
+      if (p.dbias) dbbase = reinterpret_cast<T*>(p.dbias) + lrow * Sk;
+    }
+    float ps[4], us[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * (sl >> 1) + 8 * h + 4 * (sl & 1) + e;   // acc_row(h, 4 sl + e)
+      const int qi = q0 + row;
+      float bvv = 0.0f;
+      if constexpr (BIAS) bvv = (qi < Sq && j < Sk) ? to_f32(bbase[(long)qi * Sk + j]) : 0.0f;
+      float f;
+      const float s2 = logit2<T, CAP, BIAS>(ts[e], bvv, p.sl2, p.xc, p.bc, p.cl2, f);
+      float pv = fast_exp2(s2 - sL[row]);
+      bool vis = true;
+      if (!full) vis = (qi >= lo_j && qi < hi_j);
+      if (!vis || (!full && !dense_ok(p.mask, dchk, b, qi, j))) pv = 0.0f;
+      float dp = td[e], pd = pv;
+      if (p.drop.on) {
+        const unsigned kp = keep4(p.drop, qi, j & ~3, b * p.Hq + hq);
+        const float kd = ((kp >> (j & 3)) & 1u) ? p.drop.scale : 0.0f;
+        dp *= kd;
+        pd *= kd;
+      }
+      const float du = pv * (dp - sDl[row]) * f;
+      ps[e] = pd;
+      us[e] = du;
+      if constexpr (BIAS) {
+        if (dbbase && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
+      }
+    }
+    g4[((kg * 2) * 4 + sl) * 64 + lane] = make_float4(ps[0], ps[1], ps[2], ps[3]);
+    g4[((kg * 2 + 1) * 4 + sl) * 64 + lane] = make_float4(us[0], us[1], us[2], us[3]);
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float4 a = g4[((kg * 2) * 4 + x) * 64 + lane];
+      const float4 c = g4[((kg * 2 + 1) * 4 + x) * 64 + lane];
+      sacc[4 * x] = a.x; sacc[4 * x + 1] = a.y; sacc[4 * x + 2] = a.z; sacc[4 * x + 3] = a.w;
+      dpacc[4 * x] = c.x; dpacc[4 * x + 1] = c.y; dpacc[4 * x + 2] = c.z; dpacc[4 * x + 3] = c.w;
+    }
+    pf[0] = to_frag(sacc, 0, (T*)nullptr);
+    pf[1] = to_frag(sacc, 8, (T*)nullptr);
+    uf[0] = to_frag(dpacc, 0, (T*)nullptr);
+    uf[1] = to_frag(dpacc, 8, (T*)nullptr);
+  };
   // lse (log2 units; +inf on rows past the end) and delta of the item's queries
   auto put_stats = [&](int i, float l, float dl) {
     if (threadIdx.x < BMQ) {
@@ -995,14 +1090,18 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
         mma(dpacc, ao, bv);
       }
     }
-    if constexpr (SPLIT) {
-      f32x16 sd[2] = {sacc, dpacc};
-      slice_sum<NSL, 2>(sRed, w, sl, sd);
-      sacc = sd[0];
-      dpacc = sd[1];
-    }
     F pf[2], uf[2];
-    grads(hq, q0, full, sacc, dpacc, pf, uf);
+    if constexpr (SPLIT && NSL == 4) {
+      grads_rs(hq, q0, full, sacc, dpacc, pf, uf);
+    } else {
+      if constexpr (SPLIT) {
+        f32x16 sd[2] = {sacc, dpacc};
+        slice_sum<NSL, 2>(sRed, w, sl, sd);
+        sacc = sd[0];
+        dpacc = sd[1];
+      }
+      grads(hq, q0, full, sacc, dpacc, pf, uf);
+    }
     // ---- dV^T += dO^T P,  dK^T += Q^T dU  over this wave's slice
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
