@@ -393,7 +393,7 @@ long max_token_stride(const attn_args* a) {
 // wide.hpp D = 512 without a bias), with or without dropout; the generic
 // kernels write none.
 bool du_supported(const attn_args* a) {
-  return fast_ok(is16(a), a->D, max_token_stride(a), a->Sk, a->bias != nullptr) ||
+  return a->dtype == ATTN_FP32 || fast_ok(is16(a), a->D, max_token_stride(a), a->Sk, a->bias != nullptr) ||
          wide_ok(is16(a), a->D, max_token_stride(a), a->bias != nullptr);
 }
 
@@ -439,8 +439,8 @@ attn_status validate(const attn_args* a) {
   if (a->dq_mode != ATTN_DQ_AUTO && a->dq_mode != ATTN_DQ_DU_BLOCKS && a->dq_mode != ATTN_DQ_RECOMPUTE)
     return fail(ATTN_INVALID_ARGUMENT, "dq_mode must be ATTN_DQ_AUTO, ATTN_DQ_DU_BLOCKS or ATTN_DQ_RECOMPUTE");
   if (a->dq_mode == ATTN_DQ_DU_BLOCKS && !du_supported(a))
-    return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs bf16 with D = 64, 128 or 256 (with a bias, Sk % 8 == 0) "
-                                  "or D = 512 without a bias");
+    return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs fp32, or bf16 / fp16 with D = 64, 128 or 256 (with a bias, "
+                                  "Sk % 8 == 0) or D = 512 without a bias");
   if ((long long)a->B * a->Sq > 0 && a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
   const size_t elems = (size_t)a->B * (a->Sq + a->Sk);
   if (elems != 0 && (!a->q || !a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "q, k and v must not be NULL");
@@ -475,8 +475,11 @@ size_t fwd_ws(const attn_args* a) { return seg_bytes(a); }
 // B=1, Hq=64, Hkv=8, S=4096 with a learnable sink).
 constexpr size_t kDuAutoBytes = (size_t)16 << 30;
 
+size_t elem_bytes(const attn_args* a) { return a->dtype == ATTN_FP32 ? 4 : 2; }
+
+// 32 x 32 blocks of dU in the element type (fp32 for the fp32 path)
 size_t du_raw_bytes(const attn_args* a) {
-  return (size_t)a->B * a->Hq * (((size_t)a->Sk + 31) / 32) * (((size_t)a->Sq + 31) / 32) * 2048;
+  return (size_t)a->B * a->Hq * (((size_t)a->Sk + 31) / 32) * (((size_t)a->Sq + 31) / 32) * 1024 * elem_bytes(a);
 }
 
 bool du_path(const attn_args* a) {
@@ -517,7 +520,6 @@ size_t dkv_part_bytes(const attn_args* a) {
   return hs > 1 ? (size_t)2 * hs * a->B * a->Sk * a->Hkv * a->D * sizeof(float) : 0;
 }
 
-size_t elem_bytes(const attn_args* a) { return a->dtype == ATTN_FP32 ? 4 : 2; }
 
 // A bias broadcast over heads on the 16-key dk/dv kernel: each workgroup
 // column (KV head and query-head split) sums its heads' dbias tiles in LDS

@@ -55,9 +55,21 @@ ATL_DKDV(float, 128, 128, 2, 128)
 ATL_DKDV(float, 256, 64, 1, 64)
 ATL_DKDV(float, 512, 128, 1, 128)
 
+// fp32 dq from the dU blocks: only K^T passes through LDS, so the rows per
+// workgroup trade against K^T reuse differently than when recomputing
+template <int D> struct DqDuCfg;
+#define ATL_DQU(D_, DO_, NQG_, BN_, DC_) \
+  template <> struct DqDuCfg<D_> { static constexpr int DO = DO_, NQG = NQG_, BN = BN_, DC = DC_; };
+//      D    DO  NQG  BN   DC
+ATL_DQU(64, 64, 4, 32, 64)
+ATL_DQU(128, 128, 2, 32, 128)
+ATL_DQU(256, 128, 4, 32, 64)
+ATL_DQU(512, 256, 4, 32, 128)
+
 #undef ATL_FWD
 #undef ATL_DQ
 #undef ATL_DKDV
+#undef ATL_DQU
 
 struct Launch {
   int B, Sq, Sk;
@@ -167,6 +179,18 @@ hipError_t launch_dq(const BwdParams& p, const Launch& l) {
     if (p.du) {
       const dim3 grid((l.Sq + 127) / 128, p.Hq, l.B);
       dq_du_kernel<D, CAP, 32, 2, 2><<<grid, 512, 0, l.stream>>>(p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (std::is_same<T, float>::value) {
+    // fp32 dU blocks from the generic dk/dv kernel (cap, bias and dropout are
+    // in them already)
+    if (p.du) {
+      using U = DqDuCfg<D>;
+      constexpr int BMU = 32 * U::NQG;
+      const dim3 grid((l.Sq + BMU - 1) / BMU, p.Hq, l.B);
+      dq_kernel<T, D, U::DO, U::NQG, U::BN, U::DC, false, false, true>
+          <<<grid, dim3(64 * U::NQG * (D / U::DO)), 0, l.stream>>>(p);
       return hipGetLastError();
     }
   }

@@ -451,7 +451,10 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
 
 // ============================================================== backward: dq
 
-template <typename T, int D, int DO, int NQG, int BN, int DC, bool CAP, bool BIAS>
+// DU (fp32): dQ from the dU blocks the dk/dv kernel wrote (32 x 32 fp32 per
+// (key block, query block), row-major [query][key]) instead of recomputing S,
+// dP and the gradients: only K^T passes through LDS, and Q, dO, V are not read.
+template <typename T, int D, int DO, int NQG, int BN, int DC, bool CAP, bool BIAS, bool DU = false>
 __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   constexpr int NSL = D / DO;
   constexpr int NW = NQG * NSL;
@@ -464,15 +467,16 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   constexpr int RS = DC + Pad<T>::v;
   constexpr int TS = BN + Pad<T>::v;
   static_assert(ONE || DO % DC == 0, "a chunk must not straddle two slices");
+  static_assert(!DU || sizeof(T) == 4, "dU blocks of the generic kernels are fp32");
   using F = typename Frag<T>::type;
 
-  __shared__ __attribute__((aligned(16))) T sQ[BM * RS];
-  __shared__ __attribute__((aligned(16))) T sO[BM * RS];   // dO
-  __shared__ __attribute__((aligned(16))) T sK[BN * RS];
-  __shared__ __attribute__((aligned(16))) T sV[BN * RS];
+  __shared__ __attribute__((aligned(16))) T sQ[DU ? 4 : BM * RS];
+  __shared__ __attribute__((aligned(16))) T sO[DU ? 4 : BM * RS];   // dO
+  __shared__ __attribute__((aligned(16))) T sK[DU ? 4 : BN * RS];
+  __shared__ __attribute__((aligned(16))) T sV[DU ? 4 : BN * RS];
   __shared__ __attribute__((aligned(16))) T sKt[DC * TS];
   // the slices of a row group split each chunk's contraction for S and dP
-  constexpr bool SPLIT = !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
+  constexpr bool SPLIT = !DU && !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
                          (2 * BM * RS + 2 * BN * RS + DC * TS) * (int)sizeof(T) + NW * 2 * NKB * 4096 <= kLdsBudget;
   constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;
   __shared__ __attribute__((aligned(16))) float sRed[SPLIT ? NW * 2 * NKB * 1024 : 4];
@@ -568,7 +572,87 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
     }
   };
 
-  if constexpr (ONE) {
+  // DU: keys seen by some query of this wave's 32-row group form one interval
+  // (each query's visible keys are an interval holding its own position, and
+  // the bounds never decrease along the queries); a 32-key block outside it
+  // holds no visible pair of the group and was not necessarily written, so
+  // it counts as zero.  Otherwise lane (query n, half h) takes keys
+  // 16 sb + 8 h .. + 7 of the block's row n: the contraction order of the
+  // fp32 MFMA fragments (element s at key 16 sb + 8 h + s).
+  const int qw = q0 + qg * 32;
+  int wlo = 0, whi = 0;
+  if constexpr (DU) {
+    if (qw < Sq) {
+      int x0, x1;
+      keys_of(p.mask, b, qw, wlo, x0);
+      keys_of(p.mask, b, min(qw + 31, Sq - 1), x1, whi);
+    }
+  }
+  auto load_du = [&](int k0, F (*uf)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int kb32 = k0 + kb * 32;
+      if (qw < Sq && kb32 < whi && kb32 + 32 > wlo && kb32 < Sk) {
+        const float* blk = reinterpret_cast<const float*>(p.du) +
+                           ((((long)b * p.Hq + hq) * p.nkb32 + (kb32 >> 5)) * p.nqb32 + (qw >> 5)) * 1024 + n * 32 +
+                           8 * h;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(blk + 16 * sb);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(blk + 16 * sb + 4);
+          F f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f[e] = lo[e];
+            f[4 + e] = hi[e];
+          }
+          uf[kb][sb] = f;
+        }
+      } else {
+        uf[kb][0] = F{};
+        uf[kb][1] = F{};
+      }
+    }
+  };
+
+  if constexpr (DU) {
+  // dQ^T += K^T dU^T from the dU blocks; K^T in chunks through LDS, the next
+  // chunk's global loads issued under this chunk's MFMAs
+  const int ntile = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
+  RowPairChunks<T, BN, DC, NT> rkt;
+  auto load_t = [&](int t, int c) { rkt.load(kbase, kstride, kbeg + t * BN, Sk, c * DC); };
+  if (ntile > 0) load_t(0, 0);
+  for (int t = 0; t < ntile; ++t) {
+    const int k0 = kbeg + t * BN;
+    F uf[NKB][2];
+    load_du(k0, uf);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();
+      rkt.template store<TS, true>(sKt);
+      __syncthreads();
+      if (c + 1 < NCH) load_t(t, c + 1);
+      else if (t + 1 < ntile) load_t(t + 1, 0);
+      // chunk c belongs to slice c / (DO / DC), at its column block (c % (DO / DC)) DC / 32
+      constexpr int CPS = DO >= DC ? DO / DC : 1;
+      if (ONE || sl == c / CPS) {
+#pragma unroll
+        for (int db = 0; db < DC / 32; ++db) {
+          const int ob = ONE ? db - sl * NOB : (c % CPS) * (DC / 32) + db;
+          if (ob < 0 || ob >= NOB) continue;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+              const F ak = lds_frag<T>(sKt + (db * 32 + n) * TS + kb * 32 + 16 * sb + 8 * h);
+              mma(qacc[ob], ak, uf[kb][sb]);
+            }
+          }
+        }
+      }
+    }
+  }
+  } else if constexpr (ONE) {
   stage_rows<T, BM, DC, RS, false, NT>(sQ, qbase, qstride, q0, Sq, 0);
   stage_rows<T, BM, DC, RS, false, NT>(sO, obase, qstride, q0, Sq, 0);
   for (int k0 = kbeg; k0 < hi_last; k0 += BN) {
@@ -797,6 +881,21 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
 
   const int qbeg = (lo_first / BMQ) * BMQ;
 
+  // fp32 dU hand-off (p.du): this key group's 32 x 32 block of the item,
+  // row-major [query][key] so that the dq kernel's lanes read whole runs of
+  // keys; nullptr for 16-bit elements, without the hand-off, or for a key
+  // group past the last key.  Every lane stores its own key's column, so each
+  // store instruction writes 32 consecutive floats of two query rows.
+  auto du_block = [&](int hq, int q0) -> float* {
+    if constexpr (sizeof(T) == 4) {
+      const int kb32 = k0 + kg * 32;
+      if (!p.du || kb32 >= Sk) return nullptr;
+      return reinterpret_cast<float*>(p.du) +
+             ((((long)b * p.Hq + hq) * p.nkb32 + (kb32 >> 5)) * p.nqb32 + (q0 >> 5)) * 1024;
+    } else {
+      return nullptr;
+    }
+  };
   // ---- P, dU of one (query head, 32-query tile) item from S and dP
   // (lane: key j; register r: query q0 + acc_row(h, r)), as operand fragments
   auto grads = [&](int hq, int q0, bool full, f32x16& sacc, f32x16& dpacc, F* pf, F* uf) {
@@ -815,6 +914,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       bbase = reinterpret_cast<const T*>(p.bias) + b * p.bias_bs + hq * p.bias_hs;
       if (p.dbias) dbbase = reinterpret_cast<T*>(p.dbias) + lrow * Sk;
     }
+    float* ublk = du_block(hq, q0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = q0 + acc_row(h, r);
@@ -840,6 +940,9 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       dpacc[r] = du;
       if constexpr (BIAS) {
         if (dbbase && sl == 0 && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
+      }
+      if constexpr (sizeof(T) == 4) {
+        if (ublk && sl == 0) __builtin_nontemporal_store(du, ublk + acc_row(h, r) * 32 + n);
       }
     }
     pf[0] = to_frag(sacc, 0, (T*)nullptr);
@@ -900,6 +1003,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       bbase = reinterpret_cast<const T*>(p.bias) + b * p.bias_bs + hq * p.bias_hs;
       if (p.dbias) dbbase = reinterpret_cast<T*>(p.dbias) + lrow * Sk;
     }
+    float* ublk = du_block(hq, q0);
     float ps[4], us[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -925,6 +1029,9 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       us[e] = du;
       if constexpr (BIAS) {
         if (dbbase && vis && qi < Sq && j < Sk) dbbase[(long)qi * Sk + j] = (T)du;
+      }
+      if constexpr (sizeof(T) == 4) {
+        if (ublk) __builtin_nontemporal_store(du, ublk + row * 32 + n);
       }
     }
     g4[((kg * 2) * 4 + sl) * 64 + lane] = make_float4(ps[0], ps[1], ps[2], ps[3]);

@@ -108,11 +108,12 @@ typedef enum attn_bias_bcast {
 
 /* How the backward forms dq (the same result either way, to rounding).
  *  - ATTN_DQ_DU_BLOCKS: the dk/dv kernel hands dU = dS * (1 - tanh^2) to the
- *    dq kernel through the workspace as bf16 blocks of 32 keys x 32 queries,
- *    B*Hq*ceil(Sk/32)*ceil(Sq/32)*2 KiB (4 GiB at B=4, Hq=32, S=4096; only
- *    the visible blocks are written and read).  bf16 or fp16 with D = 64, 128
- *    or 256 (with a bias also Sk % 8 == 0), or D = 512 without a bias;
- *    ATTN_UNSUPPORTED otherwise.
+ *    dq kernel through the workspace as blocks of 32 keys x 32 queries in
+ *    the element type, B*Hq*ceil(Sk/32)*ceil(Sq/32) blocks of 2 KiB (bf16,
+ *    fp16) or 4 KiB (fp32): 4 GiB at B=4, Hq=32, S=4096 in bf16; only the
+ *    visible blocks are written and read.  fp32 at any D; bf16 or fp16 with
+ *    D = 64, 128 or 256 (with a bias also Sk % 8 == 0), or D = 512 without a
+ *    bias; ATTN_UNSUPPORTED otherwise.
  *  - ATTN_DQ_RECOMPUTE: the dq kernel recomputes the logits, probabilities
  *    and dP itself; the workspace stays O(B*Hq*Sq).
  *  - ATTN_DQ_AUTO (0): DU_BLOCKS where supported, D >= 128 (or dropout is
@@ -121,7 +122,7 @@ typedef enum attn_bias_bcast {
  * The [b, h, q, kv] materialisation and its memory cost are what the MaxText
  * commit quoted on "Support logits soft-capping in the Pallas-Triton
  * attention VJP" weighs (12.5 against 3.3 GiB at 8k tokens); the blocks here
- * are bf16 and touched only where visible. */
+ * are in the element type and touched only where visible. */
 typedef enum attn_dq_mode {
   ATTN_DQ_AUTO = 0,
   ATTN_DQ_DU_BLOCKS = 1,

@@ -83,7 +83,6 @@ BAD = {
     "misaligned_q": (dict(q=0x1002), 1, "aligned"),
     "misaligned_bias": (dict(bias=0x2008), 1, "aligned"),
     "bad_dq_mode": (dict(dq_mode=3), 1, "dq_mode"),
-    "du_blocks_fp32": (dict(dtype=1, dq_mode=1), 2, "DU_BLOCKS"),
     "du_blocks_d512_bias": (dict(D=512, dq_mode=1, bias=0x2000), 2, "DU_BLOCKS"),
     "du_blocks_ragged_bias": (dict(Sq=250, Sk=250, bias=0x2000, dq_mode=1), 2, "DU_BLOCKS"),
     "keys_empty": (dict(Sk=0, causal=0), 2, "Sk == 0"),
@@ -92,7 +91,6 @@ BAD = {
     "mask_misaligned": (dict(mask=0x3001), 1, "mask"),
     "dropout_one": (dict(dropout_p=1.0), 1, "dropout_p"),
     "dropout_negative": (dict(dropout_p=-0.1), 1, "dropout_p"),
-    "dropout_with_du_blocks_fp32": (dict(dropout_p=0.1, dq_mode=1, dtype=1), 2, "DU_BLOCKS"),
     "bad_layout": (dict(layout=2), 1, "layout"),
 }
 
@@ -198,8 +196,19 @@ def test_bwd_workspace_carries_du_blocks_by_dq_mode():
     d512 = dict(D=512)
     assert L.attn_bwd_workspace_size(ctypes.byref(_args(**d512))) - \
         L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **d512))) == 2 * 8 * 8 * 8 * 2048
-    f32 = _args(dtype=1)
-    g32 = _args(dtype=1, D=256)
+    # fp32: the same blocks in 4-byte elements (4 KiB each), auto from D = 128 on, with a bias or
+    # dropout as well (the generic kernels write and read them)
+    for extra in ({}, dict(bias=0x2000), dict(dropout_p=0.1), dict(D=512)):
+        f32 = dict(dtype=1, **extra)
+        assert L.attn_bwd_workspace_size(ctypes.byref(_args(**f32))) - \
+            L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **f32))) == 2 * 8 * 8 * 8 * 4096, extra
+    f64 = dict(dtype=1, D=64)
+    assert L.attn_bwd_workspace_size(ctypes.byref(_args(**f64))) == \
+        L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **f64)))
+    assert L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=1, **f64))) - \
+        L.attn_bwd_workspace_size(ctypes.byref(_args(dq_mode=2, **f64))) == 2 * 8 * 8 * 8 * 4096
+    f32 = _args(dtype=1, dq_mode=2)
+    g32 = _args(dtype=1, D=256, dq_mode=2)
     # the bf16 run also carries the fp32 dK/dV partials of its head split
     assert L.attn_bwd_workspace_size(ctypes.byref(f32)) == without - _split_partials(_args())
     assert L.attn_bwd_workspace_size(ctypes.byref(g32)) == without - _split_partials(_args())
@@ -230,7 +239,7 @@ def test_bwd_workspace_carries_split_partials_only_for_small_grids():
                                  (1, 4096, 24, 8, 128, 3)):
         assert _head_split(B, S, Hq, Hkv) == hs
         bf = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D, dq_mode=2)
-        fp = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D, dtype=1)
+        fp = _args(B=B, Sq=S, Sk=S, Hq=Hq, Hkv=Hkv, D=D, dtype=1, dq_mode=2)
         diff = L.attn_bwd_workspace_size(ctypes.byref(bf)) - L.attn_bwd_workspace_size(ctypes.byref(fp))
         assert diff == _split_partials(bf), (B, S, Hq, Hkv, D)
 

@@ -102,6 +102,20 @@ def test_feature_matrix_other_dq_mode(D, feat):
     _check(case(**kw), dq_mode=mode)
 
 
+# fp32: the generic dk/dv kernel writes fp32 dU blocks that the generic dq kernel reads (auto at
+# D >= 128, or with dropout), else dq recomputes; both modes at every D and feature
+FP32_DQ_FEATURES = dict(FEATURES, dropout=dict(dropout_p=0.2, sink_mode="learnable"))
+
+
+@pytest.mark.parametrize("dq_mode", ["du_blocks", "recompute"])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("feat", list(FP32_DQ_FEATURES))
+def test_fp32_both_dq_modes(D, feat, dq_mode):
+    kw = dict(dtype="fp32", D=D, B=2, S=203, Hq=4, Hkv=2)
+    kw.update(FP32_DQ_FEATURES[feat])
+    _check(case(**kw), dq_mode=dq_mode)
+
+
 @pytest.mark.parametrize("D", [64, 128, 256, 512])
 def test_without_the_output_residual(D):
     """bf16 without out_lo: delta comes from the bf16 output alone (the

@@ -3,8 +3,9 @@
 Every workspace the binding allocates is filled with 0xFF bytes first (NaN as bf16, fp16 and
 fp32, -1 as int32), and the results must be bitwise those of a run on a fresh workspace.  A
 kernel that read a part of the workspace no earlier kernel of the call wrote (the visibility
-bounds, delta, the sink partials, the dU blocks, the head-split dK/dV partials, the full or
-head-summed dbias of a broadcast bias) would turn NaN or a wrong bound into its results.
+bounds, delta, the sink partials, the 16-bit or fp32 dU blocks, the head-split dK/dV partials,
+the full or head-summed dbias of a broadcast bias) would turn NaN or a wrong bound into its
+results.
 """
 import numpy as np
 import pytest
@@ -22,6 +23,9 @@ CASES = {
     "bias_heads_partials": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True, bias_bcast="heads",
                                 softcap=50.0),
     "bias_batch_fp32": dict(dtype="fp32", D=128, B=2, S=131, Hq=4, Hkv=2, bias=True, bias_bcast="batch"),
+    "du_blocks_fp32": dict(dtype="fp32", D=256, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]],
+                           sink_mode="learnable", window=50),
+    "du_blocks_fp32_d64_dropout": dict(dtype="fp32", D=64, B=2, S=203, Hq=4, Hkv=2, dropout_p=0.2),
     "dense_mask": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]]),
     "k_start": dict(dtype="bf16", D=256, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]]),
     "dropout": dict(dtype="bf16", D=128, B=2, S=203, Hq=4, Hkv=2, dropout_p=0.2, sink_mode="learnable"),
