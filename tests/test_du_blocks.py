@@ -1,13 +1,16 @@
-"""Host-side check of the dU hand-off between the bf16 dk/dv and dq kernels.
+"""Host-side check of the dU hand-off between the dk/dv and dq kernels.
 
-The dk/dv kernel stores dU in 2 KiB blocks (one per head, 32-key block and
-32-query block; two 1 KiB halves of 16 keys each) and the dq kernel reads a
-block whenever some query of its 32-query tile sees some key of the 32-key
-block.  This test walks the store rule of both dk/dv kernels (32-key waves at
-D = 64; 16-key waves, 8 per workgroup, 64-query items at D = 128) and the read
-rule of the dq kernel over ragged causal / windowed / full masks and checks
-that every store lands inside the workspace region, no half is stored twice,
-and every half the dq kernel reads has been stored.  No GPU needed.
+The dk/dv kernel stores dU in blocks (one per head, 32-key block and 32-query
+block; in 16-bit two 1 KiB halves of 16 keys each, in fp32 one 4 KiB block
+written by one 32-key group) and the dq kernel reads a block whenever some
+query of its 32-query tile sees some key of the 32-key block.  This test walks
+the store rule of the dk/dv kernels (16-bit: 32-key waves at D = 64, 16-key
+waves, 8 per workgroup, 64-query items at D = 128; fp32: 1, 2 or 4 groups of
+32 keys per workgroup and 32-query items, both halves of a block from its
+group) and the read rule of the dq kernel over ragged causal / windowed / full
+masks and checks that every store lands inside the workspace region, no half
+is stored twice, and every half the dq kernel reads has been stored.  No GPU
+needed.
 """
 import pytest
 
@@ -68,7 +71,7 @@ CASES = [(200, True, 0), (200, False, 0), (97, True, 0), (333, True, 50), (333, 
 
 
 @pytest.mark.parametrize("S,causal,window", CASES)
-@pytest.mark.parametrize("keys_per_wave,nw,bmq", [(32, 4, 32), (16, 8, 64), (16, 4, 32)])
+@pytest.mark.parametrize("keys_per_wave,nw,bmq", [(32, 4, 32), (16, 8, 64), (16, 4, 32), (32, 1, 32), (32, 2, 32)])
 def test_du_blocks_cover_dq_reads(S, causal, window, keys_per_wave, nw, bmq):
     B, Hq, Hkv = 1, 4, 2
     nkb32, nqb32 = (S + 31) // 32, (S + 31) // 32
