@@ -826,12 +826,19 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   // (Keeping the key block's K and V chunks in LDS instead, where only one of
   // the two fits, was slower.)
   constexpr bool QTALL = !ONE && (2 * BNK * RS + 2 * BMQ * RS + 2 * NCH * DC * TS) * (int)sizeof(T) + RED <= 150 * 1024;
+  // fp32 where they do not fit (D = 512): staging one Q^T / dO^T chunk at a
+  // time would leave each chunk stage to the one slice that owns its columns
+  // (the other SIMDs waiting at the stage barriers); instead every slice reads
+  // the Q^T and dO^T operands of its own columns straight from global memory
+  // (each load a 128-byte run of one query row, mostly L2 hits after the S/dP
+  // stages), and the slices' dV / dK MFMAs run at the same time.
+  constexpr bool TDIRECT = !ONE && !QTALL && sizeof(T) == 4 && DO == DC;
   __shared__ __attribute__((aligned(16))) T sK[BNK * RS];
   __shared__ __attribute__((aligned(16))) T sV[BNK * RS];
   __shared__ __attribute__((aligned(16))) T sQ[BMQ * RS];
   __shared__ __attribute__((aligned(16))) T sO[BMQ * RS];
-  __shared__ __attribute__((aligned(16))) T sQt[(QTALL ? NCH : 1) * DC * TS];
-  __shared__ __attribute__((aligned(16))) T sOt[(QTALL ? NCH : 1) * DC * TS];
+  __shared__ __attribute__((aligned(16))) T sQt[TDIRECT ? 4 : (QTALL ? NCH : 1) * DC * TS];
+  __shared__ __attribute__((aligned(16))) T sOt[TDIRECT ? 4 : (QTALL ? NCH : 1) * DC * TS];
   __shared__ __attribute__((aligned(16))) float sL[BMQ];
   __shared__ __attribute__((aligned(16))) float sDl[BMQ];
   __shared__ __attribute__((aligned(16))) float sRed[SPLIT ? NW * 2 * 1024 : 4];
@@ -1181,7 +1188,7 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       __syncthreads();
       if (c + 1 < NCH) {
         load_s(it, c + 1);
-      } else if constexpr (QTALL) {
+      } else if constexpr (QTALL || TDIRECT) {
         if (it + 1 < nitems) load_s(it + 1, 0);
       } else {
         load_t(it, 0);
@@ -1210,6 +1217,29 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
       grads(hq, q0, full, sacc, dpacc, pf, uf);
     }
     // ---- dV^T += dO^T P,  dK^T += Q^T dU  over this wave's slice
+    if constexpr (TDIRECT) {
+      // lane (n, half h) takes column swp(n) of block db (the staged
+      // transposes store column c at row swp(c), which puts the accumulator
+      // rows in acc_row order) and queries 16 sb + 8 h + s, s = 0..7
+      const T* qg = qb_of(hq) + sl * DO + swp(n);
+      const T* og = ob_of(hq) + sl * DO + swp(n);
+#pragma unroll
+      for (int db = 0; db < NOB; ++db) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          F ao, aq;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int qi = q0 + 16 * sb + 8 * h + e;
+            const long off = (long)min(qi, Sq - 1) * qstride + db * 32;
+            ao[e] = qi < Sq ? og[off] : 0.0f;
+            aq[e] = qi < Sq ? qg[off] : 0.0f;
+          }
+          mma(vacc[db], ao, pf[sb]);
+          mma(kacc[db], aq, uf[sb]);
+        }
+      }
+    } else
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if constexpr (!QTALL) {
