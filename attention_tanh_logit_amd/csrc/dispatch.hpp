@@ -63,8 +63,8 @@ template <int D> struct DqDuCfg;
 //      D    DO  NQG  BN   DC
 ATL_DQU(64, 64, 4, 32, 64)
 ATL_DQU(128, 128, 2, 32, 128)
-ATL_DQU(256, 128, 4, 32, 64)
-ATL_DQU(512, 256, 4, 32, 128)
+ATL_DQU(256, 64, 2, 32, 64)
+ATL_DQU(512, 64, 1, 32, 64)
 
 #undef ATL_FWD
 #undef ATL_DQ

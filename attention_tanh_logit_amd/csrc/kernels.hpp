@@ -453,7 +453,8 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
 
 // DU (fp32): dQ from the dU blocks the dk/dv kernel wrote (32 x 32 fp32 per
 // (key block, query block), row-major [query][key]) instead of recomputing S,
-// dP and the gradients: only K^T passes through LDS, and Q, dO, V are not read.
+// dP and the gradients: Q, dO and V are not read, and K^T comes from global
+// memory without LDS.
 template <typename T, int D, int DO, int NQG, int BN, int DC, bool CAP, bool BIAS, bool DU = false>
 __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   constexpr int NSL = D / DO;
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T sO[DU ? 4 : BM * RS];   // dO
   __shared__ __attribute__((aligned(16))) T sK[DU ? 4 : BN * RS];
   __shared__ __attribute__((aligned(16))) T sV[DU ? 4 : BN * RS];
-  __shared__ __attribute__((aligned(16))) T sKt[DC * TS];
+  __shared__ __attribute__((aligned(16))) T sKt[DU ? 4 : DC * TS];
   // the slices of a row group split each chunk's contraction for S and dP
   constexpr bool SPLIT = !DU && !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
                          (2 * BM * RS + 2 * BN * RS + DC * TS) * (int)sizeof(T) + NW * 2 * NKB * 4096 <= kLdsBudget;
@@ -616,38 +617,32 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   };
 
   if constexpr (DU) {
-  // dQ^T += K^T dU^T from the dU blocks; K^T in chunks through LDS, the next
-  // chunk's global loads issued under this chunk's MFMAs
+  // dQ^T += K^T dU^T from the dU blocks.  Each wave reads the K^T operands of
+  // its own output columns straight from global memory -- lane (n, half h)
+  // takes column swp(n) of each 32-column block (the order staged transposes
+  // would give, which puts the accumulator rows in acc_row order) and keys
+  // 16 sb + 8 h + s, s = 0..7, each load a 128-byte run of one key row --
+  // so no LDS and no barrier: the slices of a row group never wait for each
+  // other.
   const int ntile = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
-  RowPairChunks<T, BN, DC, NT> rkt;
-  auto load_t = [&](int t, int c) { rkt.load(kbase, kstride, kbeg + t * BN, Sk, c * DC); };
-  if (ntile > 0) load_t(0, 0);
+  const T* kcol = kbase + sl * DO + swp(n);
   for (int t = 0; t < ntile; ++t) {
     const int k0 = kbeg + t * BN;
     F uf[NKB][2];
     load_du(k0, uf);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      __syncthreads();
-      rkt.template store<TS, true>(sKt);
-      __syncthreads();
-      if (c + 1 < NCH) load_t(t, c + 1);
-      else if (t + 1 < ntile) load_t(t + 1, 0);
-      // chunk c belongs to slice c / (DO / DC), at its column block (c % (DO / DC)) DC / 32
-      constexpr int CPS = DO >= DC ? DO / DC : 1;
-      if (ONE || sl == c / CPS) {
+    for (int ob = 0; ob < NOB; ++ob) {
 #pragma unroll
-        for (int db = 0; db < DC / 32; ++db) {
-          const int ob = ONE ? db - sl * NOB : (c % CPS) * (DC / 32) + db;
-          if (ob < 0 || ob >= NOB) continue;
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
+        for (int sb = 0; sb < 2; ++sb) {
+          F ak;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-              const F ak = lds_frag<T>(sKt + (db * 32 + n) * TS + kb * 32 + 16 * sb + 8 * h);
-              mma(qacc[ob], ak, uf[kb][sb]);
-            }
+          for (int e = 0; e < 8; ++e) {
+            const int key = k0 + kb * 32 + 16 * sb + 8 * h + e;
+            ak[e] = key < Sk ? kcol[(long)key * kstride + ob * 32] : 0.0f;
           }
+          mma(qacc[ob], ak, uf[kb][sb]);
         }
       }
     }
