@@ -181,20 +181,25 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   static_assert(ONE || DO % DC == 0, "a chunk must not straddle two slices");
   using F = typename Frag<T>::type;
 
+  // fp32 with several column slices: each V^T stage holds one chunk per
+  // slice (chunk k of every slice's columns), so that all slices have P V
+  // work in every stage instead of taking turns on the chunks
+  constexpr bool VPAIR = sizeof(T) == 4 && !ONE && NSL > 1;
+  constexpr int VST = (VPAIR ? NSL : 1) * DC * VS;   // V^T staging elements
   // the slices of a row group split each chunk's contraction for S
   // (fp32 only: with bf16 the partial sums cost the forward more than the
   // MFMA work they save)
   constexpr bool SPLIT = sizeof(T) == 4 && !ONE && NSL > 1 && (DC / 16) % NSL == 0 &&
-                         (BM * QS + BN * KS + DC * VS) * (int)sizeof(T) + NW * NKB * 4096 <= kLdsBudget;
+                         (BM * QS + BN * KS + VST) * (int)sizeof(T) + NW * NKB * 4096 <= kLdsBudget;
   constexpr int CPW = SPLIT ? DC / 16 / NSL : DC / 16;   // 16-column steps per wave and chunk
   constexpr int RED = SPLIT ? NW * NKB * 4096 : 0;
   // with the head dimension in chunks, all chunks of the Q tile stay in LDS
   // for the whole key sweep where they fit (instead of being staged again
   // for every key tile)
-  constexpr bool QRES = !ONE && (NCH * BM * QS + BN * KS + DC * VS) * (int)sizeof(T) + RED <= 150 * 1024;
+  constexpr bool QRES = !ONE && (NCH * BM * QS + BN * KS + VST) * (int)sizeof(T) + RED <= 150 * 1024;
   __shared__ __attribute__((aligned(16))) T sQ[(QRES ? NCH : 1) * BM * QS];
   __shared__ __attribute__((aligned(16))) T sK[BN * KS];
-  __shared__ __attribute__((aligned(16))) T sV[DC * VS];
+  __shared__ __attribute__((aligned(16))) T sV[VST];
   __shared__ __attribute__((aligned(16))) float sRed[SPLIT ? NW * NKB * 1024 : 4];
 
   // XCD-aware, longest-first numbering: the query tiles of a head share its K/V
@@ -355,7 +360,10 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
   const int ntile = hi_last > kbeg ? (hi_last - kbeg + BN - 1) / BN : 0;
   RowChunks<T, BN, DC, NT> rk;
   RowChunks<T, BM, DC, NT> rq;
-  RowPairChunks<T, BN, DC, NT> rvt;
+  constexpr int NVS = VPAIR ? NSL : 1;       // V^T chunks per stage
+  constexpr int CPS = DO / DC;               // chunks per slice
+  constexpr int NVSTAGE = VPAIR ? CPS : NCH; // V^T stages per key tile
+  RowPairChunks<T, BN, DC, NT> rvt[NVS];
   auto load_s = [&](int t, int c) {
     rk.load(kbase, kstride, kbeg + t * BN, Sk, c * DC);
     if constexpr (!QRES) rq.load(qbase, qstride, q0, Sq, c * DC);
@@ -364,7 +372,11 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) stage_rows<T, BM, DC, QS, false, NT>(sQ + c * BM * QS, qbase, qstride, q0, Sq, c * DC);
   }
-  auto load_v = [&](int t, int c) { rvt.load(vbase, kstride, kbeg + t * BN, Sk, c * DC); };
+  // V^T stage c: chunk c, or (VPAIR) chunk c of every slice, slice s2's in rvt[s2]
+  auto load_v = [&](int t, int c) {
+#pragma unroll
+    for (int s2 = 0; s2 < NVS; ++s2) rvt[s2].load(vbase, kstride, kbeg + t * BN, Sk, ((VPAIR ? s2 * CPS : 0) + c) * DC);
+  };
   if (ntile > 0) load_s(0, 0);
   for (int t = 0; t < ntile; ++t) {
     const int k0 = kbeg + t * BN;
@@ -397,23 +409,25 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
     softmax(k0, full, sacc, pf);
     // ---- O^T += V^T P^T over this wave's slice of the head dimension
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < NVSTAGE; ++c) {
       __syncthreads();
-      rvt.template store<VS, true>(sV);
+#pragma unroll
+      for (int s2 = 0; s2 < NVS; ++s2) rvt[s2].template store<VS, true>(sV + s2 * DC * VS);
       __syncthreads();
-      if (c + 1 < NCH) load_v(t, c + 1);
+      if (c + 1 < NVSTAGE) load_v(t, c + 1);
       else if (t + 1 < ntile) load_s(t + 1, 0);
-      // chunk c belongs to slice c / (DO / DC), at its column block (c % (DO / DC)) DC / 32
-      constexpr int CPS = DO / DC;
-      if (sl == c / CPS) {
+      // VPAIR: this slice's chunk c sits at sV + sl DC VS; else chunk c
+      // belongs to slice c / CPS, at its column block (c % CPS) DC / 32
+      const T* tV = sV + (VPAIR ? sl * DC * VS : 0);
+      if (VPAIR || sl == c / CPS) {
 #pragma unroll
         for (int db = 0; db < DC / 32; ++db) {
-          const int ob = (c % CPS) * (DC / 32) + db;
+          const int ob = (VPAIR ? c : c % CPS) * (DC / 32) + db;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
-              const F av = lds_frag<T>(sV + (db * 32 + n) * VS + kb * 32 + 16 * sb + 8 * h);
+              const F av = lds_frag<T>(tV + (db * 32 + n) * VS + kb * 32 + 16 * sb + 8 * h);
               mma(oacc[ob], av, pf[kb][sb]);
             }
           }
