@@ -829,19 +829,21 @@ __global__ __launch_bounds__(64 * NKG * (D / DO)) void dkdv_kernel(BwdParams p) 
   // and V (NCH * CPW fragments of each, 4 registers apiece), which it keeps
   // in registers for the whole sweep instead of staging K and V per item
   constexpr bool KVREG = SPLIT && sizeof(T) == 2;
-  // With the head dimension in chunks and LDS to spare, the Q^T and dO^T
-  // chunks of an item all stay in LDS: staged with Q and dO (the same global
-  // lines, loaded back to back) instead of read again for the gradient stages.
-  // (Keeping the key block's K and V chunks in LDS instead, where only one of
-  // the two fits, was slower.)
-  constexpr bool QTALL = !ONE && (2 * BNK * RS + 2 * BMQ * RS + 2 * NCH * DC * TS) * (int)sizeof(T) + RED <= 150 * 1024;
-  // fp32 where they do not fit (D = 512): staging one Q^T / dO^T chunk at a
-  // time would leave each chunk stage to the one slice that owns its columns
-  // (the other SIMDs waiting at the stage barriers); instead every slice reads
-  // the Q^T and dO^T operands of its own columns straight from global memory
-  // (each load a 128-byte run of one query row, mostly L2 hits after the S/dP
-  // stages), and the slices' dV / dK MFMAs run at the same time.
-  constexpr bool TDIRECT = !ONE && !QTALL && sizeof(T) == 4 && DO == DC;
+  // fp32 with one chunk per slice (D = 256, 512): every slice reads the Q^T
+  // and dO^T operands of its own columns straight from global memory (each
+  // load a 128-byte run of one query row, mostly L2 hits after the S/dP
+  // stages) instead of staging them.  Staged one chunk at a time (where all
+  // do not fit, D = 512) each chunk stage would fall to the one slice owning
+  // its columns, the other SIMDs waiting at the stage barriers; kept all in
+  // LDS (D = 256) they would hold 74 KiB and one workgroup per CU.
+  constexpr bool TDIRECT = !ONE && sizeof(T) == 4 && DO == DC;
+  // Otherwise, with the head dimension in chunks and LDS to spare, the Q^T
+  // and dO^T chunks of an item all stay in LDS: staged with Q and dO (the
+  // same global lines, loaded back to back) instead of read again for the
+  // gradient stages.  (Keeping the key block's K and V chunks in LDS
+  // instead, where only one of the two fits, was slower.)
+  constexpr bool QTALL = !TDIRECT && !ONE &&
+                         (2 * BNK * RS + 2 * BMQ * RS + 2 * NCH * DC * TS) * (int)sizeof(T) + RED <= 150 * 1024;
   __shared__ __attribute__((aligned(16))) T sK[BNK * RS];
   __shared__ __attribute__((aligned(16))) T sV[BNK * RS];
   __shared__ __attribute__((aligned(16))) T sQ[BMQ * RS];
