@@ -151,14 +151,15 @@ def test_d512_running_maximum(dtype, feat):
     _check(case(dtype=dtype, D=512, B=2, S=203, Hq=4, Hkv=2, softcap=50.0, **WIDE_CAP50[feat]))
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("fp32", 64), ("bf16", 128), ("fp32", 256), ("bf16", 512)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("fp32", 64), ("bf16", 128), ("fp32", 256), ("bf16", 512),
+                                     ("fp32", 512), ("fp16", 512)])
 def test_cross_attention_lengths_differ(dtype, D):
     _check(case(dtype=dtype, D=D, B=1, S=77, Sk=301, causal=False, Hq=2, Hkv=1))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_thd_varlen_matches_oracle(dtype):
-    c = case(dtype=dtype, D=128, B=2, S=160, segments=[[7, 64, 65, 130], [100]], sink_mode="learnable")
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 128), ("bf16", 512), ("fp32", 512)])
+def test_thd_varlen_matches_oracle(dtype, D):
+    c = case(dtype=dtype, D=D, B=2, S=160, segments=[[7, 64, 65, 130], [100]], sink_mode="learnable")
     _check(c, thd=True)
 
 
