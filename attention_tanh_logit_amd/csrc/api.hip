@@ -394,7 +394,7 @@ long max_token_stride(const attn_args* a) {
 // kernels write none.
 bool du_supported(const attn_args* a) {
   return a->dtype == ATTN_FP32 || fast_ok(is16(a), a->D, max_token_stride(a), a->Sk, a->bias != nullptr) ||
-         wide_ok(is16(a), a->D, max_token_stride(a), a->bias != nullptr);
+         wide_ok(is16(a), a->D, max_token_stride(a), a->Sk, a->bias != nullptr);
 }
 
 attn_status validate(const attn_args* a) {
@@ -439,8 +439,8 @@ attn_status validate(const attn_args* a) {
   if (a->dq_mode != ATTN_DQ_AUTO && a->dq_mode != ATTN_DQ_DU_BLOCKS && a->dq_mode != ATTN_DQ_RECOMPUTE)
     return fail(ATTN_INVALID_ARGUMENT, "dq_mode must be ATTN_DQ_AUTO, ATTN_DQ_DU_BLOCKS or ATTN_DQ_RECOMPUTE");
   if (a->dq_mode == ATTN_DQ_DU_BLOCKS && !du_supported(a))
-    return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs fp32, or bf16 / fp16 with D = 64, 128 or 256 (with a bias, "
-                                  "Sk % 8 == 0) or D = 512 without a bias");
+    return fail(ATTN_UNSUPPORTED, "ATTN_DQ_DU_BLOCKS needs fp32, or bf16 / fp16 with D = 64, 128, 256 or 512 (with a "
+                                  "bias, Sk % 8 == 0)");
   if ((long long)a->B * a->Sq > 0 && a->Sk == 0) return fail(ATTN_UNSUPPORTED, "Sk == 0 with Sq > 0");
   const size_t elems = (size_t)a->B * (a->Sq + a->Sk);
   if (elems != 0 && (!a->q || !a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "q, k and v must not be NULL");
@@ -504,7 +504,7 @@ bool dkdv_writes_dbias_zeros(const attn_args* a) {
 // the GPU to a few long workgroups; 1 when there are enough already.
 int head_split(const attn_args* a) {
   const bool bf = is16(a), bias = a->bias != nullptr;
-  const bool wide = wide_ok(bf, a->D, max_token_stride(a), bias);
+  const bool wide = wide_ok(bf, a->D, max_token_stride(a), a->Sk, bias);
   if (!fast_ok(bf, a->D, max_token_stride(a), a->Sk, bias) && !wide) return 1;
   const int bnk = wide ? 32 : 128;   // keys per dk/dv workgroup (as counted here)
   const long wgs = (long)((a->Sk + bnk - 1) / bnk) * a->Hkv * a->B;

@@ -96,13 +96,13 @@ inline bool fast_ok(bool bf16_input, int D, long tstride, int Sk, bool bias) {
   return bf16_input && (D == 64 || D == 128 || D == 256) && 128L * tstride * 2 < (1L << 31) &&
          (!bias || (Sk % 8 == 0 && Sk >= 8));
 }
-// bf16 with D = 512 and no bias takes the kernels of wide.hpp (same 32-bit
-// buffer offsets as the fast kernels)
-inline bool wide_ok(bool bf16_input, int D, long tstride, bool bias) {
-  return bf16_input && D == 512 && !bias && 128L * tstride * 2 < (1L << 31);
+// bf16 with D = 512 takes the kernels of wide.hpp (same 32-bit buffer
+// offsets as the fast kernels; with a bias, Sk % 8 == 0 as on the fast path)
+inline bool wide_ok(bool bf16_input, int D, long tstride, int Sk, bool bias) {
+  return bf16_input && D == 512 && 128L * tstride * 2 < (1L << 31) && (!bias || (Sk % 8 == 0 && Sk >= 8));
 }
 template <typename T, int D, bool BIAS> constexpr bool use_wide() {
-  return std::is_same<T, bf16>::value && D == 512 && !BIAS;
+  return std::is_same<T, bf16>::value && D == 512;
 }
 
 template <int D, class Params>
@@ -132,15 +132,15 @@ hipError_t launch_fwd(const FwdParams& p, const Launch& l) {
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, l.Sk, BIAS)) {
       const dim3 grid((l.Sq + 63) / 64, p.Hq, l.B);
       const bool fixm = CAP && p.cl2 <= 60.0f && !kNarrow16;
       if (p.drop.on) {
-        if (fixm) fwd512_kernel<CAP, CAP, true><<<grid, 512, 0, l.stream>>>(p);
-        else fwd512_kernel<CAP, false, true><<<grid, 512, 0, l.stream>>>(p);
+        if (fixm) fwd512_kernel<CAP, CAP, true, BIAS><<<grid, 512, 0, l.stream>>>(p);
+        else fwd512_kernel<CAP, false, true, BIAS><<<grid, 512, 0, l.stream>>>(p);
       } else {
-        if (fixm) fwd512_kernel<CAP, CAP, false><<<grid, 512, 0, l.stream>>>(p);
-        else fwd512_kernel<CAP, false, false><<<grid, 512, 0, l.stream>>>(p);
+        if (fixm) fwd512_kernel<CAP, CAP, false, BIAS><<<grid, 512, 0, l.stream>>>(p);
+        else fwd512_kernel<CAP, false, false, BIAS><<<grid, 512, 0, l.stream>>>(p);
       }
       return hipGetLastError();
     }
@@ -264,10 +264,10 @@ hipError_t launch_dkdv(const BwdParams& p, const Launch& l) {
     }
   }
   if constexpr (use_wide<T, D, BIAS>()) {
-    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, false)) {
+    if (wide_ok(true, D, p.qts > p.kts ? p.qts : p.kts, l.Sk, BIAS)) {
       const dim3 grid((l.Sk + 31) / 32, p.Hkv * p.hsplit, l.B);
-      if (p.drop.on) dkdv512_kernel<CAP, true><<<grid, 512, 0, l.stream>>>(p);
-      else dkdv512_kernel<CAP, false><<<grid, 512, 0, l.stream>>>(p);
+      if (p.drop.on) dkdv512_kernel<CAP, true, BIAS><<<grid, 512, 0, l.stream>>>(p);
+      else dkdv512_kernel<CAP, false, BIAS><<<grid, 512, 0, l.stream>>>(p);
       if (p.hsplit > 1) {
         const long nel = (long)l.B * l.Sk * p.Hkv * D;
         const float kscale = p.scale * (CAP ? 4.0f : 1.0f);

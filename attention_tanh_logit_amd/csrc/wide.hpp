@@ -1,6 +1,8 @@
 // 16-bit kernels (bf16; fp16 in the second build of these sources) for head
-// dim 512 without a bias: forward, and dk/dv, which hands dU to the dq kernel
-// through the workspace, on the fast path's tiles and fragments.
+// dim 512: forward, and dk/dv, which hands dU to the dq kernel through the
+// workspace, on the fast path's tiles and fragments.  With a bias (Sk % 8 ==
+// 0), each quarter's owner reads the bias of its own pairs from global memory
+// and dk/dv writes their dbias, so no slice repeats that work.
 //
 // A workgroup is 8 waves: two row (or key) groups x four column slices of
 // 128.  A wave keeps only its slice of the fixed operand (Q columns in the
@@ -40,7 +42,7 @@ namespace ATL_NS {
 // slice's columns.  The quarters' row sums are added once, at the end.
 // DROP: dropout as in fwd_fast_kernel (one Philox4x32-10 evaluation per run
 // of four keys of a lane's query, the run of the wave's quarter).
-template <bool CAP, bool FIXM, bool DROP>
+template <bool CAP, bool FIXM, bool DROP, bool BIAS>
 __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
   constexpr int D = 512, NT = 512, BM = 64, BN = 32;
@@ -92,6 +94,11 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   keys_of(p.mask, b, ilast, lo_last, hi_last);
   const bool dchk = dense_row(p.mask, b);
   const bool rows_full = (q0 + BM <= Sq) && !dchk;
+  // BIAS: this lane's query row of the bias (Sk % 8 == 0 on this path, so a
+  // run of four keys starting below Sk lies wholly inside the row)
+  const bf16* brow = nullptr;
+  if constexpr (BIAS)
+    brow = reinterpret_cast<const bf16*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + (long)min(i, Sq - 1) * Sk;
 
   bf16x8 qf[NCW];
   {
@@ -146,10 +153,16 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
     }
     // logits of the quarter: CAP keeps r = 1/(1+2^y) (masked: +inf), else y (masked: -inf)
     float ext = CAP ? INFINITY : -INFINITY;
+    bf16x4 bq = {};
+    if constexpr (BIAS) {
+      const int key0 = k0 + acc_row(h, 4 * sl);
+      if (key0 < Sk) bq = *reinterpret_cast<const bf16x4*>(brow + key0);
+    }
     auto logits = [&](auto masked) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float y = lq[e] * lk.a;
+        float y = lq[e] * lk.a;
+        if constexpr (BIAS) y = fmaf((float)bq[e], lk.bb, y);
         float v;
         if constexpr (FIXM) v = __builtin_amdgcn_rcpf(fmaf(fast_exp2(y), kfix, kfix));
         else if constexpr (CAP) v = __builtin_amdgcn_rcpf(1.0f + fast_exp2(y));
@@ -277,7 +290,7 @@ __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
 // Q^T, dO^T from transposing reads.  Slice 0 writes the dU block halves for
 // dq.  DROP: dropout, the keep decisions shared in quads of lanes as in
 // dkdv16_kernel (each wave evaluates those of its quarter).
-template <bool CAP, bool DROP>
+template <bool CAP, bool DROP, bool BIAS>
 __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
   constexpr int D = 512, NT = 512, BNK = 32, BMQ = 32;
   constexpr int NCW = 4;   // 32-column contraction steps per slice
@@ -443,6 +456,16 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
       kq = (unsigned)(((n0 >> t) & 1) | (((n1 >> t) & 1) << 1));
     }
     float pq[2], uq[2];
+    // BIAS: the bias of this wave's two pairs, and where their dbias goes
+    float bv[2] = {0.0f, 0.0f};
+    const long brow0 = (long)b * p.bias_bs + hq * p.bias_hs + jc;
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int qi = q0 + 16 * qbw + 4 * g + ew + t;
+        bv[t] = (float)reinterpret_cast<const bf16*>(p.bias)[brow0 + (long)min(qi, Sq - 1) * Sk];
+      }
+    }
     auto grads = [&](auto masked) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -452,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
           l = (qi >= lo_j && qi < hi_j && dense_ok(p.mask, dchk, b, qi, j)) ? l : -INFINITY;
         }
         float gg;
-        const float pv = prob_fast<CAP, false>(tot[t], 0.0f, lk, l, gg);
+        const float pv = prob_fast<CAP, BIAS>(tot[t], bv[t], lk, l, gg);
         if constexpr (DROP) {
           // m dP - delta with m = keep / (1 - p); md = -delta
           const float mk = ((kq >> t) & 1u) ? p.drop.scale : 0.0f;
@@ -466,6 +489,19 @@ __global__ __launch_bounds__(512, 1) void dkdv512_kernel(BwdParams p) {
     };
     if (keys_full && q0 >= lo_last && q0 + BMQ <= hi_first) grads(bool_c<false>{});
     else grads(bool_c<true>{});
+    // dbias of this wave's pairs that the visibility range covers (the pairs
+    // outside it were zeroed by the fill pass); a pair the dense mask drops
+    // inside the range has P = 0 and writes 0
+    if constexpr (BIAS) {
+      if (p.dbias && j < Sk) {
+        bf16* drow = reinterpret_cast<bf16*>(p.dbias) + ((long)b * p.Hq + hq) * Sq * Sk + j;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int qi = q0 + 16 * qbw + 4 * g + ew + t;
+          if (qi < Sq && qi >= lo_j && qi < hi_j) drow[(long)qi * Sk] = (bf16)(uq[t] * kGrad4<CAP>);
+        }
+      }
+    }
     // gather the quarters: element 4 qbw + ew + t of the lane's fragments
     {
       bf16x2 pp, uu;

@@ -112,8 +112,8 @@ typedef enum attn_bias_bcast {
  *    the element type, B*Hq*ceil(Sk/32)*ceil(Sq/32) blocks of 2 KiB (bf16,
  *    fp16) or 4 KiB (fp32): 4 GiB at B=4, Hq=32, S=4096 in bf16; only the
  *    visible blocks are written and read.  fp32 at any D; bf16 or fp16 with
- *    D = 64, 128 or 256 (with a bias also Sk % 8 == 0), or D = 512 without a
- *    bias; ATTN_UNSUPPORTED otherwise.
+ *    D = 64, 128, 256 or 512 (with a bias also Sk % 8 == 0); ATTN_UNSUPPORTED
+ *    otherwise.
  *  - ATTN_DQ_RECOMPUTE: the dq kernel recomputes the logits, probabilities
  *    and dP itself; the workspace stays O(B*Hq*Sq).
  *  - ATTN_DQ_AUTO (0): DU_BLOCKS where supported, D >= 128 (or dropout is
@@ -209,11 +209,11 @@ attn_status attn_validate(const attn_args* a);
  *    already summed over each workgroup's heads, of which only the query
  *    rows that see some key of a key block are written and read; reduced
  *    into the caller's dbias), and for bf16 / fp16 with D = 64, 128 or 256 when
- *    B*Hkv*ceil(Sk/128) < 1024 (D = 512 without a bias: B*Hkv*ceil(Sk/32) <
- *    1024), 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial dK/dV: the dk/dv kernel
- *    then splits each GQA group's query heads over s workgroups (s the
- *    smallest divisor of Hq/Hkv reaching 1024 workgroups, else the largest),
- *    summed afterwards in a fixed order. */
+ *    B*Hkv*ceil(Sk/128) < 1024 (D = 512, with a bias only when Sk % 8 == 0:
+ *    B*Hkv*ceil(Sk/32) < 1024), 2*s*B*Sk*Hkv*D*4 bytes of fp32 partial
+ *    dK/dV: the dk/dv kernel then splits each GQA group's query heads over s
+ *    workgroups (s the smallest divisor of Hq/Hkv reaching 1024 workgroups,
+ *    else the largest), summed afterwards in a fixed order. */
 size_t attn_fwd_workspace_size(const attn_args* a);
 size_t attn_bwd_workspace_size(const attn_args* a);
 

@@ -83,7 +83,7 @@ BAD = {
     "misaligned_q": (dict(q=0x1002), 1, "aligned"),
     "misaligned_bias": (dict(bias=0x2008), 1, "aligned"),
     "bad_dq_mode": (dict(dq_mode=3), 1, "dq_mode"),
-    "du_blocks_d512_bias": (dict(D=512, dq_mode=1, bias=0x2000), 2, "DU_BLOCKS"),
+    "du_blocks_d512_ragged_bias": (dict(D=512, Sq=250, Sk=250, dq_mode=1, bias=0x2000), 2, "DU_BLOCKS"),
     "du_blocks_ragged_bias": (dict(Sq=250, Sk=250, bias=0x2000, dq_mode=1), 2, "DU_BLOCKS"),
     "keys_empty": (dict(Sk=0, causal=0), 2, "Sk == 0"),
     "bias_bcast_without_bias": (dict(bias_bcast=1), 1, "bias_bcast"),

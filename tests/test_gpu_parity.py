@@ -145,6 +145,27 @@ WIDE_CAP50 = {
 }
 
 
+# D = 512 with a bias and Sk % 8 == 0 runs on the four-slice kernels too: each quarter's owner reads
+# its pairs' bias and writes their dbias (S = 200 here; S = 203 above takes the generic kernels)
+WIDE_BIAS = {
+    "cap30": dict(bias=True, softcap=30.0),
+    "cap50": dict(bias=True, softcap=50.0),
+    "no_cap_sink": dict(bias=True, softcap=0.0, sink_mode="learnable"),
+    "heads_bcast": dict(bias=True, softcap=50.0, bias_bcast="heads"),
+    "batch_bcast": dict(bias=True, softcap=30.0, bias_bcast="batch"),
+    "segments_window": dict(bias=True, softcap=50.0, segments=[[45, 70, 190], [128]], window=40),
+    "dropout": dict(bias=True, softcap=30.0, dropout_p=0.2, sink_mode="learnable"),
+    "no_causal": dict(bias=True, softcap=50.0, causal=False),
+}
+
+
+@pytest.mark.parametrize("dq_mode", ["auto", "recompute"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("feat", list(WIDE_BIAS))
+def test_d512_bias_on_the_wide_kernels(dtype, feat, dq_mode):
+    _check(case(dtype=dtype, D=512, B=2, S=200, Hq=4, Hkv=2, **WIDE_BIAS[feat]), dq_mode=dq_mode)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("feat", list(WIDE_CAP50))
 def test_d512_running_maximum(dtype, feat):

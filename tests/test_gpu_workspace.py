@@ -30,6 +30,8 @@ CASES = {
     "k_start": dict(dtype="bf16", D=256, B=2, S=200, Hq=4, Hkv=2, segments=[[45, 70, 190], [128]]),
     "dropout": dict(dtype="bf16", D=128, B=2, S=203, Hq=4, Hkv=2, dropout_p=0.2, sink_mode="learnable"),
     "wide_d512": dict(dtype="bf16", D=512, B=1, S=150, Hq=2, Hkv=1, sink_mode="learnable"),
+    "wide_d512_bias": dict(dtype="bf16", D=512, B=2, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0,
+                           segments=[[45, 70, 190], [128]]),
 }
 
 
