@@ -616,12 +616,12 @@ void bias_strides(const attn_args* a, long& bs, long& hs) {
 Dropout dropout_of(const attn_args* a) {
   Dropout d;
   d.on = a->dropout_p > 0.0f;
-  const double t = std::floor((double)a->dropout_p * 4294967296.0);
-  d.thresh = (uint32_t)(t > 4294967295.0 ? 4294967295.0 : t);
+  const double t = std::floor((double)a->dropout_p * 65536.0);
+  d.thresh = (uint32_t)(t > 65535.0 ? 65535.0 : t);
   d.seed_lo = (uint32_t)(a->dropout_seed & 0xFFFFFFFFu);
   d.seed_hi = (uint32_t)(a->dropout_seed >> 32);
   d.offset = (uint32_t)(a->dropout_offset & 0xFFFFFFFFu);
-  d.scale = (float)(1.0 / (1.0 - (double)a->dropout_p));
+  d.scale = (float)(65536.0 / (65536.0 - (double)d.thresh));
   return d;
 }
 

@@ -412,15 +412,17 @@ __device__ __forceinline__ bool dense_ok(const Mask& m, bool chk, int b, int i, 
 // 2011): ten rounds over a four-word counter and a two-word key; each round
 // forms the full 64-bit products of words 0 and 2 with 0xD2511F53 and
 // 0xCD9E8D57 and crosses their halves with words 1 and 3 and the key, which
-// grows by 0x9E3779B9 and 0xBB67AE85 between rounds.  Pair (query i, key j)
-// of batch row b, query head h uses word j % 4 at counter (j / 4, i,
-// b * Hq + h, offset) under key (seed low, seed high) and is kept iff that
-// word is at least thresh = floor(p 2^32); kept probabilities are scaled by
-// 1 / (1 - p).
+// grows by 0x9E3779B9 and 0xBB67AE85 between rounds.  One evaluation decides
+// eight pairs: pair (query i, key j) of batch row b, query head h takes the
+// 16-bit half j % 8 (low half of word (j % 8) / 2 for even j % 8, high half
+// for odd) of the output at counter (j / 8, i, b * Hq + h, offset) under key
+// (seed low, seed high), and is kept iff that half is at least thresh =
+// floor(p 2^16).  The drop probability is thus p' = thresh / 2^16, and kept
+// probabilities are scaled by 1 / (1 - p'), which keeps the expectation exact.
 struct Dropout {
   int on;
-  uint32_t thresh, seed_lo, seed_hi, offset;
-  float scale;   // 1 / (1 - p)
+  uint32_t thresh, seed_lo, seed_hi, offset;   // thresh < 2^16
+  float scale;   // 1 / (1 - thresh / 2^16)
 };
 
 __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
@@ -442,12 +444,51 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
   }
 }
 
-// the four keep decisions of keys j4 .. j4 + 3 (j4 a multiple of 4), bit e for key j4 + e
-__device__ __forceinline__ unsigned keep4(const Dropout& d, int i, int j4, int bh) {
-  uint32_t c[4] = {(uint32_t)j4 >> 2, (uint32_t)i, (uint32_t)bh, d.offset};
+// the Philox output c[4] that decides keys j8 .. j8 + 7 (j8 a multiple of 8) at query i
+__device__ __forceinline__ void draw8(const Dropout& d, int i, int j8, int bh, uint32_t c[4]) {
+  c[0] = (uint32_t)j8 >> 3;
+  c[1] = (uint32_t)i;
+  c[2] = (uint32_t)bh;
+  c[3] = d.offset;
   philox4x32_10(c, d.seed_lo, d.seed_hi);
-  return (c[0] >= d.thresh ? 1u : 0u) | (c[1] >= d.thresh ? 2u : 0u) | (c[2] >= d.thresh ? 4u : 0u) |
-         (c[3] >= d.thresh ? 8u : 0u);
+}
+
+// decision e (0..7) of a draw: 16-bit half e is at least thresh, compared as
+// the word (odd e) or the word shifted up by 16 (even e) against th16 = thresh << 16
+__device__ __forceinline__ bool kept(const uint32_t c[4], int e, uint32_t th16) {
+  const uint32_t w = c[e >> 1];
+  return ((e & 1) ? w : (w << 16)) >= th16;
+}
+
+// the eight keep decisions of keys j8 .. j8 + 7 (j8 a multiple of 8), bit e for key j8 + e
+__device__ __forceinline__ unsigned keep8(const Dropout& d, int i, int j8, int bh) {
+  uint32_t c[4];
+  draw8(d, i, j8, bh, c);
+  const uint32_t th16 = d.thresh << 16;
+  unsigned r = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r |= (kept(c, e, th16) ? 1u : 0u) << e;
+  return r;
+}
+
+// the four keep decisions of keys j4 .. j4 + 3 (j4 a multiple of 4), bit e for key j4 + e:
+// half of one evaluation, for kernels whose lanes hold no more of its keys
+__device__ __forceinline__ unsigned keep4(const Dropout& d, int i, int j4, int bh) {
+  uint32_t c[4];
+  draw8(d, i, j4 & ~7, bh, c);
+  const uint32_t th16 = d.thresh << 16;
+  const bool up = (j4 & 4) != 0;
+  const uint32_t w[2] = {up ? c[2] : c[0], up ? c[3] : c[1]};
+  return ((w[0] << 16) >= th16 ? 1u : 0u) | (w[0] >= th16 ? 2u : 0u) | ((w[1] << 16) >= th16 ? 4u : 0u) |
+         (w[1] >= th16 ? 8u : 0u);
+}
+
+// x of lane l ^ 4 (both lanes in one row of 16): DPP row_shl:4 reads lane l + 4,
+// row_shr:4 lane l - 4
+__device__ __forceinline__ int from_lane_xor4(int x, int lane) {
+  const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);
+  const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  return (lane & 4) ? dn : up;
 }
 
 // shuffle with the partner lane l ^ 32 (the other half of a 32x32 column)

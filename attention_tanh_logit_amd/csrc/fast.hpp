@@ -377,10 +377,10 @@ struct TilePlan {
 // whole row of Q^T fragments.
 //
 // DROP: dropout on the probabilities.  A lane's 16 logits of a 32-key block
-// are four runs of 4 consecutive keys of its query, so one Philox4x32-10
+// are two runs of 8 consecutive keys of its query, so one Philox4x32-10
 // evaluation gives the keep decisions of a run; the row sum (and lse) takes
 // the undropped probabilities, P.V the kept ones, and the epilogue scales O
-// by 1 / (1 - p).
+// by 1 / (1 - p').
 template <int D, bool CAP, bool BIAS, bool FIXM, bool DROP>
 __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast_kernel(FwdParams p) {
   static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");
@@ -568,12 +568,15 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
         pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
         ps = sum_bf16x8(pf[1], sum_bf16x8(pf[0], ps));
         if constexpr (DROP) {
-          // run q4 = keys k0 + 32 kb + acc_row(h, 4 q4 + e), e = 0..3
+          // registers 8 m + e hold keys k0 + 32 kb + acc_row(h, 8 m + e) = k0 + 32 kb + 16 m + 8 h + e,
+          // e = 0..7: the eight keys of one Philox evaluation
+          const uint32_t th16 = p.drop.thresh << 16;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const unsigned kp = keep4(p.drop, i, k0 + kb * 32 + acc_row(h, 4 * q4), b * p.Hq + hq);
+          for (int m = 0; m < 2; ++m) {
+            uint32_t c[4];
+            draw8(p.drop, i, k0 + kb * 32 + acc_row(h, 8 * m), b * p.Hq + hq, c);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) scur[kb][4 * q4 + e] = ((kp >> e) & 1u) ? scur[kb][4 * q4 + e] : 0.0f;
+            for (int e = 0; e < 8; ++e) scur[kb][8 * m + e] = kept(c, e, th16) ? scur[kb][8 * m + e] : 0.0f;
           }
           pf[0] = to_frag(scur[kb], 0, (bf16*)nullptr);
           pf[1] = to_frag(scur[kb], 8, (bf16*)nullptr);
@@ -664,7 +667,8 @@ __global__ __launch_bounds__(D > 128 ? 512 : 256, D > 128 ? 1 : 2) void fwd_fast
 //
 // DROP: dropout, with the keep decisions shared in quads of lanes (keys 4m ..
 // 4m + 3) as in dkdv16_kernel: per run of four consecutive queries of a
-// lane, lane t evaluates Philox4x32-10 for query t of the run.
+// lane, lane t evaluates Philox4x32-10 for query t of the run, and the two
+// quads of one eight-key evaluation split the runs between them.
 template <int D, bool CAP, bool BIAS, bool DROP>
 __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
   static_assert(D == 64, "32-key waves at D = 64 only");
@@ -808,9 +812,22 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
       unsigned kq = 0;
       if constexpr (DROP) {
         const int t = n & 3;
+        // lanes n and n ^ 4 hold the two halves of the eight keys j & ~7 of one
+        // evaluation: this lane evaluates runs 2 hf and 2 hf + 1 (hf = its half),
+        // keeps its own four decisions and hands the other four to its partner
+        const int hf = (n >> 2) & 1;
+        int own[2], give = 0;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int u = 2 * hf + v;
+          const unsigned k8 = keep8(p.drop, q0 + acc_row(h, 4 * u) + t, j & ~7, b * p.Hq + hq);
+          own[v] = (int)((k8 >> (4 * hf)) & 15u);
+          give |= (int)((k8 >> (4 - 4 * hf)) & 15u) << (4 * v);
+        }
+        const int got = from_lane_xor4(give, n);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int w4 = (int)keep4(p.drop, q0 + acc_row(h, 4 * u) + t, j & ~3, b * p.Hq + hq);
+          const int w4 = ((u >> 1) == hf) ? own[u & 1] : ((got >> (4 * (u & 1))) & 15);
           const int n0 = __builtin_amdgcn_update_dpp(0, w4, 0x00, 0xF, 0xF, false);
           const int n1 = __builtin_amdgcn_update_dpp(0, w4, 0x55, 0xF, 0xF, false);
           const int n2 = __builtin_amdgcn_update_dpp(0, w4, 0xAA, 0xF, 0xF, false);
@@ -964,10 +981,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_fast_kernel(BwdParams p) {
 // kappa + 16 g' holding dU(16 kh + kappa, queries sigma(g', 0..7)).
 //
 // DROP: dropout.  The lanes of a quad (keys 4m .. 4m + 3, one lane each)
-// hold the same four queries; lane t evaluates Philox4x32-10 once for query
-// t of the four and key run 4m, which gives the decisions of all four keys
-// at that query, and the quad exchanges them (DPP broadcasts), so a pair
-// costs a quarter of an evaluation as in the forward.  dV takes the kept
+// hold the same four queries; lane t takes the decisions of query t of the
+// four at keys 4m .. 4m + 3, and the quad exchanges them (DPP broadcasts).
+// One Philox4x32-10 evaluation decides eight keys, held by two quads (lanes
+// r and r ^ 4): with two or four query blocks per wave they split the blocks
+// and swap halves, so a pair costs an eighth of an evaluation as in the
+// forward (a quarter with one block per wave, at D = 256).  dV takes the kept
 // probabilities times 1 / (1 - p), and dS = P (m dP - delta) with m = keep /
 // (1 - p).
 //
@@ -1205,6 +1224,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
 
     const int bcol = 16 * kgi + r;      // this lane's key column in the bias tiles
     auto grads = [&](auto masked) {
+      // DROP: lanes r and r ^ 4 hold the two halves of the eight keys j & ~7 of
+      // one evaluation; with an even number of items, at each even item i lane
+      // r evaluates item i + (its half) and hands its partner the partner's
+      // half, which gives both lanes the decisions of items i and i + 1
+      int w4n = 0;
 #pragma unroll
       for (int i = 0; i < NQL; ++i) {
         const int qb = qb0 + i;
@@ -1213,7 +1237,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
         f32x4 md4{};          // -delta of those queries
         if constexpr (DROP) {
           const int t = r & 3;
-          const int w4 = (int)keep4(p.drop, q0 + 16 * qb + 4 * g + t, j & ~3, b * p.Hq + hq);
+          int w4;   // the decisions of query q0 + 16 qb + 4g + t at keys (j & ~3) + 0..3
+          if constexpr (NQL % 2 == 0) {
+            if (i % 2 == 0) {
+              const int hf = (r >> 2) & 1;
+              const unsigned k8 = keep8(p.drop, q0 + 16 * (qb + hf) + 4 * g + t, j & ~7, b * p.Hq + hq);
+              const int own = (int)((k8 >> (4 * hf)) & 15u);
+              const int got = from_lane_xor4((int)((k8 >> (4 - 4 * hf)) & 15u), r);
+              w4 = hf ? got : own;
+              w4n = hf ? own : got;
+            } else {
+              w4 = w4n;
+            }
+          } else {
+            w4 = (int)keep4(p.drop, q0 + 16 * qb + 4 * g + t, j & ~3, b * p.Hq + hq);
+          }
           const int n0 = __builtin_amdgcn_update_dpp(0, w4, 0x00, 0xF, 0xF, false);
           const int n1 = __builtin_amdgcn_update_dpp(0, w4, 0x55, 0xF, 0xF, false);
           const int n2 = __builtin_amdgcn_update_dpp(0, w4, 0xAA, 0xF, 0xF, false);

@@ -298,12 +298,15 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void fwd_kernel(FwdParams p) {
       if (p.drop.on) {
         // the row sum (lse) is that of the undropped softmax; V sees the kept
         // probabilities, scaled by 1 / (1 - p) in the epilogue
+        // registers 8 m + e: keys k0 + 32 kb + 16 m + 8 h + e, the eight keys of one evaluation
+        const uint32_t th16 = p.drop.thresh << 16;
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const unsigned kp = keep4(p.drop, i, k0 + kb * 32 + acc_row(h, 4 * j4), b * p.Hq + hq);
+        for (int m = 0; m < 2; ++m) {
+          uint32_t c[4];
+          draw8(p.drop, i, k0 + kb * 32 + acc_row(h, 8 * m), b * p.Hq + hq, c);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!((kp >> e) & 1u)) sacc[kb][4 * j4 + e] = 0.0f;
+          for (int e = 0; e < 8; ++e)
+            if (!kept(c, e, th16)) sacc[kb][8 * m + e] = 0.0f;
         }
       }
       pf[kb][0] = to_frag(sacc[kb], 0, (T*)nullptr);

@@ -40,8 +40,9 @@ namespace ATL_NS {
 // 2 c log2(e) <= 120 a fixed reference maximum; see fwd_fast_kernel), keeps
 // the row sum of its quarter, and after the gather O^T += V^T P^T over the
 // slice's columns.  The quarters' row sums are added once, at the end.
-// DROP: dropout as in fwd_fast_kernel (one Philox4x32-10 evaluation per run
-// of four keys of a lane's query, the run of the wave's quarter).
+// DROP: dropout as in fwd_fast_kernel; a lane's quarter is four keys of its
+// query, half of a Philox4x32-10 evaluation (the other half belongs to
+// another wave's quarter), so each lane evaluates once per key block.
 template <bool CAP, bool FIXM, bool DROP, bool BIAS>
 __global__ __launch_bounds__(512, 1) void fwd512_kernel(FwdParams p) {
   static_assert(CAP || !FIXM, "a fixed reference maximum needs bounded logits");

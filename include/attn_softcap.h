@@ -171,11 +171,14 @@ typedef struct attn_args {
    * exclude it or reject it with packing: tokamax PR description, MaxText
    * commit; the learnable-sink page's "What changed" carries the rng state
    * among the forward's outputs).  After the softmax each probability is kept
-   * with probability 1 - p and scaled by 1 / (1 - p); lse is that of the
-   * undropped softmax.  Pair (query i, key j) of batch row b, query head h is
-   * kept iff word j % 4 of Philox4x32-10 at counter (j / 4, i, b * Hq + h,
-   * offset % 2^32) under key (seed % 2^32, seed / 2^32) is at least
-   * floor(p * 2^32).  The backward must get the same p, seed and offset.
+   * with probability 1 - p' and scaled by 1 / (1 - p'), where p' = floor(p *
+   * 2^16) / 2^16 is p rounded down to a multiple of 2^-16 (the decisions
+   * compare 16-bit draws); lse is that of the undropped softmax.  Pair (query
+   * i, key j) of batch row b, query head h is kept iff 16-bit half j % 8 of
+   * Philox4x32-10 at counter (j / 8, i, b * Hq + h, offset % 2^32) under key
+   * (seed % 2^32, seed / 2^32) is at least floor(p * 2^16); half m is the low
+   * (m even) or high (m odd) 16 bits of output word m / 2.  The backward must
+   * get the same p, seed and offset.
    * bf16 / fp16 run it on the fast kernels where those take the problem (D
    * = 64 .. 256, and 512 without a bias; dq from the dU blocks, or on the
    * generic kernel with ATTN_DQ_RECOMPUTE); fp32 and the rest run the

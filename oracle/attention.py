@@ -35,10 +35,12 @@ each line can be checked against the sources by eye:
   rejects packing with dropout where the fallback kernels have none; the
   learnable-sink page ("What changed") carries the rng state among the
   forward's auxiliary outputs.  Read here as the usual attention dropout:
-  after the softmax, each probability is kept with probability 1 - p and
-  scaled by 1/(1 - p); lse is that of the softmax before dropout.  The keep
-  decisions come from a counter-based generator (``oracle/philox.py``) keyed
-  by the caller's seed and offset.
+  after the softmax, each probability is kept with probability 1 - p' and
+  scaled by 1/(1 - p'); lse is that of the softmax before dropout.  The keep
+  decisions compare 16-bit draws of a counter-based generator
+  (``oracle/philox.py``), keyed by the caller's seed and offset, with a
+  threshold, so p' is p rounded down to a multiple of 2^-16 (the pages fix
+  no generator or precision for these draws).
 * "Support logits soft-capping in the Pallas-Triton attention VJP", PR
   description: besides segment ids, a packed batch can be given as
   ``k_start`` (per query, the first key it may see) or as a dense boolean
@@ -232,15 +234,17 @@ def _prepare(q, k, v, bias, segment_ids, cu_seqlens, k_start=None, mask=None):
 
 
 def _dropout(p, seed, offset, b, hq0, Hq, Sk):
-    """(p, keep) for the group whose first query head is hq0, or None without dropout."""
+    """(drop probability, keep) for the group whose first query head is hq0, or None without
+    dropout.  The drop probability is p rounded down to a multiple of 2^-16 (the keep decisions
+    compare 16-bit draws), so that 1 / (1 - it) makes the kept values' expectation exact."""
     if not p:
         return None
-    from .philox import dropout_keep
+    from .philox import drop_probability, dropout_keep
 
     def keep(g, rows):
         r = np.arange(rows.start, rows.stop) if isinstance(rows, slice) else np.asarray(rows)
         return dropout_keep(b, hq0 + g, Hq, r, Sk, p, seed, offset)
-    return (float(p), keep)
+    return (drop_probability(p), keep)
 
 
 def _groups(B, Hkv, groups):

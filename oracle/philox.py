@@ -40,19 +40,27 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 def dropout_keep(b: int, hq: int, Hq: int, rows: np.ndarray, Sk: int, p: float, seed: int, offset: int) -> np.ndarray:
     """Keep decisions [len(rows), Sk] of batch row b, query head hq.
 
-    Element (i, j) draws word j % 4 of Philox4x32-10 at counter
-    (j // 4, i, b * Hq + hq, low 32 bits of offset) under key (low, high 32 bits
-    of seed), and is kept iff that word is at least floor(p * 2^32).
+    Element (i, j) draws 16-bit half j % 8 of Philox4x32-10 at counter
+    (j // 8, i, b * Hq + hq, low 32 bits of offset) under key (low, high 32 bits
+    of seed): half m of the output is the low (m even) or high (m odd) 16 bits
+    of word m // 2.  It is kept iff that half is at least threshold(p).
     """
     i = np.asarray(rows, dtype=np.uint64)[:, None]
     j = np.arange(Sk, dtype=np.uint64)[None, :]
-    words = philox4x32_10(j >> np.uint64(2), i, np.uint64(b * Hq + hq), np.uint64(offset & 0xFFFFFFFF),
+    words = philox4x32_10(j >> np.uint64(3), i, np.uint64(b * Hq + hq), np.uint64(offset & 0xFFFFFFFF),
                           seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    sel = (j & np.uint64(3)).astype(np.int64)
-    w = np.choose(np.broadcast_to(sel, words[0].shape), words)
-    return w >= np.uint64(threshold(p))
+    m = (j & np.uint64(7)).astype(np.int64)
+    w = np.choose(np.broadcast_to(m >> 1, words[0].shape), words)
+    half = (w >> (np.uint64(16) * (np.broadcast_to(m, w.shape) & 1).astype(np.uint64))) & np.uint64(0xFFFF)
+    return half >= np.uint64(threshold(p))
 
 
 def threshold(p: float) -> int:
-    """The 32-bit threshold of drop probability p (0 <= p < 1): floor(p * 2^32)."""
-    return min(int(np.floor(p * 4294967296.0)), 0xFFFFFFFF)
+    """The 16-bit threshold of drop probability p (0 <= p < 1): floor(p * 2^16), at most 2^16 - 1."""
+    return min(int(np.floor(p * 65536.0)), 0xFFFF)
+
+
+def drop_probability(p: float) -> float:
+    """The probability with which an element is dropped: threshold(p) / 2^16, p rounded down to a
+    multiple of 2^-16.  Kept elements are scaled by 1 / (1 - drop_probability(p))."""
+    return threshold(p) / 65536.0
