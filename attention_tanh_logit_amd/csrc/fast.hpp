@@ -1579,7 +1579,9 @@ __global__ __launch_bounds__(256 * NSL, NSL > 1 ? 1 : (NST >= 3 ? 3 : 2)) void d
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) qacc[ob] = f32x16{};
 
-  auto visible = [&](int kb32) { return kb32 < whi && kb32 + 32 > wlo && kb32 < Sk; };
+  // (a wave whose queries see no key has wlo == whi: an empty interval, which
+  // dk/dv wrote no block for, even where a 32-key block holds that point)
+  auto visible = [&](int kb32) { return wlo < whi && kb32 < whi && kb32 + 32 > wlo && kb32 < Sk; };
   // the tile's K rows (all waves) and this wave's dU^T blocks; every thread
   // issues the same number of loads per tile (a block no query of the wave
   // sees is read through an empty range, which fills zeros and touches no

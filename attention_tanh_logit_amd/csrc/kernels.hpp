@@ -594,7 +594,8 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
   // (each query's visible keys are an interval holding its own position, and
   // the bounds never decrease along the queries); a 32-key block outside it
   // holds no visible pair of the group and was not necessarily written, so
-  // it counts as zero.  Otherwise lane (query n, half h) takes keys
+  // it counts as zero (as does every block when the interval is empty: a
+  // group whose queries see no key).  Otherwise lane (query n, half h) takes keys
   // 16 sb + 8 h .. + 7 of the block's row n: the contraction order of the
   // fp32 MFMA fragments (element s at key 16 sb + 8 h + s).
   const int qw = q0 + qg * 32;
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int kb32 = k0 + kb * 32;
-      if (qw < Sq && kb32 < whi && kb32 + 32 > wlo && kb32 < Sk) {
+      if (qw < Sq && wlo < whi && kb32 < whi && kb32 + 32 > wlo && kb32 < Sk) {
         const float* blk = reinterpret_cast<const float*>(p.du) +
                            ((((long)b * p.Hq + hq) * p.nkb32 + (kb32 >> 5)) * p.nqb32 + (qw >> 5)) * 1024 + n * 32 +
                            8 * h;

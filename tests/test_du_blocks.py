@@ -66,6 +66,37 @@ def reads(B, Hq, Sq, Sk, causal, window):
                         yield b, hq, kb, qb, 1
 
 
+def keys_of(i, Sk, causal, window):
+    """The kernels' key interval [lo, hi) of query i (causal / window masks): a query that sees
+    no key gets an empty interval at lo == hi, clamped into [0, Sk]."""
+    lo, hi = 0, Sk
+    if causal:
+        hi = min(hi, i + 1)
+    if window > 0:
+        lo = max(lo, i - window + 1)
+        if not causal:
+            hi = min(hi, i + window)
+    lo = min(lo, Sk)
+    return lo, max(hi, lo)
+
+
+def kernel_reads(B, Hq, Sq, Sk, causal, window):
+    """The dq kernels' own read rule: a wave of 32 queries reads the block of keys kb32 .. + 31
+    when its keys, from the first query's lo to the last query's hi, are a non-empty interval
+    that meets the block (and the block starts below Sk)."""
+    for b in range(B):
+        for hq in range(Hq):
+            for qb in range((Sq + 31) // 32):
+                qw = 32 * qb
+                wlo = keys_of(qw, Sk, causal, window)[0]
+                whi = keys_of(min(qw + 31, Sq - 1), Sk, causal, window)[1]
+                for kb in range((Sk + 31) // 32):
+                    kb32 = 32 * kb
+                    if wlo < whi and kb32 < whi and kb32 + 32 > wlo and kb32 < Sk:
+                        yield b, hq, kb, qb, 0
+                        yield b, hq, kb, qb, 1
+
+
 CASES = [(200, True, 0), (200, False, 0), (97, True, 0), (333, True, 50), (333, False, 40), (64, True, 0),
          (1, True, 0), (129, False, 0), (161, True, 16)]
 
@@ -83,3 +114,34 @@ def test_du_blocks_cover_dq_reads(S, causal, window, keys_per_wave, nw, bmq):
         seen.add(key)
     missing = [r for r in reads(B, Hq, S, S, causal, window) if r not in seen]
     assert not missing, f"dq reads unwritten halves, e.g. {missing[:3]}"
+
+
+# Sq != Sk (no causal mask): with Sq > Sk and a window the last queries see no key, whole
+# 32-query waves of them when Sk + window falls far enough below Sq; their empty intervals sit
+# at Sk, inside a 32-key block when Sk is not a multiple of 32, and dk/dv writes no block for
+# them, so the kernels' read rule must treat an empty interval as no keys at all.
+CROSS = [(252, 56, 47), (184, 59, 42), (171, 89, 38), (96, 32, 40), (100, 181, 60), (160, 181, 60),
+         (129, 70, 0), (300, 33, 5)]
+
+
+@pytest.mark.parametrize("Sq,Sk,window", CROSS)
+@pytest.mark.parametrize("keys_per_wave,nw,bmq", [(32, 4, 32), (16, 8, 64), (16, 8, 32), (32, 1, 32), (32, 2, 32)])
+def test_du_blocks_cover_the_kernels_reads_across_lengths(Sq, Sk, window, keys_per_wave, nw, bmq):
+    B, Hq, Hkv = 1, 2, 1
+    nkb32, nqb32 = (Sk + 31) // 32, (Sq + 31) // 32
+    seen = set()
+    for b, hq, kb, qb, half in stores(B, Hq, Hkv, Sq, Sk, False, window, keys_per_wave, nw, bmq):
+        assert 0 <= kb < nkb32 and 0 <= qb < nqb32, (kb, qb)
+        key = (b, hq, kb, qb, half)
+        assert key not in seen, f"half stored twice: {key}"
+        seen.add(key)
+    ideal = set(reads(B, Hq, Sq, Sk, False, window))
+    got = set(kernel_reads(B, Hq, Sq, Sk, False, window))
+    assert ideal <= got, "the read rule skips a block holding a visible pair"
+    missing = sorted(r for r in got if r not in seen)
+    assert not missing, f"dq reads unwritten halves, e.g. {missing[:3]}"
+
+
+@pytest.mark.parametrize("S,causal,window", CASES)
+def test_kernel_read_rule_equals_the_ideal_one_at_equal_lengths(S, causal, window):
+    assert set(kernel_reads(1, 1, S, S, causal, window)) == set(reads(1, 1, S, S, causal, window))

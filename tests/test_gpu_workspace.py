@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import attention_tanh_logit_amd.ops as ops
-from harness import as_dense_mask, as_k_start, case, run_gpu
+from harness import TOL, as_dense_mask, as_k_start, case, compare, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -58,3 +58,31 @@ def test_results_do_not_depend_on_the_workspace_contents(name, monkeypatch):
             continue
         assert not np.isnan(x).any(), f"{name}: {n} has NaN on a fresh workspace"
         assert x.tobytes() == dirty[n].tobytes(), f"{name}: {n} depends on the workspace contents"
+
+
+# Sq > Sk + window - 1 without a causal mask: the last queries see no key, whole 32-query waves
+# of them, and Sk is not a multiple of 32, so their empty key intervals sit inside the last
+# 32-key block.  dk/dv writes no dU block for those waves; the dq kernels must read none.
+BLIND = {
+    "bf16_d128": dict(dtype="bf16", D=128, B=1, S=252, Sk=56, Hq=2, Hkv=1, causal=False, window=47),
+    "bf16_d512": dict(dtype="bf16", D=512, B=1, S=184, Sk=59, Hq=2, Hkv=1, causal=False, window=42),
+    "fp16_d64": dict(dtype="fp16", D=64, B=1, S=300, Sk=33, Hq=2, Hkv=1, causal=False, window=5),
+    "fp32_d128": dict(dtype="fp32", D=128, B=2, S=171, Sk=89, Hq=2, Hkv=1, causal=False, window=38,
+                      bias=True, bias_bcast="batch"),
+}
+
+
+@pytest.mark.parametrize("name", list(BLIND))
+def test_queries_that_see_no_key_get_zero_dq_from_the_du_blocks(name, monkeypatch):
+    c = case(**BLIND[name])
+    Sk, window = c["k"].shape[1], c["window"]
+    blind = np.arange(c["q"].shape[1]) >= Sk + window - 1
+    assert any(blind[32 * w:32 * w + 32].all() for w in range(len(blind) // 32)), "no whole blind wave"
+    print(f"blind query waves: {name}", flush=True)
+    monkeypatch.setattr(ops, "_workspace", _poisoned)
+    gpu = run_gpu(c, dq_mode="du_blocks")
+    assert (gpu["dq"][:, blind] == 0).all(), f"{name}: dq of queries that see no key is not zero"
+    assert (gpu["out"][:, blind] == 0).all()
+    errs = compare(gpu, run_oracle(c), c["dtype"], per_head=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL[c["dtype"]]}
+    assert not bad, f"over tolerance {TOL[c['dtype']]}: {bad}"
