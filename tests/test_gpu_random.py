@@ -24,6 +24,16 @@ The bars are those of the other parity tests (harness.TOL), per tensor and per
 (batch row, head) slice.  Segments are at least 4 tokens long and fp32 cases
 have S >= 17.  That keeps every row's dS away from the near-total cancellation
 of two-key rows, which the tiny-length test covers with its own derived bar.
+
+Two readings of the bars follow from the arithmetic, not from the kernels:
+- dsink = -sum_i p_sink,i delta_i is one sum per head whose terms can cancel to
+  a small fraction of their absolute sum.  Each term carries the rounding of
+  delta = <dO, O>, so the error of the sum is bounded relative to
+  sum_i p_sink,i sum_d |dO_id O_id|, and that is the scale its error is divided by.
+- fp16 sinks are drawn with a spread of 2 instead of 5.  A sink logit 15 above a
+  row's logits leaves the keys 1e-7 of the mass, and that head's whole output
+  then lies below fp16's normal range (2^-14).  There the format's own spacing
+  (2^-24) is more than the bar allows.
 """
 from __future__ import annotations
 
@@ -34,7 +44,7 @@ from harness import TOL, as_dense_mask, as_k_start, case, compare, run_gpu, run_
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 80
+N_CASES = 240
 
 
 def _segments(rng, S):
@@ -86,6 +96,8 @@ def draw(seed):
 def build(seed):
     kw, run, form = draw(seed)
     c = case(**kw)
+    if c["dtype"] == "fp16" and c["sink"] is not None:   # keep fp16 outputs in the normal range
+        c["sink"] = (c["sink"] * 0.4).astype(np.float32)
     if form == "k_start":
         c = as_k_start(c)
         if c["window"] == 0 and seed % 2:   # a k_start that also cuts a window into each segment
@@ -106,6 +118,14 @@ def describe(seed):
     return " ".join(f"{k}={kw[k]}" for k in keep) + f" form={form} " + " ".join(f"{k}={v}" for k, v in run.items())
 
 
+def dsink_scale(c, ref):
+    """Per query head: sum over batch rows and queries of p_sink * sum_d |dO O|, the absolute sum
+    of dsink's terms with delta's own terms taken absolutely (fp64, from the oracle)."""
+    absd = np.abs(ref["out"] * c["dout"].astype(np.float64)).sum(-1)      # [B, S, Hq]
+    p_sink = np.exp(c["sink"].astype(np.float64)[None, :, None] - ref["lse"])  # [B, Hq, S]
+    return (p_sink * absd.transpose(0, 2, 1)).sum(axis=(0, 2))
+
+
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_combination_matches_oracle(seed):
     print(f"seed {seed}: {describe(seed)}", flush=True)
@@ -113,6 +133,8 @@ def test_random_combination_matches_oracle(seed):
     gpu = run_gpu(c, thd=form == "thd", **run)
     ref = run_oracle(c)
     errs = compare(gpu, ref, c["dtype"], per_head=True)
+    if ref.get("dsink") is not None:
+        errs["dsink"] = float(np.abs(gpu["dsink"] - ref["dsink"]).max() / dsink_scale(c, ref).max())
     whole = {k: f"{v:.2e}" for k, v in errs.items() if "[" not in k}
     print("errors:", whole, flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL[c["dtype"]]}
