@@ -1125,6 +1125,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
       const int q0 = qbeg + (nqt - 1 - it / GS) * BMQ;
       const bf16* g0 = reinterpret_cast<const bf16*>(p.bias) + b * p.bias_bs + hq * p.bias_hs + k0;
       const auto rsrc = rows_rsrc(g0, Sk, q0, Sq);
+      const int past = (int)min((long)max(Sq - q0, 0) * Sk * 2, 0x7fffffffL);   // first byte past the range
       const int w64 = threadIdx.x >> 6;
 #pragma unroll
       for (int u = 0; u < (BMQ * BCPR + NT - 1) / NT; ++u) {
@@ -1132,7 +1133,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void dkdv16_kernel(BwdParams p) {
         if (pw < BMQ * BCPR) {
           const int pc = pw + lane;
           const int R = pc / BCPR, c = pc % BCPR;
-          dma16(rsrc, 2 * (R * Sk + 8 * (c ^ bsw(R))), nB + pw * 8);
+          const int kc = 8 * (c ^ bsw(R));   // the chunk's first key in the tile (Sk % 8 == 0)
+          // a chunk of keys past Sk reads as zeros (an offset past the buffer's
+          // range, as rows past Sq do): the range holds whole rows from key k0
+          // on, so those keys would otherwise read the next row, and past the
+          // last row the bytes after the bias, which need not be finite
+          dma16(rsrc, k0 + kc < Sk ? 2 * (R * Sk + kc) : past, nB + pw * 8);
         }
       }
     }
@@ -1562,15 +1568,9 @@ __global__ __launch_bounds__(256 * NSL, NSL > 1 ? 1 : (NST >= 3 ? 3 : 2)) void d
   int lo_first, hi_first, lo_last, hi_last;
   keys_of(p.mask, b, q0, lo_first, hi_first);
   keys_of(p.mask, b, ilast, lo_last, hi_last);
-  // keys seen by some query of this wave: one interval (each query's
-  // visible keys are an interval holding its own position, and the bounds
-  // never decrease along the queries)
-  int wlo = 0, whi = 0;
-  if (qw < Sq) {
-    int x0, x1;
-    keys_of(p.mask, b, qw, wlo, x0);
-    keys_of(p.mask, b, min(qw + 31, Sq - 1), x1, whi);
-  }
+  // this lane's query's visible keys [ilo, ihi) (empty past Sq)
+  int ilo = 0, ihi = 0;
+  if (i < Sq) keys_of(p.mask, b, i, ilo, ihi);
   const bf16* ublocks = reinterpret_cast<const bf16*>(p.du) +
                         (((long)b * p.Hq + hq) * p.nkb32 * p.nqb32 + (qw >> 5)) * 1024;
   const long ukstride = (long)p.nqb32 * 1024;   // elements between key blocks
@@ -1579,9 +1579,15 @@ __global__ __launch_bounds__(256 * NSL, NSL > 1 ? 1 : (NST >= 3 ? 3 : 2)) void d
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) qacc[ob] = f32x16{};
 
-  // (a wave whose queries see no key has wlo == whi: an empty interval, which
-  // dk/dv wrote no block for, even where a 32-key block holds that point)
-  auto visible = [&](int kb32) { return wlo < whi && kb32 < whi && kb32 + 32 > wlo && kb32 < Sk; };
+  // a 32-key block is read when some query of the wave sees one of its keys
+  // (a wave vote, so the same on every lane).  dk/dv wrote every such block:
+  // the queries that see a key are an interval whose bounds never decrease
+  // with the key, so the query tiles dk/dv covers for a key block hold them.
+  // A query that sees no key contributes nothing, wherever keys_of puts its
+  // empty interval (with k_start it can lie beyond the query's own position).
+  auto visible = [&](int kb32) {
+    return kb32 < Sk && __any(ilo < ihi && ilo < kb32 + 32 && ihi > kb32);
+  };
   // the tile's K rows (all waves) and this wave's dU^T blocks; every thread
   // issues the same number of loads per tile (a block no query of the wave
   // sees is read through an empty range, which fills zeros and touches no

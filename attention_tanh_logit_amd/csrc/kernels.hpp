@@ -590,28 +590,24 @@ __global__ __launch_bounds__(64 * NQG * (D / DO)) void dq_kernel(BwdParams p) {
     }
   };
 
-  // DU: keys seen by some query of this wave's 32-row group form one interval
-  // (each query's visible keys are an interval holding its own position, and
-  // the bounds never decrease along the queries); a 32-key block outside it
-  // holds no visible pair of the group and was not necessarily written, so
-  // it counts as zero (as does every block when the interval is empty: a
-  // group whose queries see no key).  Otherwise lane (query n, half h) takes keys
-  // 16 sb + 8 h .. + 7 of the block's row n: the contraction order of the
-  // fp32 MFMA fragments (element s at key 16 sb + 8 h + s).
+  // DU: a 32-key block is read when some query of this wave's 32-row group
+  // sees one of its keys (a wave vote over the lanes' own queries); dk/dv
+  // wrote every such block.  Any other block holds no visible pair of the
+  // group and was not necessarily written, so it counts as zero; a query that
+  // sees no key contributes nothing, wherever keys_of puts its empty interval.
+  // Lane (query n, half h) takes keys 16 sb + 8 h .. + 7 of the block's row n:
+  // the contraction order of the fp32 MFMA fragments (element s at key
+  // 16 sb + 8 h + s).
   const int qw = q0 + qg * 32;
-  int wlo = 0, whi = 0;
+  int ilo = 0, ihi = 0;
   if constexpr (DU) {
-    if (qw < Sq) {
-      int x0, x1;
-      keys_of(p.mask, b, qw, wlo, x0);
-      keys_of(p.mask, b, min(qw + 31, Sq - 1), x1, whi);
-    }
+    if (qw + n < Sq) keys_of(p.mask, b, qw + n, ilo, ihi);
   }
   auto load_du = [&](int k0, F (*uf)[2]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int kb32 = k0 + kb * 32;
-      if (qw < Sq && wlo < whi && kb32 < whi && kb32 + 32 > wlo && kb32 < Sk) {
+      if (kb32 < Sk && __any(ilo < ihi && ilo < kb32 + 32 && ihi > kb32)) {
         const float* blk = reinterpret_cast<const float*>(p.du) +
                            ((((long)b * p.Hq + hq) * p.nkb32 + (kb32 >> 5)) * p.nqb32 + (qw >> 5)) * 1024 + n * 32 +
                            8 * h;

@@ -101,9 +101,11 @@ def as_dense_mask(c):
     return dict(c, segment_ids=None, mask=seg[:, :, None] == seg[:, None, :])
 
 
-def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True, layout="bshd"):
+def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True, layout="bshd", nan_after_bias=False):
     """The case through the C ABI; results as numpy in BSHD order.  layout="sbhd"
-    hands the library [S, B, H, D] tensors (and transposes the results back)."""
+    hands the library [S, B, H, D] tensors (and transposes the results back).
+    nan_after_bias: the bias sits at the start of a larger buffer whose tail is NaN,
+    so that a read past the bias's last element shows."""
     import attention_tanh_logit_amd as A
     dt = c["dtype"]
     sb = layout == "sbhd"
@@ -118,6 +120,11 @@ def run_gpu(c, backward=True, thd=False, dq_mode="auto", residual=True, layout="
         kw["sink"] = torch.from_numpy(c["sink"]).cuda()
     if c["bias"] is not None:
         kw["bias"] = to_dev(c["bias"], dt)
+        if nan_after_bias:
+            n = kw["bias"].numel()
+            buf = torch.full((n + 8192,), float("nan"), dtype=kw["bias"].dtype, device=kw["bias"].device)
+            buf[:n] = kw["bias"].reshape(-1)
+            kw["bias"] = buf[:n].view(kw["bias"].shape)
     if thd:
         assert c["segment_ids"] is not None and c["segment_ids"].shape[0] == 1 or c.get("k_start") is None
         cu = W.cu_seqlens_from_segments(c["segment_ids"])

@@ -12,21 +12,25 @@ masks and checks that every store lands inside the workspace region, no half
 is stored twice, and every half the dq kernel reads has been stored.  No GPU
 needed.
 """
+import numpy as np
 import pytest
 
 
-def visible_queries(j, Sq, causal, window):
-    """Queries that see key j: an interval [lo, hi) (Sq == Sk when causal)."""
+def visible_queries(j, Sq, causal, window, ks=None):
+    """Queries that see key j: an interval [lo, hi) (Sq == Sk when causal).  ks: a non-decreasing
+    k_start (query i sees keys j >= ks[i]), whose queries for key j end at the first ks above j."""
     lo, hi = (j, Sq) if causal else (0, Sq)
     if window > 0:
         if causal:
             hi = min(hi, j + window)
         else:
             lo, hi = max(lo, j - window + 1), min(hi, j + window)
-    return lo, hi
+    if ks is not None:
+        hi = min(hi, int(np.searchsorted(ks, j, side="right")))
+    return lo, max(hi, lo)
 
 
-def stores(B, Hq, Hkv, Sq, Sk, causal, window, keys_per_wave, nw, bmq):
+def stores(B, Hq, Hkv, Sq, Sk, causal, window, keys_per_wave, nw, bmq, ks=None):
     """Yield (b, hq, key block, query block, half) for every dU store."""
     G = Hq // Hkv
     bnk = keys_per_wave * nw
@@ -34,8 +38,8 @@ def stores(B, Hq, Hkv, Sq, Sk, causal, window, keys_per_wave, nw, bmq):
         for hk in range(Hkv):
             for kb in range((Sk + bnk - 1) // bnk):
                 k0 = kb * bnk
-                lo_first, _ = visible_queries(k0, Sq, causal, window)
-                _, hi_last = visible_queries(min(k0 + bnk, Sk) - 1, Sq, causal, window)
+                lo_first, _ = visible_queries(k0, Sq, causal, window, ks)
+                _, hi_last = visible_queries(min(k0 + bnk, Sk) - 1, Sq, causal, window, ks)
                 qbeg = (lo_first // bmq) * bmq
                 nqt = (hi_last - qbeg + bmq - 1) // bmq if hi_last > qbeg else 0
                 for it in range(G * nqt):
@@ -66,10 +70,12 @@ def reads(B, Hq, Sq, Sk, causal, window):
                         yield b, hq, kb, qb, 1
 
 
-def keys_of(i, Sk, causal, window):
-    """The kernels' key interval [lo, hi) of query i (causal / window masks): a query that sees
-    no key gets an empty interval at lo == hi, clamped into [0, Sk]."""
+def keys_of(i, Sk, causal, window, ks=None):
+    """The kernels' key interval [lo, hi) of query i: a query that sees no key gets an empty
+    interval at lo == hi, clamped into [0, Sk] (with k_start it can lie beyond i itself)."""
     lo, hi = 0, Sk
+    if ks is not None:
+        lo = int(ks[i])
     if causal:
         hi = min(hi, i + 1)
     if window > 0:
@@ -80,19 +86,16 @@ def keys_of(i, Sk, causal, window):
     return lo, max(hi, lo)
 
 
-def kernel_reads(B, Hq, Sq, Sk, causal, window):
-    """The dq kernels' own read rule: a wave of 32 queries reads the block of keys kb32 .. + 31
-    when its keys, from the first query's lo to the last query's hi, are a non-empty interval
-    that meets the block (and the block starts below Sk)."""
+def kernel_reads(B, Hq, Sq, Sk, causal, window, ks=None):
+    """The dq kernels' read rule: a wave of 32 queries reads the block of keys kb32 .. + 31 when
+    one of its queries has a non-empty key interval that meets the block (a wave vote)."""
     for b in range(B):
         for hq in range(Hq):
             for qb in range((Sq + 31) // 32):
-                qw = 32 * qb
-                wlo = keys_of(qw, Sk, causal, window)[0]
-                whi = keys_of(min(qw + 31, Sq - 1), Sk, causal, window)[1]
+                iv = [keys_of(q, Sk, causal, window, ks) for q in range(32 * qb, min(32 * qb + 32, Sq))]
                 for kb in range((Sk + 31) // 32):
                     kb32 = 32 * kb
-                    if wlo < whi and kb32 < whi and kb32 + 32 > wlo and kb32 < Sk:
+                    if kb32 < Sk and any(lo < hi and lo < kb32 + 32 and hi > kb32 for lo, hi in iv):
                         yield b, hq, kb, qb, 0
                         yield b, hq, kb, qb, 1
 
@@ -145,3 +148,17 @@ def test_du_blocks_cover_the_kernels_reads_across_lengths(Sq, Sk, window, keys_p
 @pytest.mark.parametrize("S,causal,window", CASES)
 def test_kernel_read_rule_equals_the_ideal_one_at_equal_lengths(S, causal, window):
     assert set(kernel_reads(1, 1, S, S, causal, window)) == set(reads(1, 1, S, S, causal, window))
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("keys_per_wave,nw,bmq", [(32, 4, 32), (16, 8, 64), (16, 8, 32), (32, 1, 32)])
+def test_du_blocks_cover_the_kernels_reads_with_k_start(seed, keys_per_wave, nw, bmq):
+    """Causal with a random non-decreasing k_start: queries with k_start above their own position
+    see no key, and their empty intervals sit at k_start, beyond them."""
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(40, 300))
+    ks = np.sort(rng.integers(0, S + 1, size=S))
+    seen = set(stores(1, 2, 1, S, S, True, 0, keys_per_wave, nw, bmq, ks))
+    got = set(kernel_reads(1, 2, S, S, True, 0, ks))
+    missing = sorted(r for r in got if r not in seen)
+    assert not missing, f"dq reads unwritten halves, e.g. {missing[:3]}"

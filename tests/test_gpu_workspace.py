@@ -86,3 +86,27 @@ def test_queries_that_see_no_key_get_zero_dq_from_the_du_blocks(name, monkeypatc
     errs = compare(gpu, run_oracle(c), c["dtype"], per_head=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL[c["dtype"]]}
     assert not bad, f"over tolerance {TOL[c['dtype']]}: {bad}"
+
+
+# The 16-bit dk/dv kernels stage the bias tile of an item in LDS.  In the last key block some
+# keys lie past Sk; their chunks must read as zeros, not as the next row's keys and, after the
+# last row, not as whatever follows the bias in memory (here NaN): the dU blocks carry those
+# keys' values to the dq kernel, which multiplies them by zero K rows.
+BIAS_TAIL = {
+    "d128": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True, softcap=50.0),
+    "d256": dict(dtype="bf16", D=256, B=2, S=200, Hq=4, Hkv=1, bias=True, softcap=30.0),
+    "d128_fp16_noncausal": dict(dtype="fp16", D=128, B=1, S=136, Hq=2, Hkv=1, bias=True, causal=False),
+}
+
+
+@pytest.mark.parametrize("name", list(BIAS_TAIL))
+def test_bias_tiles_read_nothing_past_the_last_key(name):
+    c = case(**BIAS_TAIL[name])
+    print(f"NaN after the bias: {name}", flush=True)
+    clean = run_gpu(c, dq_mode="du_blocks")
+    tail = run_gpu(c, dq_mode="du_blocks", nan_after_bias=True)
+    for n, x in clean.items():
+        if x is None:
+            continue
+        assert not np.isnan(tail[n]).any(), f"{name}: {n} picked up the NaN after the bias"
+        assert x.tobytes() == tail[n].tobytes(), f"{name}: {n} depends on the memory after the bias"
