@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import attention_tanh_logit_amd.ops as ops
+import harness
 from harness import TOL, as_dense_mask, as_k_start, case, compare, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
@@ -110,3 +111,36 @@ def test_bias_tiles_read_nothing_past_the_last_key(name):
             continue
         assert not np.isnan(tail[n]).any(), f"{name}: {n} picked up the NaN after the bias"
         assert x.tobytes() == tail[n].tobytes(), f"{name}: {n} depends on the memory after the bias"
+
+
+# Every uploaded input (q, k, v, dO, bias) at the start of a buffer whose tail is NaN: no kernel
+# may read past an input's last element.
+TAILS = {
+    "bf16_d128_segments_bias": dict(dtype="bf16", D=128, B=2, S=200, Hq=4, Hkv=2, bias=True,
+                                    segments=[[45, 70, 190], [128]], sink_mode="learnable"),
+    "bf16_d512_bias_dropout": dict(dtype="bf16", D=512, B=1, S=200, Hq=2, Hkv=1, bias=True, dropout_p=0.1),
+    "fp32_d256_window": dict(dtype="fp32", D=256, B=2, S=131, Hq=4, Hkv=2, window=40, bias=True,
+                             bias_bcast="heads"),
+    "fp16_d64_cross": dict(dtype="fp16", D=64, B=2, S=150, Sk=97, Hq=4, Hkv=1, causal=False, window=30),
+}
+
+
+@pytest.mark.parametrize("name", list(TAILS))
+def test_no_kernel_reads_past_an_input(name, monkeypatch):
+    c = case(**TAILS[name])
+    print(f"NaN after every input: {name}", flush=True)
+    clean = run_gpu(c, dq_mode="du_blocks")
+    orig = harness.to_dev
+
+    def to_dev_tail(x, dtype, device="cuda"):
+        t = orig(x, dtype, device)
+        buf = torch.full((t.numel() + 8192,), float("nan"), dtype=t.dtype, device=t.device)
+        buf[:t.numel()] = t.reshape(-1)
+        return buf[:t.numel()].view(t.shape)
+
+    monkeypatch.setattr(harness, "to_dev", to_dev_tail)
+    tail = run_gpu(c, dq_mode="du_blocks")
+    for n, x in clean.items():
+        if x is None:
+            continue
+        assert x.tobytes() == tail[n].tobytes(), f"{name}: {n} depends on the memory after the inputs"
