@@ -79,7 +79,10 @@ typedef enum attn_status {
  * page, "Not covered"; here it takes the same kernels as bf16, built a
  * second time for fp16 elements, except that the forward keeps a running
  * maximum: probabilities relative to a fixed reference at the cap could
- * leave fp16's exponent range.) */
+ * leave fp16's exponent range.  A sink that takes all but a tiny share of a
+ * row's mass still leaves that row's output, and the probabilities behind
+ * it, small: values below fp16's normal range (2^-14) carry an absolute
+ * spacing of 2^-24 rather than 11 bits of relative precision.) */
 typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1, ATTN_FP16 = 2 } attn_dtype;
 
 /* Softmax sink ("softmax_type" on the learnable-sink page, "What changed"):
